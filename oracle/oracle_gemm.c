@@ -1,0 +1,235 @@
+/*
+ * oracle_gemm.c -- reference implementation of the dense matrix product
+ * C = A x B, used ONLY as test infrastructure.
+ *
+ * Who may use it: the test-suite (tests/), the smoke check in
+ * __graft_entry__.smoke() and the "cpu_baseline" leg of bench.py.  The GPU
+ * library never includes, links or calls this file, and this file includes
+ * nothing from the GPU library: the two share no code, header, table or
+ * constant.
+ *
+ * What it computes (the plain definition, written out):
+ *   C[i][j] = sum_{k=0}^{K-1} a(i,k) * b(k,j)
+ * where A is M x K, B is K x N and C is M x N, all row-major.  This is the
+ * product that the tiled kernel of page "企业官网建设流程全解析" (a TileLang
+ * article despite its title), §3.3, is written to compute, with A of size
+ * M x K, B of size K x N and C of size M x N, and the triple loop of page
+ * "TileLang实战：用Python DSL自动生成高性能GPU计算内核", §3.1.  The
+ * page about the DeepSeek/Ascend TileLang toolkit, §3.3 (first step of its
+ * verification procedure), asks for exactly this: a naive CPU implementation
+ * that only aims at being right, used as ground truth.
+ *
+ * Precision: a(i,k) and b(k,j) are the EXACT values of the stored binary16,
+ * bfloat16 or binary32 inputs, widened to binary64 by the decoders below,
+ * which are written from the bit-level definitions of those formats (IEEE
+ * 754-2008 binary16/binary32; bfloat16 = the upper 16 bits of a binary32).
+ * Every product of two such values is exact in binary64 (at most 22 or 48
+ * significant bits), so the only rounding is that of the binary64 running
+ * sum, taken in increasing k.  The result is returned in binary64.
+ *
+ * Steps, in order:
+ *   1. decode the requested rows of A and columns of B to binary64;
+ *   2. for every requested (i, j): s = 0; for k = 0 .. K-1: s += a*b;
+ *   3. store s.
+ * K == 0 gives s = 0 (the empty sum).  Rows and columns may be a subset
+ * (the "sampled" mode used at large sizes); the value of an entry does not
+ * depend on which other entries are requested.
+ *
+ * Threads: output rows are dealt round-robin to plain POSIX threads; each
+ * entry is still summed by one thread in increasing k, so the result does not
+ * depend on the thread count.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fPIC -shared -pthread (see build.py).
+ * -ffp-contract=off keeps "s += a*b" a separate multiply and add; since the
+ * product is exact it makes no numerical difference, but it keeps the code
+ * literally what it says.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* Element type codes understood by this file (its own numbering). */
+#define ORACLE_BINARY32 0
+#define ORACLE_BINARY16 1
+#define ORACLE_BFLOAT16 2
+
+/* binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.
+ *   e == 0      : (-1)^s * f * 2^-24            (zero and subnormals)
+ *   e == 31     : infinity (f == 0) or NaN
+ *   otherwise   : (-1)^s * (1024 + f) * 2^(e-25) */
+double oracle_decode_binary16(uint16_t h) {
+    int s = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int f = h & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + f), e - 25);
+    return s ? -v : v;
+}
+
+/* bfloat16: 1 sign bit, 8 exponent bits (bias 127), 7 fraction bits.
+ *   e == 0      : (-1)^s * f * 2^-133           (zero and subnormals)
+ *   e == 255    : infinity (f == 0) or NaN
+ *   otherwise   : (-1)^s * (128 + f) * 2^(e-134) */
+double oracle_decode_bfloat16(uint16_t h) {
+    int s = (h >> 15) & 1;
+    int e = (h >> 7) & 0xff;
+    int f = h & 0x7f;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -133);
+    else if (e == 255)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(128 + f), e - 134);
+    return s ? -v : v;
+}
+
+/* binary32: 1 sign bit, 8 exponent bits (bias 127), 23 fraction bits.
+ *   e == 0      : (-1)^s * f * 2^-149
+ *   e == 255    : infinity or NaN
+ *   otherwise   : (-1)^s * (2^23 + f) * 2^(e-150) */
+double oracle_decode_binary32(uint32_t w) {
+    int s = (int)((w >> 31) & 1u);
+    int e = (int)((w >> 23) & 0xffu);
+    uint32_t f = w & 0x7fffffu;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -149);
+    else if (e == 255)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(8388608u + f), e - 150);
+    return s ? -v : v;
+}
+
+static double decode_one(const void* base, int64_t idx, int dtype) {
+    if (dtype == ORACLE_BINARY32) {
+        uint32_t w;
+        memcpy(&w, (const char*)base + idx * 4, 4);
+        return oracle_decode_binary32(w);
+    }
+    uint16_t h;
+    memcpy(&h, (const char*)base + idx * 2, 2);
+    return dtype == ORACLE_BINARY16 ? oracle_decode_binary16(h) : oracle_decode_bfloat16(h);
+}
+
+/* Decode n consecutive stored elements of type dtype into binary64. */
+int oracle_decode_array(const void* src, int dtype, int64_t n, double* dst) {
+    if (dtype < ORACLE_BINARY32 || dtype > ORACLE_BFLOAT16 || n < 0) return -1;
+    for (int64_t i = 0; i < n; ++i) dst[i] = decode_one(src, i, dtype);
+    return 0;
+}
+
+struct job {
+    int64_t nrows, ncols, K;
+    const double* Ad;   /* nrows x K, decoded rows of A            */
+    const double* Bd;   /* K x ncols, decoded columns of B         */
+    double* C;          /* nrows x ncols, leading dimension ldc    */
+    int64_t ldc;
+    int tid, nthreads;
+};
+
+/* Step 2 for the rows r = tid, tid + nthreads, ...: for each row, every
+ * requested entry is the sum over k, in increasing k, of a(i,k)*b(k,j).  The
+ * k loop is outermost inside a row so that B is walked row by row; each
+ * entry still receives its K terms in increasing k. */
+static void* run_rows(void* p) {
+    struct job* jb = (struct job*)p;
+    for (int64_t r = jb->tid; r < jb->nrows; r += jb->nthreads) {
+        double* s = jb->C + r * jb->ldc;
+        for (int64_t c = 0; c < jb->ncols; ++c) s[c] = 0.0;
+        const double* arow = jb->Ad + r * jb->K;
+        for (int64_t k = 0; k < jb->K; ++k) {
+            const double a = arow[k];
+            const double* brow = jb->Bd + k * jb->ncols;
+            for (int64_t c = 0; c < jb->ncols; ++c) s[c] += a * brow[c];
+        }
+    }
+    return NULL;
+}
+
+/*
+ * oracle_gemm: C_out[r][c] = sum_k a(rows[r], k) * b(k, cols[c]) in binary64.
+ *
+ *   M, N, K      sizes of the product (A: M x K, B: K x N), all >= 0
+ *   A, lda       row-major A, leading dimension lda >= K (in elements)
+ *   B, ldb       row-major B, leading dimension ldb >= N (in elements)
+ *   dtype        element type of A and B (0 binary32, 1 binary16, 2 bfloat16)
+ *   rows, nrows  requested row indices of C (NULL: all M rows, nrows ignored)
+ *   cols, ncols  requested column indices of C (NULL: all N columns)
+ *   C_out, ldc   binary64 output, nrows x ncols, leading dimension ldc >= ncols
+ *   nthreads     worker threads (<= 0 means 1)
+ *
+ * Returns 0, -1 for invalid arguments (nothing written), or -2 when the
+ * host is out of memory (nothing written).
+ */
+int oracle_gemm(int64_t M, int64_t N, int64_t K,
+                const void* A, int64_t lda, const void* B, int64_t ldb, int dtype,
+                const int64_t* rows, int64_t nrows, const int64_t* cols, int64_t ncols,
+                double* C_out, int64_t ldc, int nthreads) {
+    if (M < 0 || N < 0 || K < 0) return -1;
+    if (dtype < ORACLE_BINARY32 || dtype > ORACLE_BFLOAT16) return -1;
+    if (lda < K || ldb < N) return -1;
+    if (rows == NULL) nrows = M;
+    if (cols == NULL) ncols = N;
+    if (nrows < 0 || ncols < 0 || ldc < ncols) return -1;
+    for (int64_t r = 0; rows && r < nrows; ++r)
+        if (rows[r] < 0 || rows[r] >= M) return -1;
+    for (int64_t c = 0; cols && c < ncols; ++c)
+        if (cols[c] < 0 || cols[c] >= N) return -1;
+    if (nrows == 0 || ncols == 0) return 0;
+    if (nthreads <= 0) nthreads = 1;
+    if (nthreads > nrows) nthreads = (int)nrows;
+
+    /* Step 1: decode. */
+    double* Ad = (double*)malloc(sizeof(double) * (size_t)(nrows * (K ? K : 1)));
+    double* Bd = (double*)malloc(sizeof(double) * (size_t)((K ? K : 1) * ncols));
+    if (!Ad || !Bd) {
+        free(Ad);
+        free(Bd);
+        return -2;
+    }
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t i = rows ? rows[r] : r;
+        for (int64_t k = 0; k < K; ++k) Ad[r * K + k] = decode_one(A, i * lda + k, dtype);
+    }
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t c = 0; c < ncols; ++c) {
+            const int64_t j = cols ? cols[c] : c;
+            Bd[k * ncols + c] = decode_one(B, k * ldb + j, dtype);
+        }
+
+    /* Steps 2 and 3. */
+    struct job* jobs = (struct job*)calloc((size_t)nthreads, sizeof(struct job));
+    pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+    char* started = (char*)calloc((size_t)nthreads, 1);
+    int rc = 0;
+    if (!jobs || !th || !started) {
+        rc = -2;
+    } else {
+        for (int t = 0; t < nthreads; ++t)
+            jobs[t] = (struct job){nrows, ncols, K, Ad, Bd, C_out, ldc, t, nthreads};
+        for (int t = 1; t < nthreads; ++t)
+            started[t] = pthread_create(&th[t], NULL, run_rows, &jobs[t]) == 0;
+        run_rows(&jobs[0]);
+        for (int t = 1; t < nthreads; ++t) {
+            if (started[t])
+                pthread_join(th[t], NULL);
+            else
+                run_rows(&jobs[t]); /* no thread could be started: do it here */
+        }
+    }
+    free(started);
+    free(jobs);
+    free(th);
+    free(Ad);
+    free(Bd);
+    return rc;
+}

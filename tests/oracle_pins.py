@@ -1,0 +1,262 @@
+"""Pins of the oracle: checks of oracle/ against facts that do not come from
+the oracle itself (the bit-level definitions as numpy implements them, exact
+rational arithmetic, closed forms, an independent BLAS product and the pages'
+own worked example).
+
+Every pin is a plain function `pin_xxx(lib_path)` that raises AssertionError
+on failure, so that the same pins can be run against the real oracle
+(tests/test_oracle.py) and against copies of it with a planted mistake
+(tests/test_oracle_mutants.py), where at least one pin must fail.
+"""
+import ctypes
+import os
+from fractions import Fraction
+
+import numpy as np
+
+import oracle
+from tiled_gemm_03_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+U = 2.0 ** -53
+
+
+# ---------------------------------------------------------------- helpers
+def np_values(x: np.ndarray, dtype: int) -> np.ndarray:
+    """binary64 values of stored elements, computed by numpy (independent of
+    the oracle's decoders)."""
+    if dtype == W.BF16:
+        with np.errstate(invalid="ignore"):
+            return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return x.astype(np.float64)
+
+
+def summation_bound(av: np.ndarray, bv: np.ndarray) -> np.ndarray:
+    """Elementwise bound on |s_oracle - s_other| for two binary64 sums of the
+    same exact products in different orders: each is within (K-1)*u*sum|terms|
+    of the exact value (standard recursive-summation bound)."""
+    K = av.shape[1]
+    return 2.0 * max(K - 1, 0) * U * (np.abs(av) @ np.abs(bv)) * (1 + 1e-6) + 0.0
+
+
+def _exact(av, bv):
+    """Exact product in rationals (brute force)."""
+    M, K = av.shape
+    N = bv.shape[1]
+    out = [[Fraction(0)] * N for _ in range(M)]
+    for i in range(M):
+        for j in range(N):
+            s = Fraction(0)
+            for k in range(K):
+                s += Fraction(float(av[i, k])) * Fraction(float(bv[k, j]))
+            out[i][j] = s
+    return out
+
+
+# ------------------------------------------------------------ decoder pins
+def pin_decode_binary16_exhaustive(lib_path=None):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = oracle.decode(bits, W.F16, lib_path=lib_path)
+    want = bits.view(np.float16).astype(np.float64)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan), "binary16 NaN set differs"
+    assert np.array_equal(got[~nan], want[~nan]), "binary16 decode differs"
+    # signed zeros keep their sign
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
+
+
+def pin_decode_bfloat16_exhaustive(lib_path=None):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = oracle.decode(bits, W.BF16, lib_path=lib_path)
+    want = np_values(bits, W.BF16)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan), "bfloat16 NaN set differs"
+    assert np.array_equal(got[~nan], want[~nan]), "bfloat16 decode differs"
+
+
+def pin_decode_binary32_sampled(lib_path=None):
+    rng = np.random.default_rng(123)
+    bits = rng.integers(0, 2 ** 32, size=1 << 20, dtype=np.uint64).astype(np.uint32)
+    specials = np.array([0, 0x80000000, 1, 0x807FFFFF, 0x00800000, 0x7F7FFFFF,
+                         0x7F800000, 0xFF800000, 0x3F800000, 0xBF800000], dtype=np.uint32)
+    bits = np.concatenate([bits, specials])
+    got = oracle.decode(bits, W.F32, lib_path=lib_path)
+    with np.errstate(invalid="ignore"):
+        want = bits.view(np.float32).astype(np.float64)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan]), "binary32 decode differs"
+
+
+# --------------------------------------------------------- product pins
+def pin_identity(lib_path=None):
+    """I x B == B and A x I == A exactly (closed form), every input type,
+    non-square so that a transposed operand cannot hide."""
+    for dt in (W.F32, W.F16, W.BF16):
+        a, b = W.random_inputs(37, 53, 37, dt, seed=11)
+        eye = W.to_storage(np.eye(37, dtype=np.float32), dt)
+        got = oracle.gemm(eye, b, dt, lib_path=lib_path)
+        assert np.array_equal(got, np_values(b, dt)), f"I x B != B for dtype {dt}"
+        eye2 = W.to_storage(np.eye(53, dtype=np.float32), dt)
+        a2, _ = W.random_inputs(29, 53, 53, dt, seed=12)
+        got = oracle.gemm(a2, eye2, dt, lib_path=lib_path)
+        assert np.array_equal(got, np_values(a2, dt)), f"A x I != A for dtype {dt}"
+
+
+def pin_all_ones(lib_path=None):
+    """Every entry of ones(M,K) x ones(K,N) is K (closed form), including the
+    empty sum K = 0."""
+    for dt in (W.F32, W.F16, W.BF16):
+        for (M, N, K) in ((3, 5, 0), (7, 9, 1), (17, 33, 257), (4, 4, 2051)):
+            a = W.to_storage(np.ones((M, K), np.float32), dt)
+            b = W.to_storage(np.ones((K, N), np.float32), dt)
+            got = oracle.gemm(a, b, dt, lib_path=lib_path)
+            assert got.shape == (M, N)
+            assert np.all(got == K), f"ones product != K at {(M, N, K)}"
+
+
+def pin_golden_ones_8x8(lib_path=None):
+    with open(os.path.join(GOLDEN, "ones_8x8.txt"), encoding="utf-8") as f:
+        rows = [ln.split() for ln in f if ln.strip() and not ln.startswith("#")]
+    M, N, K = map(int, rows[0])
+    want = np.array(rows[1:], dtype=np.float64)
+    for dt in (W.F32, W.F16):
+        a = W.to_storage(np.ones((M, K), np.float32), dt)
+        b = W.to_storage(np.ones((K, N), np.float32), dt)
+        assert np.array_equal(oracle.gemm(a, b, dt, lib_path=lib_path), want)
+
+
+def pin_bruteforce_rational(lib_path=None):
+    """Small products against exact rational arithmetic (4x4x4 and a
+    non-square 3x5x7), within the binary64 summation bound."""
+    for dt in (W.F32, W.F16, W.BF16):
+        for (M, N, K, seed) in ((4, 4, 4, 21), (3, 5, 7, 22)):
+            a, b = W.random_inputs(M, N, K, dt, seed=seed)
+            av, bv = np_values(a, dt), np_values(b, dt)
+            ex = _exact(av, bv)
+            got = oracle.gemm(a, b, dt, lib_path=lib_path)
+            for i in range(M):
+                for j in range(N):
+                    terms = sum(abs(Fraction(float(av[i, k])) * Fraction(float(bv[k, j])))
+                                for k in range(K))
+                    err = abs(Fraction(float(got[i, j])) - ex[i][j])
+                    assert err <= (K - 1) * Fraction(U) * terms, \
+                        f"entry ({i},{j}) off the exact value for dtype {dt}"
+
+
+def _check_vs_numpy(a, b, dt, lib_path, rows=None, cols=None, nthreads=8):
+    av, bv = np_values(a, dt), np_values(b, dt)
+    if rows is not None:
+        av = av[rows]
+    if cols is not None:
+        bv = bv[:, cols]
+    want = av @ bv
+    got = oracle.gemm(a, b, dt, rows=rows, cols=cols, nthreads=nthreads, lib_path=lib_path)
+    bound = summation_bound(av, bv)
+    bad = np.abs(got - want) > bound
+    assert not bad.any(), f"{bad.sum()} entries differ from numpy's binary64 product"
+
+
+def pin_vs_numpy_unaligned(lib_path=None):
+    """127 x 255 x 512 (the non-aligned edge case) against numpy's binary64
+    matrix product, an independent BLAS routine."""
+    for dt in (W.F16, W.F32, W.BF16):
+        a, b = W.random_inputs(127, 255, 512, dt, seed=3, dist="uniform")
+        _check_vs_numpy(a, b, dt, lib_path)
+
+
+def pin_vs_numpy_workloads(lib_path=None):
+    """The four smaller workloads in full against numpy's binary64 product."""
+    for w in W.WORKLOADS[:4]:
+        a, b = W.make_inputs(w)
+        _check_vs_numpy(a, b, w.in_dtype, lib_path)
+
+
+def pin_sampled_equals_full(lib_path=None):
+    """Sampled entries are bitwise the full result's entries."""
+    a, b = W.random_inputs(127, 255, 64, W.F16, seed=31)
+    full = oracle.gemm(a, b, W.F16, lib_path=lib_path)
+    rows = np.array([0, 5, 126, 64, 3])
+    cols = np.array([254, 0, 7, 100])
+    got = oracle.gemm(a, b, W.F16, rows=rows, cols=cols, lib_path=lib_path)
+    assert np.array_equal(got, full[rows][:, cols])
+
+
+def pin_padded_leading_dimension(lib_path=None):
+    """Operands whose rows are padded (ld > width) with NaN give the same
+    result as tight ones: the padding is never read."""
+    a, b = W.random_inputs(45, 70, 33, W.F16, seed=41)
+    tight = oracle.gemm(a, b, W.F16, lib_path=lib_path)
+    big_a = np.full((45, 40), np.nan, np.float16)
+    big_a[:, :33] = a
+    big_b = np.full((33, 77), np.nan, np.float16)
+    big_b[:, :70] = b
+    got = oracle.gemm(big_a[:, :33], big_b[:, :70], W.F16, lib_path=lib_path)
+    assert np.array_equal(got, tight)
+
+
+def pin_threads_invariant(lib_path=None):
+    a, b = W.random_inputs(50, 60, 300, W.F16, seed=51)
+    one = oracle.gemm(a, b, W.F16, nthreads=1, lib_path=lib_path)
+    many = oracle.gemm(a, b, W.F16, nthreads=7, lib_path=lib_path)
+    assert np.array_equal(one, many)
+
+
+def pin_output_overwritten(lib_path=None):
+    """An output buffer pre-filled with NaN is fully overwritten, with the
+    correct values (small integer inputs make every sum exact)."""
+    lib = oracle._load(lib_path)
+    a, b = W.integer_inputs(9, 11, 13, W.F16, seed=61)
+    want = np_values(a, W.F16) @ np_values(b, W.F16)
+    out = np.full((9, 11), np.nan)
+    rc = lib.oracle_gemm(9, 11, 13, a.ctypes.data, 13, b.ctypes.data, 11, W.F16,
+                         None, 0, None, 0, out.ctypes.data, 11, 2)
+    assert rc == 0
+    assert np.array_equal(out, want)
+
+
+def pin_large_sampled(lib_path=None):
+    """The 8192^3 workload: 64 seeded rows x 64 seeded columns against numpy
+    on the same slices."""
+    w = W.WORKLOADS[4]
+    a, b = W.make_inputs(w)
+    rows = W.sample_indices(w.M, 64, w.seed + 100)
+    cols = W.sample_indices(w.N, 64, w.seed + 200)
+    _check_vs_numpy(a, b, w.in_dtype, lib_path, rows=rows, cols=cols)
+
+
+def pin_rejects_bad_arguments(lib_path=None):
+    lib = oracle._load(lib_path)
+    out = np.zeros(4)
+    a = np.zeros(4, np.float16)
+    for args in ((-1, 2, 2, 2, 2), (2, 2, 2, 1, 2), (2, 2, 2, 2, 1)):
+        M, N, K, lda, ldb = args
+        rc = lib.oracle_gemm(M, N, K, a.ctypes.data, lda, a.ctypes.data, ldb, W.F16,
+                             None, 0, None, 0, out.ctypes.data, 2, 1)
+        assert rc == -1, args
+    rc = lib.oracle_gemm(2, 2, 2, a.ctypes.data, 2, a.ctypes.data, 2, 7,
+                         None, 0, None, 0, out.ctypes.data, 2, 1)
+    assert rc == -1
+    bad_rows = np.array([2], dtype=np.int64)
+    rc = lib.oracle_gemm(2, 2, 2, a.ctypes.data, 2, a.ctypes.data, 2, W.F16,
+                         bad_rows.ctypes.data, 1, None, 0, out.ctypes.data, 2, 1)
+    assert rc == -1
+
+
+# Pins cheap enough to run against every planted mistake.
+FAST_PINS = [
+    pin_decode_binary16_exhaustive,
+    pin_decode_bfloat16_exhaustive,
+    pin_decode_binary32_sampled,
+    pin_identity,
+    pin_all_ones,
+    pin_golden_ones_8x8,
+    pin_bruteforce_rational,
+    pin_vs_numpy_unaligned,
+    pin_sampled_equals_full,
+    pin_padded_leading_dimension,
+    pin_threads_invariant,
+    pin_output_overwritten,
+    pin_rejects_bad_arguments,
+]
+ALL_PINS = FAST_PINS + [pin_vs_numpy_workloads, pin_large_sampled]

@@ -1,0 +1,73 @@
+"""Planted mistakes: copies of the oracle source, each with one plausible
+mistake, are compiled and run against the pins in a child process; every
+copy must fail at least one pin.  The mistakes live only in temporary copies
+on the CPU; the oracle itself is unchanged."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+sys.path.insert(0, ROOT)
+from oracle import build as obuild  # noqa: E402
+
+# (name, text in oracle_gemm.c, replacement)
+MUTANTS = [
+    ("dropped_first_term", "for (int64_t k = 0; k < jb->K; ++k) {", "for (int64_t k = 1; k < jb->K; ++k) {"),
+    ("dropped_last_term", "for (int64_t k = 0; k < jb->K; ++k) {", "for (int64_t k = 0; k + 1 < jb->K; ++k) {"),
+    ("transposed_b", "decode_one(B, k * ldb + j, dtype)", "decode_one(B, j * ldb + k, dtype)"),
+    ("a_stride_ignores_lda", "decode_one(A, i * lda + k, dtype)", "decode_one(A, i * K + k, dtype)"),
+    ("b_stride_uses_n", "decode_one(B, k * ldb + j, dtype)", "decode_one(B, k * ncols + j, dtype)"),
+    ("wrong_sign", "s[c] += a * brow[c];", "s[c] -= a * brow[c];"),
+    ("no_zero_init", "for (int64_t c = 0; c < jb->ncols; ++c) s[c] = 0.0;", ""),
+    ("f16_subnormal_scale", "v = ldexp((double)f, -24);", "v = ldexp((double)f, -25);"),
+    ("f16_bias", "v = ldexp((double)(1024 + f), e - 25);", "v = ldexp((double)(1024 + f), e - 24);"),
+    ("f16_inf_as_nan", "v = f ? NAN : INFINITY;\n    else\n        v = ldexp((double)(1024", "v = NAN;\n    else\n        v = ldexp((double)(1024"),
+    ("bf16_exponent_field", "int e = (h >> 7) & 0xff;", "int e = (h >> 8) & 0xff;"),
+    ("bf16_subnormal_scale", "v = ldexp((double)f, -133);", "v = ldexp((double)f, -134);"),
+    ("f32_bias", "v = ldexp((double)(8388608u + f), e - 150);", "v = ldexp((double)(8388608u + f), e - 149);"),
+    ("sampled_rows_ignored", "const int64_t i = rows ? rows[r] : r;", "const int64_t i = r;"),
+    ("sampled_cols_ignored", "const int64_t j = cols ? cols[c] : c;", "const int64_t j = c;"),
+    ("a_times_a", "s[c] += a * brow[c];", "s[c] += a * a;"),
+    ("skips_last_row", "for (int64_t r = jb->tid; r < jb->nrows; r += jb->nthreads) {",
+     "for (int64_t r = jb->tid; r + 1 < jb->nrows; r += jb->nthreads) {"),
+]
+
+RUNNER = r"""
+import sys
+sys.path.insert(0, {root!r}); sys.path.insert(0, {tests!r})
+import oracle_pins as P
+failed = []
+for pin in P.FAST_PINS:
+    try:
+        pin({lib!r})
+    except Exception as e:
+        failed.append(pin.__name__)
+print("FAILED:", ",".join(failed))
+sys.exit(1 if failed else 0)
+"""
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(name, old, new, tmp_path):
+    src = open(obuild.SRC, encoding="utf-8").read()
+    assert src.count(old) >= 1, f"mutation site for {name} not found"
+    mutated = src.replace(old, new, 1)
+    cpath = tmp_path / "oracle_mut.c"
+    cpath.write_text(mutated, encoding="utf-8")
+    lib = str(tmp_path / "liboracle_mut.so")
+    obuild.build(str(cpath), lib)
+    code = RUNNER.format(root=ROOT, tests=HERE, lib=lib)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0, f"mutant {name} passed every pin:\n{r.stdout}\n{r.stderr}"
+
+
+def test_unmutated_copy_passes(tmp_path):
+    """Control: the same harness on an untouched copy passes every pin."""
+    lib = str(tmp_path / "liboracle_copy.so")
+    obuild.build(obuild.SRC, lib)
+    code = RUNNER.format(root=ROOT, tests=HERE, lib=lib)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stdout + r.stderr
