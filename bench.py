@@ -1,0 +1,210 @@
+"""Benchmark of the tiled matrix product on one MI355X.
+
+A step is one call of the library (one kernel launch) on the 8192 x 8192 x
+8192 workload: fp16 inputs drawn from N(0,1) with seed 5, fp32 accumulation,
+fp16 output, inputs resident in HBM before timing starts.  The metric is
+TFLOP/s = 2*M*N*K / time, the formula of page "企业官网建设流程全解析" §3.4.
+
+Printed: ONE JSON line with the contract's keys plus
+  roofline      the kernel's achieved TFLOP/s from HIP events recorded around
+                every launch on the stream it runs on, against MI355X's dense
+                fp16 MFMA peak; `traffic` comes from the committed counter
+                summary when it was taken on the current kernel source, else
+                null;
+  cpu_baseline  the oracle (test infrastructure) timed on this host on a
+                bounded sample of the same workload (whole rows of C);
+  per_config    the four smaller workloads, each timed the same way (context).
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_F16_TFLOPS = 2516.6   # 256 CU x 4096 FLOP/clk x 2.4 GHz, dense
+PEAK_F32_TFLOPS = 157.3    # dense fp32 MFMA
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = ["tiled_gemm_03_amd/csrc/gemm_kernel.hpp", "tiled_gemm_03_amd/csrc/tgemm.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_f16_8192x8192x8192.json")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def sclk_mhz():
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        d = json.loads(r.stdout)
+        for v in d.values():
+            for k, s in v.items():
+                if "sclk" in k.lower():
+                    return s
+    except Exception:
+        return None
+    return None
+
+
+def time_calls(fn, steps, warmup, stream):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        fn()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    return wall * 1e3 / steps, ev
+
+
+def cpu_baseline(a, b, budget_s=12.0):
+    """The oracle on whole rows of C (all N columns, the full K), doubling the
+    row count until the run takes budget_s seconds or more."""
+    import numpy as np
+    import oracle
+    from tiled_gemm_03_amd import workloads as W
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    M, K = a.shape
+    N = b.shape[1]
+    rows = 8
+    while True:
+        idx = W.sample_indices(M, rows, 999)
+        t0 = time.perf_counter()
+        oracle.gemm(a, b, W.F16, rows=idx, nthreads=threads)
+        dt = time.perf_counter() - t0
+        if dt >= 0.8 * budget_s or rows >= M:
+            break
+        rows = min(M, max(2 * rows, int(rows * budget_s / max(dt, 1e-3))))
+    flops = 2.0 * rows * N * K
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows} seeded rows x all {N} columns x K={K} of the 8192^3 workload "
+                      f"({flops / 1e9:.1f} GFLOP, fp64 accumulation, {dt:.1f} s)",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=-1, help="force a tile configuration (gemm_ex)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-per-config", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(a row-sharded multi-GPU product needs no collective; it is described, not built)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import tiled_gemm_03_amd as T
+    from tiled_gemm_03_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    w = W.BY_NAME["f16_8192x8192x8192"]
+    print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
+    a_np, b_np = W.make_inputs(w)
+    a = torch.from_numpy(a_np).to(dev)
+    b = torch.from_numpy(b_np).to(dev)
+    c = torch.empty((w.M, w.N), dtype=torch.float16, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        T.gemm_tensors(a, b, c, config_id=args.config, stream=stream.cuda_stream)
+
+    print(f"[bench] timing {args.steps} steps after {args.warmup} warmup", file=sys.stderr, flush=True)
+    ms_per_step, ev = time_calls(step, args.steps, args.warmup, stream)
+    flops = 2.0 * w.M * w.N * w.K
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    kern_ms = float(np.mean(ev))
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        try:
+            with open(TRAFFIC_FILE) as f:
+                tr = json.load(f)
+            if tr.get("kernel_source_hash") == kernel_source_hash():
+                traffic = tr.get("hbm_bytes_per_launch")
+        except Exception:
+            traffic = None
+
+    cfg_id = T.gemm_select_config(w.M, w.N, w.K, a.data_ptr(), w.K, b.data_ptr(), w.N, c.data_ptr(), w.N,
+                                  w.in_dtype, w.out_dtype) if args.config < 0 else args.config
+    info = T.gemm_config_info(cfg_id)
+
+    per_config = []
+    if not args.no_per_config:
+        for pw in W.WORKLOADS[:4]:
+            pa, pb = W.make_inputs(pw)
+            tdt = {W.F16: torch.float16, W.F32: torch.float32}
+            pad = torch.from_numpy(pa).to(dev)
+            pbd = torch.from_numpy(pb).to(dev)
+            pc = torch.empty((pw.M, pw.N), dtype=tdt[pw.out_dtype], device=dev)
+            pms, pev = time_calls(lambda: T.gemm_tensors(pad, pbd, pc, stream=stream.cuda_stream), 200, 20,
+                                  stream)
+            pf = 2.0 * pw.M * pw.N * pw.K
+            med = float(np.median(pev))
+            peak = PEAK_F32_TFLOPS if pw.in_dtype == W.F32 else PEAK_F16_TFLOPS
+            algo_bytes = (pw.M * pw.K + pw.K * pw.N) * (4 if pw.in_dtype == W.F32 else 2) + \
+                pw.M * pw.N * (4 if pw.out_dtype == W.F32 else 2)
+            pid = T.gemm_select_config(pw.M, pw.N, pw.K, pad.data_ptr(), pw.K, pbd.data_ptr(), pw.N,
+                                       pc.data_ptr(), pw.N, pw.in_dtype, pw.out_dtype)
+            per_config.append({
+                "workload": pw.name, "config": T.gemm_config_info(pid)["name"],
+                "us_median": med * 1e3, "us_p10": float(np.percentile(pev, 10)) * 1e3,
+                "us_p90": float(np.percentile(pev, 90)) * 1e3, "us_per_call_wall": pms * 1e3,
+                "tflops": pf / (med * 1e-3) / 1e12, "frac_of_mfma_peak": pf / (med * 1e-3) / 1e12 / peak,
+                "gbs": algo_bytes / (med * 1e-3) / 1e9})
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(a_np, b_np)
+
+    line = {
+        "metric": "GEMM TFLOP/s (fp16 in, fp32 acc) at 8192^3 and % of MI355X MFMA peak",
+        "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "f16_8192x8192x8192: C = A x B, row-major, A,B ~ N(0,1) seed 5 cast to fp16, "
+                               "fp32 accumulation, fp16 output",
+                   "M": w.M, "N": w.N, "K": w.K, "accumulate": "f32", "out_dtype": "f16",
+                   "tile_config": info["name"], "parallelism": "single GPU"},
+        "frac_of_mfma_peak": value / PEAK_F16_TFLOPS,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_F16_TFLOPS, "traffic": traffic,
+                     "kernel_ms_mean": kern_ms, "kernel_ms_p10": float(np.percentile(ev, 10)),
+                     "kernel_ms_p90": float(np.percentile(ev, 90)),
+                     "algorithmic_flop_per_launch": flops,
+                     "algorithmic_bytes_per_launch": (w.M * w.K + w.K * w.N + w.M * w.N) * 2},
+        "cpu_baseline": cpu,
+        "per_config": per_config,
+        "sclk": sclk_mhz(),
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,142 @@
+/*
+ * tgemm.h -- C ABI of the MI355X (gfx950) tiled dense matrix product library
+ * libtgemm.so.
+ *
+ * The operation is the tiled matrix product of page "企业官网建设流程全解析"
+ * (a TileLang article despite its title), §3.3: C = A x B with A of size
+ * M x K, B of size K x N and C of size M x N; each workgroup owns one output
+ * tile, walks K in steps, stages tiles of A and B in on-chip shared memory
+ * (LDS here) through a multi-stage software pipeline (§2.3, §4.2 of that
+ * page) and accumulates in an fp32 register fragment, which is converted to
+ * the output type when it is written back.  Inputs are fp16 (or bf16, or
+ * fp32), accumulation is always fp32, as in that page's listing
+ * (dtype="float16", accum_dtype="float32").
+ *
+ * Conventions shared by every entry point:
+ *  - All matrices are ROW-MAJOR, the default layout of page "TileLang实战：
+ *    用Python DSL自动生成高性能GPU计算内核", §5.1.  Leading dimensions are in
+ *    ELEMENTS: A is M x K with lda >= K, B is K x N with ldb >= N, C is M x N
+ *    with ldc >= N.  Element (i, j) of A is A[i * lda + j].
+ *  - C := A x B.  C is overwritten; there is no alpha/beta.  Elements of C
+ *    outside the M x N window (columns N .. ldc-1) are never written.
+ *  - A, B and C are DEVICE pointers (memory of the current HIP device), owned
+ *    by the caller; the library keeps no reference after the call.  C must
+ *    not overlap A or B.
+ *  - The call enqueues one kernel on `stream` (a hipStream_t; NULL = the
+ *    null stream) and returns without waiting for it.  The library allocates
+ *    no memory and keeps no per-call state; concurrent calls are safe.
+ *  - K == 0 writes zeros (the empty sum).  M == 0 or N == 0 does nothing and
+ *    returns TGEMM_OK.
+ *  - Return codes: TGEMM_OK (0); a negative TGEMM_ERR_* for invalid arguments,
+ *    detected before anything is enqueued (no side effect); a positive value
+ *    is the hipError_t reported by the kernel launch.  gemm_strerror() names
+ *    every code.
+ */
+#ifndef TGEMM_H
+#define TGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types. */
+#define TGEMM_F32 0  /* IEEE binary32 */
+#define TGEMM_F16 1  /* IEEE binary16 */
+#define TGEMM_BF16 2 /* bfloat16 (upper half of a binary32) */
+
+/* Supported (in_dtype -> out_dtype) pairs:
+ *   F32 -> F32, F16 -> F16, F16 -> F32, BF16 -> BF16, BF16 -> F32.
+ * Conversion of the fp32 accumulator to F16 / BF16 rounds to nearest, ties to
+ * even; values beyond the output range become +-Inf. */
+
+/* Error codes. */
+#define TGEMM_OK 0
+#define TGEMM_ERR_DIM (-1)         /* M, N or K negative, or above TGEMM_MAX_DIM */
+#define TGEMM_ERR_NULL (-2)        /* NULL pointer for a non-empty operand       */
+#define TGEMM_ERR_LD (-3)          /* lda < K, ldb < N or ldc < N                */
+#define TGEMM_ERR_DTYPE (-4)       /* unsupported (in_dtype, out_dtype) pair     */
+#define TGEMM_ERR_ALIAS (-5)       /* C overlaps A or B                          */
+#define TGEMM_ERR_CONFIG (-6)      /* gemm_ex: unknown config or wrong dtype     */
+
+/* Largest M, N or K accepted (tile indices are 32-bit; element offsets are
+ * 64-bit, so matrices may exceed 4 GiB). */
+#define TGEMM_MAX_DIM (1LL << 30)
+
+/*
+ * gemm: C := A x B (see the conventions above).
+ *   M, N, K              sizes; A: M x K, B: K x N, C: M x N
+ *   A, lda / B, ldb      device inputs of type in_dtype, leading dims in elements
+ *   C, ldc               device output of type out_dtype, leading dim in elements
+ *   in_dtype, out_dtype  TGEMM_F32 / TGEMM_F16 / TGEMM_BF16
+ *   stream               hipStream_t to enqueue on (NULL: null stream)
+ * The tile configuration comes from a per-shape table keyed on the element
+ * types, the sizes and the 16-byte alignment of pointers and leading
+ * dimensions (gemm_select_config).
+ */
+int gemm(int64_t M, int64_t N, int64_t K,
+         const void* A, int64_t lda, const void* B, int64_t ldb,
+         void* C, int64_t ldc, int in_dtype, int out_dtype, void* stream);
+
+/*
+ * gemm_ex: as gemm, but forces tile configuration `config_id` (0 ..
+ * gemm_num_configs()-1) instead of the table's choice; -1 means "the table's
+ * choice".  Any configuration gives a correct result for any shape, layout
+ * and alignment of its input type; it is meant for measuring one
+ * configuration against another (the tuning method of page
+ * "企业官网建设流程全解析", §4.4).  Returns TGEMM_ERR_CONFIG if the id is
+ * unknown or the configuration is for another input type.
+ */
+int gemm_ex(int64_t M, int64_t N, int64_t K,
+            const void* A, int64_t lda, const void* B, int64_t ldb,
+            void* C, int64_t ldc, int in_dtype, int out_dtype, void* stream,
+            int config_id);
+
+/* Human-readable text for a return code of gemm / gemm_ex (never NULL; the
+ * string is static). */
+const char* gemm_strerror(int code);
+
+/* Number of tile configurations in the table. */
+int gemm_num_configs(void);
+
+/* Description of one tile configuration (the tile-config tuple of page
+ * "企业官网建设流程全解析", §3.3: block_M, block_N, block_K, num_stages,
+ * threads, plus the gfx950 specifics). */
+typedef struct tgemm_config_info {
+    int id;
+    int in_dtype;       /* TGEMM_F16 configurations also serve TGEMM_BF16 */
+    int block_m, block_n, block_k;
+    int stages;         /* LDS buffers in the software pipeline            */
+    int threads;        /* workitems per workgroup (64 per wavefront)      */
+    int waves_m, waves_n;
+    int mfma_m, mfma_n, mfma_k; /* shape of one MFMA instruction           */
+    int lds_bytes;      /* LDS per workgroup                               */
+    const char* name;   /* static string                                   */
+} tgemm_config_info;
+
+/* Fills *out for config `id`; returns TGEMM_OK or TGEMM_ERR_CONFIG. */
+int gemm_config_info(int id, tgemm_config_info* out);
+
+/* Host-side table lookup only (no GPU call): the configuration id that gemm()
+ * would use for these arguments, or a negative TGEMM_ERR_* if gemm() would
+ * reject them.  Pointers are only inspected for their alignment. */
+int gemm_select_config(int64_t M, int64_t N, int64_t K,
+                       const void* A, int64_t lda, const void* B, int64_t ldb,
+                       const void* C, int64_t ldc, int in_dtype, int out_dtype);
+
+/* Host-side copy of the workgroup -> output-tile map the kernels use (no GPU
+ * call), for checking that it is a bijection: workgroup `bid` of a grid of
+ * tiles_m x tiles_n tiles, raster groups of `group_m` tile rows, computes
+ * tile (*tm, *tn).  Returns TGEMM_OK, or TGEMM_ERR_DIM for out-of-range
+ * arguments (nothing written). */
+int gemm_tile_map(int bid, int tiles_m, int tiles_n, int group_m, int* tm, int* tn);
+
+/* Library version string (static). */
+const char* gemm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TGEMM_H */

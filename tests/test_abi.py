@@ -1,0 +1,155 @@
+"""Host-side checks of libtgemm.so (no GPU needed): it loads, exports every
+function include/tgemm.h declares, rejects invalid arguments with the
+documented codes before touching the GPU, picks the table's configuration,
+and its workgroup -> tile map is a bijection."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tiled_gemm_03_amd as T
+from tiled_gemm_03_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tgemm.h")
+
+
+def declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_function():
+    lib = T.lib()
+    names = declared_functions()
+    assert set(names) == set(T.EXPORTED), names
+    for n in names:
+        assert hasattr(lib, n), f"libtgemm.so does not export {n}"
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+
+
+def test_version_and_configs():
+    assert "gfx950" in T.gemm_version()
+    n = T.gemm_num_configs()
+    assert n >= 4
+    for i in range(n):
+        c = T.gemm_config_info(i)
+        assert c["id"] == i
+        assert c["threads"] % 64 == 0
+        assert c["threads"] == 64 * c["waves_m"] * c["waves_n"]
+        assert c["lds_bytes"] <= 160 * 1024
+        eb = 4 if c["in_dtype"] == T.F32 else 2
+        # LDS holds `stages` copies of an A tile (block_m x block_k) and a B
+        # tile (block_k x block_n), the budget formula of page
+        # "企业官网建设流程全解析", §4.2
+        assert c["lds_bytes"] == c["stages"] * (c["block_m"] + c["block_n"]) * c["block_k"] * eb
+    with pytest.raises(T.TgemmError):
+        T.gemm_config_info(n)
+
+
+def test_lds_budget_formula_matches_page_example():
+    """The page's own numbers: block_M = block_N = 128, block_K = 32, fp16
+    gives 8 KB + 8 KB = 16 KB per stage, 48 KB at 3 stages, 64 KB at 4
+    ("企业官网建设流程全解析", §4.2); the formula of the DeepSeek/Ascend
+    toolkit page, §5.1, at 128/128/64/3 evaluates to 98304 bytes (the page
+    prints twice that)."""
+    def lds(bm, bn, bk, stages, eb):
+        return stages * (bm * bk + bk * bn) * eb
+    assert lds(128, 128, 32, 1, 2) == 16 * 1024
+    assert lds(128, 128, 32, 3, 2) == 48 * 1024
+    assert lds(128, 128, 32, 4, 2) == 64 * 1024
+    assert lds(128, 128, 64, 3, 2) == 98304
+    big = T.gemm_config_info(0)
+    assert big["lds_bytes"] == lds(big["block_m"], big["block_n"], big["block_k"], big["stages"], 2)
+
+
+def _codes(M, N, K, A, lda, B, ldb, C, ldc, i, o):
+    a = T.gemm(M, N, K, A, lda, B, ldb, C, ldc, i, o, None)
+    s = T.gemm_select_config(M, N, K, A, lda, B, ldb, C, ldc, i, o)
+    return a, s
+
+
+FAKE = 1 << 40  # a well-aligned address that is never dereferenced
+
+
+@pytest.mark.parametrize("args,code", [
+    ((-1, 4, 4, FAKE, 4, FAKE, 4, FAKE, 4, 1, 1), T.ERR_DIM),
+    ((4, -1, 4, FAKE, 4, FAKE, 4, FAKE, 4, 1, 1), T.ERR_DIM),
+    ((4, 4, -1, FAKE, 4, FAKE, 4, FAKE, 4, 1, 1), T.ERR_DIM),
+    (((1 << 30) + 1, 4, 4, FAKE, 4, FAKE, 4, FAKE, 4, 1, 1), T.ERR_DIM),
+    ((4, 4, 4, FAKE, 4, FAKE, 4, FAKE, 4, 1, 2), T.ERR_DTYPE),
+    ((4, 4, 4, FAKE, 4, FAKE, 4, FAKE, 4, 0, 1), T.ERR_DTYPE),
+    ((4, 4, 4, FAKE, 4, FAKE, 4, FAKE, 4, 2, 1), T.ERR_DTYPE),
+    ((4, 4, 4, FAKE, 4, FAKE, 4, FAKE, 4, 3, 0), T.ERR_DTYPE),
+    ((4, 4, 4, FAKE, 3, FAKE, 4, FAKE, 4, 1, 1), T.ERR_LD),
+    ((4, 4, 4, FAKE, 4, FAKE, 3, FAKE, 4, 1, 1), T.ERR_LD),
+    ((4, 4, 4, FAKE, 4, FAKE, 4, FAKE, 3, 1, 1), T.ERR_LD),
+    ((4, 4, 4, None, 4, FAKE, 4, FAKE, 4, 1, 1), T.ERR_NULL),
+    ((4, 4, 4, FAKE, 4, None, 4, FAKE, 4, 1, 1), T.ERR_NULL),
+    ((4, 4, 4, FAKE, 4, FAKE, 4, None, 4, 1, 1), T.ERR_NULL),
+    ((4, 4, 4, FAKE, 4, FAKE + 4096, 4, FAKE + 16, 4, 1, 1), T.ERR_ALIAS),
+    ((4, 4, 4, FAKE, 4, FAKE + 4096, 4, FAKE + 4096 + 30, 4, 1, 1), T.ERR_ALIAS),
+])
+def test_invalid_arguments_rejected_without_launch(args, code):
+    a, s = _codes(*args)
+    assert a == code and s == code
+    assert T.gemm_strerror(code) != "unknown error code"
+
+
+def test_empty_problems_are_noops():
+    # M == 0 or N == 0: nothing to do, success, even with NULL pointers
+    assert T.gemm(0, 4, 4, None, 4, None, 4, None, 4, 1, 1, None) == T.OK
+    assert T.gemm(4, 0, 4, None, 4, None, 0, None, 0, 1, 1, None) == T.OK
+    # K == 0 needs only C
+    assert T.gemm_select_config(4, 4, 0, None, 0, None, 4, FAKE, 4, 1, 1) >= 0
+
+
+def test_gemm_ex_config_checks():
+    n = T.gemm_num_configs()
+    assert T.gemm_ex(4, 4, 4, FAKE, 4, FAKE + 4096, 4, FAKE + 8192, 4, 1, 1, None, n) == T.ERR_CONFIG
+    assert T.gemm_ex(4, 4, 4, FAKE, 4, FAKE + 4096, 4, FAKE + 8192, 4, 1, 1, None, -2) == T.ERR_CONFIG
+    for i in range(n):
+        fam = T.gemm_config_info(i)["in_dtype"]
+        other = T.F32 if fam != T.F32 else T.F16
+        rc = T.gemm_ex(4, 4, 4, FAKE, 4, FAKE + 4096, 4, FAKE + 8192, 4, other, T.F32, None, i)
+        assert rc == T.ERR_CONFIG
+
+
+def test_table_choice_for_the_workloads():
+    names = {i: T.gemm_config_info(i)["name"] for i in range(T.gemm_num_configs())}
+    picks = {}
+    for w in W.WORKLOADS:
+        cid = T.gemm_select_config(w.M, w.N, w.K, FAKE, w.K, FAKE + (1 << 32), w.N, FAKE + (2 << 32), w.N,
+                                   w.in_dtype, w.out_dtype)
+        assert cid >= 0
+        info = T.gemm_config_info(cid)
+        assert info["in_dtype"] == (T.F32 if w.in_dtype == T.F32 else T.F16)
+        picks[w.name] = names[cid]
+    # the large square product takes the largest tile
+    assert picks["f16_8192x8192x8192"] == names[0]
+
+
+@pytest.mark.parametrize("tiles_m,tiles_n,group_m", [
+    (1, 1, 1), (1, 7, 4), (7, 1, 4), (32, 32, 4), (32, 32, 1), (32, 32, 8), (5, 13, 3),
+    (8, 16, 4), (33, 31, 4), (4, 8, 16), (16, 32, 6)])
+def test_tile_map_is_a_bijection(tiles_m, tiles_n, group_m):
+    seen = set()
+    for bid in range(tiles_m * tiles_n):
+        tm, tn = T.gemm_tile_map(bid, tiles_m, tiles_n, group_m)
+        assert 0 <= tm < tiles_m and 0 <= tn < tiles_n
+        seen.add((tm, tn))
+    assert len(seen) == tiles_m * tiles_n
+
+
+def test_tile_map_keeps_an_xcd_on_a_compact_block():
+    """The 32 workgroups that one XCD runs first at 8192^3 with 256x256 tiles
+    (ids x, x+8, ..., x+248) cover a 4 x 8 block of tiles: 4 A panels and 8
+    B panels shared in that XCD's L2."""
+    for xcd in range(8):
+        tiles = [T.gemm_tile_map(xcd + 8 * j, 32, 32, 4) for j in range(32)]
+        ms = {t[0] for t in tiles}
+        ns = {t[1] for t in tiles}
+        assert len(ms) == 4 and len(ns) == 8

@@ -1,0 +1,158 @@
+"""Python binding of libtgemm.so, the gfx950 tiled matrix-product library.
+
+Argument marshalling only: every function here forwards to the C entry point
+of the same name declared in include/tgemm.h; all computation happens in the
+library's HIP kernels.  There is no fallback: if the library has not been
+built, loading fails with an error that says so.
+
+    gemm(M, N, K, A, lda, B, ldb, C, ldc, in_dtype, out_dtype, stream)
+    gemm_ex(..., config_id)
+    gemm_strerror(code), gemm_num_configs(), gemm_config_info(id),
+    gemm_select_config(...), gemm_tile_map(...), gemm_version()
+
+`gemm_tensors(a, b, c)` takes torch device tensors (row-major, unit column
+stride) and passes their pointers, leading dimensions and the current HIP
+stream; torch provides only the memory and the stream.
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libtgemm.so")
+
+F32, F16, BF16 = 0, 1, 2
+OK = 0
+ERR_DIM, ERR_NULL, ERR_LD, ERR_DTYPE, ERR_ALIAS, ERR_CONFIG = -1, -2, -3, -4, -5, -6
+
+EXPORTED = ["gemm", "gemm_ex", "gemm_strerror", "gemm_num_configs", "gemm_config_info",
+            "gemm_select_config", "gemm_tile_map", "gemm_version"]
+
+
+class ConfigInfo(ctypes.Structure):
+    _fields_ = [("id", ctypes.c_int), ("in_dtype", ctypes.c_int),
+                ("block_m", ctypes.c_int), ("block_n", ctypes.c_int), ("block_k", ctypes.c_int),
+                ("stages", ctypes.c_int), ("threads", ctypes.c_int),
+                ("waves_m", ctypes.c_int), ("waves_n", ctypes.c_int),
+                ("mfma_m", ctypes.c_int), ("mfma_n", ctypes.c_int), ("mfma_k", ctypes.c_int),
+                ("lds_bytes", ctypes.c_int), ("name", ctypes.c_char_p)]
+
+    def as_dict(self):
+        d = {f: getattr(self, f) for f, _ in self._fields_}
+        d["name"] = d["name"].decode()
+        return d
+
+
+class TgemmError(RuntimeError):
+    def __init__(self, code):
+        super().__init__(f"tgemm error {code}: {gemm_strerror(code)}")
+        self.code = code
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libtgemm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                          "(there is no fallback path)")
+    L = ctypes.CDLL(LIB_PATH)
+    i64, p, i = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    L.gemm.restype = i
+    L.gemm.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, i, i, p]
+    L.gemm_ex.restype = i
+    L.gemm_ex.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, i, i, p, i]
+    L.gemm_strerror.restype = ctypes.c_char_p
+    L.gemm_strerror.argtypes = [i]
+    L.gemm_num_configs.restype = i
+    L.gemm_num_configs.argtypes = []
+    L.gemm_config_info.restype = i
+    L.gemm_config_info.argtypes = [i, ctypes.POINTER(ConfigInfo)]
+    L.gemm_select_config.restype = i
+    L.gemm_select_config.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, i, i]
+    L.gemm_tile_map.restype = i
+    L.gemm_tile_map.argtypes = [i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i)]
+    L.gemm_version.restype = ctypes.c_char_p
+    L.gemm_version.argtypes = []
+    _lib = L
+    return L
+
+
+def gemm(M, N, K, A, lda, B, ldb, C, ldc, in_dtype, out_dtype, stream=None):
+    return lib().gemm(M, N, K, A, lda, B, ldb, C, ldc, in_dtype, out_dtype, stream)
+
+
+def gemm_ex(M, N, K, A, lda, B, ldb, C, ldc, in_dtype, out_dtype, stream=None, config_id=-1):
+    return lib().gemm_ex(M, N, K, A, lda, B, ldb, C, ldc, in_dtype, out_dtype, stream, config_id)
+
+
+def gemm_strerror(code):
+    return lib().gemm_strerror(code).decode()
+
+
+def gemm_num_configs():
+    return lib().gemm_num_configs()
+
+
+def gemm_config_info(config_id):
+    info = ConfigInfo()
+    rc = lib().gemm_config_info(config_id, ctypes.byref(info))
+    if rc != OK:
+        raise TgemmError(rc)
+    return info.as_dict()
+
+
+def gemm_select_config(M, N, K, A, lda, B, ldb, C, ldc, in_dtype, out_dtype):
+    return lib().gemm_select_config(M, N, K, A, lda, B, ldb, C, ldc, in_dtype, out_dtype)
+
+
+def gemm_tile_map(bid, tiles_m, tiles_n, group_m):
+    tm, tn = ctypes.c_int(-1), ctypes.c_int(-1)
+    rc = lib().gemm_tile_map(bid, tiles_m, tiles_n, group_m, ctypes.byref(tm), ctypes.byref(tn))
+    if rc != OK:
+        raise TgemmError(rc)
+    return tm.value, tn.value
+
+
+def gemm_version():
+    return lib().gemm_version().decode()
+
+
+# ------------------------------------------------------------ torch marshalling
+def dtype_code(t):
+    import torch
+    codes = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported tensor dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def _ld(t):
+    if t.dim() != 2:
+        raise ValueError("expected a 2-D tensor")
+    if t.shape[0] > 0 and t.shape[1] > 0 and t.stride(1) != 1:
+        raise ValueError("tensor rows must be contiguous (unit column stride)")
+    return max(t.stride(0) if t.shape[0] > 1 else t.shape[1], t.shape[1])
+
+
+def gemm_tensors(a, b, c, config_id=-1, stream=None, check=True):
+    """c := a @ b on the device, through the C ABI.  a: M x K, b: K x N,
+    c: M x N torch tensors on the GPU (rows may be padded).  Returns the
+    library's return code (raises TgemmError on failure if check)."""
+    import torch
+    M, K = a.shape
+    K2, N = b.shape
+    if K2 != K or tuple(c.shape) != (M, N):
+        raise ValueError(f"shape mismatch {tuple(a.shape)} x {tuple(b.shape)} -> {tuple(c.shape)}")
+    if a.dtype != b.dtype:
+        raise TypeError("a and b must have one dtype")
+    if stream is None:
+        stream = torch.cuda.current_stream(a.device).cuda_stream
+    rc = gemm_ex(M, N, K, a.data_ptr(), _ld(a), b.data_ptr(), _ld(b), c.data_ptr(), _ld(c),
+                 dtype_code(a), dtype_code(c), stream, config_id)
+    if check and rc != OK:
+        raise TgemmError(rc)
+    return rc

@@ -1,0 +1,256 @@
+// tgemm.hip -- C ABI of libtgemm.so: argument checks, the per-shape tile
+// configuration table and the kernel launch.  The kernels are in
+// gemm_kernel.hpp; the ABI is declared (and documented) in include/tgemm.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "gemm_kernel.hpp"
+#include "tgemm.h"
+
+using namespace tgemm;
+
+namespace {
+
+// ------------------------------------------------------------- configurations
+// Tile-config tuples (block_M, block_N, block_K, waves, occupancy) in the
+// spirit of the tuning tables of page "企业官网建设流程全解析", §3.3 / §4.4, and
+// of the DeepSeek/Ascend TileLang toolkit page, §4.3, sized for gfx950:
+// 160 KiB LDS per CU, 512 registers per lane at one wave per SIMD.
+using CfgBig = TileCfg<256, 256, 64, 2, 2, 2, 1>;    // 4 waves, 128x128 per wave
+using CfgMid = TileCfg<128, 128, 64, 2, 2, 2, 2>;    // 4 waves, 64x64 per wave
+using CfgSmall = TileCfg<64, 64, 64, 2, 2, 2, 2>;    // 4 waves, 32x32 per wave
+using CfgTiny = TileCfg<32, 32, 64, 1, 1, 2, 4>;     // 1 wave
+using CfgF32Mid = TileCfg<64, 64, 32, 2, 2, 4, 2>;   // fp32 inputs
+using CfgF32Tiny = TileCfg<32, 32, 32, 1, 1, 4, 4>;  // fp32 inputs, 1 wave
+
+typedef void (*KernelFn)(GemmArgs);
+
+struct ConfigEntry {
+    const char* name;
+    int in_family;  // TGEMM_F16 (serves F16 and BF16) or TGEMM_F32
+    int bm, bn, bk, wm, wn, eb, lds_bytes, threads, cpr;
+    KernelFn (*pick)(int in, int out, bool aligned);
+};
+
+template <class T, int IN>
+KernelFn pick_out(int out, bool aligned) {
+    if (out == TGEMM_F32)
+        return aligned ? gemm_kernel<T, IN, DT_F32, true> : gemm_kernel<T, IN, DT_F32, false>;
+    if (IN == DT_F16 && out == TGEMM_F16)
+        return aligned ? gemm_kernel<T, IN, DT_F16, true> : gemm_kernel<T, IN, DT_F16, false>;
+    if (IN == DT_BF16 && out == TGEMM_BF16)
+        return aligned ? gemm_kernel<T, IN, DT_BF16, true> : gemm_kernel<T, IN, DT_BF16, false>;
+    return nullptr;
+}
+
+template <class T>
+KernelFn pick_half(int in, int out, bool aligned) {
+    if (in == TGEMM_F16) return pick_out<T, DT_F16>(out, aligned);
+    if (in == TGEMM_BF16) return pick_out<T, DT_BF16>(out, aligned);
+    return nullptr;
+}
+
+template <class T>
+KernelFn pick_f32(int in, int out, bool aligned) {
+    if (in == TGEMM_F32 && out == TGEMM_F32)
+        return aligned ? gemm_kernel<T, DT_F32, DT_F32, true> : gemm_kernel<T, DT_F32, DT_F32, false>;
+    return nullptr;
+}
+
+#define ENTRY(name, fam, T, pk) \
+    {name, fam, T::BM, T::BN, T::BK, T::WM, T::WN, T::EB, T::LDS_BYTES, T::THREADS, T::CPR, pk<T>}
+
+const ConfigEntry kConfigs[] = {
+    ENTRY("h256x256x64_w2x2", TGEMM_F16, CfgBig, pick_half),
+    ENTRY("h128x128x64_w2x2", TGEMM_F16, CfgMid, pick_half),
+    ENTRY("h64x64x64_w2x2", TGEMM_F16, CfgSmall, pick_half),
+    ENTRY("h32x32x64_w1x1", TGEMM_F16, CfgTiny, pick_half),
+    ENTRY("s64x64x32_w2x2", TGEMM_F32, CfgF32Mid, pick_f32),
+    ENTRY("s32x32x32_w1x1", TGEMM_F32, CfgF32Tiny, pick_f32),
+};
+constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
+enum { CFG_BIG = 0, CFG_MID = 1, CFG_SMALL = 2, CFG_TINY = 3, CFG_F32_MID = 4, CFG_F32_TINY = 5 };
+
+// Measurement-only switches, read once from the environment:
+//   TGEMM_GROUP_M=<n>    tile rows per raster group (default 4)
+//   TGEMM_NO_SWIZZLE=1   plain row-major LDS tiles (for bank-conflict A/B runs)
+struct Tuning {
+    int group_m = 4;
+    bool swizzle = true;
+    Tuning() {
+        if (const char* s = getenv("TGEMM_GROUP_M")) {
+            const int g = atoi(s);
+            if (g > 0) group_m = g;
+        }
+        if (const char* s = getenv("TGEMM_NO_SWIZZLE")) swizzle = !(s[0] == '1');
+    }
+};
+const Tuning& tuning() {
+    static const Tuning t;
+    return t;
+}
+
+int elem_bytes(int dt) { return dt == TGEMM_F32 ? 4 : 2; }
+
+bool pair_supported(int in, int out) {
+    switch (in) {
+        case TGEMM_F32: return out == TGEMM_F32;
+        case TGEMM_F16: return out == TGEMM_F16 || out == TGEMM_F32;
+        case TGEMM_BF16: return out == TGEMM_BF16 || out == TGEMM_F32;
+        default: return false;
+    }
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int validate(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+             const void* C, int64_t ldc, int in, int out) {
+    if (M < 0 || N < 0 || K < 0 || M > TGEMM_MAX_DIM || N > TGEMM_MAX_DIM || K > TGEMM_MAX_DIM)
+        return TGEMM_ERR_DIM;
+    if (!pair_supported(in, out)) return TGEMM_ERR_DTYPE;
+    if (lda < K || ldb < N || ldc < N) return TGEMM_ERR_LD;
+    if (M == 0 || N == 0) return TGEMM_OK;
+    if (C == nullptr) return TGEMM_ERR_NULL;
+    if (K > 0 && (A == nullptr || B == nullptr)) return TGEMM_ERR_NULL;
+    if (K > 0) {
+        const uintptr_t ie = elem_bytes(in), oe = elem_bytes(out);
+        const uintptr_t c0 = (uintptr_t)C, c1 = c0 + (uintptr_t)((M - 1) * ldc + N) * oe;
+        const uintptr_t a0 = (uintptr_t)A, a1 = a0 + (uintptr_t)((M - 1) * lda + K) * ie;
+        const uintptr_t b0 = (uintptr_t)B, b1 = b0 + (uintptr_t)((K - 1) * ldb + N) * ie;
+        if ((c0 < a1 && a0 < c1) || (c0 < b1 && b0 < c1)) return TGEMM_ERR_ALIAS;
+    }
+    return TGEMM_OK;
+}
+
+bool is_aligned(const ConfigEntry& c, const void* A, int64_t lda, const void* B, int64_t ldb, const void* C,
+                int64_t ldc, int out) {
+    const int ve = 16 / c.eb;
+    const uintptr_t oe = elem_bytes(out);
+    return ((uintptr_t)A % 16 == 0) && ((uintptr_t)B % 16 == 0) && ((uintptr_t)C % (4 * oe) == 0) &&
+           (lda % ve == 0) && (ldb % ve == 0) && (ldc % 4 == 0);
+}
+
+int64_t tiles_for(const ConfigEntry& c, int64_t M, int64_t N) { return ceil_div(M, c.bm) * ceil_div(N, c.bn); }
+
+// The per-shape table.  Each choice keeps the chip's 256 CUs busy with the
+// largest tile that still gives enough workgroups; small problems take the
+// smallest tile, which maximises parallelism where launch latency and one
+// workgroup's K loop set the time.
+int table_choice(int64_t M, int64_t N, int64_t K, int in) {
+    (void)K;
+    if (in == TGEMM_F32)
+        return tiles_for(kConfigs[CFG_F32_MID], M, N) >= 256 ? CFG_F32_MID : CFG_F32_TINY;
+    if (tiles_for(kConfigs[CFG_BIG], M, N) >= 256) return CFG_BIG;
+    if (tiles_for(kConfigs[CFG_MID], M, N) >= 256) return CFG_MID;
+    if (tiles_for(kConfigs[CFG_SMALL], M, N) >= 256) return CFG_SMALL;
+    return CFG_TINY;
+}
+
+int family_of(int in) { return in == TGEMM_F32 ? TGEMM_F32 : TGEMM_F16; }
+
+int run(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
+        int64_t ldc, int in, int out, void* stream, int config_id) {
+    const int v = validate(M, N, K, A, lda, B, ldb, C, ldc, in, out);
+    if (v != TGEMM_OK) return v;
+    if (config_id < -1 || config_id >= kNumConfigs) return TGEMM_ERR_CONFIG;
+    if (config_id >= 0 && kConfigs[config_id].in_family != family_of(in)) return TGEMM_ERR_CONFIG;
+    if (M == 0 || N == 0) return TGEMM_OK;
+    const int id = config_id >= 0 ? config_id : table_choice(M, N, K, in);
+    const ConfigEntry& c = kConfigs[id];
+    const bool aligned = is_aligned(c, A, lda, B, ldb, C, ldc, out);
+    KernelFn fn = c.pick(in, out, aligned);
+    if (fn == nullptr) return TGEMM_ERR_DTYPE;
+
+    GemmArgs args;
+    args.A = (const char*)A;
+    args.B = (const char*)B;
+    args.C = (char*)C;
+    args.lda = lda;
+    args.ldb = ldb;
+    args.ldc = ldc;
+    args.M = (int)M;
+    args.N = (int)N;
+    args.K = (int)K;
+    args.tiles_m = (int)ceil_div(M, c.bm);
+    args.tiles_n = (int)ceil_div(N, c.bn);
+    args.group_m = tuning().group_m;
+    args.swz_mask = tuning().swizzle ? c.cpr - 1 : 0;
+    const int64_t grid = (int64_t)args.tiles_m * args.tiles_n;
+    if (grid > 0x7fffffff) return TGEMM_ERR_DIM;
+
+    void* kargs[] = {&args};
+    hipError_t e = hipLaunchKernel((const void*)fn, dim3((unsigned)grid), dim3(c.threads), kargs, 0,
+                                   (hipStream_t)stream);
+    if (e == hipSuccess) e = hipGetLastError();
+    return e == hipSuccess ? TGEMM_OK : (int)e;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
+         int64_t ldc, int in_dtype, int out_dtype, void* stream) {
+    return run(M, N, K, A, lda, B, ldb, C, ldc, in_dtype, out_dtype, stream, -1);
+}
+
+int gemm_ex(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
+            int64_t ldc, int in_dtype, int out_dtype, void* stream, int config_id) {
+    return run(M, N, K, A, lda, B, ldb, C, ldc, in_dtype, out_dtype, stream, config_id);
+}
+
+const char* gemm_strerror(int code) {
+    switch (code) {
+        case TGEMM_OK: return "success";
+        case TGEMM_ERR_DIM: return "M, N or K negative or too large";
+        case TGEMM_ERR_NULL: return "NULL pointer for a non-empty operand";
+        case TGEMM_ERR_LD: return "leading dimension smaller than the row width (lda < K, ldb < N or ldc < N)";
+        case TGEMM_ERR_DTYPE: return "unsupported (in_dtype, out_dtype) pair";
+        case TGEMM_ERR_ALIAS: return "C overlaps A or B";
+        case TGEMM_ERR_CONFIG: return "unknown tile configuration or configuration for another input type";
+        default: break;
+    }
+    if (code > 0) return hipGetErrorString((hipError_t)code);
+    return "unknown error code";
+}
+
+int gemm_num_configs(void) { return kNumConfigs; }
+
+int gemm_config_info(int id, tgemm_config_info* out) {
+    if (id < 0 || id >= kNumConfigs || out == nullptr) return TGEMM_ERR_CONFIG;
+    const ConfigEntry& c = kConfigs[id];
+    out->id = id;
+    out->in_dtype = c.in_family;
+    out->block_m = c.bm;
+    out->block_n = c.bn;
+    out->block_k = c.bk;
+    out->stages = 2;
+    out->threads = c.threads;
+    out->waves_m = c.wm;
+    out->waves_n = c.wn;
+    out->mfma_m = 32;
+    out->mfma_n = 32;
+    out->mfma_k = c.eb == 4 ? 2 : 16;
+    out->lds_bytes = c.lds_bytes;
+    out->name = c.name;
+    return TGEMM_OK;
+}
+
+int gemm_select_config(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                       const void* C, int64_t ldc, int in_dtype, int out_dtype) {
+    const int v = validate(M, N, K, A, lda, B, ldb, C, ldc, in_dtype, out_dtype);
+    if (v != TGEMM_OK) return v;
+    return table_choice(M, N, K, in_dtype);
+}
+
+int gemm_tile_map(int bid, int tiles_m, int tiles_n, int group_m, int* tm, int* tn) {
+    if (tiles_m <= 0 || tiles_n <= 0 || group_m <= 0 || bid < 0 || bid >= tiles_m * tiles_n || !tm || !tn)
+        return TGEMM_ERR_DIM;
+    tile_of(bid, tiles_m, tiles_n, group_m, *tm, *tn);
+    return TGEMM_OK;
+}
+
+const char* gemm_version(void) { return "tgemm 0.1 gfx950"; }
+
+}  // extern "C"
