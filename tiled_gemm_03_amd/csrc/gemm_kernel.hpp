@@ -41,6 +41,7 @@
 
 namespace tgemm {
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -140,7 +141,7 @@ __device__ __forceinline__ u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
 template <int EB>
 __device__ __forceinline__ u32x4 load_chunk_partial(const char* p, int valid) {
     u32x4 v = zero4();
-    if (EB == 4) {
+    if constexpr (EB == 4) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             if (e < valid) v[e] = *(const uint32_t*)(p + 4 * e);
@@ -159,7 +160,7 @@ __device__ __forceinline__ u32x4 load_chunk_partial(const char* p, int valid) {
 // (columns).  16-bit elements: 32 v_perm_b32; 32-bit elements: renaming only.
 template <int EB>
 __device__ __forceinline__ void transpose_block(const u32x4 (&in)[16 / EB], u32x4 (&out)[16 / EB]) {
-    if (EB == 4) {
+    if constexpr (EB == 4) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
 #pragma unroll
@@ -177,7 +178,7 @@ __device__ __forceinline__ void transpose_block(const u32x4 (&in)[16 / EB], u32x
 
 template <int OUT>
 __device__ __forceinline__ void store4(char* p, float a, float b, float c, float d, bool vec) {
-    if (OUT == DT_F32) {
+    if constexpr (OUT == DT_F32) {
         if (vec) {
             *(u32x4*)p = u32x4{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
                                __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d)};
@@ -186,7 +187,7 @@ __device__ __forceinline__ void store4(char* p, float a, float b, float c, float
         }
     } else {
         uint16_t h[4];
-        if (OUT == DT_F16) {
+        if constexpr (OUT == DT_F16) {
             h[0] = __builtin_bit_cast(uint16_t, (_Float16)a);
             h[1] = __builtin_bit_cast(uint16_t, (_Float16)b);
             h[2] = __builtin_bit_cast(uint16_t, (_Float16)c);
@@ -208,8 +209,8 @@ __device__ __forceinline__ void store4(char* p, float a, float b, float c, float
 
 template <int OUT>
 __device__ __forceinline__ void store_elem(char* p, float v) {
-    if (OUT == DT_F32) *(float*)p = v;
-    else if (OUT == DT_F16) *(_Float16*)p = (_Float16)v;
+    if constexpr (OUT == DT_F32) *(float*)p = v;
+    else if constexpr (OUT == DT_F16) *(_Float16*)p = (_Float16)v;
     else *(__bf16*)p = (__bf16)v;
 }
 
@@ -346,18 +347,21 @@ void gemm_kernel(GemmArgs p) {
             for (int i = 0; i < T::FM; ++i)
 #pragma unroll
                 for (int j = 0; j < T::FN; ++j) {
-                    if (IN == DT_F16) {
+                    if constexpr (IN == DT_F16) {
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
                             __builtin_bit_cast(f16x8, bf[j]), __builtin_bit_cast(f16x8, af[i]), acc[i][j], 0, 0, 0);
-                    } else if (IN == DT_BF16) {
+                    } else if constexpr (IN == DT_BF16) {
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                             __builtin_bit_cast(bf16x8, bf[j]), __builtin_bit_cast(bf16x8, af[i]), acc[i][j], 0, 0, 0);
                     } else {
+                        // Bit-cast whole vectors, then index: a bit-cast of a
+                        // single ext-vector element is lowered as a cast of
+                        // element 0 by this compiler.
+                        const f32x4 bv = __builtin_bit_cast(f32x4, bf[j]);
+                        const f32x4 av = __builtin_bit_cast(f32x4, af[i]);
 #pragma unroll
                         for (int s = 0; s < 4; ++s)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                                __builtin_bit_cast(float, bf[j][s]), __builtin_bit_cast(float, af[i][s]),
-                                acc[i][j], 0, 0, 0);
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(bv[s], av[s], acc[i][j], 0, 0, 0);
                     }
                 }
         }
