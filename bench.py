@@ -43,6 +43,10 @@ def kernel_source_hash():
 
 
 def sclk_mhz():
+    # rocm-smi starts through an `env python3` shebang; under a profiler's
+    # preload that is an exec after GPU initialisation, so skip it there
+    if "rocprof" in os.environ.get("LD_PRELOAD", "") or os.environ.get("TGEMM_NO_SCLK"):
+        return None
     try:
         r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
         d = json.loads(r.stdout)
@@ -107,6 +111,9 @@ def main():
     ap.add_argument("--config", type=int, default=-1, help="force a tile configuration (gemm_ex)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-config", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one elementwise kernel that reads and writes 512 MiB "
+                         "(scale reference for the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -176,6 +183,15 @@ def main():
                 "us_p90": float(np.percentile(pev, 90)) * 1e3, "us_per_call_wall": pms * 1e3,
                 "tflops": pf / (med * 1e-3) / 1e12, "frac_of_mfma_peak": pf / (med * 1e-3) / 1e12 / peak,
                 "gbs": algo_bytes / (med * 1e-3) / 1e9})
+
+    if args.calibrate_copy:
+        src = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print("[bench] calibration: neg over 512 MiB in, 512 MiB out", file=sys.stderr, flush=True)
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -59,6 +59,8 @@ struct GemmArgs {
     int tiles_m, tiles_n;
     int group_m;            // tile rows per raster group
     int swz_mask;           // CPR-1: XOR-swizzled LDS; 0: plain row-major LDS
+    int vec_ab;             // GENERAL kernels: A, B 16-byte aligned, lda, ldb whole chunks
+    int vec_c;              // GENERAL kernels: C rows allow 4-element vector stores
 };
 
 // Compile-time tile configuration.
@@ -97,6 +99,7 @@ struct TileCfg {
     static_assert(THREADS % CPR == 0, "");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile of whole MFMA blocks");
     static_assert(BK % KG == 0, "");
+    static_assert(NKG >= 2 && NKG % 2 == 0, "fragment buffers alternate over an even number of k-groups");
     static_assert(LDS_BYTES <= 160 * 1024, "gfx950 LDS is 160 KiB per CU");
 };
 
@@ -133,6 +136,25 @@ __device__ __forceinline__ int swizzle_key(int row) {
 }
 
 // ---------------------------------------------------------------- helpers
+template <bool B>
+struct BoolTag {
+    static constexpr bool value = B;
+};
+template <int I>
+struct IntTag {
+    static constexpr int value = I;
+};
+
+// f(IntTag<i>{}) for i = B .. E-1, expanded at compile time (register
+// arrays are then only ever indexed by constants).
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(IntTag<B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
 __device__ __forceinline__ u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
 
 // One 16-byte chunk holding VE consecutive elements starting at `p`, of which
@@ -156,53 +178,51 @@ __device__ __forceinline__ u32x4 load_chunk_partial(const char* p, int valid) {
     return v;
 }
 
-// Transpose of a VE x VE block held as VE chunks (rows) into VE chunks
-// (columns).  16-bit elements: 32 v_perm_b32; 32-bit elements: renaming only.
+// Column e of a VE x VE block held as VE chunks (rows), as one chunk: the
+// block's transpose, one row at a time.  16-bit elements: 4 v_perm_b32
+// (dword q = (row 2q, col e) | (row 2q+1, col e) << 16); 32-bit elements:
+// renaming only.
 template <int EB>
-__device__ __forceinline__ void transpose_block(const u32x4 (&in)[16 / EB], u32x4 (&out)[16 / EB]) {
+__device__ __forceinline__ u32x4 transpose_col(const u32x4 (&in)[16 / EB], int e) {
+    u32x4 out;
     if constexpr (EB == 4) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) out[e][q] = in[q][e];
+        for (int q = 0; q < 4; ++q) out[q] = in[q][e];
     } else {
-        // column e, dword q = (row 2q, col e) | (row 2q+1, col e) << 16
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                out[e][q] = __builtin_amdgcn_perm(in[2 * q + 1][e >> 1], in[2 * q][e >> 1],
-                                                  (e & 1) ? 0x07060302u : 0x05040100u);
+        for (int q = 0; q < 4; ++q) out[q] = __builtin_amdgcn_perm(in[2 * q + 1][e >> 1], in[2 * q][e >> 1], sel);
     }
+    return out;
 }
 
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Four consecutive outputs; fp32 -> fp16 / bf16 rounds to nearest even.
 template <int OUT>
 __device__ __forceinline__ void store4(char* p, float a, float b, float c, float d, bool vec) {
     if constexpr (OUT == DT_F32) {
         if (vec) {
-            *(u32x4*)p = u32x4{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
-                               __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d)};
+            *(f32x4*)p = f32x4{a, b, c, d};
         } else {
             ((float*)p)[0] = a; ((float*)p)[1] = b; ((float*)p)[2] = c; ((float*)p)[3] = d;
         }
     } else {
-        uint16_t h[4];
+        uint32_t lo, hi;
         if constexpr (OUT == DT_F16) {
-            h[0] = __builtin_bit_cast(uint16_t, (_Float16)a);
-            h[1] = __builtin_bit_cast(uint16_t, (_Float16)b);
-            h[2] = __builtin_bit_cast(uint16_t, (_Float16)c);
-            h[3] = __builtin_bit_cast(uint16_t, (_Float16)d);
+            lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
+            hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{c, d}, f16x2));
         } else {
-            h[0] = __builtin_bit_cast(uint16_t, (__bf16)a);
-            h[1] = __builtin_bit_cast(uint16_t, (__bf16)b);
-            h[2] = __builtin_bit_cast(uint16_t, (__bf16)c);
-            h[3] = __builtin_bit_cast(uint16_t, (__bf16)d);
+            lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+            hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{c, d}, bf16x2));
         }
         if (vec) {
-            *(u32x2*)p = u32x2{h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16)};
+            *(u32x2*)p = u32x2{lo, hi};
         } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ((uint16_t*)p)[e] = h[e];
+            ((uint16_t*)p)[0] = (uint16_t)lo; ((uint16_t*)p)[1] = (uint16_t)(lo >> 16);
+            ((uint16_t*)p)[2] = (uint16_t)hi; ((uint16_t*)p)[3] = (uint16_t)(hi >> 16);
         }
     }
 }
@@ -215,11 +235,13 @@ __device__ __forceinline__ void store_elem(char* p, float v) {
 }
 
 // ---------------------------------------------------------------- kernel
-// IN: input type, OUT: output type.  ALIGNED: A, B, C 16-byte aligned and
-// lda, ldb multiples of a 16-byte chunk, ldc a multiple of 4 elements (then
-// whole chunks are loaded and 4-element groups stored with vector
-// instructions; otherwise every access is element-wise).
-template <class T, int IN, int OUT, bool ALIGNED>
+// IN: input type, OUT: output type.
+// FAST: every tile is whole (M % BM == 0, N % BN == 0) and A, B, C are
+// 16-byte aligned with lda, ldb whole 16-byte chunks and ldc a multiple of 4:
+// the main loop has no bounds checks (only a ragged last K step is masked).
+// Otherwise (GENERAL) every load and store is checked; 16-byte accesses are
+// still used where p.vec_ab / p.vec_c allow them.
+template <class T, int IN, int OUT, bool FAST>
 __global__ __attribute__((amdgpu_flat_work_group_size(T::THREADS, T::THREADS),
                           amdgpu_waves_per_eu(T::OCC * T::WAVES / 4 > 0 ? T::OCC * T::WAVES / 4 : 1)))
 void gemm_kernel(GemmArgs p) {
@@ -236,8 +258,8 @@ void gemm_kernel(GemmArgs p) {
     tile_of(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
     const int m0 = tm * T::BM, n0 = tn * T::BN;
     const int M = p.M, N = p.N, K = p.K;
-    const bool interior = (m0 + T::BM <= M) && (n0 + T::BN <= N);
     const int swz = p.swz_mask;
+    const bool vec_ab = FAST || p.vec_ab;
 
     // a2: per-thread load assignment
     // A chunk i: row tid/CPR + i*(THREADS/CPR), chunk tid%CPR
@@ -250,68 +272,87 @@ void gemm_kernel(GemmArgs p) {
     u32x4 ra[T::A_CHUNKS];
     u32x4 rb[T::B_BLOCKS][VE];
 
-    auto load_step = [&](int k0, bool check) {
+    // a2: global -> registers, one 16-byte chunk per call: w < A_CHUNKS is
+    // chunk w of this thread's A rows, otherwise row (w - A_CHUNKS) % VE of B
+    // block (w - A_CHUNKS) / VE, for the K step starting at k0.
+    // Without CHECK (FAST kernels, full K steps) it is one buffer_load_dwordx4
+    // whose resource starts at the tile's corner at k0 (a few scalar adds per
+    // step), with one per-lane offset per operand and the chunk's row step as
+    // the scalar offset; the host guarantees that these offsets fit in 31
+    // bits.  With CHECK the chunk is tested against M / N / K and zero-filled
+    // outside, through plain global loads.
+    const int a_voff = (int)(((int64_t)a_row0 * lda + a_c * VE) * EB);
+    int b_voff[T::B_BLOCKS];
 #pragma unroll
-        for (int i = 0; i < T::A_CHUNKS; ++i) {
-            const int r = a_row0 + i * (T::THREADS / CPR);
-            const int gm = m0 + r, gk = k0 + a_c * VE;
-            const char* src = Ab + ((int64_t)gm * lda + gk) * EB;
-            if (!check && ALIGNED) {
-                ra[i] = *(const u32x4*)src;
+    for (int i = 0; i < T::B_BLOCKS; ++i) {
+        const int idx = tid + i * T::THREADS;
+        const int kb = idx % T::KBN, nb = idx / T::KBN;
+        b_voff[i] = (int)(((int64_t)kb * VE * ldb + nb * VE) * EB);
+    }
+    auto rsrc_a = [&](int k0) {
+        return __builtin_amdgcn_make_buffer_rsrc((void*)(Ab + ((int64_t)m0 * lda + k0) * EB), (short)0, -1,
+                                                 0x00020000);
+    };
+    auto rsrc_b = [&](int k0) {
+        return __builtin_amdgcn_make_buffer_rsrc((void*)(Bb + ((int64_t)k0 * ldb + n0) * EB), (short)0, -1,
+                                                 0x00020000);
+    };
+    auto load_one = [&](auto check_tag, int k0, int w) {
+        constexpr bool CHECK = decltype(check_tag)::value || !FAST;
+        if (w < T::A_CHUNKS) {
+            if constexpr (!CHECK) {
+                const int soff = (int)((int64_t)w * (T::THREADS / CPR) * lda * EB);
+                ra[w] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc_a(k0), a_voff, soff, 0));
             } else {
+                const int r = a_row0 + w * (T::THREADS / CPR);
+                const int gm = m0 + r, gk = k0 + a_c * VE;
+                const char* src = Ab + ((int64_t)gm * lda + gk) * EB;
                 const int valid = gm < M ? (K - gk < VE ? K - gk : VE) : 0;
-                if (ALIGNED && valid == VE) ra[i] = *(const u32x4*)src;
-                else ra[i] = valid > 0 ? load_chunk_partial<EB>(src, valid) : zero4();
+                if (vec_ab && valid == VE) ra[w] = *(const u32x4*)src;
+                else ra[w] = valid > 0 ? load_chunk_partial<EB>(src, valid) : zero4();
             }
-        }
-#pragma unroll
-        for (int i = 0; i < T::B_BLOCKS; ++i) {
+        } else {
+            const int i = (w - T::A_CHUNKS) / VE, j = (w - T::A_CHUNKS) % VE;
             const int idx = tid + i * T::THREADS;
             const bool live = (T::B_TOTAL % T::THREADS == 0) || idx < T::B_TOTAL;
-            const int kb = idx % T::KBN, nb = idx / T::KBN;
-            const int gn = n0 + nb * VE;
-#pragma unroll
-            for (int j = 0; j < VE; ++j) {
+            if constexpr (!CHECK) {
+                const int soff = (int)((int64_t)j * ldb * EB);
+                const u32x4 v =
+                    __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc_b(k0), b_voff[i], soff, 0));
+                rb[i][j] = live ? v : zero4();
+            } else {
+                const int kb = idx % T::KBN, nb = idx / T::KBN;
+                const int gn = n0 + nb * VE;
                 const int gk = k0 + kb * VE + j;
                 const char* src = Bb + ((int64_t)gk * ldb + gn) * EB;
-                if (!live) {
-                    rb[i][j] = zero4();
-                } else if (!check && ALIGNED) {
-                    rb[i][j] = *(const u32x4*)src;
-                } else {
-                    const int valid = gk < K ? (N - gn < VE ? N - gn : VE) : 0;
-                    if (ALIGNED && valid == VE) rb[i][j] = *(const u32x4*)src;
-                    else rb[i][j] = valid > 0 ? load_chunk_partial<EB>(src, valid) : zero4();
-                }
+                const int valid = (live && gk < K) ? (N - gn < VE ? N - gn : VE) : 0;
+                if (vec_ab && valid == VE) rb[i][j] = *(const u32x4*)src;
+                else rb[i][j] = valid > 0 ? load_chunk_partial<EB>(src, valid) : zero4();
             }
         }
     };
+    constexpr int NLOAD = T::A_CHUNKS + T::B_BLOCKS * VE;
 
-    auto store_step = [&](int stage) {
+    // a2/a3: registers -> swizzled LDS stage.  A chunk w as loaded; B column
+    // w % VE of block w / VE, transposed to a k-contiguous row on the way.
+    auto store_a_one = [&](int stage, int w) {
         char* As = smem + stage * T::STAGE_BYTES;
-        char* Bs = As + T::A_BYTES;
-#pragma unroll
-        for (int i = 0; i < T::A_CHUNKS; ++i) {
-            const int r = a_row0 + i * (T::THREADS / CPR);
-            const int pc = a_c ^ (swizzle_key<CPR>(r) & swz);
-            *(u32x4*)(As + r * RB + pc * 16) = ra[i];
-        }
-#pragma unroll
-        for (int i = 0; i < T::B_BLOCKS; ++i) {
-            const int idx = tid + i * T::THREADS;
-            if ((T::B_TOTAL % T::THREADS == 0) || idx < T::B_TOTAL) {
-                const int kb = idx % T::KBN, nb = idx / T::KBN;
-                u32x4 cols[VE];
-                transpose_block<EB>(rb[i], cols);
-#pragma unroll
-                for (int e = 0; e < VE; ++e) {
-                    const int n = nb * VE + e;
-                    const int pc = kb ^ (swizzle_key<CPR>(n) & swz);
-                    *(u32x4*)(Bs + n * RB + pc * 16) = cols[e];
-                }
-            }
+        const int r = a_row0 + w * (T::THREADS / CPR);
+        const int pc = a_c ^ (swizzle_key<CPR>(r) & swz);
+        *(u32x4*)(As + r * RB + pc * 16) = ra[w];
+    };
+    auto store_b_one = [&](int stage, int w) {
+        char* Bs = smem + stage * T::STAGE_BYTES + T::A_BYTES;
+        const int i = w / VE, e = w % VE;
+        const int idx = tid + i * T::THREADS;
+        if ((T::B_TOTAL % T::THREADS == 0) || idx < T::B_TOTAL) {
+            const int kb = idx % T::KBN, nb = idx / T::KBN;
+            const int n = nb * VE + e;
+            const int pc = kb ^ (swizzle_key<CPR>(n) & swz);
+            *(u32x4*)(Bs + n * RB + pc * 16) = transpose_col<EB>(rb[i], e);
         }
     };
+    constexpr int NSA = T::A_CHUNKS, NSB = T::B_BLOCKS * VE;
 
     // a6: accumulators
     f32x16 acc[T::FM][T::FN];
@@ -322,99 +363,173 @@ void gemm_kernel(GemmArgs p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    // fragment addressing: row (lane & 31) of each 32-row block, chunk 2g + lane/32
+    // a5: fragments.  Lane l reads row (l & 31) of each 32-row block at
+    // chunk 2g + l/32 of k-group g; the swizzle key of a fragment row depends
+    // only on the lane (block starts are multiples of 32).
     const int frow = lane & 31, fhalf = lane >> 5;
     const int a_frow0 = wm * T::WTM + frow;
     const int b_frow0 = wn * T::WTN + frow;
-    // the swizzle key of a fragment row depends only on the lane: block
-    // starts are multiples of 32
     const int fkey_a = swizzle_key<CPR>(a_frow0) & swz;
     const int fkey_b = swizzle_key<CPR>(b_frow0) & swz;
+    u32x4 fa[2][T::FM], fb[2][T::FN];
+    constexpr int NREAD = T::FM + T::FN;
 
-    auto compute_step = [&](int stage) {
+    auto read_frag = [&](int stage, int g, int buf, int r) {
         const char* As = smem + stage * T::STAGE_BYTES;
         const char* Bs = As + T::A_BYTES;
-#pragma unroll
-        for (int g = 0; g < T::NKG; ++g) {
-            u32x4 af[T::FM], bf[T::FN];
+        if (r < T::FM) {
             const int ca = ((2 * g + fhalf) ^ fkey_a) * 16;
+            fa[buf][r] = *(const u32x4*)(As + (a_frow0 + 32 * r) * RB + ca);
+        } else {
             const int cb = ((2 * g + fhalf) ^ fkey_b) * 16;
-#pragma unroll
-            for (int i = 0; i < T::FM; ++i) af[i] = *(const u32x4*)(As + (a_frow0 + 32 * i) * RB + ca);
-#pragma unroll
-            for (int j = 0; j < T::FN; ++j) bf[j] = *(const u32x4*)(Bs + (b_frow0 + 32 * j) * RB + cb);
-#pragma unroll
-            for (int i = 0; i < T::FM; ++i)
-#pragma unroll
-                for (int j = 0; j < T::FN; ++j) {
-                    if constexpr (IN == DT_F16) {
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                            __builtin_bit_cast(f16x8, bf[j]), __builtin_bit_cast(f16x8, af[i]), acc[i][j], 0, 0, 0);
-                    } else if constexpr (IN == DT_BF16) {
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            __builtin_bit_cast(bf16x8, bf[j]), __builtin_bit_cast(bf16x8, af[i]), acc[i][j], 0, 0, 0);
-                    } else {
-                        // Bit-cast whole vectors, then index: a bit-cast of a
-                        // single ext-vector element is lowered as a cast of
-                        // element 0 by this compiler.
-                        const f32x4 bv = __builtin_bit_cast(f32x4, bf[j]);
-                        const f32x4 av = __builtin_bit_cast(f32x4, af[i]);
-#pragma unroll
-                        for (int s = 0; s < 4; ++s)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(bv[s], av[s], acc[i][j], 0, 0, 0);
-                    }
-                }
+            fb[buf][r - T::FM] = *(const u32x4*)(Bs + (b_frow0 + 32 * (r - T::FM)) * RB + cb);
         }
     };
 
-    // a4: pipeline
-    const int nk = (K + T::BK - 1) / T::BK;
-    const int kfull = K / T::BK;  // steps with no K tail
-    if (nk > 0) {
-        load_step(0, !interior || 0 >= kfull);
-        store_step(0);
-        if (nk > 1) load_step(T::BK, !interior || 1 >= kfull);
-        __syncthreads();
-        for (int kt = 0; kt < nk; ++kt) {
-            compute_step(kt & 1);
-            if (kt + 1 < nk) {
-                store_step((kt + 1) & 1);
-                if (kt + 2 < nk) load_step((kt + 2) * T::BK, !interior || kt + 2 >= kfull);
-            }
-            __syncthreads();
+    constexpr int NMF = T::FM * T::FN;
+    auto mfma_one = [&](int buf, int m) {
+        const int i = m / T::FN, j = m % T::FN;
+        if constexpr (IN == DT_F16) {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                __builtin_bit_cast(f16x8, fb[buf][j]), __builtin_bit_cast(f16x8, fa[buf][i]), acc[i][j], 0, 0, 0);
+        } else if constexpr (IN == DT_BF16) {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, fb[buf][j]), __builtin_bit_cast(bf16x8, fa[buf][i]), acc[i][j], 0, 0,
+                0);
+        } else {
+            // Bit-cast whole vectors, then index: a bit-cast of a single
+            // ext-vector element is lowered as a cast of element 0 by this
+            // compiler.
+            const f32x4 bv = __builtin_bit_cast(f32x4, fb[buf][j]);
+            const f32x4 av = __builtin_bit_cast(f32x4, fa[buf][i]);
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(bv[s], av[s], acc[i][j], 0, 0, 0);
         }
-    }
+    };
+
+    // a4: one pipelined K step.  On entry LDS stage `cur` holds this step,
+    // the fragments of k-group 0 are in buffer 0 and, with STORE, ra/rb hold
+    // the next step.  k-group g issues its NMF MFMAs one by one; between them
+    // go, spread evenly, the reads of the fragments of group g+1 and: in
+    // group 0 the LDS writes of A of the next step followed (with LOAD) by
+    // the global loads of A of the step after, in group 1 the same for B.
+    // Each load thus has almost a whole K step to arrive before its register
+    // is written to LDS again.  The barrier comes before the last group, whose
+    // MFMAs overlap the reads of the next step's first fragments.
+    // sched_barrier fences keep this order.
+    auto kstep = [&](auto check_tag, auto store_tag, auto load_tag, int cur, int k_load) {
+        constexpr bool STORE = decltype(store_tag)::value;
+        constexpr bool LOAD = decltype(load_tag)::value;
+        constexpr int NKG = T::NKG;
+        constexpr int G_B = NKG - 2 < 1 ? NKG - 2 : 1;
+        constexpr int NLA = T::A_CHUNKS, NLB = T::B_BLOCKS * VE;
+        const int nxt = cur ^ 1;
+        static_for<0, NKG>([&](auto gt) {
+            constexpr int g = decltype(gt)::value;
+            constexpr bool last = g == NKG - 1;
+            if constexpr (last) __syncthreads();
+            // work items of this group, in issue order
+            constexpr int n_read = last ? (STORE ? NREAD : 0) : NREAD;
+            constexpr bool do_a = STORE && g == 0 && !last;
+            constexpr bool do_b = STORE && g == G_B && !last;
+            constexpr int n_sa = do_a ? NSA : 0;
+            constexpr int n_la = (do_a && LOAD) ? NLA : 0;
+            constexpr int n_sb = do_b ? NSB : 0;
+            constexpr int n_lb = (do_b && LOAD) ? NLB : 0;
+            constexpr int n_work = n_read + n_sa + n_la + n_sb + n_lb;
+            static_for<0, NMF>([&](auto mt) {
+                constexpr int m = decltype(mt)::value;
+                mfma_one(g & 1, m);
+                // items [ceil(m n / NMF), ceil((m+1) n / NMF)) follow MFMA m
+                constexpr int wb = (m * n_work + NMF - 1) / NMF;
+                constexpr int we = ((m + 1) * n_work + NMF - 1) / NMF;
+                static_for<wb, we>([&](auto wt) {
+                    constexpr int w = decltype(wt)::value;
+                    if constexpr (w < n_read) {
+                        if constexpr (last) read_frag(nxt, 0, 0, w);
+                        else read_frag(cur, g + 1, (g + 1) & 1, w);
+                    } else if constexpr (w < n_read + n_sa) {
+                        store_a_one(nxt, w - n_read);
+                    } else if constexpr (w < n_read + n_sa + n_la) {
+                        load_one(check_tag, k_load, w - n_read - n_sa);
+                    } else if constexpr (w < n_read + n_sa + n_la + n_sb) {
+                        store_b_one(nxt, w - n_read - n_sa - n_la);
+                    } else {
+                        load_one(check_tag, k_load, NLA + (w - n_read - n_sa - n_la - n_sb));
+                    }
+                });
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        });
+    };
+
+    auto run = [&](auto check_tag) {
+        constexpr BoolTag<true> yes{};
+        constexpr BoolTag<false> no{};
+        const int nkf = K / T::BK;  // full K steps
+        auto fill = [&](auto ctag, int k0, int stage) {
+            static_for<0, NLOAD>([&](auto w) { load_one(ctag, k0, decltype(w)::value); });
+            static_for<0, NSA>([&](auto w) { store_a_one(stage, decltype(w)::value); });
+            static_for<0, NSB>([&](auto w) { store_b_one(stage, decltype(w)::value); });
+        };
+        auto read_all = [&](int stage) {
+            static_for<0, NREAD>([&](auto r) { read_frag(stage, 0, 0, decltype(r)::value); });
+        };
+        if (nkf > 0) {
+            fill(check_tag, 0, 0);
+            if (nkf > 1) static_for<0, NLOAD>([&](auto w) { load_one(check_tag, T::BK, decltype(w)::value); });
+            __syncthreads();
+            read_all(0);
+            int kt = 0;
+            for (; kt + 2 < nkf; ++kt) kstep(check_tag, yes, yes, kt & 1, (kt + 2) * T::BK);
+            if (kt + 1 < nkf) {
+                kstep(check_tag, yes, no, kt & 1, 0);
+                ++kt;
+            }
+            kstep(check_tag, no, no, kt & 1, 0);
+        }
+        if (K % T::BK) {
+            // the ragged last K step, zero-filled beyond K, not overlapped
+            const int st = nkf & 1;
+            fill(yes, nkf * T::BK, st);
+            __syncthreads();
+            read_all(st);
+            kstep(yes, no, no, st, 0);
+        }
+    };
+    run(BoolTag<!FAST>{});
 
     // a7: epilogue.  acc[i][j][4q + e] = C[row][col + e] with
-    // row = m0 + wm*WTM + 32 i + lane%32, col = n0 + wn*WTN + 32 j + 8 q + 4 (lane/32)
+    // row = m0 + wm*WTM + 32 i + lane%32, col = n0 + wn*WTN + 32 j + 8 q + 4 (lane/32).
+    // One 32x32 block at a time (fenced), so that only one block's values are
+    // moved out of the accumulator registers at once.
     constexpr int OB = OUT == DT_F32 ? 4 : 2;
     const int64_t ldc = p.ldc;
-#pragma unroll
-    for (int i = 0; i < T::FM; ++i) {
+    static_for<0, T::FM * T::FN>([&](auto bt) {
+        constexpr int i = decltype(bt)::value / T::FN, j = decltype(bt)::value % T::FN;
         const int row = m0 + a_frow0 + 32 * i;
-#pragma unroll
-        for (int j = 0; j < T::FN; ++j) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int col = n0 + wn * T::WTN + 32 * j + 8 * q + 4 * fhalf;
-                char* dst = p.C + ((int64_t)row * ldc + col) * OB;
-                const float v0 = acc[i][j][4 * q + 0], v1 = acc[i][j][4 * q + 1];
-                const float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
-                if (interior && ALIGNED) {
+        static_for<0, 4>([&](auto qt) {
+            constexpr int q = decltype(qt)::value;
+            const int col = n0 + wn * T::WTN + 32 * j + 8 * q + 4 * fhalf;
+            char* dst = p.C + ((int64_t)row * ldc + col) * OB;
+            const float v0 = acc[i][j][4 * q + 0], v1 = acc[i][j][4 * q + 1];
+            const float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
+            if constexpr (FAST) {
+                store4<OUT>(dst, v0, v1, v2, v3, true);
+            } else if (row < M) {
+                if (p.vec_c && col + 4 <= N) {
                     store4<OUT>(dst, v0, v1, v2, v3, true);
-                } else if (row < M) {
-                    if (ALIGNED && col + 4 <= N) {
-                        store4<OUT>(dst, v0, v1, v2, v3, true);
-                    } else {
-                        if (col + 0 < N) store_elem<OUT>(dst + 0 * OB, v0);
-                        if (col + 1 < N) store_elem<OUT>(dst + 1 * OB, v1);
-                        if (col + 2 < N) store_elem<OUT>(dst + 2 * OB, v2);
-                        if (col + 3 < N) store_elem<OUT>(dst + 3 * OB, v3);
-                    }
+                } else {
+                    if (col + 0 < N) store_elem<OUT>(dst + 0 * OB, v0);
+                    if (col + 1 < N) store_elem<OUT>(dst + 1 * OB, v1);
+                    if (col + 2 < N) store_elem<OUT>(dst + 2 * OB, v2);
+                    if (col + 3 < N) store_elem<OUT>(dst + 3 * OB, v3);
                 }
             }
-        }
-    }
+        });
+        __builtin_amdgcn_sched_barrier(0);
+    });
 }
 
 }  // namespace tgemm

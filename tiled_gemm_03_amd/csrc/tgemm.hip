@@ -30,31 +30,31 @@ struct ConfigEntry {
     const char* name;
     int in_family;  // TGEMM_F16 (serves F16 and BF16) or TGEMM_F32
     int bm, bn, bk, wm, wn, eb, lds_bytes, threads, cpr;
-    KernelFn (*pick)(int in, int out, bool aligned);
+    KernelFn (*pick)(int in, int out, bool fast);
 };
 
 template <class T, int IN>
-KernelFn pick_out(int out, bool aligned) {
+KernelFn pick_out(int out, bool fast) {
     if (out == TGEMM_F32)
-        return aligned ? gemm_kernel<T, IN, DT_F32, true> : gemm_kernel<T, IN, DT_F32, false>;
+        return fast ? gemm_kernel<T, IN, DT_F32, true> : gemm_kernel<T, IN, DT_F32, false>;
     if (IN == DT_F16 && out == TGEMM_F16)
-        return aligned ? gemm_kernel<T, IN, DT_F16, true> : gemm_kernel<T, IN, DT_F16, false>;
+        return fast ? gemm_kernel<T, IN, DT_F16, true> : gemm_kernel<T, IN, DT_F16, false>;
     if (IN == DT_BF16 && out == TGEMM_BF16)
-        return aligned ? gemm_kernel<T, IN, DT_BF16, true> : gemm_kernel<T, IN, DT_BF16, false>;
+        return fast ? gemm_kernel<T, IN, DT_BF16, true> : gemm_kernel<T, IN, DT_BF16, false>;
     return nullptr;
 }
 
 template <class T>
-KernelFn pick_half(int in, int out, bool aligned) {
-    if (in == TGEMM_F16) return pick_out<T, DT_F16>(out, aligned);
-    if (in == TGEMM_BF16) return pick_out<T, DT_BF16>(out, aligned);
+KernelFn pick_half(int in, int out, bool fast) {
+    if (in == TGEMM_F16) return pick_out<T, DT_F16>(out, fast);
+    if (in == TGEMM_BF16) return pick_out<T, DT_BF16>(out, fast);
     return nullptr;
 }
 
 template <class T>
-KernelFn pick_f32(int in, int out, bool aligned) {
+KernelFn pick_f32(int in, int out, bool fast) {
     if (in == TGEMM_F32 && out == TGEMM_F32)
-        return aligned ? gemm_kernel<T, DT_F32, DT_F32, true> : gemm_kernel<T, DT_F32, DT_F32, false>;
+        return fast ? gemm_kernel<T, DT_F32, DT_F32, true> : gemm_kernel<T, DT_F32, DT_F32, false>;
     return nullptr;
 }
 
@@ -123,12 +123,16 @@ int validate(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const 
     return TGEMM_OK;
 }
 
-bool is_aligned(const ConfigEntry& c, const void* A, int64_t lda, const void* B, int64_t ldb, const void* C,
-                int64_t ldc, int out) {
+// 16-byte loads of A and B need 16-byte aligned bases and leading dimensions
+// that are whole 16-byte chunks.
+bool loads_aligned(const ConfigEntry& c, const void* A, int64_t lda, const void* B, int64_t ldb) {
     const int ve = 16 / c.eb;
-    const uintptr_t oe = elem_bytes(out);
-    return ((uintptr_t)A % 16 == 0) && ((uintptr_t)B % 16 == 0) && ((uintptr_t)C % (4 * oe) == 0) &&
-           (lda % ve == 0) && (ldb % ve == 0) && (ldc % 4 == 0);
+    return ((uintptr_t)A % 16 == 0) && ((uintptr_t)B % 16 == 0) && (lda % ve == 0) && (ldb % ve == 0);
+}
+
+// 4-element stores of C need a base aligned to 4 elements and ldc % 4 == 0.
+bool stores_aligned(const void* C, int64_t ldc, int out) {
+    return ((uintptr_t)C % (4 * (uintptr_t)elem_bytes(out)) == 0) && (ldc % 4 == 0);
 }
 
 int64_t tiles_for(const ConfigEntry& c, int64_t M, int64_t N) { return ceil_div(M, c.bm) * ceil_div(N, c.bn); }
@@ -158,8 +162,14 @@ int run(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void*
     if (M == 0 || N == 0) return TGEMM_OK;
     const int id = config_id >= 0 ? config_id : table_choice(M, N, K, in);
     const ConfigEntry& c = kConfigs[id];
-    const bool aligned = is_aligned(c, A, lda, B, ldb, C, ldc, out);
-    KernelFn fn = c.pick(in, out, aligned);
+    const bool vec_ab = loads_aligned(c, A, lda, B, ldb);
+    const bool vec_c = stores_aligned(C, ldc, out);
+    // FAST kernels address A and B through 32-bit buffer offsets within a
+    // tile's rows (A) or one K step's rows (B)
+    const bool offsets_fit = (int64_t)c.bm * lda * c.eb + K * c.eb < (1LL << 31) &&
+                             (int64_t)c.bk * ldb * c.eb + N * c.eb < (1LL << 31);
+    const bool fast = vec_ab && vec_c && offsets_fit && M % c.bm == 0 && N % c.bn == 0;
+    KernelFn fn = c.pick(in, out, fast);
     if (fn == nullptr) return TGEMM_ERR_DTYPE;
 
     GemmArgs args;
@@ -176,6 +186,8 @@ int run(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void*
     args.tiles_n = (int)ceil_div(N, c.bn);
     args.group_m = tuning().group_m;
     args.swz_mask = tuning().swizzle ? c.cpr - 1 : 0;
+    args.vec_ab = vec_ab;
+    args.vec_c = vec_c;
     const int64_t grid = (int64_t)args.tiles_m * args.tiles_n;
     if (grid > 0x7fffffff) return TGEMM_ERR_DIM;
 
