@@ -6,6 +6,7 @@
 #include <stdlib.h>
 
 #include "gemm_kernel.hpp"
+#include "gemm_kernel_dl.hpp"
 #include "tgemm.h"
 
 using namespace tgemm;
@@ -31,7 +32,21 @@ struct ConfigEntry {
     int in_family;  // TGEMM_F16 (serves F16 and BF16) or TGEMM_F32
     int bm, bn, bk, wm, wn, eb, lds_bytes, threads, cpr;
     KernelFn (*pick)(int in, int out, bool fast);
+    // direct-to-LDS kernel of the same tile, for whole tiles and K % bk == 0
+    KernelFn (*pick_dl)(int in, int out);
 };
+
+template <class D>
+KernelFn pick_dl(int in, int out) {
+    if (in == TGEMM_F16 && out == TGEMM_F16) return gemm_kernel_dl<D, DT_F16, DT_F16>;
+    if (in == TGEMM_F16 && out == TGEMM_F32) return gemm_kernel_dl<D, DT_F16, DT_F32>;
+    if (in == TGEMM_BF16 && out == TGEMM_BF16) return gemm_kernel_dl<D, DT_BF16, DT_BF16>;
+    if (in == TGEMM_BF16 && out == TGEMM_F32) return gemm_kernel_dl<D, DT_BF16, DT_F32>;
+    return nullptr;
+}
+using DlBig = DlCfg<256, 256, 64, 2, 2>;
+using DlMid = DlCfg<128, 128, 64, 2, 2>;
+static_assert(DlBig::LDS_BYTES == CfgBig::LDS_BYTES && DlMid::LDS_BYTES == CfgMid::LDS_BYTES, "");
 
 template <class T, int IN>
 KernelFn pick_out(int out, bool fast) {
@@ -58,16 +73,16 @@ KernelFn pick_f32(int in, int out, bool fast) {
     return nullptr;
 }
 
-#define ENTRY(name, fam, T, pk) \
-    {name, fam, T::BM, T::BN, T::BK, T::WM, T::WN, T::EB, T::LDS_BYTES, T::THREADS, T::CPR, pk<T>}
+#define ENTRY(name, fam, T, pk, dl) \
+    {name, fam, T::BM, T::BN, T::BK, T::WM, T::WN, T::EB, T::LDS_BYTES, T::THREADS, T::CPR, pk<T>, dl}
 
 const ConfigEntry kConfigs[] = {
-    ENTRY("h256x256x64_w2x2", TGEMM_F16, CfgBig, pick_half),
-    ENTRY("h128x128x64_w2x2", TGEMM_F16, CfgMid, pick_half),
-    ENTRY("h64x64x64_w2x2", TGEMM_F16, CfgSmall, pick_half),
-    ENTRY("h32x32x64_w1x1", TGEMM_F16, CfgTiny, pick_half),
-    ENTRY("s64x64x32_w2x2", TGEMM_F32, CfgF32Mid, pick_f32),
-    ENTRY("s32x32x32_w1x1", TGEMM_F32, CfgF32Tiny, pick_f32),
+    ENTRY("h256x256x64_w2x2", TGEMM_F16, CfgBig, pick_half, pick_dl<DlBig>),
+    ENTRY("h128x128x64_w2x2", TGEMM_F16, CfgMid, pick_half, pick_dl<DlMid>),
+    ENTRY("h64x64x64_w2x2", TGEMM_F16, CfgSmall, pick_half, nullptr),
+    ENTRY("h32x32x64_w1x1", TGEMM_F16, CfgTiny, pick_half, nullptr),
+    ENTRY("s64x64x32_w2x2", TGEMM_F32, CfgF32Mid, pick_f32, nullptr),
+    ENTRY("s32x32x32_w1x1", TGEMM_F32, CfgF32Tiny, pick_f32, nullptr),
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 enum { CFG_BIG = 0, CFG_MID = 1, CFG_SMALL = 2, CFG_TINY = 3, CFG_F32_MID = 4, CFG_F32_TINY = 5 };
@@ -75,15 +90,18 @@ enum { CFG_BIG = 0, CFG_MID = 1, CFG_SMALL = 2, CFG_TINY = 3, CFG_F32_MID = 4, C
 // Measurement-only switches, read once from the environment:
 //   TGEMM_GROUP_M=<n>    tile rows per raster group (default 4)
 //   TGEMM_NO_SWIZZLE=1   plain row-major LDS tiles (for bank-conflict A/B runs)
+//   TGEMM_NO_DL=1        register-staged loads instead of direct-to-LDS ones
 struct Tuning {
     int group_m = 4;
     bool swizzle = true;
+    bool direct_lds = true;
     Tuning() {
         if (const char* s = getenv("TGEMM_GROUP_M")) {
             const int g = atoi(s);
             if (g > 0) group_m = g;
         }
         if (const char* s = getenv("TGEMM_NO_SWIZZLE")) swizzle = !(s[0] == '1');
+        if (const char* s = getenv("TGEMM_NO_DL")) direct_lds = !(s[0] == '1');
     }
 };
 const Tuning& tuning() {
@@ -169,7 +187,8 @@ int run(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void*
     const bool offsets_fit = (int64_t)c.bm * lda * c.eb + K * c.eb < (1LL << 31) &&
                              (int64_t)c.bk * ldb * c.eb + N * c.eb < (1LL << 31);
     const bool fast = vec_ab && vec_c && offsets_fit && M % c.bm == 0 && N % c.bn == 0;
-    KernelFn fn = c.pick(in, out, fast);
+    const bool dl = fast && K % c.bk == 0 && c.pick_dl != nullptr && tuning().direct_lds;
+    KernelFn fn = dl ? c.pick_dl(in, out) : c.pick(in, out, fast);
     if (fn == nullptr) return TGEMM_ERR_DTYPE;
 
     GemmArgs args;
