@@ -25,12 +25,12 @@
 //      chunks) and the 32 lanes of a half wave (4 rows x 4 chunks) then
 //      touch 16 different 16-byte bank groups.
 //
-// Schedule of one K step (k-groups of 16 K, NKG = BK/16 of them): the MFMAs
-// of group g run while the fragments of group g+1 are read; then the wave
-// waits for its outstanding global->LDS loads (the next step), all waves
-// meet at the barrier, and the MFMAs of the last group overlap the reads of
-// the next step's first fragments and the issue of the loads of the step
-// after it into the stage just released.
+// Schedule of one K step s (k-groups of 16 K, NKG = BK/16 of them): the
+// MFMAs of group g run while the fragments of group g+1 are read; group 0
+// also issues the B loads of step s+1; then the wave waits for its
+// outstanding global->LDS loads, all waves meet at the barrier, and the MFMAs
+// of the last group overlap the reads of the next step's first fragments and
+// the A loads of step s+2 into the stage just released.
 
 #pragma once
 #include "gemm_kernel.hpp"
@@ -152,7 +152,6 @@ void gemm_kernel_dl(GemmArgs p) {
     auto issue_loads = [&](int k0, int stage) {
         static_for<0, T::A_LOADS + T::B_LOADS>([&](auto x) { issue_load(k0, stage, decltype(x)::value); });
     };
-    constexpr int NLOADS = T::A_LOADS + T::B_LOADS;
 
     // ---------------------------------------------------------- a5: fragments
     const int l32 = lane & 31, h = lane >> 5;
@@ -213,11 +212,15 @@ void gemm_kernel_dl(GemmArgs p) {
         }
     };
 
-    // one K step on LDS stage `cur`: LOAD issues the loads of step s+2 (k0 =
-    // k_load) into `cur` after the barrier; NEXT reads the next step's first
-    // fragments from the other stage.
-    auto kstep = [&](auto load_tag, auto next_tag, int cur, int k_load) {
-        constexpr bool LOAD = decltype(load_tag)::value;
+    // One K step on LDS stage `cur`.  LOAD_A: after the barrier, issue the A
+    // loads of step s+2 (k0 = k_a) into `cur`, just released.  LOAD_B: in
+    // k-group 0, issue the B loads of step s+1 (k0 = k_b) into the other
+    // stage (released at the previous barrier); splitting the loads of a step
+    // over two k-groups keeps the wave's memory queue from filling up.
+    // NEXT: read the next step's first fragments after the barrier.
+    auto kstep = [&](auto loada_tag, auto loadb_tag, auto next_tag, int cur, int k_a, int k_b) {
+        constexpr bool LOAD_A = decltype(loada_tag)::value;
+        constexpr bool LOAD_B = decltype(loadb_tag)::value;
         constexpr bool NEXT = decltype(next_tag)::value;
         constexpr int NKG = T::NKG;
         const int nxt = cur ^ 1;
@@ -229,7 +232,7 @@ void gemm_kernel_dl(GemmArgs p) {
                 __syncthreads();
             }
             constexpr int n_read = last ? (NEXT ? NREAD : 0) : NREAD;
-            constexpr int n_load = (last && LOAD) ? NLOADS : 0;
+            constexpr int n_load = (last && LOAD_A) ? T::A_LOADS : ((g == 0 && LOAD_B) ? T::B_LOADS : 0);
             constexpr int n_work = n_read + n_load;
             static_for<0, NMF>([&](auto mt) {
                 constexpr int m = decltype(mt)::value;
@@ -241,8 +244,10 @@ void gemm_kernel_dl(GemmArgs p) {
                     if constexpr (w < n_read) {
                         if constexpr (last) read_frag(nxt, 0, 0, w);
                         else read_frag(cur, g + 1, (g + 1) & 1, w);
+                    } else if constexpr (last) {
+                        issue_load(k_a, cur, w - n_read);
                     } else {
-                        issue_load(k_load, cur, w - n_read);
+                        issue_load(k_b, nxt, T::A_LOADS + (w - n_read));
                     }
                 });
                 __builtin_amdgcn_sched_barrier(0);
@@ -254,22 +259,23 @@ void gemm_kernel_dl(GemmArgs p) {
     if (nk > 0) {
         constexpr BoolTag<true> yes{};
         constexpr BoolTag<false> no{};
+        // step 0 whole, A of step 1; B of step 1 goes out in step 0's group 0
         issue_loads(0, 0);
         if (nk > 1) {
-            issue_loads(T::BK, 1);
-            wait_vmcnt<NLOADS>();
+            static_for<0, T::A_LOADS>([&](auto x) { issue_load(T::BK, 1, decltype(x)::value); });
+            wait_vmcnt<T::A_LOADS>();
         } else {
             wait_vmcnt<0>();
         }
         __syncthreads();
         static_for<0, NREAD>([&](auto r) { read_frag(0, 0, 0, decltype(r)::value); });
         int s = 0;
-        for (; s + 2 < nk; ++s) kstep(yes, yes, s & 1, (s + 2) * T::BK);
+        for (; s + 2 < nk; ++s) kstep(yes, yes, yes, s & 1, (s + 2) * T::BK, (s + 1) * T::BK);
         if (s + 1 < nk) {
-            kstep(no, yes, s & 1, 0);
+            kstep(no, yes, yes, s & 1, 0, (s + 1) * T::BK);
             ++s;
         }
-        kstep(no, no, s & 1, 0);
+        kstep(no, no, no, s & 1, 0, 0);
     }
 
     // a7: epilogue (accumulator holds C transposed: lane owns 4 consecutive
