@@ -30,7 +30,7 @@ sys.path.insert(0, ROOT)
 PEAK_F16_TFLOPS = 2516.6   # 256 CU x 4096 FLOP/clk x 2.4 GHz, dense
 PEAK_F32_TFLOPS = 157.3    # dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCES = ["tiled_gemm_03_amd/csrc/gemm_kernel.hpp", "tiled_gemm_03_amd/csrc/gemm_kernel_dl.hpp",
+KERNEL_SOURCES = ["tiled_gemm_03_amd/csrc/gemm_kernel.hpp", "tiled_gemm_03_amd/csrc/gemm_kernel_ring.hpp",
                   "tiled_gemm_03_amd/csrc/tgemm.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_f16_8192x8192x8192.json")
 

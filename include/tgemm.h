@@ -125,6 +125,22 @@ int gemm_select_config(int64_t M, int64_t N, int64_t K,
                        const void* A, int64_t lda, const void* B, int64_t ldb,
                        const void* C, int64_t ldc, int in_dtype, int out_dtype);
 
+/* Kernels a call can run (gemm_select_kernel). */
+#define TGEMM_KERNEL_GENERAL 0 /* register-staged, every access checked (ragged or unaligned) */
+#define TGEMM_KERNEL_TILED 1   /* register-staged, whole tiles, aligned operands              */
+#define TGEMM_KERNEL_RING 2    /* direct-to-LDS rings: whole tiles of 16-bit inputs, aligned,
+                                  K a multiple of 128 (configurations 0 and 1)             */
+
+/* Host-side lookup only (no GPU call): which kernel gemm_ex(..., config_id)
+ * would launch for these arguments (config_id -1: the table's choice), as a
+ * TGEMM_KERNEL_* value, or a negative TGEMM_ERR_* if the call would be
+ * rejected.  All kernels of a configuration compute the same tile; this
+ * exists so that tests and measurements can tell which one ran.  Pointers
+ * are only inspected for their alignment. */
+int gemm_select_kernel(int64_t M, int64_t N, int64_t K,
+                       const void* A, int64_t lda, const void* B, int64_t ldb,
+                       const void* C, int64_t ldc, int in_dtype, int out_dtype, int config_id);
+
 /* Host-side copy of the workgroup -> output-tile map the kernels use (no GPU
  * call), for checking that it is a bijection: workgroup `bid` of a grid of
  * tiles_m x tiles_n tiles, raster groups of `group_m` tile rows, computes

@@ -153,3 +153,45 @@ def test_tile_map_keeps_an_xcd_on_a_compact_block():
         ms = {t[0] for t in tiles}
         ns = {t[1] for t in tiles}
         assert len(ms) == 4 and len(ns) == 8
+
+
+def _kernel(M, N, K, lda=None, ldb=None, ldc=None, in_dt=T.F16, out_dt=T.F16, cid=-1, offs=(0, 0, 0)):
+    lda = K if lda is None else lda
+    ldb = N if ldb is None else ldb
+    ldc = N if ldc is None else ldc
+    eb = 4 if in_dt == T.F32 else 2
+    return T.gemm_select_kernel(M, N, K, FAKE + offs[0] * eb, lda, FAKE + (1 << 36) + offs[1] * eb, ldb,
+                                FAKE + (2 << 36) + offs[2] * 2, ldc, in_dt, out_dt, cid)
+
+
+def test_kernel_choice_ring_path():
+    """The direct-to-LDS ring kernel runs exactly for whole tiles of 16-bit
+    inputs with K a multiple of 128 and 16-byte aligned operands; anything
+    else falls back to a register-staged kernel of the same tile."""
+    R, TI, GE = T.KERNEL_RING, T.KERNEL_TILED, T.KERNEL_GENERAL
+    assert _kernel(8192, 8192, 8192) == R
+    assert _kernel(8192, 8192, 8192, in_dt=T.BF16, out_dt=T.F32) == R
+    assert _kernel(1024, 2048, 512, out_dt=T.F32, cid=0) == R
+    assert _kernel(1024, 2048, 512, out_dt=T.F32, cid=1) == R
+    assert _kernel(256, 256, 128, cid=0) == R
+    assert _kernel(8192, 8192, 8192 + 64) == TI          # K not a multiple of 128
+    assert _kernel(8192, 8192, 8192 - 32) == TI
+    assert _kernel(8192 - 256, 8192, 8192) == R          # still whole tiles
+    assert _kernel(8191, 8192, 8192) == GE               # ragged M
+    assert _kernel(8192, 8192, 8192, lda=8196) == GE     # rows not whole 16-byte chunks
+    assert _kernel(8192, 8192, 8192, lda=8192 + 8) == R  # padded, still aligned
+    assert _kernel(8192, 8192, 8192, offs=(1, 0, 0)) == GE
+    assert _kernel(8192, 8192, 8192, cid=2) == TI        # configuration without a ring kernel
+    assert _kernel(1024, 1024, 1024, in_dt=T.F32, out_dt=T.F32) != R
+    # B offsets beyond 2^31 bytes: register-staged kernel
+    assert _kernel(256, 256, 1 << 15, ldb=1 << 15, cid=0) == TI
+    assert _kernel(-1, 4, 4) == T.ERR_DIM
+    assert _kernel(4, 4, 4, in_dt=T.F16, out_dt=T.BF16) == T.ERR_DTYPE
+    assert _kernel(4, 4, 4, cid=4) == T.ERR_CONFIG
+
+
+def test_ring_configs_report_their_ring_kernel():
+    for cid in (0, 1):
+        c = T.gemm_config_info(cid)
+        assert (c["block_k"], c["stages"]) == (32, 4)
+        assert (c["mfma_m"], c["mfma_n"], c["mfma_k"]) == (16, 16, 32)

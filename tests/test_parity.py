@@ -276,3 +276,57 @@ def test_invalid_arguments_on_gpu():
     assert T.gemm(4, 4, 4, p, 4, p, 4, c.data_ptr(), 4, 1, 2, None) == T.ERR_DTYPE
     assert T.gemm(4, 4, 4, p, 3, p, 4, c.data_ptr(), 4, 1, 1, None) == T.ERR_LD
     torch.cuda.synchronize()
+
+
+# ------------------------------------------------- the direct-to-LDS ring path
+RING_SHAPES = [(256, 256, 128, 0), (256, 256, 256, 0), (512, 768, 384, 0), (256, 512, 640, 0),
+               (128, 128, 128, 1), (384, 256, 512, 1), (1024, 2048, 512, 0), (1024, 2048, 512, 1)]
+
+
+@pytest.mark.parametrize("shape", RING_SHAPES, ids=lambda s: "x".join(map(str, s[:3])) + f"_cfg{s[3]}")
+def test_ring_path_against_oracle(shape):
+    """Shapes that take the ring kernel (1 to 5 trips of its 4-step loop),
+    every 16-bit type pair, against the oracle; the path is asserted."""
+    M, N, K, cid = shape
+    for in_dt, out_dt in ((W.F16, W.F16), (W.F16, W.F32), (W.BF16, W.BF16), (W.BF16, W.F32)):
+        a, b = W.random_inputs(M, N, K, in_dt, seed=M + 3 * N + 7 * K)
+        ad, bd = G.to_device(a, in_dt), G.to_device(b, in_dt)
+        _, cd = G.out_tensor(M, N, out_dt)
+        assert T.gemm_select_kernel(M, N, K, ad.data_ptr(), K, bd.data_ptr(), N, cd.data_ptr(), N, in_dt, out_dt,
+                                    cid) == T.KERNEL_RING
+        run_case(a, b, in_dt, out_dt, config=cid, label=f"ring {shape}")
+
+
+@pytest.mark.parametrize("cid", [0, 1])
+def test_ring_path_ignores_data_past_k(cid):
+    """The ring kernel's loads run up to 4 steps of 32 past the end of K.  A
+    and B live in NaN-filled buffers with padded rows (lda = K + 40,
+    ldb = N + 24) and NaN after the last row: none of it may reach C, which
+    must equal the oracle bit for bit (integer inputs)."""
+    M, N, K = (512, 512, 256) if cid == 0 else (256, 384, 384)
+    a, b = W.integer_inputs(M, N, K, W.F16, seed=cid + 40)
+    lda, ldb = K + 40, N + 24
+    fa = torch.full((M * lda + 4096,), float("nan"), dtype=torch.float16, device=G.DEV)
+    fb = torch.full((K * ldb + 4096,), float("nan"), dtype=torch.float16, device=G.DEV)
+    ad = fa[:M * lda].view(M, lda)[:, :K]
+    bd = fb[:K * ldb].view(K, ldb)[:, :N]
+    ad.copy_(torch.from_numpy(a).to(G.DEV))
+    bd.copy_(torch.from_numpy(b).to(G.DEV))
+    for out_dt in (W.F16, W.F32):
+        _, cd = G.out_tensor(M, N, out_dt)
+        G.say(f"[case] ring past-K {M}x{N}x{K} cfg{cid} out={out_dt}")
+        assert T.gemm_select_kernel(M, N, K, ad.data_ptr(), lda, bd.data_ptr(), ldb, cd.data_ptr(), N, W.F16,
+                                    out_dt, cid) == T.KERNEL_RING
+        G.run(ad, bd, cd, cid)
+        got = G.values(cd, out_dt)
+        want = G.round_to(G.oracle_values(a, b, W.F16), out_dt)
+        assert np.array_equal(got, want), f"{int((got != want).sum())} entries differ"
+
+
+def test_workload_8192_takes_the_ring_path():
+    w = W.WORKLOADS[4]
+    a = torch.empty((w.M, w.K), dtype=torch.float16, device=G.DEV)
+    b = torch.empty((w.K, w.N), dtype=torch.float16, device=G.DEV)
+    c = torch.empty((w.M, w.N), dtype=torch.float16, device=G.DEV)
+    assert T.gemm_select_kernel(w.M, w.N, w.K, a.data_ptr(), w.K, b.data_ptr(), w.N, c.data_ptr(), w.N, w.in_dtype,
+                                w.out_dtype) == T.KERNEL_RING

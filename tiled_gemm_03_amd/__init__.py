@@ -25,7 +25,10 @@ OK = 0
 ERR_DIM, ERR_NULL, ERR_LD, ERR_DTYPE, ERR_ALIAS, ERR_CONFIG = -1, -2, -3, -4, -5, -6
 
 EXPORTED = ["gemm", "gemm_ex", "gemm_strerror", "gemm_num_configs", "gemm_config_info",
-            "gemm_select_config", "gemm_tile_map", "gemm_version"]
+            "gemm_select_config", "gemm_select_kernel", "gemm_tile_map", "gemm_version"]
+
+# gemm_select_kernel results
+KERNEL_GENERAL, KERNEL_TILED, KERNEL_RING = 0, 1, 2
 
 
 class ConfigInfo(ctypes.Structure):
@@ -73,6 +76,8 @@ def lib():
     L.gemm_config_info.argtypes = [i, ctypes.POINTER(ConfigInfo)]
     L.gemm_select_config.restype = i
     L.gemm_select_config.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, i, i]
+    L.gemm_select_kernel.restype = i
+    L.gemm_select_kernel.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, i, i, i]
     L.gemm_tile_map.restype = i
     L.gemm_tile_map.argtypes = [i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i)]
     L.gemm_version.restype = ctypes.c_char_p
@@ -107,6 +112,10 @@ def gemm_config_info(config_id):
 
 def gemm_select_config(M, N, K, A, lda, B, ldb, C, ldc, in_dtype, out_dtype):
     return lib().gemm_select_config(M, N, K, A, lda, B, ldb, C, ldc, in_dtype, out_dtype)
+
+
+def gemm_select_kernel(M, N, K, A, lda, B, ldb, C, ldc, in_dtype, out_dtype, config_id=-1):
+    return lib().gemm_select_kernel(M, N, K, A, lda, B, ldb, C, ldc, in_dtype, out_dtype, config_id)
 
 
 def gemm_tile_map(bid, tiles_m, tiles_n, group_m):

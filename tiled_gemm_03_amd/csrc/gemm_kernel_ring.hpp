@@ -1,0 +1,311 @@
+// gemm_kernel_ring.hpp -- the gfx950 fast path of the tiled matrix product
+// for 16-bit inputs (fp16 / bf16) on whole tiles: direct-to-LDS loads into
+// S-stage LDS rings and v_mfma_f32_16x16x32_{f16,bf16}.
+//
+// The method is the tiled kernel of page "企业官网建设流程全解析" §3.3 (one
+// workgroup per BM x BN tile of C, K walked in steps, A and B tiles staged in
+// shared memory by a software pipeline of num_stages buffers, fp32 register
+// accumulators), laid out for CDNA4:
+//
+//  * a2  global -> LDS without registers.  buffer_load_dwordx4 ... lds writes
+//        the 16 bytes of lane l at LDS byte M0 + 16 l, so one instruction
+//        fills a 1 KiB block; the XOR swizzle (a3) is obtained by choosing
+//        which global 16-byte chunk each lane fetches.  The buffer resources
+//        start at the tile's corner and end at the operand's last element;
+//        the K position is the scalar offset, one add per operand and step.
+//        Loads issued past the end of K read zeros (or in-bounds data that
+//        is never used), so every step of the loop has the same shape.
+//  * a4  pipeline.  BK = 32 per step; A and B each have a ring of S = 4 LDS
+//        stages.  The loads of step s + S are issued during step s, so a
+//        load has S - 1 steps (about 3 x 1000 cycles) to arrive.  One
+//        barrier per step: after it, the stage read during the previous step
+//        is free and is refilled.
+//  * a5  MFMA.  v_mfma_f32_16x16x32: lane l holds 8 consecutive k of row /
+//        column l % 16 of each operand (k = 8 (l / 16) ..).  At the power
+//        limit that random fp16 data sets on MI355X, this shape keeps a
+//        higher clock than the 32x32x16 one (about 1.9 vs 1.6 GHz for MFMA
+//        issue alone), which more than pays for its lower issue rate.
+//        B is the first operand and A the second, so the accumulator holds C
+//        transposed: lane l owns row l % 16 and the 4 consecutive columns
+//        4 (l / 16) .. of each 16 x 16 block, stored with one write.
+//  * B stays k-major in LDS (rows of BN elements) and its operand is read
+//        with ds_read_b64_tr_b16: in each group of 16 lanes, lane i points at
+//        4 consecutive columns of k-row i / 4 and receives element i % 4 of
+//        the loads of lanes i / 4, i / 4 + 4, i / 4 + 8, i / 4 + 12, i.e.
+//        one column of a 4-row block.  Two such reads give the 8 k-values of
+//        one column.
+//  * The loop is unrolled over the ring, so every LDS read is a base
+//        register plus an immediate offset and the loop body holds no vector
+//        address arithmetic: with one wave per SIMD, every instruction between
+//        two MFMAs takes issue slots that the MFMA pipe would otherwise use.
+//
+// LDS layout: the A ring (S stages of BM rows x 64 bytes) and then the B ring
+// (S stages of 32 k-rows x 2 BN bytes).
+//   A: 16-byte chunk c of row r stored at chunk c ^ ((r / 4) % 4): the 16
+//      rows read by one quarter wave (one ds_read_b128 cycle) land in 16
+//      different bank groups.
+//   B: chunk c of k-row r stored at chunk c ^ (4 (r % 4) ^ 2 ((r / 8) % 2)):
+//      the rows r .. r+3 and r+8 .. r+11 read by one half wave of a
+//      transposing read land in 16 different bank groups.
+
+#pragma once
+#include "gemm_kernel.hpp"
+
+namespace tgemm {
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+
+// s_waitcnt that limits only the vector-memory counter, to N outstanding
+// (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Tile configuration of the ring kernel: BM x BN output tile, WM x WN waves,
+// S ring stages of BK = 32, OCC workgroups per CU the registers are sized for.
+template <int BM_, int BN_, int WM_, int WN_, int S_, int OCC_>
+struct RingCfg {
+    static constexpr int BM = BM_, BN = BN_, BK = 32, WM = WM_, WN = WN_, S = S_, OCC = OCC_;
+    static constexpr int THREADS = 64 * WM * WN, WAVES = WM * WN;
+    static constexpr int EB = 2;
+    static constexpr int RA = BK * 2;              // bytes per A row (4 chunks)
+    static constexpr int RB = BN * 2;              // bytes per B k-row
+    static constexpr int CA = RA / 16, CB = RB / 16;
+    static constexpr int A_STAGE = BM * RA, B_STAGE = BK * RB;
+    static constexpr int A_RING = S * A_STAGE, B_RING = S * B_STAGE;
+    static constexpr int LDS_BYTES = A_RING + B_RING;
+    static constexpr int A_BLOCKS = A_STAGE / 1024, B_BLOCKS = B_STAGE / 1024;
+    static constexpr int A_LOADS = A_BLOCKS / WAVES, B_LOADS = B_BLOCKS / WAVES;
+    static constexpr int L = A_LOADS + B_LOADS;    // loads per wave per step
+    static constexpr int A_RPB = 1024 / RA, B_RPB = 1024 / RB;
+    static constexpr int WTM = BM / WM, WTN = BN / WN;
+    static constexpr int FM = WTM / 16, FN = WTN / 16;
+    static constexpr int U = S;                    // steps per loop trip
+    static constexpr int K_MULT = BK * U;          // K must be a multiple of this
+    static_assert(S % 2 == 0, "fragment buffers alternate per step");
+    static_assert(CB == 16 || CB == 32, "BN of 128 or 256");
+    static_assert(A_BLOCKS % WAVES == 0 && B_BLOCKS % WAVES == 0, "");
+    static_assert(LDS_BYTES <= 160 * 1024, "gfx950 LDS is 160 KiB per CU");
+    static_assert(S >= 3 && (S - 1) * L < 64, "vmcnt range");
+    // every LDS read offset fits the 16-bit immediate of ds_read
+    static_assert(A_RING - A_STAGE + (FM - 1) * 16 * RA < 65536, "");
+    static_assert(B_RING - B_STAGE + 4 * RB < 65536, "");
+    static_assert(WTM % 16 == 0 && WTN % 16 == 0, "");
+};
+
+__device__ __forceinline__ int ring_key_a(int r) { return (r >> 2) & 3; }
+__device__ __forceinline__ int ring_key_b(int r) { return 4 * (r & 3) ^ 2 * ((r >> 3) & 1); }
+
+// Preconditions (checked by the host): 16-bit inputs; M % BM == 0,
+// N % BN == 0, K % K_MULT == 0; A and B 16-byte aligned with lda and ldb
+// multiples of 8; C aligned for 4-element stores with ldc % 4 == 0; the
+// buffer offsets (BM rows of A plus K + S*BK columns; K + S*BK rows of B)
+// below 2^31 bytes.
+template <class T, int IN, int OUT>
+__global__ __attribute__((amdgpu_flat_work_group_size(T::THREADS, T::THREADS),
+                          amdgpu_waves_per_eu(T::OCC * T::WAVES / 4 > 0 ? T::OCC * T::WAVES / 4 : 1)))
+void gemm_kernel_ring(GemmArgs p) {
+    __shared__ __attribute__((aligned(1024))) char smem[T::LDS_BYTES];
+    const int smem_base = (int)(uintptr_t)(lds_void*)smem;   // LDS byte address (M0 values)
+    lds_char* const lds = (lds_char*)smem;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / T::WN, wn = wave % T::WN;
+
+    // a1: which tile
+    int tm, tn;
+    tile_of(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+    const int m0 = tm * T::BM, n0 = tn * T::BN;
+    const int K = p.K;
+    const int64_t lda = p.lda, ldb = p.ldb;
+
+    // ---------------------------------------------------------- a2: loads
+    auto make_rsrc = [&](const char* base, int64_t bytes) __attribute__((always_inline)) {
+        const uint64_t a = (uint64_t)base;
+        const uint32_t n = bytes > 0xffffffffLL ? 0xffffffffu : (uint32_t)bytes;
+        return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+                     __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)),
+                     __builtin_amdgcn_readfirstlane((int)n), 0x00020000};
+    };
+    // byte ranges end at the operand's last element (A: row M-1, column K-1;
+    // B: row K-1, column N-1), counted from the tile's corner
+    const i32x4 rs_a = make_rsrc(p.A + (int64_t)m0 * lda * 2, ((int64_t)(p.M - 1 - m0) * lda + K) * 2);
+    const i32x4 rs_b = make_rsrc(p.B + (int64_t)n0 * 2, ((int64_t)(K - 1) * ldb + p.N - n0) * 2);
+    // load x of a wave: A block wave*A_LOADS + x (x < A_LOADS), else B block
+    // wave*B_LOADS + x - A_LOADS.  Lane l fills slot l of the 1 KiB block
+    // (row l / C, chunk l % C) with the logical chunk the swizzle puts there.
+    int voff[T::L];
+#pragma unroll
+    for (int x = 0; x < T::L; ++x) {
+        if (x < T::A_LOADS) {
+            const int r = (wave * T::A_LOADS + x) * T::A_RPB + lane / T::CA;
+            const int c = (lane % T::CA) ^ ring_key_a(r);
+            voff[x] = (int)((int64_t)r * lda * 2 + c * 16);
+        } else {
+            const int r = (wave * T::B_LOADS + (x - T::A_LOADS)) * T::B_RPB + lane / T::CB;
+            const int c = (lane % T::CB) ^ ring_key_b(r);
+            voff[x] = (int)((int64_t)r * ldb * 2 + c * 16);
+        }
+    }
+    const int a_kstep = T::BK * 2;               // bytes of A per step
+    const int b_kstep = (int)(T::BK * ldb * 2);  // bytes of B per step
+    // Issued through inline asm (M0 = LDS destination, then the load): the
+    // compiler then does not guard later LDS reads with waits for these
+    // loads; the kernel waits for them itself (vmcnt) before the barrier that
+    // publishes a stage.
+    auto dma = [&](int lds_addr, int vo, i32x4 rs, int so) __attribute__((always_inline)) {
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                     :
+                     : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(vo), "s"(rs), "s"(so)
+                     : "memory");
+    };
+    // load x of the step whose K byte offsets are (ka, kb) into ring stage st
+    auto issue_load = [&](int st, int x, int ka, int kb) __attribute__((always_inline)) {
+        if (x < T::A_LOADS)
+            dma(smem_base + st * T::A_STAGE + (wave * T::A_LOADS + x) * 1024, voff[x], rs_a, ka);
+        else
+            dma(smem_base + T::A_RING + st * T::B_STAGE + (wave * T::B_LOADS + x - T::A_LOADS) * 1024, voff[x],
+                rs_b, kb);
+    };
+
+    // ---------------------------------------------------------- a5: fragments
+    const int q = lane >> 4, i16 = lane & 15;
+    const int a_row = wm * T::WTM + i16;                     // + 16 i
+    lds_char* const a_base = lds + a_row * T::RA + (q ^ ring_key_a(a_row)) * 16;
+    // B: lane i of group q points at k-row 8q + 4h + i/4 (h: which of the two
+    // reads; in the immediate offset), columns 16 j + 4 (i%4) .. +3 of the
+    // wave's block
+    const int b_row = 8 * q + (i16 >> 2);
+    const int b_key = ring_key_b(b_row);
+    lds_char* b_base[T::FN];
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j) {
+        const int c = (wn * T::WTN + 16 * j) / 8 + ((i16 & 3) >> 1);
+        b_base[j] = lds + T::A_RING + b_row * T::RB + (c ^ b_key) * 16 + 8 * (i16 & 1);
+    }
+
+    u32x4 fa[2][T::FM];
+    i16x4 fb[2][T::FN][2];
+    constexpr int NREAD = T::FM + 2 * T::FN;
+    // read r of stage st into buffer buf: the B fragments (two reads each)
+    // first, then the A fragments, the order the MFMAs need them in
+    auto read_frag = [&](int st, int buf, int r) __attribute__((always_inline)) {
+        if (r < 2 * T::FN) {
+            const int j = r / 2, h = r % 2;
+            fb[buf][j][h] =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(b_base[j] + st * T::B_STAGE + 4 * h * T::RB));
+        } else {
+            const int i = r - 2 * T::FN;
+            fa[buf][i] = *(const lds_u32x4*)(a_base + st * T::A_STAGE + 16 * i * T::RA);
+        }
+    };
+
+    // a6: accumulators, zeroed (T.clear of §3.3).  The empty asm makes each
+    // one opaque, so that every accumulator gets registers of its own and
+    // every MFMA accumulates in place (a shared zero register would make the
+    // first MFMAs write elsewhere and the loop copy accumulators around).
+    f32x4 acc[T::FM][T::FN];
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::FN; ++j) {
+            acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            asm volatile("" : "+a"(acc[i][j]));
+        }
+
+    constexpr int NMF = T::FM * T::FN;
+    auto mfma_one = [&](int buf, int m) __attribute__((always_inline)) {
+        // snake order over j: neighbours share one operand
+        const int i = m / T::FN, jj = m % T::FN, j = (i & 1) ? T::FN - 1 - jj : jj;
+        const i16x8 bop = __builtin_shufflevector(fb[buf][j][0], fb[buf][j][1], 0, 1, 2, 3, 4, 5, 6, 7);
+        if constexpr (IN == DT_F16) {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, bop),
+                                                                __builtin_bit_cast(f16x8, fa[buf][i]), acc[i][j], 0, 0, 0);
+        } else {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bop),
+                                                                 __builtin_bit_cast(bf16x8, fa[buf][i]), acc[i][j], 0, 0, 0);
+        }
+    };
+
+    // One step on ring stage ST, fragments in buffer BUF: wait until this
+    // wave's loads of the next stage have landed ((S-2)*L loads of later
+    // steps may still be in flight), barrier (every wave has then finished
+    // the previous step, so the next stage is complete and stage ST, read
+    // during the previous step, is free), then the MFMAs, with the next
+    // stage's fragment reads and the loads of step s + S into stage ST
+    // interleaved: one load after every NREAD / L reads, spread over the
+    // MFMAs so that at most two other instructions sit between two MFMAs.
+    auto step = [&](auto st_t, auto buf_t, int ka, int kb) __attribute__((always_inline)) {
+        constexpr int ST = decltype(st_t)::value, BUF = decltype(buf_t)::value;
+        constexpr int NXT = (ST + 1) % T::S;
+        wait_vmcnt<(T::S - 2) * T::L>();
+        __syncthreads();
+        constexpr int n_work = NREAD + T::L;
+        constexpr int per = NREAD / T::L;
+        static_assert(NREAD % T::L == 0, "");
+        static_for<0, NMF>([&](auto mt) __attribute__((always_inline)) {
+            constexpr int m = decltype(mt)::value;
+            mfma_one(BUF, m);
+            constexpr int wb = (m * n_work + NMF - 1) / NMF;
+            constexpr int we = ((m + 1) * n_work + NMF - 1) / NMF;
+            static_for<wb, we>([&](auto wt) __attribute__((always_inline)) {
+                constexpr int w = decltype(wt)::value;
+                constexpr int grp = w / (per + 1);
+                if constexpr (w % (per + 1) == per) issue_load(ST, grp, ka, kb);
+                else read_frag(NXT, BUF ^ 1, w - grp);
+            });
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+
+    const int nk = K / T::BK;  // a multiple of U (host precondition)
+    if (nk > 0) {
+        // prologue: steps 0 .. S-1 into stages 0 .. S-1, then the fragments
+        // of step 0
+        static_for<0, T::S>([&](auto s_t) __attribute__((always_inline)) {
+            constexpr int s = decltype(s_t)::value;
+            static_for<0, T::L>([&](auto x) __attribute__((always_inline)) {
+                issue_load(s, decltype(x)::value, s * a_kstep, s * b_kstep);
+            });
+        });
+        wait_vmcnt<(T::S - 1) * T::L>();
+        __syncthreads();
+        static_for<0, NREAD>([&](auto r) __attribute__((always_inline)) { read_frag(0, 0, decltype(r)::value); });
+        int ka = T::S * a_kstep, kb = T::S * b_kstep;  // K offsets of the next step to load
+        for (int s = 0; s < nk; s += T::U) {
+            static_for<0, T::U>([&](auto u_t) __attribute__((always_inline)) {
+                constexpr int u = decltype(u_t)::value;
+                step(IntTag<u % T::S>{}, IntTag<u & 1>{}, ka, kb);
+                ka += a_kstep;
+                kb += b_kstep;
+            });
+        }
+        // no load may still be writing LDS when the workgroup ends
+        wait_vmcnt<0>();
+    }
+
+    // a7: epilogue.  acc[i][j] of lane l is C[row 16 i + l%16][columns
+    // 16 j + 4 (l/16) .. +3] of the wave's block; fp32 -> fp16 / bf16 rounds
+    // to nearest even.
+    constexpr int OB = OUT == DT_F32 ? 4 : 2;
+    const int64_t ldc = p.ldc;
+    static_for<0, NMF>([&](auto bt) __attribute__((always_inline)) {
+        constexpr int i = decltype(bt)::value / T::FN, j = decltype(bt)::value % T::FN;
+        const int row = m0 + wm * T::WTM + 16 * i + i16;
+        const int col = n0 + wn * T::WTN + 16 * j + 4 * q;
+        store4<OUT>(p.C + ((int64_t)row * ldc + col) * OB, acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3],
+                    true);
+    });
+}
+
+}  // namespace tgemm

@@ -1,12 +1,14 @@
 // tgemm.hip -- C ABI of libtgemm.so: argument checks, the per-shape tile
 // configuration table and the kernel launch.  The kernels are in
-// gemm_kernel.hpp; the ABI is declared (and documented) in include/tgemm.h.
+// gemm_kernel.hpp (register-staged; every shape, type and alignment) and
+// gemm_kernel_ring.hpp (direct-to-LDS rings; whole tiles of 16-bit inputs);
+// the ABI is declared (and documented) in include/tgemm.h.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
 
 #include "gemm_kernel.hpp"
-#include "gemm_kernel_dl.hpp"
+#include "gemm_kernel_ring.hpp"
 #include "tgemm.h"
 
 using namespace tgemm;
@@ -32,21 +34,24 @@ struct ConfigEntry {
     int in_family;  // TGEMM_F16 (serves F16 and BF16) or TGEMM_F32
     int bm, bn, bk, wm, wn, eb, lds_bytes, threads, cpr;
     KernelFn (*pick)(int in, int out, bool fast);
-    // direct-to-LDS kernel of the same tile, for whole tiles and K % bk == 0
-    KernelFn (*pick_dl)(int in, int out);
+    // direct-to-LDS ring kernel of the same output tile (whole tiles, K a
+    // multiple of ring_k_mult); its block_k and stage count
+    KernelFn (*pick_ring)(int in, int out);
+    int ring_bk, ring_stages, ring_k_mult, ring_lds;
 };
 
-template <class D>
-KernelFn pick_dl(int in, int out) {
-    if (in == TGEMM_F16 && out == TGEMM_F16) return gemm_kernel_dl<D, DT_F16, DT_F16>;
-    if (in == TGEMM_F16 && out == TGEMM_F32) return gemm_kernel_dl<D, DT_F16, DT_F32>;
-    if (in == TGEMM_BF16 && out == TGEMM_BF16) return gemm_kernel_dl<D, DT_BF16, DT_BF16>;
-    if (in == TGEMM_BF16 && out == TGEMM_F32) return gemm_kernel_dl<D, DT_BF16, DT_F32>;
+template <class R>
+KernelFn pick_ring(int in, int out) {
+    if (in == TGEMM_F16 && out == TGEMM_F16) return gemm_kernel_ring<R, DT_F16, DT_F16>;
+    if (in == TGEMM_F16 && out == TGEMM_F32) return gemm_kernel_ring<R, DT_F16, DT_F32>;
+    if (in == TGEMM_BF16 && out == TGEMM_BF16) return gemm_kernel_ring<R, DT_BF16, DT_BF16>;
+    if (in == TGEMM_BF16 && out == TGEMM_F32) return gemm_kernel_ring<R, DT_BF16, DT_F32>;
     return nullptr;
 }
-using DlBig = DlCfg<256, 256, 64, 2, 2>;
-using DlMid = DlCfg<128, 128, 64, 2, 2>;
-static_assert(DlBig::LDS_BYTES == CfgBig::LDS_BYTES && DlMid::LDS_BYTES == CfgMid::LDS_BYTES, "");
+using RingBig = RingCfg<256, 256, 2, 2, 4, 1>;
+using RingMid = RingCfg<128, 128, 2, 2, 4, 2>;
+static_assert(RingBig::LDS_BYTES == CfgBig::LDS_BYTES && RingMid::LDS_BYTES == CfgMid::LDS_BYTES,
+              "both kernels of a configuration use the same LDS budget");
 
 template <class T, int IN>
 KernelFn pick_out(int out, bool fast) {
@@ -73,16 +78,19 @@ KernelFn pick_f32(int in, int out, bool fast) {
     return nullptr;
 }
 
-#define ENTRY(name, fam, T, pk, dl) \
-    {name, fam, T::BM, T::BN, T::BK, T::WM, T::WN, T::EB, T::LDS_BYTES, T::THREADS, T::CPR, pk<T>, dl}
+#define ENTRY(name, fam, T, pk) \
+    {name, fam, T::BM, T::BN, T::BK, T::WM, T::WN, T::EB, T::LDS_BYTES, T::THREADS, T::CPR, pk<T>, nullptr, 0, 0, 0, 0}
+#define ENTRY_RING(name, fam, T, pk, R)                                                                      \
+    {name, fam, T::BM, T::BN, T::BK, T::WM, T::WN, T::EB, T::LDS_BYTES, T::THREADS, T::CPR, pk<T>, pick_ring<R>, \
+     R::BK, R::S, R::K_MULT, R::LDS_BYTES}
 
 const ConfigEntry kConfigs[] = {
-    ENTRY("h256x256x64_w2x2", TGEMM_F16, CfgBig, pick_half, pick_dl<DlBig>),
-    ENTRY("h128x128x64_w2x2", TGEMM_F16, CfgMid, pick_half, pick_dl<DlMid>),
-    ENTRY("h64x64x64_w2x2", TGEMM_F16, CfgSmall, pick_half, nullptr),
-    ENTRY("h32x32x64_w1x1", TGEMM_F16, CfgTiny, pick_half, nullptr),
-    ENTRY("s64x64x32_w2x2", TGEMM_F32, CfgF32Mid, pick_f32, nullptr),
-    ENTRY("s32x32x32_w1x1", TGEMM_F32, CfgF32Tiny, pick_f32, nullptr),
+    ENTRY_RING("h256x256_w2x2", TGEMM_F16, CfgBig, pick_half, RingBig),
+    ENTRY_RING("h128x128_w2x2", TGEMM_F16, CfgMid, pick_half, RingMid),
+    ENTRY("h64x64x64_w2x2", TGEMM_F16, CfgSmall, pick_half),
+    ENTRY("h32x32x64_w1x1", TGEMM_F16, CfgTiny, pick_half),
+    ENTRY("s64x64x32_w2x2", TGEMM_F32, CfgF32Mid, pick_f32),
+    ENTRY("s32x32x32_w1x1", TGEMM_F32, CfgF32Tiny, pick_f32),
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 enum { CFG_BIG = 0, CFG_MID = 1, CFG_SMALL = 2, CFG_TINY = 3, CFG_F32_MID = 4, CFG_F32_TINY = 5 };
@@ -90,7 +98,7 @@ enum { CFG_BIG = 0, CFG_MID = 1, CFG_SMALL = 2, CFG_TINY = 3, CFG_F32_MID = 4, C
 // Measurement-only switches, read once from the environment:
 //   TGEMM_GROUP_M=<n>    tile rows per raster group (default 4)
 //   TGEMM_NO_SWIZZLE=1   plain row-major LDS tiles (for bank-conflict A/B runs)
-//   TGEMM_NO_DL=1        register-staged loads instead of direct-to-LDS ones
+//   TGEMM_NO_DL=1        register-staged kernel instead of the direct-to-LDS ring
 struct Tuning {
     int group_m = 4;
     bool swizzle = true;
@@ -171,25 +179,53 @@ int table_choice(int64_t M, int64_t N, int64_t K, int in) {
 
 int family_of(int in) { return in == TGEMM_F32 ? TGEMM_F32 : TGEMM_F16; }
 
-int run(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
-        int64_t ldc, int in, int out, void* stream, int config_id) {
+// What one call runs: the configuration, the kernel and its kind.
+struct Plan {
+    int config;
+    int kind;  // TGEMM_KERNEL_*
+    KernelFn fn;
+};
+
+// Validates the arguments and picks the kernel; returns TGEMM_OK (plan
+// filled; M == 0 or N == 0 leaves plan.fn null) or a negative error code.
+int make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+              const void* C, int64_t ldc, int in, int out, int config_id, Plan& plan) {
     const int v = validate(M, N, K, A, lda, B, ldb, C, ldc, in, out);
     if (v != TGEMM_OK) return v;
     if (config_id < -1 || config_id >= kNumConfigs) return TGEMM_ERR_CONFIG;
     if (config_id >= 0 && kConfigs[config_id].in_family != family_of(in)) return TGEMM_ERR_CONFIG;
+    plan.config = config_id >= 0 ? config_id : table_choice(M, N, K, in);
+    plan.fn = nullptr;
+    plan.kind = TGEMM_KERNEL_GENERAL;
     if (M == 0 || N == 0) return TGEMM_OK;
-    const int id = config_id >= 0 ? config_id : table_choice(M, N, K, in);
-    const ConfigEntry& c = kConfigs[id];
+    const ConfigEntry& c = kConfigs[plan.config];
     const bool vec_ab = loads_aligned(c, A, lda, B, ldb);
     const bool vec_c = stores_aligned(C, ldc, out);
-    // FAST kernels address A and B through 32-bit buffer offsets within a
-    // tile's rows (A) or one K step's rows (B)
+    // the register-staged kernel addresses A and B through 32-bit buffer
+    // offsets within a tile's rows (A) or one K step's rows (B)
     const bool offsets_fit = (int64_t)c.bm * lda * c.eb + K * c.eb < (1LL << 31) &&
                              (int64_t)c.bk * ldb * c.eb + N * c.eb < (1LL << 31);
     const bool fast = vec_ab && vec_c && offsets_fit && M % c.bm == 0 && N % c.bn == 0;
-    const bool dl = fast && K % c.bk == 0 && c.pick_dl != nullptr && tuning().direct_lds;
-    KernelFn fn = dl ? c.pick_dl(in, out) : c.pick(in, out, fast);
-    if (fn == nullptr) return TGEMM_ERR_DTYPE;
+    // the ring kernel addresses A through BM rows plus K + S*BK columns and B
+    // through K + S*BK rows with 32-bit buffer offsets
+    const bool ring_fits = c.pick_ring != nullptr &&
+                           ((int64_t)c.bm * lda + K + (int64_t)c.ring_stages * c.ring_bk) * c.eb < (1LL << 31) &&
+                           ((K + (int64_t)c.ring_stages * c.ring_bk) * ldb + c.bn) * c.eb < (1LL << 31);
+    const bool ring = fast && ring_fits && K % c.ring_k_mult == 0 && tuning().direct_lds;
+    plan.kind = ring ? TGEMM_KERNEL_RING : fast ? TGEMM_KERNEL_TILED : TGEMM_KERNEL_GENERAL;
+    plan.fn = ring ? c.pick_ring(in, out) : c.pick(in, out, fast);
+    if (plan.fn == nullptr) return TGEMM_ERR_DTYPE;
+    const int64_t grid = ceil_div(M, c.bm) * ceil_div(N, c.bn);
+    if (grid > 0x7fffffff) return TGEMM_ERR_DIM;
+    return TGEMM_OK;
+}
+
+int run(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
+        int64_t ldc, int in, int out, void* stream, int config_id) {
+    Plan plan;
+    const int v = make_plan(M, N, K, A, lda, B, ldb, C, ldc, in, out, config_id, plan);
+    if (v != TGEMM_OK || plan.fn == nullptr) return v;
+    const ConfigEntry& c = kConfigs[plan.config];
 
     GemmArgs args;
     args.A = (const char*)A;
@@ -205,13 +241,12 @@ int run(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void*
     args.tiles_n = (int)ceil_div(N, c.bn);
     args.group_m = tuning().group_m;
     args.swz_mask = tuning().swizzle ? c.cpr - 1 : 0;
-    args.vec_ab = vec_ab;
-    args.vec_c = vec_c;
+    args.vec_ab = loads_aligned(c, A, lda, B, ldb);
+    args.vec_c = stores_aligned(C, ldc, out);
     const int64_t grid = (int64_t)args.tiles_m * args.tiles_n;
-    if (grid > 0x7fffffff) return TGEMM_ERR_DIM;
 
     void* kargs[] = {&args};
-    hipError_t e = hipLaunchKernel((const void*)fn, dim3((unsigned)grid), dim3(c.threads), kargs, 0,
+    hipError_t e = hipLaunchKernel((const void*)plan.fn, dim3((unsigned)grid), dim3(c.threads), kargs, 0,
                                    (hipStream_t)stream);
     if (e == hipSuccess) e = hipGetLastError();
     return e == hipSuccess ? TGEMM_OK : (int)e;
@@ -251,19 +286,20 @@ int gemm_num_configs(void) { return kNumConfigs; }
 int gemm_config_info(int id, tgemm_config_info* out) {
     if (id < 0 || id >= kNumConfigs || out == nullptr) return TGEMM_ERR_CONFIG;
     const ConfigEntry& c = kConfigs[id];
+    const bool ring = c.pick_ring != nullptr;
     out->id = id;
     out->in_dtype = c.in_family;
     out->block_m = c.bm;
     out->block_n = c.bn;
-    out->block_k = c.bk;
-    out->stages = 2;
+    out->block_k = ring ? c.ring_bk : c.bk;
+    out->stages = ring ? c.ring_stages : 2;
     out->threads = c.threads;
     out->waves_m = c.wm;
     out->waves_n = c.wn;
-    out->mfma_m = 32;
-    out->mfma_n = 32;
-    out->mfma_k = c.eb == 4 ? 2 : 16;
-    out->lds_bytes = c.lds_bytes;
+    out->mfma_m = ring ? 16 : 32;
+    out->mfma_n = ring ? 16 : 32;
+    out->mfma_k = ring ? 32 : (c.eb == 4 ? 2 : 16);
+    out->lds_bytes = ring ? c.ring_lds : c.lds_bytes;
     out->name = c.name;
     return TGEMM_OK;
 }
@@ -273,6 +309,13 @@ int gemm_select_config(int64_t M, int64_t N, int64_t K, const void* A, int64_t l
     const int v = validate(M, N, K, A, lda, B, ldb, C, ldc, in_dtype, out_dtype);
     if (v != TGEMM_OK) return v;
     return table_choice(M, N, K, in_dtype);
+}
+
+int gemm_select_kernel(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                       const void* C, int64_t ldc, int in_dtype, int out_dtype, int config_id) {
+    Plan plan;
+    const int v = make_plan(M, N, K, A, lda, B, ldb, C, ldc, in_dtype, out_dtype, config_id, plan);
+    return v != TGEMM_OK ? v : plan.kind;
 }
 
 int gemm_tile_map(int bid, int tiles_m, int tiles_n, int group_m, int* tm, int* tn) {
