@@ -112,6 +112,9 @@ def main():
     ap.add_argument("--config", type=int, default=-1, help="force a tile configuration (gemm_ex)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-config", action="store_true")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="only run the MFMA ceiling program (issue rate and clock of both fp16 MFMA shapes on "
+                         "every SIMD, N(0,1) and all-ones operands) and print its JSON lines")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one elementwise kernel that reads and writes 512 MiB "
                          "(scale reference for the HBM byte counters)")
@@ -121,6 +124,14 @@ def main():
               "(a row-sharded multi-GPU product needs no collective; it is described, not built)",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.mfma_ceiling:
+        # a child process of its own, started before this process touches the GPU
+        from tiled_gemm_03_amd import build as B
+        if not os.path.exists(B.CEILING_BIN):
+            print("bench.py: the MFMA ceiling program is not built (run __graft_entry__.build())", file=sys.stderr)
+            sys.exit(1)
+        sys.exit(subprocess.run([B.CEILING_BIN]).returncode)
 
     import numpy as np
     import torch

@@ -14,6 +14,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libtgemm.so")
+# measurement program: MFMA issue rate and clock on every SIMD (bench.py --mfma-ceiling)
+CEILING_SRC = os.path.join(CSRC, "mfma_ceiling.hip")
+CEILING_BIN = os.path.join(HERE, "mfma_ceiling")
 SOURCES = [os.path.join(CSRC, "tgemm.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -43,5 +46,20 @@ def build(out: str = LIB, extra=(), verbose: bool = False) -> str:
     return out
 
 
+def build_ceiling(out: str = CEILING_BIN, verbose: bool = False) -> str:
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-O3", "-std=c++17",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", CEILING_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    msg = "\n".join(ln for ln in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in ln)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{msg}")
+    os.replace(tmp, out)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_ceiling(verbose=True))

@@ -128,6 +128,9 @@ void gemm_kernel_ring(GemmArgs p) {
     const int m0 = tm * T::BM, n0 = tn * T::BN;
     const int K = p.K;
     const int64_t lda = p.lda, ldb = p.ldb;
+    // 1: XOR-swizzled LDS layouts; 0: plain row-major LDS rows (kept for
+    // measuring bank conflicts against the swizzle)
+    const int swz = p.swz_mask != 0 ? 1 : 0;
 
     // ---------------------------------------------------------- a2: loads
     auto make_rsrc = [&](const char* base, int64_t bytes) __attribute__((always_inline)) {
@@ -149,11 +152,11 @@ void gemm_kernel_ring(GemmArgs p) {
     for (int x = 0; x < T::L; ++x) {
         if (x < T::A_LOADS) {
             const int r = (wave * T::A_LOADS + x) * T::A_RPB + lane / T::CA;
-            const int c = (lane % T::CA) ^ ring_key_a(r);
+            const int c = (lane % T::CA) ^ (swz * ring_key_a(r));
             voff[x] = (int)((int64_t)r * lda * 2 + c * 16);
         } else {
             const int r = (wave * T::B_LOADS + (x - T::A_LOADS)) * T::B_RPB + lane / T::CB;
-            const int c = (lane % T::CB) ^ ring_key_b(r);
+            const int c = (lane % T::CB) ^ (swz * ring_key_b(r));
             voff[x] = (int)((int64_t)r * ldb * 2 + c * 16);
         }
     }
@@ -181,12 +184,12 @@ void gemm_kernel_ring(GemmArgs p) {
     // ---------------------------------------------------------- a5: fragments
     const int q = lane >> 4, i16 = lane & 15;
     const int a_row = wm * T::WTM + i16;                     // + 16 i
-    lds_char* const a_base = lds + a_row * T::RA + (q ^ ring_key_a(a_row)) * 16;
+    lds_char* const a_base = lds + a_row * T::RA + (q ^ (swz * ring_key_a(a_row))) * 16;
     // B: lane i of group q points at k-row 8q + 4h + i/4 (h: which of the two
     // reads; in the immediate offset), columns 16 j + 4 (i%4) .. +3 of the
     // wave's block
     const int b_row = 8 * q + (i16 >> 2);
-    const int b_key = ring_key_b(b_row);
+    const int b_key = swz * ring_key_b(b_row);
     lds_char* b_base[T::FN];
 #pragma unroll
     for (int j = 0; j < T::FN; ++j) {
