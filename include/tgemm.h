@@ -107,7 +107,7 @@ typedef struct tgemm_config_info {
     int id;
     int in_dtype;       /* TGEMM_F16 configurations also serve TGEMM_BF16 */
     int block_m, block_n, block_k;
-    int stages;         /* LDS buffers in the software pipeline            */
+    int stages;         /* LDS buffers in the software pipeline (0: none) */
     int threads;        /* workitems per workgroup (64 per wavefront)      */
     int waves_m, waves_n;
     int mfma_m, mfma_n, mfma_k; /* shape of one MFMA instruction           */
@@ -130,6 +130,8 @@ int gemm_select_config(int64_t M, int64_t N, int64_t K,
 #define TGEMM_KERNEL_TILED 1   /* register-staged, whole tiles, aligned operands              */
 #define TGEMM_KERNEL_RING 2    /* direct-to-LDS rings: whole tiles of 16-bit inputs, aligned,
                                   K a multiple of 128 (configurations 0 and 1)             */
+#define TGEMM_KERNEL_DIRECT 3  /* operands straight from memory to registers, no LDS: small,
+                                  ragged or unaligned products (configurations 6 and 7)     */
 
 /* Host-side lookup only (no GPU call): which kernel gemm_ex(..., config_id)
  * would launch for these arguments (config_id -1: the table's choice), as a

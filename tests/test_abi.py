@@ -41,6 +41,9 @@ def test_version_and_configs():
         assert c["threads"] % 64 == 0
         assert c["threads"] == 64 * c["waves_m"] * c["waves_n"]
         assert c["lds_bytes"] <= 160 * 1024
+        if c["stages"] == 0:  # the direct kernel: operands straight to registers
+            assert c["lds_bytes"] == 0 and c["block_m"] == c["block_n"] == 32
+            continue
         eb = 4 if c["in_dtype"] == T.F32 else 2
         # LDS holds `stages` copies of an A tile (block_m x block_k) and a B
         # tile (block_k x block_n), the budget formula of page
@@ -188,6 +191,12 @@ def test_kernel_choice_ring_path():
     assert _kernel(-1, 4, 4) == T.ERR_DIM
     assert _kernel(4, 4, 4, in_dt=T.F16, out_dt=T.BF16) == T.ERR_DTYPE
     assert _kernel(4, 4, 4, cid=4) == T.ERR_CONFIG
+    # the direct kernel takes any alignment and raggedness
+    assert _kernel(127, 255, 512, ldb=255, ldc=255, cid=6) == T.KERNEL_DIRECT
+    assert _kernel(128, 128, 128, in_dt=T.F32, out_dt=T.F32, cid=7) == T.KERNEL_DIRECT
+    assert _kernel(5, 7, 3, offs=(1, 1, 1), cid=6) == T.KERNEL_DIRECT
+    # offsets beyond 2^31 bytes: the checked register-staged kernel instead
+    assert _kernel(64, 64, 1 << 20, ldb=1 << 12, cid=6) in (T.KERNEL_GENERAL, T.KERNEL_TILED)
 
 
 def test_ring_configs_report_their_ring_kernel():

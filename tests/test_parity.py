@@ -76,12 +76,16 @@ def test_bf16_at_128x256x512():
 
 
 # --------------------------------------------------------- ragged multi-tile
-@pytest.mark.parametrize("cid", range(6))
+@pytest.mark.parametrize("cid", range(T.gemm_num_configs()))
 def test_ragged_tiles_each_config(cid):
     info = T.gemm_config_info(cid)
     in_dts = [W.F32] if info["in_dtype"] == W.F32 else [W.F16, W.BF16]
     bm, bn, bk = info["block_m"], info["block_n"], info["block_k"]
     shapes = [(2 * bm + 7, 3 * bn - 5, 3 * bk + 9), (bm - 1, bn + 1, bk - 3), (3 * bm, 2 * bn, 2 * bk + 1)]
+    if info["stages"] == 0:
+        # the direct kernel's register ring holds 8 steps of 32 (4 for 16-bit
+        # A read element by element): K below, at and past whole rings
+        shapes += [(33, 47, 255), (64, 64, 256), (50, 70, 257), (31, 33, 1000)]
     for in_dt in in_dts:
         outs = [W.F32, in_dt] if in_dt != W.F32 else [W.F32]
         for (M, N, K) in shapes:
@@ -200,13 +204,16 @@ def test_nan_canary_and_guard_band(shape):
 
 
 def test_k_zero_writes_zeros():
+    """K = 0: the empty sum, under the table's choice and every
+    configuration; the operands are empty tensors (no memory to read)."""
     for in_dt, out_dt in ((W.F16, W.F16), (W.F32, W.F32), (W.BF16, W.F32)):
-        G.say(f"[case] K=0 {in_dt}->{out_dt}")
-        a = torch.empty((37, 0), dtype=G.TORCH[in_dt], device=G.DEV)
-        b = torch.empty((0, 45), dtype=G.TORCH[in_dt], device=G.DEV)
-        _, c = G.out_tensor(37, 45, out_dt)
-        G.run(a, b, c)
-        assert bool((c == 0).all())
+        for cid in [-1] + configs_for(in_dt):
+            G.say(f"[case] K=0 {in_dt}->{out_dt} cfg{cid}")
+            a = torch.empty((37, 0), dtype=G.TORCH[in_dt], device=G.DEV)
+            b = torch.empty((0, 45), dtype=G.TORCH[in_dt], device=G.DEV)
+            _, c = G.out_tensor(37, 45, out_dt)
+            G.run(a, b, c, cid)
+            assert bool((c == 0).all())
 
 
 def test_empty_m_or_n_is_a_noop():

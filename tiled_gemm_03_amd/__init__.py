@@ -28,7 +28,7 @@ EXPORTED = ["gemm", "gemm_ex", "gemm_strerror", "gemm_num_configs", "gemm_config
             "gemm_select_config", "gemm_select_kernel", "gemm_tile_map", "gemm_version"]
 
 # gemm_select_kernel results
-KERNEL_GENERAL, KERNEL_TILED, KERNEL_RING = 0, 1, 2
+KERNEL_GENERAL, KERNEL_TILED, KERNEL_RING, KERNEL_DIRECT = 0, 1, 2, 3
 
 
 class ConfigInfo(ctypes.Structure):

@@ -141,9 +141,10 @@ void gemm_kernel_ring(GemmArgs p) {
                      __builtin_amdgcn_readfirstlane((int)n), 0x00020000};
     };
     // byte ranges end at the operand's last element (A: row M-1, column K-1;
-    // B: row K-1, column N-1), counted from the tile's corner
-    const i32x4 rs_a = make_rsrc(p.A + (int64_t)m0 * lda * 2, ((int64_t)(p.M - 1 - m0) * lda + K) * 2);
-    const i32x4 rs_b = make_rsrc(p.B + (int64_t)n0 * 2, ((int64_t)(K - 1) * ldb + p.N - n0) * 2);
+    // B: row K-1, column N-1), counted from the tile's corner; empty when
+    // K = 0 (no load is issued then)
+    const i32x4 rs_a = make_rsrc(p.A + (int64_t)m0 * lda * 2, K > 0 ? ((int64_t)(p.M - 1 - m0) * lda + K) * 2 : 0);
+    const i32x4 rs_b = make_rsrc(p.B + (int64_t)n0 * 2, K > 0 ? ((int64_t)(K - 1) * ldb + p.N - n0) * 2 : 0);
     // load x of a wave: A block wave*A_LOADS + x (x < A_LOADS), else B block
     // wave*B_LOADS + x - A_LOADS.  Lane l fills slot l of the 1 KiB block
     // (row l / C, chunk l % C) with the logical chunk the swizzle puts there.

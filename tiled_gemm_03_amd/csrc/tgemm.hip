@@ -1,13 +1,16 @@
 // tgemm.hip -- C ABI of libtgemm.so: argument checks, the per-shape tile
 // configuration table and the kernel launch.  The kernels are in
 // gemm_kernel.hpp (register-staged; every shape, type and alignment) and
-// gemm_kernel_ring.hpp (direct-to-LDS rings; whole tiles of 16-bit inputs);
-// the ABI is declared (and documented) in include/tgemm.h.
+// gemm_kernel_ring.hpp (direct-to-LDS rings; whole tiles of 16-bit inputs)
+// and gemm_kernel_direct.hpp (operands straight to registers; small, ragged
+// or unaligned products); the ABI is declared (and documented) in
+// include/tgemm.h.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
 
 #include "gemm_kernel.hpp"
+#include "gemm_kernel_direct.hpp"
 #include "gemm_kernel_ring.hpp"
 #include "tgemm.h"
 
@@ -32,6 +35,7 @@ typedef void (*KernelFn)(GemmArgs);
 struct ConfigEntry {
     const char* name;
     int in_family;  // TGEMM_F16 (serves F16 and BF16) or TGEMM_F32
+    bool direct;    // the direct kernel (32 x 32 per workgroup, no LDS)
     int bm, bn, bk, wm, wn, eb, lds_bytes, threads, cpr;
     KernelFn (*pick)(int in, int out, bool fast);
     // direct-to-LDS ring kernel of the same output tile (whole tiles, K a
@@ -78,11 +82,29 @@ KernelFn pick_f32(int in, int out, bool fast) {
     return nullptr;
 }
 
-#define ENTRY(name, fam, T, pk) \
-    {name, fam, T::BM, T::BN, T::BK, T::WM, T::WN, T::EB, T::LDS_BYTES, T::THREADS, T::CPR, pk<T>, nullptr, 0, 0, 0, 0}
-#define ENTRY_RING(name, fam, T, pk, R)                                                                      \
-    {name, fam, T::BM, T::BN, T::BK, T::WM, T::WN, T::EB, T::LDS_BYTES, T::THREADS, T::CPR, pk<T>, pick_ring<R>, \
-     R::BK, R::S, R::K_MULT, R::LDS_BYTES}
+#define ENTRY(name, fam, T, pk)                                                                         \
+    {name, fam, false, T::BM, T::BN, T::BK, T::WM, T::WN, T::EB, T::LDS_BYTES, T::THREADS, T::CPR, pk<T>, nullptr, \
+     0, 0, 0, 0}
+#define ENTRY_RING(name, fam, T, pk, R)                                                                          \
+    {name, fam, false, T::BM, T::BN, T::BK, T::WM, T::WN, T::EB, T::LDS_BYTES, T::THREADS, T::CPR, pk<T>,        \
+     pick_ring<R>, R::BK, R::S, R::K_MULT, R::LDS_BYTES}
+// direct kernel: 32 x 32 per workgroup of 2 x 2 waves, steps of 32 of K
+#define ENTRY_DIRECT(name, fam, eb, pk) \
+    {name, fam, true, 32, 32, 32, 2, 2, eb, 0, 256, 1, pk, nullptr, 0, 0, 0, 0}
+
+// direct kernel for (in, out); `avec`: A rows are whole 16-byte chunks
+KernelFn pick_direct(int in, int out, bool avec) {
+    if (in == TGEMM_F32) return out == TGEMM_F32 ? gemm_kernel_direct<DT_F32, DT_F32, false> : nullptr;
+    if (in == TGEMM_F16 && out == TGEMM_F16)
+        return avec ? gemm_kernel_direct<DT_F16, DT_F16, true> : gemm_kernel_direct<DT_F16, DT_F16, false>;
+    if (in == TGEMM_F16 && out == TGEMM_F32)
+        return avec ? gemm_kernel_direct<DT_F16, DT_F32, true> : gemm_kernel_direct<DT_F16, DT_F32, false>;
+    if (in == TGEMM_BF16 && out == TGEMM_BF16)
+        return avec ? gemm_kernel_direct<DT_BF16, DT_BF16, true> : gemm_kernel_direct<DT_BF16, DT_BF16, false>;
+    if (in == TGEMM_BF16 && out == TGEMM_F32)
+        return avec ? gemm_kernel_direct<DT_BF16, DT_F32, true> : gemm_kernel_direct<DT_BF16, DT_F32, false>;
+    return nullptr;
+}
 
 const ConfigEntry kConfigs[] = {
     ENTRY_RING("h256x256_w2x2", TGEMM_F16, CfgBig, pick_half, RingBig),
@@ -91,9 +113,12 @@ const ConfigEntry kConfigs[] = {
     ENTRY("h32x32x64_w1x1", TGEMM_F16, CfgTiny, pick_half),
     ENTRY("s64x64x32_w2x2", TGEMM_F32, CfgF32Mid, pick_f32),
     ENTRY("s32x32x32_w1x1", TGEMM_F32, CfgF32Tiny, pick_f32),
+    ENTRY_DIRECT("h32x32_direct", TGEMM_F16, 2, pick_direct),
+    ENTRY_DIRECT("s32x32_direct", TGEMM_F32, 4, pick_direct),
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
-enum { CFG_BIG = 0, CFG_MID = 1, CFG_SMALL = 2, CFG_TINY = 3, CFG_F32_MID = 4, CFG_F32_TINY = 5 };
+enum { CFG_BIG = 0, CFG_MID = 1, CFG_SMALL = 2, CFG_TINY = 3, CFG_F32_MID = 4, CFG_F32_TINY = 5,
+       CFG_DIRECT = 6, CFG_F32_DIRECT = 7 };
 
 // Measurement-only switches, read once from the environment:
 //   TGEMM_GROUP_M=<n>    tile rows per raster group (default 4)
@@ -163,17 +188,53 @@ bool stores_aligned(const void* C, int64_t ldc, int out) {
 
 int64_t tiles_for(const ConfigEntry& c, int64_t M, int64_t N) { return ceil_div(M, c.bm) * ceil_div(N, c.bn); }
 
-// The per-shape table.  Each choice keeps the chip's 256 CUs busy with the
-// largest tile that still gives enough workgroups; small problems take the
-// smallest tile, which maximises parallelism where launch latency and one
-// workgroup's K loop set the time.
-int table_choice(int64_t M, int64_t N, int64_t K, int in) {
-    (void)K;
-    if (in == TGEMM_F32)
-        return tiles_for(kConfigs[CFG_F32_MID], M, N) >= 256 ? CFG_F32_MID : CFG_F32_TINY;
+// Whether a register-staged configuration runs its unchecked path: whole
+// tiles, 16-byte aligned operands, 4-element aligned C rows, offsets within
+// 31 bits.
+bool tiled_fast(const ConfigEntry& c, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                int64_t ldb, const void* C, int64_t ldc, int out) {
+    const bool offsets_fit = (int64_t)c.bm * lda * c.eb + K * c.eb < (1LL << 31) &&
+                             (int64_t)c.bk * ldb * c.eb + N * c.eb < (1LL << 31);
+    return loads_aligned(c, A, lda, B, ldb) && stores_aligned(C, ldc, out) && offsets_fit && M % c.bm == 0 &&
+           N % c.bn == 0;
+}
+
+// Whether a configuration with a ring kernel runs it.
+bool ring_applies(const ConfigEntry& c, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                  int64_t ldb, const void* C, int64_t ldc, int out) {
+    return c.pick_ring != nullptr && tiled_fast(c, M, N, K, A, lda, B, ldb, C, ldc, out) &&
+           ((int64_t)c.bm * lda + K + (int64_t)c.ring_stages * c.ring_bk) * c.eb < (1LL << 31) &&
+           ((K + (int64_t)c.ring_stages * c.ring_bk) * ldb + c.bn) * c.eb < (1LL << 31) &&
+           K % c.ring_k_mult == 0 && tuning().direct_lds;
+}
+
+// The per-shape table (measured on MI355X; kernel times from rocprofv3
+// traces of the five workloads under every configuration):
+//  * enough 256 x 256 tiles for all 256 CUs: the 256 x 256 configuration
+//    (the direct-to-LDS ring kernel when it applies);
+//  * the 128 x 128 ring kernel from 128 tiles up when it applies (it beats
+//    64 x 64 register-staged tiles at 1024 x 2048 x 512: 8.6 vs 11.1 us),
+//    otherwise the largest register-staged tile that still gives 256 tiles;
+//  * small products (M N <= 2^18) whose register-staged tile would run its
+//    checked path (ragged or unaligned operands) take the direct kernel
+//    (127 x 255 x 512 with ldb = 255: about 8 us instead of 60-90 us);
+//  * other small products the smallest register-staged tile, which
+//    maximises parallelism where launch latency and one workgroup's K loop
+//    set the time.
+int table_choice(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                 const void* C, int64_t ldc, int in, int out) {
+    const bool small = M * N <= (1LL << 18);
+    if (in == TGEMM_F32) {
+        if (tiles_for(kConfigs[CFG_F32_MID], M, N) >= 256) return CFG_F32_MID;
+        if (small && !tiled_fast(kConfigs[CFG_F32_TINY], M, N, K, A, lda, B, ldb, C, ldc, out)) return CFG_F32_DIRECT;
+        return CFG_F32_TINY;
+    }
     if (tiles_for(kConfigs[CFG_BIG], M, N) >= 256) return CFG_BIG;
+    if (tiles_for(kConfigs[CFG_MID], M, N) >= 128 && ring_applies(kConfigs[CFG_MID], M, N, K, A, lda, B, ldb, C, ldc, out))
+        return CFG_MID;
     if (tiles_for(kConfigs[CFG_MID], M, N) >= 256) return CFG_MID;
     if (tiles_for(kConfigs[CFG_SMALL], M, N) >= 256) return CFG_SMALL;
+    if (small && !tiled_fast(kConfigs[CFG_TINY], M, N, K, A, lda, B, ldb, C, ldc, out)) return CFG_DIRECT;
     return CFG_TINY;
 }
 
@@ -186,6 +247,9 @@ struct Plan {
     KernelFn fn;
 };
 
+int plan_tiled(const ConfigEntry& c, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+               int64_t ldb, const void* C, int64_t ldc, int in, int out, Plan& plan);
+
 // Validates the arguments and picks the kernel; returns TGEMM_OK (plan
 // filled; M == 0 or N == 0 leaves plan.fn null) or a negative error code.
 int make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
@@ -194,24 +258,32 @@ int make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const
     if (v != TGEMM_OK) return v;
     if (config_id < -1 || config_id >= kNumConfigs) return TGEMM_ERR_CONFIG;
     if (config_id >= 0 && kConfigs[config_id].in_family != family_of(in)) return TGEMM_ERR_CONFIG;
-    plan.config = config_id >= 0 ? config_id : table_choice(M, N, K, in);
+    plan.config = config_id >= 0 ? config_id : table_choice(M, N, K, A, lda, B, ldb, C, ldc, in, out);
     plan.fn = nullptr;
     plan.kind = TGEMM_KERNEL_GENERAL;
     if (M == 0 || N == 0) return TGEMM_OK;
     const ConfigEntry& c = kConfigs[plan.config];
-    const bool vec_ab = loads_aligned(c, A, lda, B, ldb);
-    const bool vec_c = stores_aligned(C, ldc, out);
-    // the register-staged kernel addresses A and B through 32-bit buffer
-    // offsets within a tile's rows (A) or one K step's rows (B)
-    const bool offsets_fit = (int64_t)c.bm * lda * c.eb + K * c.eb < (1LL << 31) &&
-                             (int64_t)c.bk * ldb * c.eb + N * c.eb < (1LL << 31);
-    const bool fast = vec_ab && vec_c && offsets_fit && M % c.bm == 0 && N % c.bn == 0;
-    // the ring kernel addresses A through BM rows plus K + S*BK columns and B
-    // through K + S*BK rows with 32-bit buffer offsets
-    const bool ring_fits = c.pick_ring != nullptr &&
-                           ((int64_t)c.bm * lda + K + (int64_t)c.ring_stages * c.ring_bk) * c.eb < (1LL << 31) &&
-                           ((K + (int64_t)c.ring_stages * c.ring_bk) * ldb + c.bn) * c.eb < (1LL << 31);
-    const bool ring = fast && ring_fits && K % c.ring_k_mult == 0 && tuning().direct_lds;
+    if (c.direct) {
+        // buffer offsets: 32 rows of A plus K + 320 columns; K + 320 rows of B
+        if (((int64_t)32 * lda + K + 320) * c.eb >= (1LL << 31) || ((K + 320) * ldb + 32) * c.eb >= (1LL << 31))
+            plan.config = in == TGEMM_F32 ? CFG_F32_TINY : CFG_TINY;  // offsets too wide: the checked kernel
+        else {
+            const bool avec = in != TGEMM_F32 && (uintptr_t)A % 16 == 0 && lda % 8 == 0 && K % 8 == 0;
+            plan.kind = TGEMM_KERNEL_DIRECT;
+            plan.fn = c.pick(in, out, avec);
+            if (plan.fn == nullptr) return TGEMM_ERR_DTYPE;
+            if (ceil_div(M, c.bm) * ceil_div(N, c.bn) > 0x7fffffff) return TGEMM_ERR_DIM;
+            return TGEMM_OK;
+        }
+    }
+    const ConfigEntry& t = kConfigs[plan.config];
+    return plan_tiled(t, M, N, K, A, lda, B, ldb, C, ldc, in, out, plan);
+}
+
+int plan_tiled(const ConfigEntry& c, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+               int64_t ldb, const void* C, int64_t ldc, int in, int out, Plan& plan) {
+    const bool fast = tiled_fast(c, M, N, K, A, lda, B, ldb, C, ldc, out);
+    const bool ring = ring_applies(c, M, N, K, A, lda, B, ldb, C, ldc, out);
     plan.kind = ring ? TGEMM_KERNEL_RING : fast ? TGEMM_KERNEL_TILED : TGEMM_KERNEL_GENERAL;
     plan.fn = ring ? c.pick_ring(in, out) : c.pick(in, out, fast);
     if (plan.fn == nullptr) return TGEMM_ERR_DTYPE;
@@ -291,16 +363,26 @@ int gemm_config_info(int id, tgemm_config_info* out) {
     out->in_dtype = c.in_family;
     out->block_m = c.bm;
     out->block_n = c.bn;
-    out->block_k = ring ? c.ring_bk : c.bk;
-    out->stages = ring ? c.ring_stages : 2;
     out->threads = c.threads;
     out->waves_m = c.wm;
     out->waves_n = c.wn;
+    out->name = c.name;
+    if (c.direct) {
+        // operands go straight to registers: no LDS stage
+        out->block_k = 32;
+        out->stages = 0;
+        out->mfma_m = 16;
+        out->mfma_n = 16;
+        out->mfma_k = c.eb == 4 ? 4 : 32;
+        out->lds_bytes = 0;
+        return TGEMM_OK;
+    }
+    out->block_k = ring ? c.ring_bk : c.bk;
+    out->stages = ring ? c.ring_stages : 2;
     out->mfma_m = ring ? 16 : 32;
     out->mfma_n = ring ? 16 : 32;
     out->mfma_k = ring ? 32 : (c.eb == 4 ? 2 : 16);
     out->lds_bytes = ring ? c.ring_lds : c.lds_bytes;
-    out->name = c.name;
     return TGEMM_OK;
 }
 
@@ -308,7 +390,7 @@ int gemm_select_config(int64_t M, int64_t N, int64_t K, const void* A, int64_t l
                        const void* C, int64_t ldc, int in_dtype, int out_dtype) {
     const int v = validate(M, N, K, A, lda, B, ldb, C, ldc, in_dtype, out_dtype);
     if (v != TGEMM_OK) return v;
-    return table_choice(M, N, K, in_dtype);
+    return table_choice(M, N, K, A, lda, B, ldb, C, ldc, in_dtype, out_dtype);
 }
 
 int gemm_select_kernel(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
