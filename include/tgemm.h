@@ -58,7 +58,15 @@ extern "C" {
 #define TGEMM_ERR_LD (-3)          /* lda < K, ldb < N or ldc < N                */
 #define TGEMM_ERR_DTYPE (-4)       /* unsupported (in_dtype, out_dtype) pair     */
 #define TGEMM_ERR_ALIAS (-5)       /* C overlaps A or B                          */
-#define TGEMM_ERR_CONFIG (-6)      /* gemm_ex: unknown config or wrong dtype     */
+#define TGEMM_ERR_CONFIG (-6)      /* gemm_ex / gemm_t: unknown config, wrong
+                                      dtype, or a config without a kernel for
+                                      column-major operands                  */
+#define TGEMM_ERR_LAYOUT (-7)      /* gemm_t: layout not ROW_MAJOR / COL_MAJOR  */
+
+/* Operand layouts (gemm_t): the row-major default and the column-major option
+ * of page "TileLang实战：用Python DSL自动生成高性能GPU计算内核", §5.1. */
+#define TGEMM_ROW_MAJOR 0 /* element (i, j) of X at X[i * ld + j] */
+#define TGEMM_COL_MAJOR 1 /* element (i, j) of X at X[j * ld + i] */
 
 /* Largest M, N or K accepted (tile indices are 32-bit; element offsets are
  * 64-bit, so matrices may exceed 4 GiB). */
@@ -93,8 +101,28 @@ int gemm_ex(int64_t M, int64_t N, int64_t K,
             void* C, int64_t ldc, int in_dtype, int out_dtype, void* stream,
             int config_id);
 
-/* Human-readable text for a return code of gemm / gemm_ex (never NULL; the
- * string is static). */
+/*
+ * gemm_t: C := A x B with a layout per matrix (TGEMM_ROW_MAJOR or
+ * TGEMM_COL_MAJOR).  A is logically M x K, B K x N, C M x N; a column-major
+ * X stores its transpose row by row, so lda >= K for a row-major A and
+ * lda >= M for a column-major one (ldb >= N or K, ldc >= N or M likewise).
+ * gemm(...) is gemm_t(..., ROW_MAJOR, ..., ROW_MAJOR, ..., ROW_MAJOR, ..., -1).
+ * A column-major C is computed as the row-major C^T = B^T x A^T.  Kernels:
+ * row-major A and B take every configuration; with a column-major operand
+ * the direct-to-LDS ring kernels of configurations 0 and 1 run whole aligned
+ * tiles, the direct kernels of configurations 6 and 7 everything else
+ * (configurations 2 to 5 return TGEMM_ERR_CONFIG there, and products whose
+ * 32-bit buffer offsets would overflow return TGEMM_ERR_DIM).  config_id -1:
+ * the table's choice.  Other arguments, ownership and errors as gemm_ex.
+ */
+int gemm_t(int64_t M, int64_t N, int64_t K,
+           const void* A, int64_t lda, int layout_a,
+           const void* B, int64_t ldb, int layout_b,
+           void* C, int64_t ldc, int layout_c,
+           int in_dtype, int out_dtype, void* stream, int config_id);
+
+/* Human-readable text for a return code of gemm / gemm_ex / gemm_t (never
+ * NULL; the string is static). */
 const char* gemm_strerror(int code);
 
 /* Number of tile configurations in the table. */
@@ -142,6 +170,14 @@ int gemm_select_config(int64_t M, int64_t N, int64_t K,
 int gemm_select_kernel(int64_t M, int64_t N, int64_t K,
                        const void* A, int64_t lda, const void* B, int64_t ldb,
                        const void* C, int64_t ldc, int in_dtype, int out_dtype, int config_id);
+
+/* gemm_select_kernel for gemm_t's arguments; also stores the configuration
+ * that would run in *config_out (if not NULL).  Host-side lookup only. */
+int gemm_select_kernel_t(int64_t M, int64_t N, int64_t K,
+                         const void* A, int64_t lda, int layout_a,
+                         const void* B, int64_t ldb, int layout_b,
+                         const void* C, int64_t ldc, int layout_c,
+                         int in_dtype, int out_dtype, int config_id, int* config_out);
 
 /* Host-side copy of the workgroup -> output-tile map the kernels use (no GPU
  * call), for checking that it is a bijection: workgroup `bid` of a grid of

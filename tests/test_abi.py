@@ -204,3 +204,58 @@ def test_ring_configs_report_their_ring_kernel():
         c = T.gemm_config_info(cid)
         assert (c["block_k"], c["stages"]) == (32, 4)
         assert (c["mfma_m"], c["mfma_n"], c["mfma_k"]) == (16, 16, 32)
+
+
+R_, C_ = T.ROW_MAJOR, T.COL_MAJOR
+
+
+def _kernel_t(M, N, K, la, lb, lc, lda=None, ldb=None, ldc=None, in_dt=T.F16, out_dt=T.F16, cid=-1):
+    lda = (K if la == R_ else M) if lda is None else lda
+    ldb = (N if lb == R_ else K) if ldb is None else ldb
+    ldc = (N if lc == R_ else M) if ldc is None else ldc
+    return T.gemm_select_kernel_t(M, N, K, FAKE, lda, la, FAKE + (1 << 36), ldb, lb, FAKE + (2 << 36), ldc, lc,
+                                  in_dt, out_dt, cid)
+
+
+def test_layout_arguments_are_checked():
+    # layouts other than 0 / 1
+    assert T.gemm_t(4, 4, 4, FAKE, 4, 2, FAKE + 4096, 4, 0, FAKE + 8192, 4, 0, 1, 1, None, -1) == T.ERR_LAYOUT
+    assert T.gemm_t(4, 4, 4, FAKE, 4, 0, FAKE + 4096, 4, -1, FAKE + 8192, 4, 0, 1, 1, None, -1) == T.ERR_LAYOUT
+    assert T.gemm_t(4, 4, 4, FAKE, 4, 0, FAKE + 4096, 4, 0, FAKE + 8192, 4, 7, 1, 1, None, -1) == T.ERR_LAYOUT
+    # leading dimensions follow the stored shape: a column-major A (K x M
+    # stored) needs lda >= M, a column-major B ldb >= K, a column-major C
+    # ldc >= M
+    assert T.gemm_t(8, 4, 2, FAKE, 7, C_, FAKE + 4096, 4, R_, FAKE + 8192, 4, R_, 1, 1, None, -1) == T.ERR_LD
+    assert T.gemm_t(8, 4, 2, FAKE, 8, C_, FAKE + 4096, 4, R_, FAKE + 8192, 4, R_, 1, 1, None, -1) != T.ERR_LD
+    assert T.gemm_t(8, 4, 6, FAKE, 6, R_, FAKE + 4096, 5, C_, FAKE + 8192, 4, R_, 1, 1, None, -1) == T.ERR_LD
+    assert T.gemm_t(8, 4, 6, FAKE, 6, R_, FAKE + 4096, 4, R_, FAKE + 8192, 7, C_, 1, 1, None, -1) == T.ERR_LD
+    # gemm is gemm_t with every operand row-major
+    assert T.gemm(-1, 4, 4, FAKE, 4, FAKE, 4, FAKE, 4, 1, 1, None) == T.ERR_DIM
+
+
+def test_kernel_choice_for_layouts():
+    RING, DIRECT = T.KERNEL_RING, T.KERNEL_DIRECT
+    for la in (R_, C_):
+        for lb in (R_, C_):
+            for lc in (R_, C_):
+                k, cfg = _kernel_t(8192, 8192, 8192, la, lb, lc)
+                assert (k, cfg) == (RING, 0), (la, lb, lc)
+                k, cfg = _kernel_t(1024, 2048, 512, la, lb, lc, out_dt=T.F32)
+                assert (k, cfg) == (RING, 1), (la, lb, lc)
+                k, cfg = _kernel_t(127, 255, 512, la, lb, lc, out_dt=T.F32)
+                if (la, lb, lc) == (R_, R_, R_):
+                    assert k == DIRECT or k >= 0
+                else:
+                    assert (k, cfg) == (DIRECT, 6), (la, lb, lc)
+                k, cfg = _kernel_t(100, 60, 30, la, lb, lc, in_dt=T.F32, out_dt=T.F32)
+                if (la, lb, lc) != (R_, R_, R_):
+                    assert (k, cfg) == (DIRECT, 7)
+    # a column-major operand and a configuration that has only a
+    # register-staged kernel
+    assert _kernel_t(256, 256, 256, C_, R_, R_, cid=2)[0] == T.ERR_CONFIG
+    assert _kernel_t(256, 256, 256, R_, R_, R_, cid=2)[0] == T.KERNEL_TILED
+    # forced ring configuration on a ragged shape: the direct kernel runs
+    assert _kernel_t(250, 256, 256, C_, C_, R_, cid=0) == (DIRECT, 6)
+    # a column-major C swaps the roles of A and B: its 128 rows become the
+    # N of the row-major product (128 x 128 tiles)
+    assert _kernel_t(128, 8192, 8192, R_, R_, C_)[0] == RING

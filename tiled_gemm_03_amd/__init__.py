@@ -22,10 +22,13 @@ LIB_PATH = os.path.join(HERE, "libtgemm.so")
 
 F32, F16, BF16 = 0, 1, 2
 OK = 0
-ERR_DIM, ERR_NULL, ERR_LD, ERR_DTYPE, ERR_ALIAS, ERR_CONFIG = -1, -2, -3, -4, -5, -6
+ERR_DIM, ERR_NULL, ERR_LD, ERR_DTYPE, ERR_ALIAS, ERR_CONFIG, ERR_LAYOUT = -1, -2, -3, -4, -5, -6, -7
 
-EXPORTED = ["gemm", "gemm_ex", "gemm_strerror", "gemm_num_configs", "gemm_config_info",
-            "gemm_select_config", "gemm_select_kernel", "gemm_tile_map", "gemm_version"]
+EXPORTED = ["gemm", "gemm_ex", "gemm_t", "gemm_strerror", "gemm_num_configs", "gemm_config_info",
+            "gemm_select_config", "gemm_select_kernel", "gemm_select_kernel_t", "gemm_tile_map", "gemm_version"]
+
+# operand layouts (gemm_t)
+ROW_MAJOR, COL_MAJOR = 0, 1
 
 # gemm_select_kernel results
 KERNEL_GENERAL, KERNEL_TILED, KERNEL_RING, KERNEL_DIRECT = 0, 1, 2, 3
@@ -76,6 +79,10 @@ def lib():
     L.gemm_config_info.argtypes = [i, ctypes.POINTER(ConfigInfo)]
     L.gemm_select_config.restype = i
     L.gemm_select_config.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, i, i]
+    L.gemm_t.restype = i
+    L.gemm_t.argtypes = [i64, i64, i64, p, i64, i, p, i64, i, p, i64, i, i, i, p, i]
+    L.gemm_select_kernel_t.restype = i
+    L.gemm_select_kernel_t.argtypes = [i64, i64, i64, p, i64, i, p, i64, i, p, i64, i, i, i, i, ctypes.POINTER(i)]
     L.gemm_select_kernel.restype = i
     L.gemm_select_kernel.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, i, i, i]
     L.gemm_tile_map.restype = i
@@ -114,6 +121,21 @@ def gemm_select_config(M, N, K, A, lda, B, ldb, C, ldc, in_dtype, out_dtype):
     return lib().gemm_select_config(M, N, K, A, lda, B, ldb, C, ldc, in_dtype, out_dtype)
 
 
+def gemm_t(M, N, K, A, lda, layout_a, B, ldb, layout_b, C, ldc, layout_c, in_dtype, out_dtype, stream=None,
+           config_id=-1):
+    return lib().gemm_t(M, N, K, A, lda, layout_a, B, ldb, layout_b, C, ldc, layout_c, in_dtype, out_dtype, stream,
+                        config_id)
+
+
+def gemm_select_kernel_t(M, N, K, A, lda, layout_a, B, ldb, layout_b, C, ldc, layout_c, in_dtype, out_dtype,
+                         config_id=-1):
+    """(kernel kind or negative error, configuration that would run)."""
+    cfg = ctypes.c_int(-1)
+    k = lib().gemm_select_kernel_t(M, N, K, A, lda, layout_a, B, ldb, layout_b, C, ldc, layout_c, in_dtype,
+                                   out_dtype, config_id, ctypes.byref(cfg))
+    return k, cfg.value
+
+
 def gemm_select_kernel(M, N, K, A, lda, B, ldb, C, ldc, in_dtype, out_dtype, config_id=-1):
     return lib().gemm_select_kernel(M, N, K, A, lda, B, ldb, C, ldc, in_dtype, out_dtype, config_id)
 
@@ -147,10 +169,25 @@ def _ld(t):
     return max(t.stride(0) if t.shape[0] > 1 else t.shape[1], t.shape[1])
 
 
+def _layout(t):
+    """(layout, leading dimension) of a 2-D tensor: row-major when its rows
+    are contiguous, column-major when its columns are (a transposed view)."""
+    if t.dim() != 2:
+        raise ValueError("expected a 2-D tensor")
+    r, c = t.shape
+    if r == 0 or c == 0 or t.stride(1) == 1:
+        return ROW_MAJOR, max(t.stride(0) if r > 1 else c, c, 1)
+    if t.stride(0) == 1:
+        return COL_MAJOR, max(t.stride(1) if c > 1 else r, r, 1)
+    raise ValueError("tensor needs contiguous rows or contiguous columns")
+
+
 def gemm_tensors(a, b, c, config_id=-1, stream=None, check=True):
     """c := a @ b on the device, through the C ABI.  a: M x K, b: K x N,
-    c: M x N torch tensors on the GPU (rows may be padded).  Returns the
-    library's return code (raises TgemmError on failure if check)."""
+    c: M x N torch tensors on the GPU, each with contiguous rows (row-major,
+    rows may be padded) or contiguous columns (column-major, e.g. a
+    transposed view).  Returns the library's return code (raises TgemmError
+    on failure if check)."""
     import torch
     M, K = a.shape
     K2, N = b.shape
@@ -160,8 +197,11 @@ def gemm_tensors(a, b, c, config_id=-1, stream=None, check=True):
         raise TypeError("a and b must have one dtype")
     if stream is None:
         stream = torch.cuda.current_stream(a.device).cuda_stream
-    rc = gemm_ex(M, N, K, a.data_ptr(), _ld(a), b.data_ptr(), _ld(b), c.data_ptr(), _ld(c),
-                 dtype_code(a), dtype_code(c), stream, config_id)
+    la, lda = _layout(a)
+    lb, ldb = _layout(b)
+    lc, ldc = _layout(c)
+    rc = gemm_t(M, N, K, a.data_ptr(), lda, la, b.data_ptr(), ldb, lb, c.data_ptr(), ldc, lc,
+                dtype_code(a), dtype_code(c), stream, config_id)
     if check and rc != OK:
         raise TgemmError(rc)
     return rc

@@ -17,7 +17,10 @@ LIB = os.path.join(HERE, "libtgemm.so")
 # measurement program: MFMA issue rate and clock on every SIMD (bench.py --mfma-ceiling)
 CEILING_SRC = os.path.join(CSRC, "mfma_ceiling.hip")
 CEILING_BIN = os.path.join(HERE, "mfma_ceiling")
-SOURCES = [os.path.join(CSRC, "tgemm.hip")]
+# the host code and the kernel units (compiled in parallel, then linked)
+SOURCES = [os.path.join(CSRC, f) for f in (
+    "tgemm.hip", "k_tiled_big.hip", "k_tiled_mid.hip", "k_tiled_small.hip", "k_tiled_tiny.hip", "k_tiled_f32.hip",
+    "k_ring_big.hip", "k_ring_mid.hip", "k_direct.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -29,20 +32,44 @@ HIPFLAGS = [
 ]
 
 
-def build(out: str = LIB, extra=(), verbose: bool = False) -> str:
-    tmp = out + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *HIPFLAGS, *extra, *SOURCES, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+def _hipcc(cmd):
     r = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass does not know the packed-fp32-ops feature and says so
-    noise = "packed-fp32-ops"
-    msg = "\n".join(ln for ln in (r.stdout + r.stderr).splitlines() if noise not in ln)
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{msg}")
-    if msg.strip() and verbose:
-        print(msg, file=sys.stderr)
-    os.replace(tmp, out)
+    msg = "\n".join(ln for ln in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in ln)
+    return r.returncode, msg
+
+
+def build(out: str = LIB, extra=(), verbose: bool = False, jobs: int = 0) -> str:
+    """Compiles every source to an object (in parallel), then links them."""
+    from concurrent.futures import ThreadPoolExecutor
+    jobs = jobs or max(1, min(len(SOURCES), os.cpu_count() or 1))
+    tag = "%d" % os.getpid()
+    objs = [os.path.join(HERE, "_obj_" + os.path.splitext(os.path.basename(src))[0] + "." + tag + ".o")
+            for src in SOURCES]
+    compile_flags = [f for f in HIPFLAGS if f != "-shared"] + ["-c"]
+    cmds = [[HIPCC, *compile_flags, *extra, src, "-o", obj] for src, obj in zip(SOURCES, objs)]
+    try:
+        with ThreadPoolExecutor(jobs) as ex:
+            results = list(ex.map(_hipcc, cmds))
+        for cmd, (rc, msg) in zip(cmds, results):
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            if rc != 0:
+                raise RuntimeError(f"hipcc failed ({rc}) on {cmd[-3]}:\n{msg}")
+            if msg.strip() and verbose:
+                print(msg, file=sys.stderr)
+        tmp = out + ".tmp" + tag
+        link = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+        if verbose:
+            print(" ".join(link), flush=True)
+        rc, msg = _hipcc(link)
+        if rc != 0:
+            raise RuntimeError(f"link failed ({rc}):\n{msg}")
+        os.replace(tmp, out)
+    finally:
+        for o in objs:
+            if os.path.exists(o):
+                os.remove(o)
     return out
 
 

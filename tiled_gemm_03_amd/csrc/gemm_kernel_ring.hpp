@@ -28,8 +28,8 @@
 //        B is the first operand and A the second, so the accumulator holds C
 //        transposed: lane l owns row l % 16 and the 4 consecutive columns
 //        4 (l / 16) .. of each 16 x 16 block, stored with one write.
-//  * B stays k-major in LDS (rows of BN elements) and its operand is read
-//        with ds_read_b64_tr_b16: in each group of 16 lanes, lane i points at
+//  * A k-strided operand is read with ds_read_b64_tr_b16: in each group of
+//        16 lanes, lane i points at
 //        4 consecutive columns of k-row i / 4 and receives element i % 4 of
 //        the loads of lanes i / 4, i / 4 + 4, i / 4 + 8, i / 4 + 12, i.e.
 //        one column of a 4-row block.  Two such reads give the 8 k-values of
@@ -39,13 +39,20 @@
 //        address arithmetic: with one wave per SIMD, every instruction between
 //        two MFMAs takes issue slots that the MFMA pipe would otherwise use.
 //
-// LDS layout: the A ring (S stages of BM rows x 64 bytes) and then the B ring
-// (S stages of 32 k-rows x 2 BN bytes).
-//   A: 16-byte chunk c of row r stored at chunk c ^ ((r / 4) % 4): the 16
-//      rows read by one quarter wave (one ds_read_b128 cycle) land in 16
-//      different bank groups.
-//   B: chunk c of k-row r stored at chunk c ^ (4 (r % 4) ^ 2 ((r / 8) % 2)):
-//      the rows r .. r+3 and r+8 .. r+11 read by one half wave of a
+// Operand layouts (the row-major default and the column-major option of page
+// "TileLang实战：用Python DSL自动生成高性能GPU计算内核" §5.1): an operand
+// whose k is contiguous in memory (A row-major, B column-major) is staged as
+// rows of 32 k (64 bytes) per row / column and read with ds_read_b128; one
+// whose k is strided (A column-major, B row-major) is staged as 32 k-rows of
+// the tile's width and read with ds_read_b64_tr_b16.
+//
+// LDS: the A ring (S stages), then the B ring (S stages), each stage
+// width x 32 x 2 bytes.
+//   k contiguous: 16-byte chunk c of row r stored at chunk c ^ ((r / 4) % 4):
+//      the 16 rows read by one quarter wave (one ds_read_b128 cycle) land in
+//      16 different bank groups.
+//   k strided: chunk c of k-row r stored at chunk c ^ (4 (r % 4) ^ 2 ((r/8)
+//      % 2)): the rows r .. r+3 and r+8 .. r+11 read by one half wave of a
 //      transposing read land in 16 different bank groups.
 
 #pragma once
@@ -61,6 +68,10 @@ typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
+// operand layouts (gemm_t): element (i, j) of a row-major matrix at
+// X[i * ld + j], of a column-major one at X[j * ld + i]
+enum { LAYOUT_ROW = 0, LAYOUT_COL = 1 };
+
 // s_waitcnt that limits only the vector-memory counter, to N outstanding
 // (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[15:14]).
 template <int N>
@@ -69,6 +80,23 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// One operand's tile in the ring: EXT rows / columns (BM for A, BN for B) by
+// 32 of K; KC: k contiguous in memory.
+template <int EXT, bool KC_>
+struct RingOperand {
+    static constexpr bool KC = KC_;
+    static constexpr int STAGE = EXT * 64;               // bytes per stage
+    static constexpr int ROW = KC ? 64 : EXT * 2;        // bytes per LDS row
+    static constexpr int CHUNKS = ROW / 16;              // 16-byte chunks per row
+    static constexpr int RPB = 1024 / ROW;               // LDS rows per 1 KiB load
+    static constexpr int BLOCKS = STAGE / 1024;
+    static constexpr int READS = KC ? 1 : 2;             // LDS reads per fragment
+    static_assert(KC || CHUNKS == 16 || CHUNKS == 32, "k-strided tiles of 128 or 256");
+};
+
+__device__ __forceinline__ int ring_key_kc(int r) { return (r >> 2) & 3; }
+__device__ __forceinline__ int ring_key_ks(int r) { return 4 * (r & 3) ^ 2 * ((r >> 3) & 1); }
+
 // Tile configuration of the ring kernel: BM x BN output tile, WM x WN waves,
 // S ring stages of BK = 32, OCC workgroups per CU the registers are sized for.
 template <int BM_, int BN_, int WM_, int WN_, int S_, int OCC_>
@@ -76,43 +104,39 @@ struct RingCfg {
     static constexpr int BM = BM_, BN = BN_, BK = 32, WM = WM_, WN = WN_, S = S_, OCC = OCC_;
     static constexpr int THREADS = 64 * WM * WN, WAVES = WM * WN;
     static constexpr int EB = 2;
-    static constexpr int RA = BK * 2;              // bytes per A row (4 chunks)
-    static constexpr int RB = BN * 2;              // bytes per B k-row
-    static constexpr int CA = RA / 16, CB = RB / 16;
-    static constexpr int A_STAGE = BM * RA, B_STAGE = BK * RB;
+    static constexpr int A_STAGE = BM * 64, B_STAGE = BN * 64;
     static constexpr int A_RING = S * A_STAGE, B_RING = S * B_STAGE;
     static constexpr int LDS_BYTES = A_RING + B_RING;
     static constexpr int A_BLOCKS = A_STAGE / 1024, B_BLOCKS = B_STAGE / 1024;
     static constexpr int A_LOADS = A_BLOCKS / WAVES, B_LOADS = B_BLOCKS / WAVES;
     static constexpr int L = A_LOADS + B_LOADS;    // loads per wave per step
-    static constexpr int A_RPB = 1024 / RA, B_RPB = 1024 / RB;
     static constexpr int WTM = BM / WM, WTN = BN / WN;
     static constexpr int FM = WTM / 16, FN = WTN / 16;
     static constexpr int U = S;                    // steps per loop trip
     static constexpr int K_MULT = BK * U;          // K must be a multiple of this
     static_assert(S % 2 == 0, "fragment buffers alternate per step");
-    static_assert(CB == 16 || CB == 32, "BN of 128 or 256");
     static_assert(A_BLOCKS % WAVES == 0 && B_BLOCKS % WAVES == 0, "");
     static_assert(LDS_BYTES <= 160 * 1024, "gfx950 LDS is 160 KiB per CU");
     static_assert(S >= 3 && (S - 1) * L < 64, "vmcnt range");
-    // every LDS read offset fits the 16-bit immediate of ds_read
-    static_assert(A_RING - A_STAGE + (FM - 1) * 16 * RA < 65536, "");
-    static_assert(B_RING - B_STAGE + 4 * RB < 65536, "");
+    // every LDS read offset fits the 16-bit immediate of ds_read, in either
+    // layout of either operand
+    static_assert(A_RING - A_STAGE + (FM - 1) * 16 * 64 < 65536 && A_RING - A_STAGE + 4 * BM * 2 < 65536, "");
+    static_assert(B_RING - B_STAGE + (FN - 1) * 16 * 64 < 65536 && B_RING - B_STAGE + 4 * BN * 2 < 65536, "");
     static_assert(WTM % 16 == 0 && WTN % 16 == 0, "");
 };
-
-__device__ __forceinline__ int ring_key_a(int r) { return (r >> 2) & 3; }
-__device__ __forceinline__ int ring_key_b(int r) { return 4 * (r & 3) ^ 2 * ((r >> 3) & 1); }
 
 // Preconditions (checked by the host): 16-bit inputs; M % BM == 0,
 // N % BN == 0, K % K_MULT == 0; A and B 16-byte aligned with lda and ldb
 // multiples of 8; C aligned for 4-element stores with ldc % 4 == 0; the
-// buffer offsets (BM rows of A plus K + S*BK columns; K + S*BK rows of B)
-// below 2^31 bytes.
-template <class T, int IN, int OUT>
+// buffer offsets (a tile's rows or columns of each operand over K + S*BK of
+// K) below 2^31 bytes.  LA / LB: LAYOUT_ROW or LAYOUT_COL; C is row-major.
+template <class T, int IN, int OUT, int LA, int LB>
 __global__ __attribute__((amdgpu_flat_work_group_size(T::THREADS, T::THREADS),
                           amdgpu_waves_per_eu(T::OCC * T::WAVES / 4 > 0 ? T::OCC * T::WAVES / 4 : 1)))
 void gemm_kernel_ring(GemmArgs p) {
+    // A is k-contiguous when row-major, B when column-major
+    using OA = RingOperand<T::BM, LA == LAYOUT_ROW>;
+    using OB_ = RingOperand<T::BN, LB == LAYOUT_COL>;
     __shared__ __attribute__((aligned(1024))) char smem[T::LDS_BYTES];
     const int smem_base = (int)(uintptr_t)(lds_void*)smem;   // LDS byte address (M0 values)
     lds_char* const lds = (lds_char*)smem;
@@ -128,41 +152,49 @@ void gemm_kernel_ring(GemmArgs p) {
     const int m0 = tm * T::BM, n0 = tn * T::BN;
     const int K = p.K;
     const int64_t lda = p.lda, ldb = p.ldb;
-    // 1: XOR-swizzled LDS layouts; 0: plain row-major LDS rows (kept for
-    // measuring bank conflicts against the swizzle)
+    // 1: XOR-swizzled LDS layouts; 0: plain LDS rows (kept for measuring
+    // bank conflicts against the swizzle)
     const int swz = p.swz_mask != 0 ? 1 : 0;
 
     // ---------------------------------------------------------- a2: loads
     auto make_rsrc = [&](const char* base, int64_t bytes) __attribute__((always_inline)) {
         const uint64_t a = (uint64_t)base;
-        const uint32_t n = bytes > 0xffffffffLL ? 0xffffffffu : (uint32_t)bytes;
+        const uint32_t n = bytes <= 0 ? 0u : bytes > 0xffffffffLL ? 0xffffffffu : (uint32_t)bytes;
         return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
                      __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)),
                      __builtin_amdgcn_readfirstlane((int)n), 0x00020000};
     };
-    // byte ranges end at the operand's last element (A: row M-1, column K-1;
-    // B: row K-1, column N-1), counted from the tile's corner; empty when
-    // K = 0 (no load is issued then)
-    const i32x4 rs_a = make_rsrc(p.A + (int64_t)m0 * lda * 2, K > 0 ? ((int64_t)(p.M - 1 - m0) * lda + K) * 2 : 0);
-    const i32x4 rs_b = make_rsrc(p.B + (int64_t)n0 * 2, K > 0 ? ((int64_t)(K - 1) * ldb + p.N - n0) * 2 : 0);
-    // load x of a wave: A block wave*A_LOADS + x (x < A_LOADS), else B block
-    // wave*B_LOADS + x - A_LOADS.  Lane l fills slot l of the 1 KiB block
-    // (row l / C, chunk l % C) with the logical chunk the swizzle puts there.
+    // Buffer resource of one operand: it starts at the tile's corner and ends
+    // at the operand's last element (empty when K = 0: no load is issued
+    // then).  outer0: the tile's first row (A) / column (B); outer: M / N.
+    auto operand_rsrc = [&](auto op_t, const char* X, int64_t ld, int outer0, int outer) __attribute__((always_inline)) {
+        using O = decltype(op_t);
+        if (K <= 0) return make_rsrc(X, 0);
+        if constexpr (O::KC)  // element (o, k) at o * ld + k
+            return make_rsrc(X + (int64_t)outer0 * ld * 2, ((int64_t)(outer - 1 - outer0) * ld + K) * 2);
+        else                  // element (o, k) at k * ld + o
+            return make_rsrc(X + (int64_t)outer0 * 2, ((int64_t)(K - 1) * ld + outer - outer0) * 2);
+    };
+    const i32x4 rs_a = operand_rsrc(OA{}, p.A, lda, m0, p.M);
+    const i32x4 rs_b = operand_rsrc(OB_{}, p.B, ldb, n0, p.N);
+    // per-lane byte offset of load x (block blk of the stage): lane l fills
+    // slot l of the 1 KiB block (LDS row l / CHUNKS, chunk l % CHUNKS) with
+    // the logical chunk the swizzle puts there
+    auto load_voff = [&](auto op_t, int blk, int64_t ld) __attribute__((always_inline)) {
+        using O = decltype(op_t);
+        const int r = blk * O::RPB + lane / O::CHUNKS;   // LDS row: outer index (KC) or k (KS)
+        const int key = O::KC ? ring_key_kc(r) : ring_key_ks(r);
+        const int c = (lane % O::CHUNKS) ^ (swz * key);
+        return (int)((int64_t)r * ld * 2 + c * 16);
+    };
     int voff[T::L];
 #pragma unroll
-    for (int x = 0; x < T::L; ++x) {
-        if (x < T::A_LOADS) {
-            const int r = (wave * T::A_LOADS + x) * T::A_RPB + lane / T::CA;
-            const int c = (lane % T::CA) ^ (swz * ring_key_a(r));
-            voff[x] = (int)((int64_t)r * lda * 2 + c * 16);
-        } else {
-            const int r = (wave * T::B_LOADS + (x - T::A_LOADS)) * T::B_RPB + lane / T::CB;
-            const int c = (lane % T::CB) ^ (swz * ring_key_b(r));
-            voff[x] = (int)((int64_t)r * ldb * 2 + c * 16);
-        }
-    }
-    const int a_kstep = T::BK * 2;               // bytes of A per step
-    const int b_kstep = (int)(T::BK * ldb * 2);  // bytes of B per step
+    for (int x = 0; x < T::L; ++x)
+        voff[x] = x < T::A_LOADS ? load_voff(OA{}, wave * T::A_LOADS + x, lda)
+                                 : load_voff(OB_{}, wave * T::B_LOADS + (x - T::A_LOADS), ldb);
+    // K advance per step: 32 elements along a row (KC) or 32 rows (KS)
+    const int a_kstep = OA::KC ? 64 : (int)(32 * lda * 2);
+    const int b_kstep = OB_::KC ? 64 : (int)(32 * ldb * 2);
     // Issued through inline asm (M0 = LDS destination, then the load): the
     // compiler then does not guard later LDS reads with waits for these
     // loads; the kernel waits for them itself (vmcnt) before the barrier that
@@ -183,35 +215,60 @@ void gemm_kernel_ring(GemmArgs p) {
     };
 
     // ---------------------------------------------------------- a5: fragments
+    // v_mfma_f32_16x16x32: lane l holds 8 consecutive k (8q .., q = l / 16) of
+    // row / column l % 16 of each operand.
     const int q = lane >> 4, i16 = lane & 15;
-    const int a_row = wm * T::WTM + i16;                     // + 16 i
-    lds_char* const a_base = lds + a_row * T::RA + (q ^ (swz * ring_key_a(a_row))) * 16;
-    // B: lane i of group q points at k-row 8q + 4h + i/4 (h: which of the two
-    // reads; in the immediate offset), columns 16 j + 4 (i%4) .. +3 of the
-    // wave's block
-    const int b_row = 8 * q + (i16 >> 2);
-    const int b_key = swz * ring_key_b(b_row);
-    lds_char* b_base[T::FN];
-#pragma unroll
-    for (int j = 0; j < T::FN; ++j) {
-        const int c = (wn * T::WTN + 16 * j) / 8 + ((i16 & 3) >> 1);
-        b_base[j] = lds + T::A_RING + b_row * T::RB + (c ^ b_key) * 16 + 8 * (i16 & 1);
-    }
-
-    u32x4 fa[2][T::FM];
-    i16x4 fb[2][T::FN][2];
-    constexpr int NREAD = T::FM + 2 * T::FN;
-    // read r of stage st into buffer buf: the B fragments (two reads each)
-    // first, then the A fragments, the order the MFMAs need them in
-    auto read_frag = [&](int st, int buf, int r) __attribute__((always_inline)) {
-        if (r < 2 * T::FN) {
-            const int j = r / 2, h = r % 2;
-            fb[buf][j][h] =
-                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(b_base[j] + st * T::B_STAGE + 4 * h * T::RB));
+    // per-lane LDS base of fragment f of an operand whose wave block starts
+    // at outer index wo (the stage and the second transposing read go in the
+    // immediate offset)
+    auto frag_base = [&](auto op_t, lds_char* ring, int wo, int f) __attribute__((always_inline)) {
+        using O = decltype(op_t);
+        if constexpr (O::KC) {
+            // row wo + 16 f + l%16, chunk q
+            const int r = wo + 16 * f + i16;
+            return ring + r * O::ROW + (q ^ (swz * ring_key_kc(r))) * 16;
         } else {
-            const int i = r - 2 * T::FN;
-            fa[buf][i] = *(const lds_u32x4*)(a_base + st * T::A_STAGE + 16 * i * T::RA);
+            // lane i of group q: k-row 8q + i/4 (+4 for the second read),
+            // columns wo + 16 f + 4 (i%4) .. +3
+            const int r = 8 * q + (i16 >> 2);
+            const int c = (wo + 16 * f) / 8 + ((i16 & 3) >> 1);
+            return ring + r * O::ROW + (c ^ (swz * ring_key_ks(r))) * 16 + 8 * (i16 & 1);
         }
+    };
+    // k-contiguous operands need one base (the fragments are 1 KiB apart);
+    // k-strided ones one per fragment (the swizzle permutes their columns)
+    constexpr int NBA = OA::KC ? 1 : T::FM, NBB = OB_::KC ? 1 : T::FN;
+    lds_char* a_base[NBA];
+    lds_char* b_base[NBB];
+#pragma unroll
+    for (int f = 0; f < NBA; ++f) a_base[f] = frag_base(OA{}, lds, wm * T::WTM, f);
+#pragma unroll
+    for (int f = 0; f < NBB; ++f) b_base[f] = frag_base(OB_{}, lds + T::A_RING, wn * T::WTN, f);
+
+    // fragments: h[0] (k 0..3) and h[1] (k 4..7) of a lane's 8 k
+    i16x4 fa[2][T::FM][2], fb[2][T::FN][2];
+    auto read_one = [&](auto op_t, lds_char* const* base, int stage_bytes, int st, int f, int h,
+                        i16x4 (&dst)[2]) __attribute__((always_inline)) {
+        using O = decltype(op_t);
+        if constexpr (O::KC) {
+            const u32x4 v = *(const lds_u32x4*)(base[0] + st * stage_bytes + f * 16 * O::ROW);
+            const i16x8 w = __builtin_bit_cast(i16x8, v);
+            dst[0] = __builtin_shufflevector(w, w, 0, 1, 2, 3);
+            dst[1] = __builtin_shufflevector(w, w, 4, 5, 6, 7);
+        } else {
+            dst[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base[f] + st * stage_bytes + 4 * h * O::ROW));
+        }
+    };
+    constexpr int NRB = T::FN * OB_::READS, NRA = T::FM * OA::READS;
+    constexpr int NREAD = NRA + NRB;
+    // read r of stage st into buffer buf: the B fragments first, then the A
+    // fragments, the order the MFMAs need them in
+    auto read_frag = [&](int st, int buf, int r) __attribute__((always_inline)) {
+        if (r < NRB)
+            read_one(OB_{}, b_base, T::B_STAGE, st, r / OB_::READS, r % OB_::READS, fb[buf][r / OB_::READS]);
+        else
+            read_one(OA{}, a_base, T::A_STAGE, st, (r - NRB) / OA::READS, (r - NRB) % OA::READS,
+                     fa[buf][(r - NRB) / OA::READS]);
     };
 
     // a6: accumulators, zeroed (T.clear of §3.3).  The empty asm makes each
@@ -228,16 +285,20 @@ void gemm_kernel_ring(GemmArgs p) {
         }
 
     constexpr int NMF = T::FM * T::FN;
+    // B is the first operand and A the second, so the accumulator holds C
+    // transposed: lane l owns row l % 16 and the 4 consecutive columns
+    // 4 (l / 16) .. of each 16 x 16 block
     auto mfma_one = [&](int buf, int m) __attribute__((always_inline)) {
         // snake order over j: neighbours share one operand
         const int i = m / T::FN, jj = m % T::FN, j = (i & 1) ? T::FN - 1 - jj : jj;
         const i16x8 bop = __builtin_shufflevector(fb[buf][j][0], fb[buf][j][1], 0, 1, 2, 3, 4, 5, 6, 7);
+        const i16x8 aop = __builtin_shufflevector(fa[buf][i][0], fa[buf][i][1], 0, 1, 2, 3, 4, 5, 6, 7);
         if constexpr (IN == DT_F16) {
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, bop),
-                                                                __builtin_bit_cast(f16x8, fa[buf][i]), acc[i][j], 0, 0, 0);
+                                                                __builtin_bit_cast(f16x8, aop), acc[i][j], 0, 0, 0);
         } else {
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bop),
-                                                                 __builtin_bit_cast(bf16x8, fa[buf][i]), acc[i][j], 0, 0, 0);
+                                                                 __builtin_bit_cast(bf16x8, aop), acc[i][j], 0, 0, 0);
         }
     };
 

@@ -1,0 +1,51 @@
+// kernels.hpp -- the tile configurations of the table and the kernel
+// selectors.  Each kernel family is compiled in translation units of its own
+// (k_*.hip, built in parallel); the host code (tgemm.hip) only sees these
+// selectors, which return the launchable kernel of a configuration, type pair
+// and operand layout.
+#pragma once
+#include "gemm_kernel.hpp"
+#include "gemm_kernel_ring.hpp"
+
+namespace tgemm {
+
+// Tile-config tuples (block_M, block_N, block_K, waves, occupancy) in the
+// spirit of the tuning tables of page "企业官网建设流程全解析", §3.3 / §4.4, and
+// of the DeepSeek/Ascend TileLang toolkit page, §4.3, sized for gfx950:
+// 160 KiB LDS per CU, 512 registers per lane at one wave per SIMD.
+using CfgBig = TileCfg<256, 256, 64, 2, 2, 2, 1>;    // 4 waves, 128x128 per wave
+using CfgMid = TileCfg<128, 128, 64, 2, 2, 2, 2>;    // 4 waves, 64x64 per wave
+using CfgSmall = TileCfg<64, 64, 64, 2, 2, 2, 2>;    // 4 waves, 32x32 per wave
+using CfgTiny = TileCfg<32, 32, 64, 1, 1, 2, 4>;     // 1 wave
+using CfgF32Mid = TileCfg<64, 64, 32, 2, 2, 4, 2>;   // fp32 inputs
+using CfgF32Tiny = TileCfg<32, 32, 32, 1, 1, 4, 4>;  // fp32 inputs, 1 wave
+// direct-to-LDS ring kernels of the two largest tiles
+using RingBig = RingCfg<256, 256, 2, 2, 4, 1>;
+using RingMid = RingCfg<128, 128, 2, 2, 4, 2>;
+static_assert(RingBig::LDS_BYTES == CfgBig::LDS_BYTES && RingMid::LDS_BYTES == CfgMid::LDS_BYTES,
+              "both kernels of a configuration use the same LDS budget");
+
+enum { CFG_BIG = 0, CFG_MID = 1, CFG_SMALL = 2, CFG_TINY = 3, CFG_F32_MID = 4, CFG_F32_TINY = 5,
+       CFG_DIRECT = 6, CFG_F32_DIRECT = 7, NUM_CONFIGS = 8 };
+
+typedef void (*KernelFn)(GemmArgs);
+
+// Register-staged kernel of configuration cfg (CFG_BIG .. CFG_F32_TINY) for
+// (in, out) (DT_* values); fast: the unchecked whole-tile path.  nullptr if
+// the pair is not served.  One definition per configuration (k_tiled_<cfg>.hip).
+KernelFn tiled_kernel_big(int in, int out, bool fast);
+KernelFn tiled_kernel_mid(int in, int out, bool fast);
+KernelFn tiled_kernel_small(int in, int out, bool fast);
+KernelFn tiled_kernel_tiny(int in, int out, bool fast);
+KernelFn tiled_kernel_f32(int cfg, int in, int out, bool fast);
+
+// Ring kernel of CFG_BIG or CFG_MID for (in, out) and the layouts of A and B
+// (LAYOUT_ROW / LAYOUT_COL).  k_ring_big.hip, k_ring_mid.hip.
+KernelFn ring_kernel_big(int in, int out, int la, int lb);
+KernelFn ring_kernel_mid(int in, int out, int la, int lb);
+
+// Direct kernel for (in, out), the layouts of A and B, and whether each
+// operand takes 16-byte loads.  k_direct.hip.
+KernelFn direct_kernel(int in, int out, int la, int lb, bool va, bool vb);
+
+}  // namespace tgemm

@@ -1,17 +1,16 @@
 // tgemm.hip -- C ABI of libtgemm.so: argument checks, the per-shape tile
 // configuration table and the kernel launch.  The kernels are in
-// gemm_kernel.hpp (register-staged; every shape, type and alignment) and
-// gemm_kernel_ring.hpp (direct-to-LDS rings; whole tiles of 16-bit inputs)
-// and gemm_kernel_direct.hpp (operands straight to registers; small, ragged
-// or unaligned products); the ABI is declared (and documented) in
-// include/tgemm.h.
+// gemm_kernel.hpp (register-staged; every shape, type and alignment, both
+// operands row-major), gemm_kernel_ring.hpp (direct-to-LDS rings; whole tiles
+// of 16-bit inputs, any operand layout) and gemm_kernel_direct.hpp (operands
+// straight to registers; small, ragged or unaligned products, any operand
+// layout), compiled in units of their own (k_*.hip) behind the selectors of
+// kernels.hpp; the ABI is declared (and documented) in include/tgemm.h.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
 
-#include "gemm_kernel.hpp"
-#include "gemm_kernel_direct.hpp"
-#include "gemm_kernel_ring.hpp"
+#include "kernels.hpp"
 #include "tgemm.h"
 
 using namespace tgemm;
@@ -19,110 +18,48 @@ using namespace tgemm;
 namespace {
 
 // ------------------------------------------------------------- configurations
-// Tile-config tuples (block_M, block_N, block_K, waves, occupancy) in the
-// spirit of the tuning tables of page "企业官网建设流程全解析", §3.3 / §4.4, and
-// of the DeepSeek/Ascend TileLang toolkit page, §4.3, sized for gfx950:
-// 160 KiB LDS per CU, 512 registers per lane at one wave per SIMD.
-using CfgBig = TileCfg<256, 256, 64, 2, 2, 2, 1>;    // 4 waves, 128x128 per wave
-using CfgMid = TileCfg<128, 128, 64, 2, 2, 2, 2>;    // 4 waves, 64x64 per wave
-using CfgSmall = TileCfg<64, 64, 64, 2, 2, 2, 2>;    // 4 waves, 32x32 per wave
-using CfgTiny = TileCfg<32, 32, 64, 1, 1, 2, 4>;     // 1 wave
-using CfgF32Mid = TileCfg<64, 64, 32, 2, 2, 4, 2>;   // fp32 inputs
-using CfgF32Tiny = TileCfg<32, 32, 32, 1, 1, 4, 4>;  // fp32 inputs, 1 wave
-
-typedef void (*KernelFn)(GemmArgs);
-
 struct ConfigEntry {
     const char* name;
     int in_family;  // TGEMM_F16 (serves F16 and BF16) or TGEMM_F32
     bool direct;    // the direct kernel (32 x 32 per workgroup, no LDS)
     int bm, bn, bk, wm, wn, eb, lds_bytes, threads, cpr;
-    KernelFn (*pick)(int in, int out, bool fast);
-    // direct-to-LDS ring kernel of the same output tile (whole tiles, K a
-    // multiple of ring_k_mult); its block_k and stage count
-    KernelFn (*pick_ring)(int in, int out);
+    // register-staged kernels (row-major operands only)
+    KernelFn (*tiled)(int in, int out, bool fast);
+    // direct-to-LDS ring kernels of the same output tile (whole tiles, K a
+    // multiple of ring_k_mult; any operand layout), with their block_k,
+    // stage count and LDS bytes
+    KernelFn (*ring)(int in, int out, int la, int lb);
     int ring_bk, ring_stages, ring_k_mult, ring_lds;
 };
 
-template <class R>
-KernelFn pick_ring(int in, int out) {
-    if (in == TGEMM_F16 && out == TGEMM_F16) return gemm_kernel_ring<R, DT_F16, DT_F16>;
-    if (in == TGEMM_F16 && out == TGEMM_F32) return gemm_kernel_ring<R, DT_F16, DT_F32>;
-    if (in == TGEMM_BF16 && out == TGEMM_BF16) return gemm_kernel_ring<R, DT_BF16, DT_BF16>;
-    if (in == TGEMM_BF16 && out == TGEMM_F32) return gemm_kernel_ring<R, DT_BF16, DT_F32>;
-    return nullptr;
-}
-using RingBig = RingCfg<256, 256, 2, 2, 4, 1>;
-using RingMid = RingCfg<128, 128, 2, 2, 4, 2>;
-static_assert(RingBig::LDS_BYTES == CfgBig::LDS_BYTES && RingMid::LDS_BYTES == CfgMid::LDS_BYTES,
-              "both kernels of a configuration use the same LDS budget");
+KernelFn tiled_f32_mid(int in, int out, bool fast) { return tiled_kernel_f32(CFG_F32_MID, in, out, fast); }
+KernelFn tiled_f32_tiny(int in, int out, bool fast) { return tiled_kernel_f32(CFG_F32_TINY, in, out, fast); }
 
-template <class T, int IN>
-KernelFn pick_out(int out, bool fast) {
-    if (out == TGEMM_F32)
-        return fast ? gemm_kernel<T, IN, DT_F32, true> : gemm_kernel<T, IN, DT_F32, false>;
-    if (IN == DT_F16 && out == TGEMM_F16)
-        return fast ? gemm_kernel<T, IN, DT_F16, true> : gemm_kernel<T, IN, DT_F16, false>;
-    if (IN == DT_BF16 && out == TGEMM_BF16)
-        return fast ? gemm_kernel<T, IN, DT_BF16, true> : gemm_kernel<T, IN, DT_BF16, false>;
-    return nullptr;
-}
-
-template <class T>
-KernelFn pick_half(int in, int out, bool fast) {
-    if (in == TGEMM_F16) return pick_out<T, DT_F16>(out, fast);
-    if (in == TGEMM_BF16) return pick_out<T, DT_BF16>(out, fast);
-    return nullptr;
-}
-
-template <class T>
-KernelFn pick_f32(int in, int out, bool fast) {
-    if (in == TGEMM_F32 && out == TGEMM_F32)
-        return fast ? gemm_kernel<T, DT_F32, DT_F32, true> : gemm_kernel<T, DT_F32, DT_F32, false>;
-    return nullptr;
-}
-
-#define ENTRY(name, fam, T, pk)                                                                         \
-    {name, fam, false, T::BM, T::BN, T::BK, T::WM, T::WN, T::EB, T::LDS_BYTES, T::THREADS, T::CPR, pk<T>, nullptr, \
+#define ENTRY(name, fam, T, sel)                                                                                \
+    {name, fam, false, T::BM, T::BN, T::BK, T::WM, T::WN, T::EB, T::LDS_BYTES, T::THREADS, T::CPR, sel, nullptr, \
      0, 0, 0, 0}
-#define ENTRY_RING(name, fam, T, pk, R)                                                                          \
-    {name, fam, false, T::BM, T::BN, T::BK, T::WM, T::WN, T::EB, T::LDS_BYTES, T::THREADS, T::CPR, pk<T>,        \
-     pick_ring<R>, R::BK, R::S, R::K_MULT, R::LDS_BYTES}
+#define ENTRY_RING(name, fam, T, sel, R, rsel)                                                              \
+    {name, fam, false, T::BM, T::BN, T::BK, T::WM, T::WN, T::EB, T::LDS_BYTES, T::THREADS, T::CPR, sel, rsel, \
+     R::BK, R::S, R::K_MULT, R::LDS_BYTES}
 // direct kernel: 32 x 32 per workgroup of 2 x 2 waves, steps of 32 of K
-#define ENTRY_DIRECT(name, fam, eb, pk) \
-    {name, fam, true, 32, 32, 32, 2, 2, eb, 0, 256, 1, pk, nullptr, 0, 0, 0, 0}
-
-// direct kernel for (in, out); `avec`: A rows are whole 16-byte chunks
-KernelFn pick_direct(int in, int out, bool avec) {
-    if (in == TGEMM_F32) return out == TGEMM_F32 ? gemm_kernel_direct<DT_F32, DT_F32, false> : nullptr;
-    if (in == TGEMM_F16 && out == TGEMM_F16)
-        return avec ? gemm_kernel_direct<DT_F16, DT_F16, true> : gemm_kernel_direct<DT_F16, DT_F16, false>;
-    if (in == TGEMM_F16 && out == TGEMM_F32)
-        return avec ? gemm_kernel_direct<DT_F16, DT_F32, true> : gemm_kernel_direct<DT_F16, DT_F32, false>;
-    if (in == TGEMM_BF16 && out == TGEMM_BF16)
-        return avec ? gemm_kernel_direct<DT_BF16, DT_BF16, true> : gemm_kernel_direct<DT_BF16, DT_BF16, false>;
-    if (in == TGEMM_BF16 && out == TGEMM_F32)
-        return avec ? gemm_kernel_direct<DT_BF16, DT_F32, true> : gemm_kernel_direct<DT_BF16, DT_F32, false>;
-    return nullptr;
-}
+#define ENTRY_DIRECT(name, fam, eb) {name, fam, true, 32, 32, 32, 2, 2, eb, 0, 256, 1, nullptr, nullptr, 0, 0, 0, 0}
 
 const ConfigEntry kConfigs[] = {
-    ENTRY_RING("h256x256_w2x2", TGEMM_F16, CfgBig, pick_half, RingBig),
-    ENTRY_RING("h128x128_w2x2", TGEMM_F16, CfgMid, pick_half, RingMid),
-    ENTRY("h64x64x64_w2x2", TGEMM_F16, CfgSmall, pick_half),
-    ENTRY("h32x32x64_w1x1", TGEMM_F16, CfgTiny, pick_half),
-    ENTRY("s64x64x32_w2x2", TGEMM_F32, CfgF32Mid, pick_f32),
-    ENTRY("s32x32x32_w1x1", TGEMM_F32, CfgF32Tiny, pick_f32),
-    ENTRY_DIRECT("h32x32_direct", TGEMM_F16, 2, pick_direct),
-    ENTRY_DIRECT("s32x32_direct", TGEMM_F32, 4, pick_direct),
+    ENTRY_RING("h256x256_w2x2", TGEMM_F16, CfgBig, tiled_kernel_big, RingBig, ring_kernel_big),
+    ENTRY_RING("h128x128_w2x2", TGEMM_F16, CfgMid, tiled_kernel_mid, RingMid, ring_kernel_mid),
+    ENTRY("h64x64x64_w2x2", TGEMM_F16, CfgSmall, tiled_kernel_small),
+    ENTRY("h32x32x64_w1x1", TGEMM_F16, CfgTiny, tiled_kernel_tiny),
+    ENTRY("s64x64x32_w2x2", TGEMM_F32, CfgF32Mid, tiled_f32_mid),
+    ENTRY("s32x32x32_w1x1", TGEMM_F32, CfgF32Tiny, tiled_f32_tiny),
+    ENTRY_DIRECT("h32x32_direct", TGEMM_F16, 2),
+    ENTRY_DIRECT("s32x32_direct", TGEMM_F32, 4),
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
-enum { CFG_BIG = 0, CFG_MID = 1, CFG_SMALL = 2, CFG_TINY = 3, CFG_F32_MID = 4, CFG_F32_TINY = 5,
-       CFG_DIRECT = 6, CFG_F32_DIRECT = 7 };
+static_assert(kNumConfigs == NUM_CONFIGS, "");
 
 // Measurement-only switches, read once from the environment:
 //   TGEMM_GROUP_M=<n>    tile rows per raster group (default 4)
-//   TGEMM_NO_SWIZZLE=1   plain row-major LDS tiles (for bank-conflict A/B runs)
+//   TGEMM_NO_SWIZZLE=1   plain LDS rows (for bank-conflict A/B runs)
 //   TGEMM_NO_DL=1        register-staged kernel instead of the direct-to-LDS ring
 struct Tuning {
     int group_m = 4;
@@ -155,20 +92,43 @@ bool pair_supported(int in, int out) {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-int validate(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
-             const void* C, int64_t ldc, int in, int out) {
+// One product after a column-major C has been turned into a row-major one
+// (C^T = B^T A^T): logical A is M x K, B is K x N, C row-major M x N.
+struct Problem {
+    int64_t M, N, K;
+    const void* A;
+    int64_t lda;
+    int la;  // LAYOUT_ROW: A(i, k) at A[i * lda + k]; LAYOUT_COL: at A[k * lda + i]
+    const void* B;
+    int64_t ldb;
+    int lb;  // LAYOUT_ROW: B(k, j) at B[k * ldb + j]; LAYOUT_COL: at B[j * ldb + k]
+    void* C;
+    int64_t ldc;
+    int in, out;
+};
+
+bool layout_ok(int l) { return l == TGEMM_ROW_MAJOR || l == TGEMM_COL_MAJOR; }
+
+// Bytes spanned by a stored matrix of `rows` x `cols` in its storage order.
+uintptr_t span(int64_t rows, int64_t cols, int64_t ld, int eb) { return (uintptr_t)((rows - 1) * ld + cols) * eb; }
+
+int validate(const Problem& p) {
+    const int64_t M = p.M, N = p.N, K = p.K;
     if (M < 0 || N < 0 || K < 0 || M > TGEMM_MAX_DIM || N > TGEMM_MAX_DIM || K > TGEMM_MAX_DIM)
         return TGEMM_ERR_DIM;
-    if (!pair_supported(in, out)) return TGEMM_ERR_DTYPE;
-    if (lda < K || ldb < N || ldc < N) return TGEMM_ERR_LD;
+    if (!pair_supported(p.in, p.out)) return TGEMM_ERR_DTYPE;
+    // stored shapes: A is M x K (row-major) or K x M (column-major); so is B
+    const int64_t a_rows = p.la == LAYOUT_ROW ? M : K, a_cols = p.la == LAYOUT_ROW ? K : M;
+    const int64_t b_rows = p.lb == LAYOUT_ROW ? K : N, b_cols = p.lb == LAYOUT_ROW ? N : K;
+    if (p.lda < a_cols || p.ldb < b_cols || p.ldc < N) return TGEMM_ERR_LD;
     if (M == 0 || N == 0) return TGEMM_OK;
-    if (C == nullptr) return TGEMM_ERR_NULL;
-    if (K > 0 && (A == nullptr || B == nullptr)) return TGEMM_ERR_NULL;
+    if (p.C == nullptr) return TGEMM_ERR_NULL;
+    if (K > 0 && (p.A == nullptr || p.B == nullptr)) return TGEMM_ERR_NULL;
     if (K > 0) {
-        const uintptr_t ie = elem_bytes(in), oe = elem_bytes(out);
-        const uintptr_t c0 = (uintptr_t)C, c1 = c0 + (uintptr_t)((M - 1) * ldc + N) * oe;
-        const uintptr_t a0 = (uintptr_t)A, a1 = a0 + (uintptr_t)((M - 1) * lda + K) * ie;
-        const uintptr_t b0 = (uintptr_t)B, b1 = b0 + (uintptr_t)((K - 1) * ldb + N) * ie;
+        const int ie = elem_bytes(p.in);
+        const uintptr_t c0 = (uintptr_t)p.C, c1 = c0 + span(M, N, p.ldc, elem_bytes(p.out));
+        const uintptr_t a0 = (uintptr_t)p.A, a1 = a0 + span(a_rows, a_cols, p.lda, ie);
+        const uintptr_t b0 = (uintptr_t)p.B, b1 = b0 + span(b_rows, b_cols, p.ldb, ie);
         if ((c0 < a1 && a0 < c1) || (c0 < b1 && b0 < c1)) return TGEMM_ERR_ALIAS;
     }
     return TGEMM_OK;
@@ -176,36 +136,52 @@ int validate(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const 
 
 // 16-byte loads of A and B need 16-byte aligned bases and leading dimensions
 // that are whole 16-byte chunks.
-bool loads_aligned(const ConfigEntry& c, const void* A, int64_t lda, const void* B, int64_t ldb) {
+bool loads_aligned(const ConfigEntry& c, const Problem& p) {
     const int ve = 16 / c.eb;
-    return ((uintptr_t)A % 16 == 0) && ((uintptr_t)B % 16 == 0) && (lda % ve == 0) && (ldb % ve == 0);
+    return ((uintptr_t)p.A % 16 == 0) && ((uintptr_t)p.B % 16 == 0) && (p.lda % ve == 0) && (p.ldb % ve == 0);
 }
 
 // 4-element stores of C need a base aligned to 4 elements and ldc % 4 == 0.
-bool stores_aligned(const void* C, int64_t ldc, int out) {
-    return ((uintptr_t)C % (4 * (uintptr_t)elem_bytes(out)) == 0) && (ldc % 4 == 0);
+bool stores_aligned(const Problem& p) {
+    return ((uintptr_t)p.C % (4 * (uintptr_t)elem_bytes(p.out)) == 0) && (p.ldc % 4 == 0);
 }
 
 int64_t tiles_for(const ConfigEntry& c, int64_t M, int64_t N) { return ceil_div(M, c.bm) * ceil_div(N, c.bn); }
 
+bool row_row(const Problem& p) { return p.la == LAYOUT_ROW && p.lb == LAYOUT_ROW; }
+
 // Whether a register-staged configuration runs its unchecked path: whole
 // tiles, 16-byte aligned operands, 4-element aligned C rows, offsets within
 // 31 bits.
-bool tiled_fast(const ConfigEntry& c, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
-                int64_t ldb, const void* C, int64_t ldc, int out) {
-    const bool offsets_fit = (int64_t)c.bm * lda * c.eb + K * c.eb < (1LL << 31) &&
-                             (int64_t)c.bk * ldb * c.eb + N * c.eb < (1LL << 31);
-    return loads_aligned(c, A, lda, B, ldb) && stores_aligned(C, ldc, out) && offsets_fit && M % c.bm == 0 &&
-           N % c.bn == 0;
+bool tiled_fast(const ConfigEntry& c, const Problem& p) {
+    const bool offsets_fit = (int64_t)c.bm * p.lda * c.eb + p.K * c.eb < (1LL << 31) &&
+                             (int64_t)c.bk * p.ldb * c.eb + p.N * c.eb < (1LL << 31);
+    return loads_aligned(c, p) && stores_aligned(p) && offsets_fit && p.M % c.bm == 0 && p.N % c.bn == 0;
+}
+
+// Largest buffer offset (bytes) of an operand whose tile spans `ext` rows /
+// columns, read over K + extra of K: k contiguous in memory (row-major A,
+// column-major B) or strided.
+int64_t operand_reach(bool kcontig, int64_t ext, int64_t ld, int64_t K, int64_t extra, int eb) {
+    return (kcontig ? ext * ld + K + extra : (K + extra) * ld + ext) * eb;
 }
 
 // Whether a configuration with a ring kernel runs it.
-bool ring_applies(const ConfigEntry& c, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
-                  int64_t ldb, const void* C, int64_t ldc, int out) {
-    return c.pick_ring != nullptr && tiled_fast(c, M, N, K, A, lda, B, ldb, C, ldc, out) &&
-           ((int64_t)c.bm * lda + K + (int64_t)c.ring_stages * c.ring_bk) * c.eb < (1LL << 31) &&
-           ((K + (int64_t)c.ring_stages * c.ring_bk) * ldb + c.bn) * c.eb < (1LL << 31) &&
-           K % c.ring_k_mult == 0 && tuning().direct_lds;
+bool ring_applies(const ConfigEntry& c, const Problem& p) {
+    if (c.ring == nullptr || !tuning().direct_lds) return false;
+    const int64_t extra = (int64_t)c.ring_stages * c.ring_bk;
+    return loads_aligned(c, p) && stores_aligned(p) && p.M % c.bm == 0 && p.N % c.bn == 0 &&
+           p.K % c.ring_k_mult == 0 &&
+           operand_reach(p.la == LAYOUT_ROW, c.bm, p.lda, p.K, extra, c.eb) < (1LL << 31) &&
+           operand_reach(p.lb == LAYOUT_COL, c.bn, p.ldb, p.K, extra, c.eb) < (1LL << 31);
+}
+
+// Whether the direct kernel's buffer offsets fit (32 rows / columns of each
+// operand over K + 320 of K).
+bool direct_fits(const Problem& p) {
+    const int eb = elem_bytes(p.in);
+    return operand_reach(p.la == LAYOUT_ROW, 32, p.lda, p.K, 320, eb) < (1LL << 31) &&
+           operand_reach(p.lb == LAYOUT_COL, 32, p.ldb, p.K, 320, eb) < (1LL << 31);
 }
 
 // The per-shape table (measured on MI355X; kernel times from rocprofv3
@@ -221,20 +197,27 @@ bool ring_applies(const ConfigEntry& c, int64_t M, int64_t N, int64_t K, const v
 //  * other small products the smallest register-staged tile, which
 //    maximises parallelism where launch latency and one workgroup's K loop
 //    set the time.
-int table_choice(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
-                 const void* C, int64_t ldc, int in, int out) {
+// Column-major operands have no register-staged kernel: the ring kernels
+// where they apply, the direct kernel elsewhere.
+int table_choice(const Problem& p) {
+    const int64_t M = p.M, N = p.N;
     const bool small = M * N <= (1LL << 18);
-    if (in == TGEMM_F32) {
+    if (p.in == TGEMM_F32) {
+        if (!row_row(p)) return CFG_F32_DIRECT;
         if (tiles_for(kConfigs[CFG_F32_MID], M, N) >= 256) return CFG_F32_MID;
-        if (small && !tiled_fast(kConfigs[CFG_F32_TINY], M, N, K, A, lda, B, ldb, C, ldc, out)) return CFG_F32_DIRECT;
+        if (small && !tiled_fast(kConfigs[CFG_F32_TINY], p)) return CFG_F32_DIRECT;
         return CFG_F32_TINY;
     }
+    if (!row_row(p)) {
+        if (tiles_for(kConfigs[CFG_BIG], M, N) >= 256 && ring_applies(kConfigs[CFG_BIG], p)) return CFG_BIG;
+        if (ring_applies(kConfigs[CFG_MID], p)) return CFG_MID;
+        return CFG_DIRECT;
+    }
     if (tiles_for(kConfigs[CFG_BIG], M, N) >= 256) return CFG_BIG;
-    if (tiles_for(kConfigs[CFG_MID], M, N) >= 128 && ring_applies(kConfigs[CFG_MID], M, N, K, A, lda, B, ldb, C, ldc, out))
-        return CFG_MID;
+    if (tiles_for(kConfigs[CFG_MID], M, N) >= 128 && ring_applies(kConfigs[CFG_MID], p)) return CFG_MID;
     if (tiles_for(kConfigs[CFG_MID], M, N) >= 256) return CFG_MID;
     if (tiles_for(kConfigs[CFG_SMALL], M, N) >= 256) return CFG_SMALL;
-    if (small && !tiled_fast(kConfigs[CFG_TINY], M, N, K, A, lda, B, ldb, C, ldc, out)) return CFG_DIRECT;
+    if (small && !tiled_fast(kConfigs[CFG_TINY], p)) return CFG_DIRECT;
     return CFG_TINY;
 }
 
@@ -247,74 +230,93 @@ struct Plan {
     KernelFn fn;
 };
 
-int plan_tiled(const ConfigEntry& c, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
-               int64_t ldb, const void* C, int64_t ldc, int in, int out, Plan& plan);
-
-// Validates the arguments and picks the kernel; returns TGEMM_OK (plan
-// filled; M == 0 or N == 0 leaves plan.fn null) or a negative error code.
-int make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
-              const void* C, int64_t ldc, int in, int out, int config_id, Plan& plan) {
-    const int v = validate(M, N, K, A, lda, B, ldb, C, ldc, in, out);
-    if (v != TGEMM_OK) return v;
-    if (config_id < -1 || config_id >= kNumConfigs) return TGEMM_ERR_CONFIG;
-    if (config_id >= 0 && kConfigs[config_id].in_family != family_of(in)) return TGEMM_ERR_CONFIG;
-    plan.config = config_id >= 0 ? config_id : table_choice(M, N, K, A, lda, B, ldb, C, ldc, in, out);
-    plan.fn = nullptr;
-    plan.kind = TGEMM_KERNEL_GENERAL;
-    if (M == 0 || N == 0) return TGEMM_OK;
-    const ConfigEntry& c = kConfigs[plan.config];
-    if (c.direct) {
-        // buffer offsets: 32 rows of A plus K + 320 columns; K + 320 rows of B
-        if (((int64_t)32 * lda + K + 320) * c.eb >= (1LL << 31) || ((K + 320) * ldb + 32) * c.eb >= (1LL << 31))
-            plan.config = in == TGEMM_F32 ? CFG_F32_TINY : CFG_TINY;  // offsets too wide: the checked kernel
-        else {
-            const bool avec = in != TGEMM_F32 && (uintptr_t)A % 16 == 0 && lda % 8 == 0 && K % 8 == 0;
-            plan.kind = TGEMM_KERNEL_DIRECT;
-            plan.fn = c.pick(in, out, avec);
-            if (plan.fn == nullptr) return TGEMM_ERR_DTYPE;
-            if (ceil_div(M, c.bm) * ceil_div(N, c.bn) > 0x7fffffff) return TGEMM_ERR_DIM;
-            return TGEMM_OK;
-        }
-    }
-    const ConfigEntry& t = kConfigs[plan.config];
-    return plan_tiled(t, M, N, K, A, lda, B, ldb, C, ldc, in, out, plan);
-}
-
-int plan_tiled(const ConfigEntry& c, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
-               int64_t ldb, const void* C, int64_t ldc, int in, int out, Plan& plan) {
-    const bool fast = tiled_fast(c, M, N, K, A, lda, B, ldb, C, ldc, out);
-    const bool ring = ring_applies(c, M, N, K, A, lda, B, ldb, C, ldc, out);
-    plan.kind = ring ? TGEMM_KERNEL_RING : fast ? TGEMM_KERNEL_TILED : TGEMM_KERNEL_GENERAL;
-    plan.fn = ring ? c.pick_ring(in, out) : c.pick(in, out, fast);
+int plan_direct(const Problem& p, Plan& plan) {
+    const bool kca = p.la == LAYOUT_ROW, kcb = p.lb == LAYOUT_COL;
+    const bool half = p.in != TGEMM_F32;
+    const bool va = half && kca && (uintptr_t)p.A % 16 == 0 && p.lda % 8 == 0 && p.K % 8 == 0;
+    const bool vb = half && kcb && (uintptr_t)p.B % 16 == 0 && p.ldb % 8 == 0 && p.K % 8 == 0;
+    plan.kind = TGEMM_KERNEL_DIRECT;
+    plan.fn = direct_kernel(p.in, p.out, p.la, p.lb, va, vb);
     if (plan.fn == nullptr) return TGEMM_ERR_DTYPE;
-    const int64_t grid = ceil_div(M, c.bm) * ceil_div(N, c.bn);
-    if (grid > 0x7fffffff) return TGEMM_ERR_DIM;
+    if (ceil_div(p.M, 32) * ceil_div(p.N, 32) > 0x7fffffff) return TGEMM_ERR_DIM;
     return TGEMM_OK;
 }
 
-int run(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
-        int64_t ldc, int in, int out, void* stream, int config_id) {
+// Validates the arguments and picks the kernel; returns TGEMM_OK (plan
+// filled; M == 0 or N == 0 leaves plan.fn null) or a negative error code.
+int make_plan(const Problem& p, int config_id, Plan& plan) {
+    const int v = validate(p);
+    if (v != TGEMM_OK) return v;
+    if (config_id < -1 || config_id >= kNumConfigs) return TGEMM_ERR_CONFIG;
+    if (config_id >= 0 && kConfigs[config_id].in_family != family_of(p.in)) return TGEMM_ERR_CONFIG;
+    // configurations with only a register-staged kernel serve row-major
+    // operands only
+    if (config_id >= 0 && !row_row(p) && !kConfigs[config_id].direct && kConfigs[config_id].ring == nullptr)
+        return TGEMM_ERR_CONFIG;
+    plan.config = config_id >= 0 ? config_id : table_choice(p);
+    plan.fn = nullptr;
+    plan.kind = TGEMM_KERNEL_GENERAL;
+    if (p.M == 0 || p.N == 0) return TGEMM_OK;
+    const ConfigEntry& c = kConfigs[plan.config];
+    if (!c.direct && ring_applies(c, p)) {
+        plan.kind = TGEMM_KERNEL_RING;
+        plan.fn = c.ring(p.in, p.out, p.la, p.lb);
+        if (plan.fn == nullptr) return TGEMM_ERR_DTYPE;
+        return ceil_div(p.M, c.bm) * ceil_div(p.N, c.bn) > 0x7fffffff ? TGEMM_ERR_DIM : TGEMM_OK;
+    }
+    if (c.direct || !row_row(p)) {
+        // column-major operands outside the ring kernel's cases run direct
+        if (direct_fits(p)) {
+            if (!c.direct) plan.config = p.in == TGEMM_F32 ? CFG_F32_DIRECT : CFG_DIRECT;
+            return plan_direct(p, plan);
+        }
+        if (!row_row(p)) return TGEMM_ERR_DIM;  // offsets beyond 31 bits: no kernel
+        plan.config = p.in == TGEMM_F32 ? CFG_F32_TINY : CFG_TINY;  // the checked kernel instead
+    }
+    const ConfigEntry& t = kConfigs[plan.config];
+    const bool fast = tiled_fast(t, p);
+    plan.kind = fast ? TGEMM_KERNEL_TILED : TGEMM_KERNEL_GENERAL;
+    plan.fn = t.tiled(p.in, p.out, fast);
+    if (plan.fn == nullptr) return TGEMM_ERR_DTYPE;
+    return ceil_div(p.M, t.bm) * ceil_div(p.N, t.bn) > 0x7fffffff ? TGEMM_ERR_DIM : TGEMM_OK;
+}
+
+// The problem of a call: a column-major C is computed as the row-major
+// C^T = B^T A^T (M and N swapped, A and B swapped, each operand's layout
+// flipped: a row-major K x N B read as an N x K matrix is column-major).
+int make_problem(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int la, const void* B, int64_t ldb,
+                 int lb, void* C, int64_t ldc, int lc, int in, int out, Problem& p) {
+    if (!layout_ok(la) || !layout_ok(lb) || !layout_ok(lc)) return TGEMM_ERR_LAYOUT;
+    if (lc == TGEMM_ROW_MAJOR)
+        p = Problem{M, N, K, A, lda, la, B, ldb, lb, C, ldc, in, out};
+    else
+        p = Problem{N, M, K, B, ldb, lb ^ 1, A, lda, la ^ 1, C, ldc, in, out};
+    return TGEMM_OK;
+}
+
+int run(const Problem& p, void* stream, int config_id) {
     Plan plan;
-    const int v = make_plan(M, N, K, A, lda, B, ldb, C, ldc, in, out, config_id, plan);
+    const int v = make_plan(p, config_id, plan);
     if (v != TGEMM_OK || plan.fn == nullptr) return v;
     const ConfigEntry& c = kConfigs[plan.config];
 
     GemmArgs args;
-    args.A = (const char*)A;
-    args.B = (const char*)B;
-    args.C = (char*)C;
-    args.lda = lda;
-    args.ldb = ldb;
-    args.ldc = ldc;
-    args.M = (int)M;
-    args.N = (int)N;
-    args.K = (int)K;
-    args.tiles_m = (int)ceil_div(M, c.bm);
-    args.tiles_n = (int)ceil_div(N, c.bn);
+    args.A = (const char*)p.A;
+    args.B = (const char*)p.B;
+    args.C = (char*)p.C;
+    args.lda = p.lda;
+    args.ldb = p.ldb;
+    args.ldc = p.ldc;
+    args.M = (int)p.M;
+    args.N = (int)p.N;
+    args.K = (int)p.K;
+    args.tiles_m = (int)ceil_div(p.M, c.bm);
+    args.tiles_n = (int)ceil_div(p.N, c.bn);
     args.group_m = tuning().group_m;
     args.swz_mask = tuning().swizzle ? c.cpr - 1 : 0;
-    args.vec_ab = loads_aligned(c, A, lda, B, ldb);
-    args.vec_c = stores_aligned(C, ldc, out);
+    if (plan.kind == TGEMM_KERNEL_RING) args.swz_mask = tuning().swizzle ? 1 : 0;
+    args.vec_ab = loads_aligned(c, p);
+    args.vec_c = stores_aligned(p);
     const int64_t grid = (int64_t)args.tiles_m * args.tiles_n;
 
     void* kargs[] = {&args};
@@ -330,12 +332,23 @@ extern "C" {
 
 int gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
          int64_t ldc, int in_dtype, int out_dtype, void* stream) {
-    return run(M, N, K, A, lda, B, ldb, C, ldc, in_dtype, out_dtype, stream, -1);
+    return gemm_t(M, N, K, A, lda, TGEMM_ROW_MAJOR, B, ldb, TGEMM_ROW_MAJOR, C, ldc, TGEMM_ROW_MAJOR, in_dtype,
+                  out_dtype, stream, -1);
 }
 
 int gemm_ex(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
             int64_t ldc, int in_dtype, int out_dtype, void* stream, int config_id) {
-    return run(M, N, K, A, lda, B, ldb, C, ldc, in_dtype, out_dtype, stream, config_id);
+    return gemm_t(M, N, K, A, lda, TGEMM_ROW_MAJOR, B, ldb, TGEMM_ROW_MAJOR, C, ldc, TGEMM_ROW_MAJOR, in_dtype,
+                  out_dtype, stream, config_id);
+}
+
+int gemm_t(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int layout_a, const void* B, int64_t ldb,
+           int layout_b, void* C, int64_t ldc, int layout_c, int in_dtype, int out_dtype, void* stream,
+           int config_id) {
+    Problem p;
+    const int v = make_problem(M, N, K, A, lda, layout_a, B, ldb, layout_b, C, ldc, layout_c, in_dtype, out_dtype, p);
+    if (v != TGEMM_OK) return v;
+    return run(p, stream, config_id);
 }
 
 const char* gemm_strerror(int code) {
@@ -343,10 +356,13 @@ const char* gemm_strerror(int code) {
         case TGEMM_OK: return "success";
         case TGEMM_ERR_DIM: return "M, N or K negative or too large";
         case TGEMM_ERR_NULL: return "NULL pointer for a non-empty operand";
-        case TGEMM_ERR_LD: return "leading dimension smaller than the row width (lda < K, ldb < N or ldc < N)";
+        case TGEMM_ERR_LD: return "leading dimension smaller than the stored row width";
         case TGEMM_ERR_DTYPE: return "unsupported (in_dtype, out_dtype) pair";
         case TGEMM_ERR_ALIAS: return "C overlaps A or B";
-        case TGEMM_ERR_CONFIG: return "unknown tile configuration or configuration for another input type";
+        case TGEMM_ERR_CONFIG:
+            return "unknown tile configuration, configuration for another input type, or one without a kernel for "
+                   "column-major operands";
+        case TGEMM_ERR_LAYOUT: return "layout is neither TGEMM_ROW_MAJOR nor TGEMM_COL_MAJOR";
         default: break;
     }
     if (code > 0) return hipGetErrorString((hipError_t)code);
@@ -358,7 +374,7 @@ int gemm_num_configs(void) { return kNumConfigs; }
 int gemm_config_info(int id, tgemm_config_info* out) {
     if (id < 0 || id >= kNumConfigs || out == nullptr) return TGEMM_ERR_CONFIG;
     const ConfigEntry& c = kConfigs[id];
-    const bool ring = c.pick_ring != nullptr;
+    const bool ring = c.ring != nullptr;
     out->id = id;
     out->in_dtype = c.in_family;
     out->block_m = c.bm;
@@ -388,16 +404,29 @@ int gemm_config_info(int id, tgemm_config_info* out) {
 
 int gemm_select_config(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
                        const void* C, int64_t ldc, int in_dtype, int out_dtype) {
-    const int v = validate(M, N, K, A, lda, B, ldb, C, ldc, in_dtype, out_dtype);
+    const Problem p{M, N, K, A, lda, LAYOUT_ROW, B, ldb, LAYOUT_ROW, (void*)C, ldc, in_dtype, out_dtype};
+    const int v = validate(p);
     if (v != TGEMM_OK) return v;
-    return table_choice(M, N, K, A, lda, B, ldb, C, ldc, in_dtype, out_dtype);
+    return table_choice(p);
 }
 
 int gemm_select_kernel(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
                        const void* C, int64_t ldc, int in_dtype, int out_dtype, int config_id) {
+    return gemm_select_kernel_t(M, N, K, A, lda, TGEMM_ROW_MAJOR, B, ldb, TGEMM_ROW_MAJOR, C, ldc, TGEMM_ROW_MAJOR,
+                                in_dtype, out_dtype, config_id, nullptr);
+}
+
+int gemm_select_kernel_t(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int layout_a, const void* B,
+                         int64_t ldb, int layout_b, const void* C, int64_t ldc, int layout_c, int in_dtype,
+                         int out_dtype, int config_id, int* config_out) {
+    Problem p;
+    int v = make_problem(M, N, K, A, lda, layout_a, B, ldb, layout_b, (void*)C, ldc, layout_c, in_dtype, out_dtype, p);
+    if (v != TGEMM_OK) return v;
     Plan plan;
-    const int v = make_plan(M, N, K, A, lda, B, ldb, C, ldc, in_dtype, out_dtype, config_id, plan);
-    return v != TGEMM_OK ? v : plan.kind;
+    v = make_plan(p, config_id, plan);
+    if (v != TGEMM_OK) return v;
+    if (config_out != nullptr) *config_out = plan.config;
+    return plan.kind;
 }
 
 int gemm_tile_map(int bid, int tiles_m, int tiles_n, int group_m, int* tm, int* tn) {
@@ -407,6 +436,6 @@ int gemm_tile_map(int bid, int tiles_m, int tiles_n, int group_m, int* tm, int* 
     return TGEMM_OK;
 }
 
-const char* gemm_version(void) { return "tgemm 0.1 gfx950"; }
+const char* gemm_version(void) { return "tgemm 0.2 gfx950"; }
 
 }  // extern "C"
