@@ -214,6 +214,27 @@ def main():
                 "tflops_back_to_back": pf / (b2b_ms * 1e-3) / 1e12,
                 "gbs_back_to_back": algo_bytes / (b2b_ms * 1e-3) / 1e9})
 
+    # the same 8192^3 product with column-major operands or output (gemm_t):
+    # each matrix holds the same values, stored transposed
+    layouts = []
+    if not args.no_per_config:
+        a_col = a.t().contiguous().t()
+        b_col = b.t().contiguous().t()
+        c_col = torch.empty((w.N, w.M), dtype=torch.float16, device=dev).t()
+        kinds = {0: "general", 1: "tiled", 2: "ring", 3: "direct"}
+        for name, la_, lb_, lc_ in (("A col-major", a_col, b, c), ("B col-major", a, b_col, c),
+                                    ("A, B col-major", a_col, b_col, c), ("C col-major", a, b, c_col)):
+            call = lambda: T.gemm_tensors(la_, lb_, lc_, stream=stream.cuda_stream)
+            _, lev = time_calls(call, 20, 3, stream)
+            (xa, lda_), (xb, ldb_), (xc, ldc_) = T._layout(la_), T._layout(lb_), T._layout(lc_)
+            kind, lcfg = T.gemm_select_kernel_t(w.M, w.N, w.K, la_.data_ptr(), lda_, xa, lb_.data_ptr(), ldb_, xb,
+                                                lc_.data_ptr(), ldc_, xc, w.in_dtype, w.out_dtype)
+            med = float(np.median(lev))
+            layouts.append({"layouts": name, "config": T.gemm_config_info(lcfg)["name"],
+                            "kernel": kinds.get(kind, str(kind)), "us_median": med * 1e3,
+                            "tflops": flops / (med * 1e-3) / 1e12})
+        del a_col, b_col, c_col
+
     if args.calibrate_copy:
         src = torch.ones(128 << 20, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -246,6 +267,7 @@ def main():
                      "algorithmic_bytes_per_launch": (w.M * w.K + w.K * w.N + w.M * w.N) * 2},
         "cpu_baseline": cpu,
         "per_config": per_config,
+        "layouts_8192": layouts,
         "sclk": sclk_mhz(),
         "kernel_source_hash": kernel_source_hash(),
     }

@@ -141,6 +141,12 @@ typedef struct tgemm_config_info {
     int mfma_m, mfma_n, mfma_k; /* shape of one MFMA instruction           */
     int lds_bytes;      /* LDS per workgroup                               */
     const char* name;   /* static string                                   */
+    /* The ring of a row-major A when it differs from B's (block_k, stages):
+     * the direct-to-LDS ring kernel stages row-major A in 2 stages of 64 of
+     * K, so that every load reads whole 128-byte lines.  Otherwise equal to
+     * block_k and stages.  lds_bytes = (a_stages * a_block_k * block_m +
+     * stages * block_k * block_n) * element bytes. */
+    int a_block_k, a_stages;
 } tgemm_config_info;
 
 /* Fills *out for config `id`; returns TGEMM_OK or TGEMM_ERR_CONFIG. */

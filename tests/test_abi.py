@@ -47,8 +47,13 @@ def test_version_and_configs():
         eb = 4 if c["in_dtype"] == T.F32 else 2
         # LDS holds `stages` copies of an A tile (block_m x block_k) and a B
         # tile (block_k x block_n), the budget formula of page
-        # "企业官网建设流程全解析", §4.2
-        assert c["lds_bytes"] == c["stages"] * (c["block_m"] + c["block_n"]) * c["block_k"] * eb
+        # "企业官网建设流程全解析", §4.2, with A's own stage count and depth
+        # where they differ (the ring kernel's row-major A)
+        assert c["lds_bytes"] == (c["a_stages"] * c["a_block_k"] * c["block_m"] +
+                                  c["stages"] * c["block_k"] * c["block_n"]) * eb
+        if c["a_stages"] == c["stages"]:
+            assert c["a_block_k"] == c["block_k"]
+            assert c["lds_bytes"] == c["stages"] * (c["block_m"] + c["block_n"]) * c["block_k"] * eb
     with pytest.raises(T.TgemmError):
         T.gemm_config_info(n)
 
@@ -65,8 +70,11 @@ def test_lds_budget_formula_matches_page_example():
     assert lds(128, 128, 32, 3, 2) == 48 * 1024
     assert lds(128, 128, 32, 4, 2) == 64 * 1024
     assert lds(128, 128, 64, 3, 2) == 98304
+    # the 256 x 256 configuration: A in 2 stages of 64, B in 4 stages of 32,
+    # each ring 64 KiB
     big = T.gemm_config_info(0)
-    assert big["lds_bytes"] == lds(big["block_m"], big["block_n"], big["block_k"], big["stages"], 2)
+    assert big["lds_bytes"] == (lds(big["block_m"], 0, big["a_block_k"], big["a_stages"], 2) +
+                                lds(0, big["block_n"], big["block_k"], big["stages"], 2)) == 128 * 1024
 
 
 def _codes(M, N, K, A, lda, B, ldb, C, ldc, i, o):
@@ -203,6 +211,7 @@ def test_ring_configs_report_their_ring_kernel():
     for cid in (0, 1):
         c = T.gemm_config_info(cid)
         assert (c["block_k"], c["stages"]) == (32, 4)
+        assert (c["a_block_k"], c["a_stages"]) == (64, 2)
         assert (c["mfma_m"], c["mfma_n"], c["mfma_k"]) == (16, 16, 32)
 
 

@@ -40,7 +40,8 @@ class ConfigInfo(ctypes.Structure):
                 ("stages", ctypes.c_int), ("threads", ctypes.c_int),
                 ("waves_m", ctypes.c_int), ("waves_n", ctypes.c_int),
                 ("mfma_m", ctypes.c_int), ("mfma_n", ctypes.c_int), ("mfma_k", ctypes.c_int),
-                ("lds_bytes", ctypes.c_int), ("name", ctypes.c_char_p)]
+                ("lds_bytes", ctypes.c_int), ("name", ctypes.c_char_p),
+                ("a_block_k", ctypes.c_int), ("a_stages", ctypes.c_int)]
 
     def as_dict(self):
         d = {f: getattr(self, f) for f, _ in self._fields_}

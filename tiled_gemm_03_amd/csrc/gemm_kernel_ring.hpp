@@ -1,6 +1,6 @@
 // gemm_kernel_ring.hpp -- the gfx950 fast path of the tiled matrix product
 // for 16-bit inputs (fp16 / bf16) on whole tiles: direct-to-LDS loads into
-// S-stage LDS rings and v_mfma_f32_16x16x32_{f16,bf16}.
+// multi-stage LDS rings and v_mfma_f32_16x16x32_{f16,bf16}.
 //
 // The method is the tiled kernel of page "企业官网建设流程全解析" §3.3 (one
 // workgroup per BM x BN tile of C, K walked in steps, A and B tiles staged in
@@ -15,11 +15,14 @@
 //        the K position is the scalar offset, one add per operand and step.
 //        Loads issued past the end of K read zeros (or in-bounds data that
 //        is never used), so every step of the loop has the same shape.
-//  * a4  pipeline.  BK = 32 per step; A and B each have a ring of S = 4 LDS
-//        stages.  The loads of step s + S are issued during step s, so a
-//        load has S - 1 steps (about 3 x 1000 cycles) to arrive.  One
-//        barrier per step: after it, the stage read during the previous step
-//        is free and is refilled.
+//  * a4  pipeline.  Steps of BK = 32.  B has a ring of 4 LDS stages of one
+//        step; a row-major A (k contiguous) a ring of 2 stages of two steps,
+//        so that each of its loads reads whole 128-byte lines (loads of
+//        64-byte half lines run at about 60% of that rate).  A stage is
+//        refilled at the step that frees it, with the loads of the stage
+//        that starts 4 steps later; they have 2 (A) or 3 (B) steps, about
+//        1000 cycles each, to arrive.  One barrier per step: after it, the
+//        stages read during the previous step for the last time are free.
 //  * a5  MFMA.  v_mfma_f32_16x16x32: lane l holds 8 consecutive k of row /
 //        column l % 16 of each operand (k = 8 (l / 16) ..).  At the power
 //        limit that random fp16 data sets on MI355X, this shape keeps a
@@ -42,18 +45,12 @@
 // Operand layouts (the row-major default and the column-major option of page
 // "TileLang实战：用Python DSL自动生成高性能GPU计算内核" §5.1): an operand
 // whose k is contiguous in memory (A row-major, B column-major) is staged as
-// rows of 32 k (64 bytes) per row / column and read with ds_read_b128; one
+// 64 bytes (32 k) per row / column and step and read with ds_read_b128; one
 // whose k is strided (A column-major, B row-major) is staged as 32 k-rows of
 // the tile's width and read with ds_read_b64_tr_b16.
 //
-// LDS: the A ring (S stages), then the B ring (S stages), each stage
-// width x 32 x 2 bytes.
-//   k contiguous: 16-byte chunk c of row r stored at chunk c ^ ((r / 4) % 4):
-//      the 16 rows read by one quarter wave (one ds_read_b128 cycle) land in
-//      16 different bank groups.
-//   k strided: chunk c of k-row r stored at chunk c ^ (4 (r % 4) ^ 2 ((r/8)
-//      % 2)): the rows r .. r+3 and r+8 .. r+11 read by one half wave of a
-//      transposing read land in 16 different bank groups.
+// LDS: the A ring, then the B ring, 64 KiB each for a 256 x 256 tile (the
+// stage layouts and swizzles are described at RingOperand).
 
 #pragma once
 #include "gemm_kernel.hpp"
@@ -80,64 +77,150 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// One operand's tile in the ring: EXT rows / columns (BM for A, BN for B) by
-// 32 of K; KC: k contiguous in memory.
-template <int EXT, bool KC_>
+__device__ __forceinline__ constexpr int ring_key_kc(int r) { return (r >> 1) & 3; }
+__device__ __forceinline__ constexpr int ring_key_ks(int r) { return 4 * (r & 3) ^ 2 * ((r >> 3) & 1); }
+
+// The ring of one operand: EXT rows (A) / columns (B) of the tile; KC: k
+// contiguous in memory; D steps of 32 k per stage, NS stages.
+//
+// Layout of a stage, as (r, c) -> byte position, r the LDS row (KC: row of A
+// / column of B; KS: k) and c its 16-byte chunk (KC: 8 k; KS: 8 columns):
+//   KC, D = 1: rows of 64 bytes, chunk c of row r at c ^ key(r);
+//   KC, D = 2: 1 KiB blocks of 8 rows; in a block, the first 64 bytes of
+//              each row (the stage's first step), then the second 64 bytes;
+//              chunk slots swizzled as for D = 1.  A fragment read of one
+//              step then touches 512 bytes of each of two blocks, and a load
+//              brings whole 128-byte lines of 8 rows;
+//   KS:        rows of EXT * 2 bytes, chunk c of row r at c ^ key_ks(r).
+// Loads fill 1 KiB blocks lane by lane (lane l: byte 16 l of the block), so a
+// layout is realised by choosing which global chunk each lane fetches (at).
+// The keys were chosen by measuring the reads of one wave: key (r / 2) % 4
+// makes a k-contiguous fragment read (16 rows, chunk l / 16 for lane l) as
+// fast as a contiguous 1 KiB ds_read_b128 (256 bytes per clock, no bank
+// conflict cycles), while plain rows and the keys (r / 4) % 4, r % 4,
+// 2 ((r / 2) % 2) take twice as long; key_ks puts the 16 k-rows of one
+// transposing read in different bank groups.
+template <int EXT, bool KC_, int D_, int NS_>
 struct RingOperand {
     static constexpr bool KC = KC_;
-    static constexpr int STAGE = EXT * 64;               // bytes per stage
-    static constexpr int ROW = KC ? 64 : EXT * 2;        // bytes per LDS row
-    static constexpr int CHUNKS = ROW / 16;              // 16-byte chunks per row
-    static constexpr int RPB = 1024 / ROW;               // LDS rows per 1 KiB load
+    static constexpr int D = D_, NS = NS_;
+    static constexpr int STAGE = EXT * 64 * D;           // bytes per stage
+    static constexpr int RING = NS * STAGE;
+    static constexpr int ROW = KC ? 64 : EXT * 2;        // bytes per LDS row (a D = 2 row: two of 64)
     static constexpr int BLOCKS = STAGE / 1024;
-    static constexpr int READS = KC ? 1 : 2;             // LDS reads per fragment
-    static_assert(KC || CHUNKS == 16 || CHUNKS == 32, "k-strided tiles of 128 or 256");
+    static_assert(KC || D == 1, "k-strided operands take one step per stage");
+    static_assert(D == 1 || D == 2, "");
+    static_assert(KC || EXT == 128 || EXT == 256, "k-strided tiles of 128 or 256");
+    // byte position of chunk c of row r in a stage (swz = 0: no swizzle,
+    // kept for measuring bank conflicts against the swizzle)
+    static constexpr int pos(int r, int c, int swz = 1) {
+        if (KC && D == 2)
+            return (r >> 3) * 1024 + (c >> 2) * 512 + (r & 7) * 64 + (((c & 3) ^ (swz * ring_key_kc(r))) * 16);
+        if (KC) return r * 64 + ((c ^ (swz * ring_key_kc(r))) * 16);
+        return r * ROW + ((c ^ (swz * ring_key_ks(r))) * 16);
+    }
+    // the (row, chunk) stored at byte position p (p a multiple of 16)
+    static constexpr void at(int p, int& r, int& c, int swz = 1) {
+        if (KC && D == 2) {
+            r = (p >> 10) * 8 + ((p >> 6) & 7);
+            c = ((p >> 9) & 1) * 4 + (((p >> 4) & 3) ^ (swz * ring_key_kc(r)));
+        } else if (KC) {
+            r = p >> 6;
+            c = ((p >> 4) & 3) ^ (swz * ring_key_kc(r));
+        } else {
+            r = p / ROW;
+            c = ((p % ROW) >> 4) ^ (swz * ring_key_ks(r));
+        }
+    }
+    // stage of step j and the step's place in it
+    static constexpr int stage_of(int j) { return (j / D) % NS; }
+    static constexpr int sub_of(int j) { return j % D; }
+    // a stage is refilled at the step that frees it (its last step): at step v
+    // with v % D == D - 1 the loads of the stage that starts at v - D + 1 + NS D
+    static constexpr bool issues_at(int v) { return ((v % D) + D) % D == D - 1; }
+    static constexpr int first_loaded_at(int v) { return v - D + 1 + NS * D; }
+    // the step at which the stage holding step j was loaded
+    static constexpr int loaded_at(int j) { return j - j % D + D - 1 - NS * D; }
+    // Reads: fragment f of step j is at a per-lane base plus an immediate
+    // offset.  k-contiguous: one base per 64 KiB of ring (stage, fragment
+    // and step in the immediate); k-strided: one base per fragment (the
+    // swizzle permutes the columns; stage and second read in the immediate).
+    static constexpr int kc_off(int f, int j) {
+        return stage_of(j) * STAGE + (D == 1 ? f * 1024 : f * 2048 + sub_of(j) * 512);
+    }
+    static constexpr int bases(int F) { return KC ? ((RING - 1) >> 16) + 1 : F; }
+    static constexpr bool imm_ok(int F) {
+        return KC ? true : (NS - 1) * STAGE + 4 * ROW < 65536;
+    }
 };
 
-__device__ __forceinline__ int ring_key_kc(int r) { return (r >> 2) & 3; }
-__device__ __forceinline__ int ring_key_ks(int r) { return 4 * (r & 3) ^ 2 * ((r >> 3) & 1); }
-
 // Tile configuration of the ring kernel: BM x BN output tile, WM x WN waves,
-// S ring stages of BK = 32, OCC workgroups per CU the registers are sized for.
-template <int BM_, int BN_, int WM_, int WN_, int S_, int OCC_>
+// OCC workgroups per CU the registers and LDS are sized for; steps of BK = 32.
+template <int BM_, int BN_, int WM_, int WN_, int OCC_>
 struct RingCfg {
-    static constexpr int BM = BM_, BN = BN_, BK = 32, WM = WM_, WN = WN_, S = S_, OCC = OCC_;
+    static constexpr int BM = BM_, BN = BN_, BK = 32, WM = WM_, WN = WN_, OCC = OCC_;
     static constexpr int THREADS = 64 * WM * WN, WAVES = WM * WN;
-    static constexpr int EB = 2;
-    static constexpr int A_STAGE = BM * 64, B_STAGE = BN * 64;
-    static constexpr int A_RING = S * A_STAGE, B_RING = S * B_STAGE;
-    static constexpr int LDS_BYTES = A_RING + B_RING;
-    static constexpr int A_BLOCKS = A_STAGE / 1024, B_BLOCKS = B_STAGE / 1024;
-    static constexpr int A_LOADS = A_BLOCKS / WAVES, B_LOADS = B_BLOCKS / WAVES;
-    static constexpr int L = A_LOADS + B_LOADS;    // loads per wave per step
     static constexpr int WTM = BM / WM, WTN = BN / WN;
     static constexpr int FM = WTM / 16, FN = WTN / 16;
-    static constexpr int U = S;                    // steps per loop trip
-    static constexpr int K_MULT = BK * U;          // K must be a multiple of this
-    static_assert(S % 2 == 0, "fragment buffers alternate per step");
-    static_assert(A_BLOCKS % WAVES == 0 && B_BLOCKS % WAVES == 0, "");
-    static_assert(LDS_BYTES <= 160 * 1024, "gfx950 LDS is 160 KiB per CU");
-    static_assert(S >= 3 && (S - 1) * L < 64, "vmcnt range");
-    // every LDS read offset fits the 16-bit immediate of ds_read, in either
-    // layout of either operand
-    static_assert(A_RING - A_STAGE + (FM - 1) * 16 * 64 < 65536 && A_RING - A_STAGE + 4 * BM * 2 < 65536, "");
-    static_assert(B_RING - B_STAGE + (FN - 1) * 16 * 64 < 65536 && B_RING - B_STAGE + 4 * BN * 2 < 65536, "");
+    static constexpr int K_MULT = 4 * BK;          // K must be a multiple of this
+    // Ring of each operand for the layouts of A and B.  A k-contiguous
+    // operand reads 64 bytes of every row per step, half a 128-byte line, and
+    // such loads run at about 60% of the rate of whole lines: a k-contiguous
+    // A takes two stages of two steps (128 bytes per row) instead of four of
+    // one, in the same LDS.  B keeps four stages of one step in every layout:
+    // with a two-step B ring beside a k-strided A, the register allocator no
+    // longer keeps every accumulator in place.
+    template <bool KCA, bool KCB>
+    struct Plan {
+        static constexpr bool DA = KCA;
+        using OA = RingOperand<BM, KCA, DA ? 2 : 1, DA ? 2 : 4>;
+        using OB = RingOperand<BN, KCB, 1, 4>;
+        static constexpr int LA = OA::BLOCKS / WAVES, LB = OB::BLOCKS / WAVES;  // loads per wave and stage
+        static constexpr int LDS_BYTES = OA::RING + OB::RING;
+        // steps per loop trip: both rings and the two fragment buffers return
+        // to their first state
+        static constexpr int U = 4;
+        static constexpr int loads_at(int v) { return (OA::issues_at(v) ? LA : 0) + (OB::issues_at(v) ? LB : 0); }
+        // loads issued after those that step j's stages need, counted at the
+        // start of step `now` (the wait before step j's fragments are read)
+        static constexpr int after(int j, int now) {
+            const int t = OA::loaded_at(j) > OB::loaded_at(j) ? OA::loaded_at(j) : OB::loaded_at(j);
+            int n = 0;
+            for (int v = t + 1; v < now; ++v) n += loads_at(v);
+            return n;
+        }
+        static_assert(OA::BLOCKS % WAVES == 0 && OB::BLOCKS % WAVES == 0, "");
+        static_assert(LDS_BYTES * OCC <= 160 * 1024, "gfx950 LDS is 160 KiB per CU");
+        static_assert(U % (OA::D * OA::NS) == 0 && U % (OB::D * OB::NS) == 0 && U % 4 == 0, "");
+        // every LDS read offset fits the 16-bit immediate of ds_read
+        static_assert(OA::imm_ok(FM) && OB::imm_ok(FN), "");
+    };
+    // LDS per workgroup (the same for every layout)
+    static constexpr int LDS_BYTES = Plan<true, false>::LDS_BYTES;
+    static_assert(LDS_BYTES == Plan<false, false>::LDS_BYTES, "");
+    // how far past K the ring loads (steps of 32)
+    static constexpr int LOOKAHEAD = 4;
+    // the rings of row-major A and B (the default layouts)
+    static constexpr int A_BK = 32 * Plan<true, false>::OA::D, A_STAGES = Plan<true, false>::OA::NS;
+    static constexpr int B_BK = 32, B_STAGES = Plan<true, false>::OB::NS;
     static_assert(WTM % 16 == 0 && WTN % 16 == 0, "");
 };
 
 // Preconditions (checked by the host): 16-bit inputs; M % BM == 0,
 // N % BN == 0, K % K_MULT == 0; A and B 16-byte aligned with lda and ldb
 // multiples of 8; C aligned for 4-element stores with ldc % 4 == 0; the
-// buffer offsets (a tile's rows or columns of each operand over K + S*BK of
-// K) below 2^31 bytes.  LA / LB: LAYOUT_ROW or LAYOUT_COL; C is row-major.
+// buffer offsets (a tile's rows or columns of each operand over
+// K + LOOKAHEAD * BK of K) below 2^31 bytes.  LA / LB: LAYOUT_ROW or
+// LAYOUT_COL; C is row-major.
 template <class T, int IN, int OUT, int LA, int LB>
 __global__ __attribute__((amdgpu_flat_work_group_size(T::THREADS, T::THREADS),
                           amdgpu_waves_per_eu(T::OCC * T::WAVES / 4 > 0 ? T::OCC * T::WAVES / 4 : 1)))
 void gemm_kernel_ring(GemmArgs p) {
     // A is k-contiguous when row-major, B when column-major
-    using OA = RingOperand<T::BM, LA == LAYOUT_ROW>;
-    using OB_ = RingOperand<T::BN, LB == LAYOUT_COL>;
-    __shared__ __attribute__((aligned(1024))) char smem[T::LDS_BYTES];
+    using P = typename T::template Plan<LA == LAYOUT_ROW, LB == LAYOUT_COL>;
+    using OA = typename P::OA;
+    using OB_ = typename P::OB;
+    __shared__ __attribute__((aligned(1024))) char smem[P::LDS_BYTES];
     const int smem_base = (int)(uintptr_t)(lds_void*)smem;   // LDS byte address (M0 values)
     lds_char* const lds = (lds_char*)smem;
 
@@ -177,24 +260,22 @@ void gemm_kernel_ring(GemmArgs p) {
     };
     const i32x4 rs_a = operand_rsrc(OA{}, p.A, lda, m0, p.M);
     const i32x4 rs_b = operand_rsrc(OB_{}, p.B, ldb, n0, p.N);
-    // per-lane byte offset of load x (block blk of the stage): lane l fills
-    // slot l of the 1 KiB block (LDS row l / CHUNKS, chunk l % CHUNKS) with
-    // the logical chunk the swizzle puts there
+    // per-lane byte offset of a load (block blk of a stage): lane l fills
+    // byte 16 l of the block with the chunk the layout puts there
     auto load_voff = [&](auto op_t, int blk, int64_t ld) __attribute__((always_inline)) {
         using O = decltype(op_t);
-        const int r = blk * O::RPB + lane / O::CHUNKS;   // LDS row: outer index (KC) or k (KS)
-        const int key = O::KC ? ring_key_kc(r) : ring_key_ks(r);
-        const int c = (lane % O::CHUNKS) ^ (swz * key);
+        int r, c;
+        O::at(blk * 1024 + 16 * lane, r, c, swz);
         return (int)((int64_t)r * ld * 2 + c * 16);
     };
-    int voff[T::L];
+    int voff_a[P::LA], voff_b[P::LB];
 #pragma unroll
-    for (int x = 0; x < T::L; ++x)
-        voff[x] = x < T::A_LOADS ? load_voff(OA{}, wave * T::A_LOADS + x, lda)
-                                 : load_voff(OB_{}, wave * T::B_LOADS + (x - T::A_LOADS), ldb);
-    // K advance per step: 32 elements along a row (KC) or 32 rows (KS)
-    const int a_kstep = OA::KC ? 64 : (int)(32 * lda * 2);
-    const int b_kstep = OB_::KC ? 64 : (int)(32 * ldb * 2);
+    for (int x = 0; x < P::LA; ++x) voff_a[x] = load_voff(OA{}, wave * P::LA + x, lda);
+#pragma unroll
+    for (int x = 0; x < P::LB; ++x) voff_b[x] = load_voff(OB_{}, wave * P::LB + x, ldb);
+    // K advance per stage: 32 D elements along a row (KC) or 32 rows (KS)
+    const int a_kstep = OA::KC ? 64 * OA::D : (int)(32 * lda * 2);
+    const int b_kstep = OB_::KC ? 64 * OB_::D : (int)(32 * ldb * 2);
     // Issued through inline asm (M0 = LDS destination, then the load): the
     // compiler then does not guard later LDS reads with waits for these
     // loads; the kernel waits for them itself (vmcnt) before the barrier that
@@ -205,70 +286,73 @@ void gemm_kernel_ring(GemmArgs p) {
                      : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(vo), "s"(rs), "s"(so)
                      : "memory");
     };
-    // load x of the step whose K byte offsets are (ka, kb) into ring stage st
-    auto issue_load = [&](int st, int x, int ka, int kb) __attribute__((always_inline)) {
-        if (x < T::A_LOADS)
-            dma(smem_base + st * T::A_STAGE + (wave * T::A_LOADS + x) * 1024, voff[x], rs_a, ka);
-        else
-            dma(smem_base + T::A_RING + st * T::B_STAGE + (wave * T::B_LOADS + x - T::A_LOADS) * 1024, voff[x],
-                rs_b, kb);
+    // the loads of one operand's stage st at K byte offset k
+    auto load_a = [&](int st, int x, int k) __attribute__((always_inline)) {
+        dma(smem_base + st * OA::STAGE + (wave * P::LA + x) * 1024, voff_a[x], rs_a, k);
+    };
+    auto load_b = [&](int st, int x, int k) __attribute__((always_inline)) {
+        dma(smem_base + OA::RING + st * OB_::STAGE + (wave * P::LB + x) * 1024, voff_b[x], rs_b, k);
     };
 
     // ---------------------------------------------------------- a5: fragments
     // v_mfma_f32_16x16x32: lane l holds 8 consecutive k (8q .., q = l / 16) of
     // row / column l % 16 of each operand.
     const int q = lane >> 4, i16 = lane & 15;
-    // per-lane LDS base of fragment f of an operand whose wave block starts
-    // at outer index wo (the stage and the second transposing read go in the
-    // immediate offset)
-    auto frag_base = [&](auto op_t, lds_char* ring, int wo, int f) __attribute__((always_inline)) {
+    // per-lane LDS bases of an operand whose wave block starts at outer index
+    // wo (RingOperand: reads)
+    auto make_bases = [&](auto op_t, lds_char* ring, int wo, lds_char** out, int n) __attribute__((always_inline)) {
         using O = decltype(op_t);
-        if constexpr (O::KC) {
-            // row wo + 16 f + l%16, chunk q
-            const int r = wo + 16 * f + i16;
-            return ring + r * O::ROW + (q ^ (swz * ring_key_kc(r))) * 16;
-        } else {
-            // lane i of group q: k-row 8q + i/4 (+4 for the second read),
-            // columns wo + 16 f + 4 (i%4) .. +3
-            const int r = 8 * q + (i16 >> 2);
-            const int c = (wo + 16 * f) / 8 + ((i16 & 3) >> 1);
-            return ring + r * O::ROW + (c ^ (swz * ring_key_ks(r))) * 16 + 8 * (i16 & 1);
+#pragma unroll
+        for (int b = 0; b < n; ++b) {
+            if constexpr (O::KC) {
+                // row wo + l%16, chunk q of the stage's first step
+                out[b] = ring + O::pos(wo + i16, q, swz) + b * 65536;
+            } else {
+                // fragment b: lane i of group q reads k-row 8q + i/4 (+4 for
+                // the second read), columns wo + 16 b + 4 (i%4) .. +3
+                const int r = 8 * q + (i16 >> 2);
+                const int c = (wo + 16 * b) / 8 + ((i16 & 3) >> 1);
+                out[b] = ring + O::pos(r, c, swz) + 8 * (i16 & 1);
+            }
         }
     };
-    // k-contiguous operands need one base (the fragments are 1 KiB apart);
-    // k-strided ones one per fragment (the swizzle permutes their columns)
-    constexpr int NBA = OA::KC ? 1 : T::FM, NBB = OB_::KC ? 1 : T::FN;
+    constexpr int NBA = OA::bases(T::FM), NBB = OB_::bases(T::FN);
     lds_char* a_base[NBA];
     lds_char* b_base[NBB];
-#pragma unroll
-    for (int f = 0; f < NBA; ++f) a_base[f] = frag_base(OA{}, lds, wm * T::WTM, f);
-#pragma unroll
-    for (int f = 0; f < NBB; ++f) b_base[f] = frag_base(OB_{}, lds + T::A_RING, wn * T::WTN, f);
+    make_bases(OA{}, lds, wm * T::WTM, a_base, NBA);
+    make_bases(OB_{}, lds + OA::RING, wn * T::WTN, b_base, NBB);
 
-    // fragments: h[0] (k 0..3) and h[1] (k 4..7) of a lane's 8 k
-    i16x4 fa[2][T::FM][2], fb[2][T::FN][2];
-    auto read_one = [&](auto op_t, lds_char* const* base, int stage_bytes, int st, int f, int h,
-                        i16x4 (&dst)[2]) __attribute__((always_inline)) {
+    // fragments: a lane's 8 k of one row of A / column of B.  A k-strided
+    // fragment takes two transposing reads (k 0..3, then k 4..7, 4 LDS rows
+    // further); both are issued together and joined at once: reads of the two
+    // halves scattered over the step let the register allocator split the
+    // fragments and then copy accumulators around the loop.
+    i16x8 fa[2][T::FM], fb[2][T::FN];
+    // fragment f of step j (compile-time j: stage and step in the stage)
+    auto read_one = [&](auto op_t, lds_char* const* base, auto j_t, int f, i16x8& dst) __attribute__((always_inline)) {
         using O = decltype(op_t);
+        constexpr int j = decltype(j_t)::value;
+        constexpr int st = O::stage_of(j);
         if constexpr (O::KC) {
-            const u32x4 v = *(const lds_u32x4*)(base[0] + st * stage_bytes + f * 16 * O::ROW);
-            const i16x8 w = __builtin_bit_cast(i16x8, v);
-            dst[0] = __builtin_shufflevector(w, w, 0, 1, 2, 3);
-            dst[1] = __builtin_shufflevector(w, w, 4, 5, 6, 7);
+            const int off = O::kc_off(f, j);
+            dst = __builtin_bit_cast(i16x8, *(const lds_u32x4*)(base[off >> 16] + (off & 0xffff)));
         } else {
-            dst[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base[f] + st * stage_bytes + 4 * h * O::ROW));
+            lds_char* at = base[f] + st * O::STAGE;
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)at);
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(at + 4 * O::ROW));
+            dst = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
     };
-    constexpr int NRB = T::FN * OB_::READS, NRA = T::FM * OA::READS;
+    // one unit of read work per fragment
+    constexpr int NRB = T::FN, NRA = T::FM;
     constexpr int NREAD = NRA + NRB;
-    // read r of stage st into buffer buf: the B fragments first, then the A
+    // read r of step j into buffer buf: the B fragments first, then the A
     // fragments, the order the MFMAs need them in
-    auto read_frag = [&](int st, int buf, int r) __attribute__((always_inline)) {
+    auto read_frag = [&](auto j_t, int buf, int r) __attribute__((always_inline)) {
         if (r < NRB)
-            read_one(OB_{}, b_base, T::B_STAGE, st, r / OB_::READS, r % OB_::READS, fb[buf][r / OB_::READS]);
+            read_one(OB_{}, b_base, j_t, r, fb[buf][r]);
         else
-            read_one(OA{}, a_base, T::A_STAGE, st, (r - NRB) / OA::READS, (r - NRB) % OA::READS,
-                     fa[buf][(r - NRB) / OA::READS]);
+            read_one(OA{}, a_base, j_t, r - NRB, fa[buf][r - NRB]);
     };
 
     // a6: accumulators, zeroed (T.clear of §3.3).  The empty asm makes each
@@ -291,8 +375,7 @@ void gemm_kernel_ring(GemmArgs p) {
     auto mfma_one = [&](int buf, int m) __attribute__((always_inline)) {
         // snake order over j: neighbours share one operand
         const int i = m / T::FN, jj = m % T::FN, j = (i & 1) ? T::FN - 1 - jj : jj;
-        const i16x8 bop = __builtin_shufflevector(fb[buf][j][0], fb[buf][j][1], 0, 1, 2, 3, 4, 5, 6, 7);
-        const i16x8 aop = __builtin_shufflevector(fa[buf][i][0], fa[buf][i][1], 0, 1, 2, 3, 4, 5, 6, 7);
+        const i16x8 bop = fb[buf][j], aop = fa[buf][i];
         if constexpr (IN == DT_F16) {
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, bop),
                                                                 __builtin_bit_cast(f16x8, aop), acc[i][j], 0, 0, 0);
@@ -302,22 +385,36 @@ void gemm_kernel_ring(GemmArgs p) {
         }
     };
 
-    // One step on ring stage ST, fragments in buffer BUF: wait until this
-    // wave's loads of the next stage have landed ((S-2)*L loads of later
-    // steps may still be in flight), barrier (every wave has then finished
-    // the previous step, so the next stage is complete and stage ST, read
-    // during the previous step, is free), then the MFMAs, with the next
-    // stage's fragment reads and the loads of step s + S into stage ST
-    // interleaved: one load after every NREAD / L reads, spread over the
-    // MFMAs so that at most two other instructions sit between two MFMAs.
-    auto step = [&](auto st_t, auto buf_t, int ka, int kb) __attribute__((always_inline)) {
-        constexpr int ST = decltype(st_t)::value, BUF = decltype(buf_t)::value;
-        constexpr int NXT = (ST + 1) % T::S;
-        wait_vmcnt<(T::S - 2) * T::L>();
+    // The loads of (virtual) step v: each operand refills the stage that step
+    // v frees (B loads first, then A), the x-th load of the step.
+    int ka = 0, kb = 0;  // K byte offsets of the next stage to load
+    auto issue = [&](auto v_t, int x) __attribute__((always_inline)) {
+        constexpr int v = decltype(v_t)::value;
+        constexpr int nb = OB_::issues_at(v) ? P::LB : 0;
+        if (x < nb) {
+            load_b(OB_::stage_of(OB_::first_loaded_at(v)), x, kb);
+            if (x == nb - 1) kb += b_kstep;
+        } else {
+            load_a(OA::stage_of(OA::first_loaded_at(v)), x - nb, ka);
+            if (x == P::loads_at(v) - 1) ka += a_kstep;
+        }
+    };
+
+    // One step u of the loop trip (compile-time; the ring state repeats every
+    // U steps): wait until this wave's loads of the stages of step u + 1 have
+    // landed, barrier (every wave has then finished step u - 1, so those
+    // stages are complete and the stages step u frees, read for the last time
+    // during step u - 1, can be refilled), then the MFMAs of step u with the
+    // fragment reads of step u + 1 and this step's loads interleaved: one
+    // load after every few reads, spread over the MFMAs so that at most two
+    // other instructions sit between two MFMAs.
+    auto step = [&](auto u_t) __attribute__((always_inline)) {
+        constexpr int u = decltype(u_t)::value;
+        constexpr int BUF = u & 1;
+        constexpr int NL = P::loads_at(u);
+        wait_vmcnt<P::after(u + 1, u)>();
         __syncthreads();
-        constexpr int n_work = NREAD + T::L;
-        constexpr int per = NREAD / T::L;
-        static_assert(NREAD % T::L == 0, "");
+        constexpr int n_work = NREAD + NL;
         static_for<0, NMF>([&](auto mt) __attribute__((always_inline)) {
             constexpr int m = decltype(mt)::value;
             mfma_one(BUF, m);
@@ -325,9 +422,10 @@ void gemm_kernel_ring(GemmArgs p) {
             constexpr int we = ((m + 1) * n_work + NMF - 1) / NMF;
             static_for<wb, we>([&](auto wt) __attribute__((always_inline)) {
                 constexpr int w = decltype(wt)::value;
-                constexpr int grp = w / (per + 1);
-                if constexpr (w % (per + 1) == per) issue_load(ST, grp, ka, kb);
-                else read_frag(NXT, BUF ^ 1, w - grp);
+                // work item w: a load when w * NL / n_work steps up, else a read
+                constexpr int lo = w * NL / n_work, hi = (w + 1) * NL / n_work;
+                if constexpr (hi > lo) issue(IntTag<u>{}, lo);
+                else read_frag(IntTag<(u + 1) % P::U>{}, BUF ^ 1, w - lo);
             });
             __builtin_amdgcn_sched_barrier(0);
         });
@@ -335,26 +433,26 @@ void gemm_kernel_ring(GemmArgs p) {
 
     const int nk = K / T::BK;  // a multiple of U (host precondition)
     if (nk > 0) {
-        // prologue: steps 0 .. S-1 into stages 0 .. S-1, then the fragments
-        // of step 0
-        static_for<0, T::S>([&](auto s_t) __attribute__((always_inline)) {
-            constexpr int s = decltype(s_t)::value;
-            static_for<0, T::L>([&](auto x) __attribute__((always_inline)) {
-                issue_load(s, decltype(x)::value, s * a_kstep, s * b_kstep);
-            });
+        // prologue: the loads of the virtual steps before step 0, then the
+        // fragments of step 0
+        constexpr int V0 = -(OA::NS * OA::D > OB_::NS * OB_::D ? OA::NS * OA::D : OB_::NS * OB_::D);
+        static_for<V0, 0>([&](auto v_t) __attribute__((always_inline)) {
+            constexpr int v = decltype(v_t)::value;
+            if constexpr (OB_::issues_at(v) && OB_::first_loaded_at(v) >= 0)
+                static_for<0, P::LB>([&](auto x) __attribute__((always_inline)) {
+                    load_b(OB_::stage_of(OB_::first_loaded_at(v)), decltype(x)::value, kb);
+                });
+            if constexpr (OB_::issues_at(v) && OB_::first_loaded_at(v) >= 0) kb += b_kstep;
+            if constexpr (OA::issues_at(v) && OA::first_loaded_at(v) >= 0)
+                static_for<0, P::LA>([&](auto x) __attribute__((always_inline)) {
+                    load_a(OA::stage_of(OA::first_loaded_at(v)), decltype(x)::value, ka);
+                });
+            if constexpr (OA::issues_at(v) && OA::first_loaded_at(v) >= 0) ka += a_kstep;
         });
-        wait_vmcnt<(T::S - 1) * T::L>();
+        wait_vmcnt<P::after(0, 0)>();
         __syncthreads();
-        static_for<0, NREAD>([&](auto r) __attribute__((always_inline)) { read_frag(0, 0, decltype(r)::value); });
-        int ka = T::S * a_kstep, kb = T::S * b_kstep;  // K offsets of the next step to load
-        for (int s = 0; s < nk; s += T::U) {
-            static_for<0, T::U>([&](auto u_t) __attribute__((always_inline)) {
-                constexpr int u = decltype(u_t)::value;
-                step(IntTag<u % T::S>{}, IntTag<u & 1>{}, ka, kb);
-                ka += a_kstep;
-                kb += b_kstep;
-            });
-        }
+        static_for<0, NREAD>([&](auto r) __attribute__((always_inline)) { read_frag(IntTag<0>{}, 0, decltype(r)::value); });
+        for (int s = 0; s < nk; s += P::U) static_for<0, P::U>([&](auto u) __attribute__((always_inline)) { step(u); });
         // no load may still be writing LDS when the workgroup ends
         wait_vmcnt<0>();
     }

@@ -20,10 +20,8 @@ using CfgTiny = TileCfg<32, 32, 64, 1, 1, 2, 4>;     // 1 wave
 using CfgF32Mid = TileCfg<64, 64, 32, 2, 2, 4, 2>;   // fp32 inputs
 using CfgF32Tiny = TileCfg<32, 32, 32, 1, 1, 4, 4>;  // fp32 inputs, 1 wave
 // direct-to-LDS ring kernels of the two largest tiles
-using RingBig = RingCfg<256, 256, 2, 2, 4, 1>;
-using RingMid = RingCfg<128, 128, 2, 2, 4, 2>;
-static_assert(RingBig::LDS_BYTES == CfgBig::LDS_BYTES && RingMid::LDS_BYTES == CfgMid::LDS_BYTES,
-              "both kernels of a configuration use the same LDS budget");
+using RingBig = RingCfg<256, 256, 2, 2, 1>;
+using RingMid = RingCfg<128, 128, 2, 2, 2>;
 
 enum { CFG_BIG = 0, CFG_MID = 1, CFG_SMALL = 2, CFG_TINY = 3, CFG_F32_MID = 4, CFG_F32_TINY = 5,
        CFG_DIRECT = 6, CFG_F32_DIRECT = 7, NUM_CONFIGS = 8 };

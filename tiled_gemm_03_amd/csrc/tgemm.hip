@@ -30,6 +30,8 @@ struct ConfigEntry {
     // stage count and LDS bytes
     KernelFn (*ring)(int in, int out, int la, int lb);
     int ring_bk, ring_stages, ring_k_mult, ring_lds;
+    int ring_lookahead;               // steps of ring_bk that the ring loads past K
+    int ring_a_bk, ring_a_stages;     // the ring of a row-major A
 };
 
 KernelFn tiled_f32_mid(int in, int out, bool fast) { return tiled_kernel_f32(CFG_F32_MID, in, out, fast); }
@@ -37,12 +39,13 @@ KernelFn tiled_f32_tiny(int in, int out, bool fast) { return tiled_kernel_f32(CF
 
 #define ENTRY(name, fam, T, sel)                                                                                \
     {name, fam, false, T::BM, T::BN, T::BK, T::WM, T::WN, T::EB, T::LDS_BYTES, T::THREADS, T::CPR, sel, nullptr, \
-     0, 0, 0, 0}
+     0, 0, 0, 0, 0, 0, 0}
 #define ENTRY_RING(name, fam, T, sel, R, rsel)                                                              \
     {name, fam, false, T::BM, T::BN, T::BK, T::WM, T::WN, T::EB, T::LDS_BYTES, T::THREADS, T::CPR, sel, rsel, \
-     R::BK, R::S, R::K_MULT, R::LDS_BYTES}
+     R::B_BK, R::B_STAGES, R::K_MULT, R::LDS_BYTES, R::LOOKAHEAD, R::A_BK, R::A_STAGES}
 // direct kernel: 32 x 32 per workgroup of 2 x 2 waves, steps of 32 of K
-#define ENTRY_DIRECT(name, fam, eb) {name, fam, true, 32, 32, 32, 2, 2, eb, 0, 256, 1, nullptr, nullptr, 0, 0, 0, 0}
+#define ENTRY_DIRECT(name, fam, eb) \
+    {name, fam, true, 32, 32, 32, 2, 2, eb, 0, 256, 1, nullptr, nullptr, 0, 0, 0, 0, 0, 0, 0}
 
 const ConfigEntry kConfigs[] = {
     ENTRY_RING("h256x256_w2x2", TGEMM_F16, CfgBig, tiled_kernel_big, RingBig, ring_kernel_big),
@@ -169,7 +172,7 @@ int64_t operand_reach(bool kcontig, int64_t ext, int64_t ld, int64_t K, int64_t 
 // Whether a configuration with a ring kernel runs it.
 bool ring_applies(const ConfigEntry& c, const Problem& p) {
     if (c.ring == nullptr || !tuning().direct_lds) return false;
-    const int64_t extra = (int64_t)c.ring_stages * c.ring_bk;
+    const int64_t extra = (int64_t)c.ring_lookahead * c.ring_bk;
     return loads_aligned(c, p) && stores_aligned(p) && p.M % c.bm == 0 && p.N % c.bn == 0 &&
            p.K % c.ring_k_mult == 0 &&
            operand_reach(p.la == LAYOUT_ROW, c.bm, p.lda, p.K, extra, c.eb) < (1LL << 31) &&
@@ -391,10 +394,14 @@ int gemm_config_info(int id, tgemm_config_info* out) {
         out->mfma_n = 16;
         out->mfma_k = c.eb == 4 ? 4 : 32;
         out->lds_bytes = 0;
+        out->a_block_k = out->block_k;
+        out->a_stages = out->stages;
         return TGEMM_OK;
     }
     out->block_k = ring ? c.ring_bk : c.bk;
     out->stages = ring ? c.ring_stages : 2;
+    out->a_block_k = ring ? c.ring_a_bk : out->block_k;
+    out->a_stages = ring ? c.ring_a_stages : out->stages;
     out->mfma_m = ring ? 16 : 32;
     out->mfma_n = ring ? 16 : 32;
     out->mfma_k = ring ? 32 : (c.eb == 4 ? 2 : 16);
