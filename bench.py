@@ -117,6 +117,9 @@ def main():
     ap.add_argument("--mfma-ceiling", action="store_true",
                     help="only run the MFMA ceiling program (issue rate and clock of both fp16 MFMA shapes on "
                          "every SIMD, N(0,1) and all-ones operands) and print its JSON lines")
+    ap.add_argument("--lds-probes", action="store_true",
+                    help="only run the LDS probe program (read rate of each candidate LDS layout, direct-to-LDS "
+                         "load rate of each global footprint) and print its JSON lines")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one elementwise kernel that reads and writes 512 MiB "
                          "(scale reference for the HBM byte counters)")
@@ -127,13 +130,14 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    if args.mfma_ceiling:
+    if args.mfma_ceiling or args.lds_probes:
         # a child process of its own, started before this process touches the GPU
         from tiled_gemm_03_amd import build as B
-        if not os.path.exists(B.CEILING_BIN):
-            print("bench.py: the MFMA ceiling program is not built (run __graft_entry__.build())", file=sys.stderr)
+        prog = B.CEILING_BIN if args.mfma_ceiling else B.PROBES_BIN
+        if not os.path.exists(prog):
+            print(f"bench.py: {prog} is not built (run __graft_entry__.build())", file=sys.stderr)
             sys.exit(1)
-        sys.exit(subprocess.run([B.CEILING_BIN]).returncode)
+        sys.exit(subprocess.run([prog]).returncode)
 
     import numpy as np
     import torch
