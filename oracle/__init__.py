@@ -7,7 +7,9 @@ it never imports the GPU library.
 `gemm(a, b, dtype)` returns the binary64 product C[i, j] = sum_k a(i,k) b(k,j)
 of the exact stored values of a and b (see oracle_gemm.c for the definition,
 the decoders and the summation order).  `decode(bits, dtype)` exposes the
-decoders so that they can be pinned on their own.
+decoders so that they can be pinned on their own.  `epilogue(...)` and
+`gemm_fused(...)` add the fused epilogue act(alpha P + beta C_old + bias)
+(oracle_gemm.c, oracle_epilogue).
 """
 import ctypes
 import os
@@ -17,6 +19,8 @@ import numpy as np
 from . import build as _build
 
 BINARY32, BINARY16, BFLOAT16 = 0, 1, 2
+ACT_NONE, ACT_RELU, ACT_GELU, ACT_GELU_TANH, ACT_SILU = 0, 1, 2, 3, 4
+BIAS_NONE, BIAS_ROW, BIAS_COL = 0, 1, 2
 _NAMES = {"f32": BINARY32, "f16": BINARY16, "bf16": BFLOAT16}
 
 _lib = None
@@ -38,6 +42,11 @@ def _load(path=None):
                                 p, i64, p, i64, p, i64, ctypes.c_int]
     lib.oracle_decode_array.restype = ctypes.c_int
     lib.oracle_decode_array.argtypes = [p, ctypes.c_int, i64, p]
+    d = ctypes.c_double
+    lib.oracle_activation.restype = d
+    lib.oracle_activation.argtypes = [d, ctypes.c_int]
+    lib.oracle_epilogue.restype = ctypes.c_int
+    lib.oracle_epilogue.argtypes = [i64, i64, p, i64, d, d, p, i64, p, p, ctypes.c_int, p, i64]
     if path is None:
         _lib = lib
     return lib
@@ -104,3 +113,58 @@ def decode(bits: np.ndarray, dtype, lib_path=None) -> np.ndarray:
     if lib.oracle_decode_array(x.ctypes.data, code, x.size, out.ctypes.data) != 0:
         raise ValueError("bad dtype")
     return out.reshape(x.shape)
+
+
+def activation(x, act: int, lib_path=None) -> np.ndarray:
+    """act(x) in binary64 for an array of values (oracle_activation)."""
+    lib = _load(lib_path)
+    x = np.asarray(x, dtype=np.float64)
+    out = np.array([lib.oracle_activation(float(v), int(act)) for v in x.ravel()], dtype=np.float64)
+    return out.reshape(x.shape)
+
+
+def epilogue(s: np.ndarray, alpha=1.0, beta=0.0, c_old=None, bias=None, bias_kind=BIAS_NONE, act=ACT_NONE,
+             lib_path=None) -> np.ndarray:
+    """act(alpha * s + beta * c_old + bias) in binary64 (oracle_epilogue).
+
+    s: binary64 product values (nr x nc); c_old: binary64 values of the same
+    entries of C (read only when beta != 0); bias: binary64 vector, one value
+    per row of s (bias_kind BIAS_ROW) or per column (BIAS_COL)."""
+    lib = _load(lib_path)
+    s = np.ascontiguousarray(s, dtype=np.float64)
+    nr, nc = s.shape
+    out = np.empty((nr, nc), dtype=np.float64)
+    co = None if c_old is None else np.ascontiguousarray(c_old, dtype=np.float64)
+    if co is not None and co.shape != s.shape:
+        raise ValueError("c_old must have the shape of s")
+    bv = None if bias is None or bias_kind == BIAS_NONE else np.ascontiguousarray(bias, dtype=np.float64)
+    if bv is not None and bv.size != (nr if bias_kind == BIAS_ROW else nc):
+        raise ValueError("bias length does not match its kind")
+    brow = bv.ctypes.data if bv is not None and bias_kind == BIAS_ROW else None
+    bcol = bv.ctypes.data if bv is not None and bias_kind == BIAS_COL else None
+    rc = lib.oracle_epilogue(nr, nc, s.ctypes.data, max(nc, 1), float(alpha), float(beta),
+                             None if co is None else co.ctypes.data, max(nc, 1), brow, bcol, int(act),
+                             out.ctypes.data, max(nc, 1))
+    if rc != 0:
+        raise ValueError(f"oracle_epilogue rejected its arguments (code {rc})")
+    return out
+
+
+def gemm_fused(a, b, dtype, alpha=1.0, beta=0.0, c_old=None, out_dtype=None, bias=None, bias_dtype=None,
+               bias_kind=BIAS_NONE, act=ACT_NONE, rows=None, cols=None, nthreads: int = 1, lib_path=None):
+    """act(alpha * (a x b) + beta * c_old + bias) in binary64 on the requested
+    entries.  c_old: the STORED bits of the whole M x N output (of out_dtype),
+    read only when beta != 0; bias: stored bits of a vector of bias_dtype, M
+    values (BIAS_ROW) or N values (BIAS_COL)."""
+    s = gemm(a, b, dtype, rows=rows, cols=cols, nthreads=nthreads, lib_path=lib_path)
+    M, N = a.shape[0], b.shape[1]
+    ri = np.arange(M) if rows is None else np.asarray(rows)
+    ci = np.arange(N) if cols is None else np.asarray(cols)
+    co = None
+    if beta != 0.0:
+        co = decode(np.ascontiguousarray(c_old), out_dtype, lib_path=lib_path)[np.ix_(ri, ci)]
+    bv = None
+    if bias_kind != BIAS_NONE:
+        full = decode(np.ascontiguousarray(bias).ravel(), bias_dtype, lib_path=lib_path)
+        bv = full[ri] if bias_kind == BIAS_ROW else full[ci]
+    return epilogue(s, alpha, beta, co, bv, bias_kind, act, lib_path=lib_path)

@@ -233,3 +233,76 @@ int oracle_gemm(int64_t M, int64_t N, int64_t K,
     free(Bd);
     return rc;
 }
+
+/*
+ * The fused epilogue (the operator fusion of page "企业官网建设流程全解析",
+ * §6.2: further operators merged into the product's kernel so that the
+ * product never makes a round trip through memory).  The pages name no
+ * operator; the ones computed here are the usual ones after a matrix
+ * product, applied in this order:
+ *
+ *   D[i][j] = act( alpha * P[i][j] + beta * C_old[i][j] + bias )
+ *
+ * where P = A x B (oracle_gemm), C_old is the previous content of C (not
+ * read at all when beta == 0, so that whatever C holds, NaN included, has no
+ * effect), and bias is bias_col[j] (one value per output column, the bias of
+ * a linear layer) or bias_row[i] (one per output row), or absent.
+ *
+ * Activations, in binary64 with the C library's erf, tanh and exp:
+ *   0 none       act(x) = x
+ *   1 relu       act(x) = x if x > 0, else 0
+ *   2 gelu       act(x) = x * Phi(x) = x / 2 * (1 + erf(x / sqrt(2)))
+ *                (Gaussian error linear unit, Phi the standard normal CDF)
+ *   3 gelu_tanh  act(x) = x / 2 * (1 + tanh(sqrt(2 / pi) * (x + 0.044715 x^3)))
+ *                (the tanh approximation of the same function)
+ *   4 silu       act(x) = x / (1 + exp(-x))  (x times the logistic function)
+ */
+#define ORACLE_ACT_NONE 0
+#define ORACLE_ACT_RELU 1
+#define ORACLE_ACT_GELU 2
+#define ORACLE_ACT_GELU_TANH 3
+#define ORACLE_ACT_SILU 4
+
+double oracle_activation(double x, int act) {
+    switch (act) {
+        case ORACLE_ACT_RELU: return x > 0.0 ? x : 0.0;
+        case ORACLE_ACT_GELU: return 0.5 * x * (1.0 + erf(x / sqrt(2.0)));
+        case ORACLE_ACT_GELU_TANH: {
+            const double c = sqrt(2.0 / M_PI);
+            return 0.5 * x * (1.0 + tanh(c * (x + 0.044715 * x * x * x)));
+        }
+        case ORACLE_ACT_SILU: return x / (1.0 + exp(-x));
+        default: return x;
+    }
+}
+
+/*
+ * oracle_epilogue: out[r][c] = act(alpha * s[r][c] + beta * c_old[r][c] + bias)
+ * for r < nr, c < nc, all binary64.
+ *
+ *   s, lds            product values (from oracle_gemm), leading dimension lds
+ *   alpha, beta       scalars; beta == 0 means c_old is not read (may be NULL)
+ *   c_old, ldco       previous values of the same entries of C
+ *   bias_row, bias_col  bias per output row (nr values) or per output column
+ *                     (nc values); at most one of them non-NULL
+ *   act               activation code (0 .. 4 above)
+ *   out, ldo          result
+ * Returns 0, or -1 for invalid arguments (nothing written).
+ */
+int oracle_epilogue(int64_t nr, int64_t nc, const double* s, int64_t lds, double alpha, double beta,
+                    const double* c_old, int64_t ldco, const double* bias_row, const double* bias_col, int act,
+                    double* out, int64_t ldo) {
+    if (nr < 0 || nc < 0 || lds < nc || ldo < nc) return -1;
+    if (act < ORACLE_ACT_NONE || act > ORACLE_ACT_SILU) return -1;
+    if (beta != 0.0 && (c_old == NULL || ldco < nc)) return -1;
+    if (bias_row != NULL && bias_col != NULL) return -1;
+    for (int64_t r = 0; r < nr; ++r)
+        for (int64_t c = 0; c < nc; ++c) {
+            double t = alpha * s[r * lds + c];
+            if (beta != 0.0) t += beta * c_old[r * ldco + c];
+            if (bias_row) t += bias_row[r];
+            if (bias_col) t += bias_col[c];
+            out[r * ldo + c] = oracle_activation(t, act);
+        }
+    return 0;
+}

@@ -243,6 +243,97 @@ def pin_rejects_bad_arguments(lib_path=None):
     assert rc == -1
 
 
+# ------------------------------------------------------------ epilogue pins
+def pin_activations_vs_torch(lib_path=None):
+    """Each activation on a grid of points against torch.nn.functional in
+    float64 on the CPU (an independent library implementation)."""
+    import torch
+    import torch.nn.functional as F
+    x = np.concatenate([np.linspace(-8.0, 8.0, 161), [0.0, -0.0, 1e-8, -1e-8, 30.0, -30.0, 3.5, -0.7]])
+    t = torch.from_numpy(x)
+    refs = {oracle.ACT_NONE: t, oracle.ACT_RELU: F.relu(t), oracle.ACT_GELU: F.gelu(t, approximate="none"),
+            oracle.ACT_GELU_TANH: F.gelu(t, approximate="tanh"), oracle.ACT_SILU: F.silu(t)}
+    for act, ref in refs.items():
+        got = oracle.activation(x, act, lib_path=lib_path)
+        want = ref.numpy()
+        # the two libraries round their constants and intermediate steps differently
+        assert np.allclose(got, want, rtol=1e-13, atol=1e-14), (act, np.max(np.abs(got - want)))
+
+
+def pin_activation_constants(lib_path=None):
+    """Published values: Phi(1) = 0.8413447460685429 (standard normal table),
+    so gelu(1) = Phi(1) and gelu(-1) = -(1 - Phi(1)); the logistic function
+    at 1 is 1 / (1 + 1/e) = 0.7310585786300049; the tanh form of gelu differs
+    from gelu by less than 1e-3 everywhere."""
+    act = lambda v, a: float(oracle.activation(np.array([v]), a, lib_path=lib_path)[0])
+    assert abs(act(1.0, oracle.ACT_GELU) - 0.8413447460685429) < 1e-15
+    assert abs(act(-1.0, oracle.ACT_GELU) + 0.15865525393145707) < 1e-15
+    assert abs(act(1.0, oracle.ACT_SILU) - 0.7310585786300049) < 1e-15
+    assert abs(act(-1.0, oracle.ACT_SILU) + 0.2689414213699951) < 1e-15
+    assert act(-3.0, oracle.ACT_RELU) == 0.0 and act(3.0, oracle.ACT_RELU) == 3.0 and act(-3.0, oracle.ACT_NONE) == -3.0
+    xs = np.linspace(-6, 6, 241)
+    d = oracle.activation(xs, oracle.ACT_GELU_TANH, lib_path=lib_path) - oracle.activation(xs, oracle.ACT_GELU,
+                                                                                        lib_path=lib_path)
+    assert np.max(np.abs(d)) < 1e-3 and np.max(np.abs(d)) > 1e-5
+
+
+def pin_epilogue_worked_example(lib_path=None):
+    """A 2 x 2 x 4 all-ones product (every entry 4) through the epilogue,
+    with values worked out by hand: alpha = 0.5 -> 2; beta = 3 times
+    C_old = [[1, 2], [3, 4]]; a column bias [10, -20] or a row bias
+    [10, -20]; relu."""
+    ones = np.ones((2, 4), np.float16)
+    onesb = np.ones((4, 2), np.float16)
+    c_old = np.array([[1, 2], [3, 4]], np.float16)
+    bias = np.array([10, -20], np.float16)
+    got = oracle.gemm_fused(ones, onesb, W.F16, alpha=0.5, beta=3.0, c_old=c_old, out_dtype=W.F16, bias=bias,
+                            bias_dtype=W.F16, bias_kind=oracle.BIAS_COL, act=oracle.ACT_RELU, lib_path=lib_path)
+    assert np.array_equal(got, [[15.0, 0.0], [21.0, 0.0]]), got
+    got = oracle.gemm_fused(ones, onesb, W.F16, alpha=0.5, beta=3.0, c_old=c_old, out_dtype=W.F16, bias=bias,
+                            bias_dtype=W.F16, bias_kind=oracle.BIAS_ROW, act=oracle.ACT_NONE, lib_path=lib_path)
+    assert np.array_equal(got, [[15.0, 18.0], [-9.0, -6.0]]), got
+    # the activation comes last: relu(2 - 3) = 0, not relu(2) - 3
+    got = oracle.gemm_fused(ones, onesb, W.F16, alpha=0.5, bias=np.array([-3, 1], np.float16), bias_dtype=W.F16,
+                            bias_kind=oracle.BIAS_COL, act=oracle.ACT_RELU, lib_path=lib_path)
+    assert np.array_equal(got, [[0.0, 3.0], [0.0, 3.0]]), got
+
+
+def pin_epilogue_beta_zero_ignores_c(lib_path=None):
+    """beta = 0: C is not read, so NaN or Inf stored there has no effect;
+    with alpha = 1, no bias and no activation the epilogue is the product."""
+    a, b = W.random_inputs(5, 7, 9, W.F16, seed=11)
+    c_old = np.full((5, 7), np.nan, np.float16)
+    c_old[0, 0] = np.inf
+    p = oracle.gemm(a, b, W.F16, lib_path=lib_path)
+    got = oracle.gemm_fused(a, b, W.F16, alpha=1.0, beta=0.0, c_old=c_old, out_dtype=W.F16, lib_path=lib_path)
+    assert np.array_equal(got, p)
+    got = oracle.gemm_fused(a, b, W.F16, alpha=-2.0, beta=0.0, c_old=c_old, out_dtype=W.F16, lib_path=lib_path)
+    assert np.array_equal(got, -2.0 * p)
+
+
+def pin_epilogue_sampled_equals_full(lib_path=None):
+    a, b = W.random_inputs(20, 30, 40, W.BF16, seed=12)
+    c_old = W.random_inputs(20, 30, 1, W.F32, seed=13)[0][:, :1].repeat(30, axis=1).astype(np.float32)
+    bias = W.random_inputs(1, 30, 1, W.BF16, seed=14)[1].ravel()
+    kw = dict(alpha=1.5, beta=-0.25, c_old=c_old, out_dtype=W.F32, bias=bias, bias_dtype=W.BF16,
+              bias_kind=oracle.BIAS_COL, act=oracle.ACT_GELU_TANH, lib_path=lib_path)
+    full = oracle.gemm_fused(a, b, W.BF16, **kw)
+    rows, cols = np.array([0, 7, 19]), np.array([29, 3, 0, 11])
+    part = oracle.gemm_fused(a, b, W.BF16, rows=rows, cols=cols, **kw)
+    assert np.array_equal(part, full[np.ix_(rows, cols)])
+
+
+def pin_epilogue_rejects_bad_arguments(lib_path=None):
+    lib = oracle._load(lib_path)
+    s = np.zeros(4)
+    out = np.zeros(4)
+    assert lib.oracle_epilogue(2, 2, s.ctypes.data, 2, 1.0, 0.0, None, 2, None, None, 9, out.ctypes.data, 2) == -1
+    assert lib.oracle_epilogue(2, 2, s.ctypes.data, 2, 1.0, 1.0, None, 2, None, None, 0, out.ctypes.data, 2) == -1
+    assert lib.oracle_epilogue(2, 2, s.ctypes.data, 2, 1.0, 0.0, None, 2, s.ctypes.data, s.ctypes.data, 0,
+                               out.ctypes.data, 2) == -1
+    assert lib.oracle_epilogue(2, 2, s.ctypes.data, 1, 1.0, 0.0, None, 2, None, None, 0, out.ctypes.data, 2) == -1
+
+
 # Pins cheap enough to run against every planted mistake.
 FAST_PINS = [
     pin_decode_binary16_exhaustive,
@@ -258,5 +349,11 @@ FAST_PINS = [
     pin_threads_invariant,
     pin_output_overwritten,
     pin_rejects_bad_arguments,
+    pin_activations_vs_torch,
+    pin_activation_constants,
+    pin_epilogue_worked_example,
+    pin_epilogue_beta_zero_ignores_c,
+    pin_epilogue_sampled_equals_full,
+    pin_epilogue_rejects_bad_arguments,
 ]
 ALL_PINS = FAST_PINS + [pin_vs_numpy_workloads, pin_large_sampled]

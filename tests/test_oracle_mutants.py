@@ -33,6 +33,17 @@ MUTANTS = [
     ("a_times_a", "s[c] += a * brow[c];", "s[c] += a * a;"),
     ("skips_last_row", "for (int64_t r = jb->tid; r < jb->nrows; r += jb->nthreads) {",
      "for (int64_t r = jb->tid; r + 1 < jb->nrows; r += jb->nthreads) {"),
+    # the fused epilogue
+    ("alpha_ignored", "double t = alpha * s[r * lds + c];", "double t = s[r * lds + c];"),
+    ("beta_sign", "t += beta * c_old[r * ldco + c];", "t -= beta * c_old[r * ldco + c];"),
+    ("c_read_when_beta_zero", "if (beta != 0.0) t += beta", "t += beta"),
+    ("bias_row_indexed_by_column", "if (bias_row) t += bias_row[r];", "if (bias_row) t += bias_row[c];"),
+    ("activation_before_bias", "out[r * ldo + c] = oracle_activation(t, act);",
+     "out[r * ldo + c] = oracle_activation(t - (bias_row ? bias_row[r] : bias_col ? bias_col[c] : 0.0), act) + (bias_row ? bias_row[r] : bias_col ? bias_col[c] : 0.0);"),
+    ("gelu_wrong_scale", "erf(x / sqrt(2.0))", "erf(x * sqrt(2.0))"),
+    ("gelu_tanh_cubic_term", "0.044715 * x * x * x", "0.044715 * x * x"),
+    ("silu_sign", "return x / (1.0 + exp(-x));", "return x / (1.0 + exp(x));"),
+    ("relu_inverted", "return x > 0.0 ? x : 0.0;", "return x < 0.0 ? x : 0.0;"),
 ]
 
 RUNNER = r"""
