@@ -239,6 +239,18 @@ def main():
                             "tflops": flops / (med * 1e-3) / 1e12})
         del a_col, b_col, c_col
 
+    # the same product with the fused epilogue (gemm_fused)
+    fused = []
+    if not args.no_per_config:
+        bias = torch.randn(w.N, device=dev).half()
+        for name, kw in (("column bias + gelu (tanh form)", dict(bias=bias, activation=T.ACT_GELU_TANH)),
+                         ("alpha 0.5, beta 1 (C read) + relu", dict(alpha=0.5, beta=1.0, activation=T.ACT_RELU))):
+            call = lambda: T.gemm_tensors(a, b, c, stream=stream.cuda_stream, **kw)
+            _, fev = time_calls(call, 20, 3, stream)
+            med = float(np.median(fev))
+            fused.append({"epilogue": name, "us_median": med * 1e3, "tflops": flops / (med * 1e-3) / 1e12})
+        del bias
+
     if args.calibrate_copy:
         src = torch.ones(128 << 20, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -272,6 +284,7 @@ def main():
         "cpu_baseline": cpu,
         "per_config": per_config,
         "layouts_8192": layouts,
+        "fused_8192": fused,
         "sclk": sclk_mhz(),
         "kernel_source_hash": kernel_source_hash(),
     }

@@ -57,11 +57,13 @@ extern "C" {
 #define TGEMM_ERR_NULL (-2)        /* NULL pointer for a non-empty operand       */
 #define TGEMM_ERR_LD (-3)          /* lda < K, ldb < N or ldc < N                */
 #define TGEMM_ERR_DTYPE (-4)       /* unsupported (in_dtype, out_dtype) pair     */
-#define TGEMM_ERR_ALIAS (-5)       /* C overlaps A or B                          */
+#define TGEMM_ERR_ALIAS (-5)       /* C overlaps A, B or the epilogue's bias     */
 #define TGEMM_ERR_CONFIG (-6)      /* gemm_ex / gemm_t: unknown config, wrong
                                       dtype, or a config without a kernel for
                                       column-major operands                  */
 #define TGEMM_ERR_LAYOUT (-7)      /* gemm_t: layout not ROW_MAJOR / COL_MAJOR  */
+#define TGEMM_ERR_EPILOGUE (-8)    /* gemm_fused: bad activation, bias kind or
+                                      bias type, or a bias kind without bias  */
 
 /* Operand layouts (gemm_t): the row-major default and the column-major option
  * of page "TileLang实战：用Python DSL自动生成高性能GPU计算内核", §5.1. */
@@ -121,8 +123,59 @@ int gemm_t(int64_t M, int64_t N, int64_t K,
            void* C, int64_t ldc, int layout_c,
            int in_dtype, int out_dtype, void* stream, int config_id);
 
-/* Human-readable text for a return code of gemm / gemm_ex / gemm_t (never
- * NULL; the string is static). */
+/*
+ * The fused epilogue (gemm_fused): further operators merged into the
+ * product's kernel, so that the product makes no round trip through memory
+ * (the operator fusion of page "企业官网建设流程全解析", §6.2).  The page names
+ * no operator; these are the usual ones after a matrix product:
+ *
+ *   C := act(alpha * (A x B) + beta * C + bias)
+ *
+ * evaluated in fp32 on the fp32 accumulator, then rounded to the output type
+ * (nearest even).  beta == 0: C is not read (it may hold anything, NaN
+ * included).  bias: one value per row of C (bias_kind TGEMM_BIAS_ROW, M
+ * values) or per column (TGEMM_BIAS_COL, N values, the bias of a linear
+ * layer), contiguous, of type bias_dtype (TGEMM_F32 / F16 / BF16), device
+ * memory owned by the caller, not overlapping C.  Activations:
+ *   TGEMM_ACT_RELU       max(x, 0)
+ *   TGEMM_ACT_GELU       x * Phi(x) = x/2 (1 + erf(x / sqrt 2))
+ *   TGEMM_ACT_GELU_TANH  x/2 (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3)))
+ *   TGEMM_ACT_SILU       x / (1 + exp(-x))
+ */
+#define TGEMM_ACT_NONE 0
+#define TGEMM_ACT_RELU 1
+#define TGEMM_ACT_GELU 2
+#define TGEMM_ACT_GELU_TANH 3
+#define TGEMM_ACT_SILU 4
+#define TGEMM_BIAS_NONE 0
+#define TGEMM_BIAS_ROW 1
+#define TGEMM_BIAS_COL 2
+
+typedef struct tgemm_epilogue {
+    float alpha;       /* scales A x B (1 for the plain product)        */
+    float beta;        /* scales the previous C (0: C not read)         */
+    const void* bias;  /* device vector, or NULL with TGEMM_BIAS_NONE   */
+    int bias_kind;     /* TGEMM_BIAS_NONE / ROW / COL                   */
+    int bias_dtype;    /* TGEMM_F32 / F16 / BF16                        */
+    int activation;    /* TGEMM_ACT_*                                   */
+} tgemm_epilogue;
+
+/*
+ * gemm_fused: gemm_t with the fused epilogue *epilogue (NULL: exactly
+ * gemm_t).  The same kernels, tile table and layouts as gemm_t; with a
+ * column-major C the bias kinds keep their meaning for C.  Errors as gemm_t,
+ * plus TGEMM_ERR_EPILOGUE for bad epilogue arguments and TGEMM_ERR_ALIAS if
+ * the bias overlaps C.  M == 0 or N == 0: nothing is read or written;
+ * K == 0: C := act(beta * C + bias).
+ */
+int gemm_fused(int64_t M, int64_t N, int64_t K,
+               const void* A, int64_t lda, int layout_a,
+               const void* B, int64_t ldb, int layout_b,
+               void* C, int64_t ldc, int layout_c,
+               int in_dtype, int out_dtype, const tgemm_epilogue* epilogue, void* stream, int config_id);
+
+/* Human-readable text for a return code of gemm / gemm_ex / gemm_t /
+ * gemm_fused (never NULL; the string is static). */
 const char* gemm_strerror(int code);
 
 /* Number of tile configurations in the table. */

@@ -268,3 +268,32 @@ def test_kernel_choice_for_layouts():
     # a column-major C swaps the roles of A and B: its 128 rows become the
     # N of the row-major product (128 x 128 tiles)
     assert _kernel_t(128, 8192, 8192, R_, R_, C_)[0] == RING
+
+
+def test_fused_epilogue_arguments_are_checked():
+    """gemm_fused rejects bad epilogue arguments before touching the GPU."""
+    FAKE = 1 << 40
+    def call(ep, M=64, N=64, K=64, C=None):
+        C = FAKE + (2 << 36) if C is None else C
+        return T.gemm_fused(M, N, K, FAKE, K, T.ROW_MAJOR, FAKE + (1 << 36), N, T.ROW_MAJOR, C, N, T.ROW_MAJOR,
+                            T.F16, T.F16, ep, None, -1)
+    assert call(T.Epilogue(1.0, 0.0, None, T.BIAS_NONE, T.F32, 9)) == T.ERR_EPILOGUE
+    assert call(T.Epilogue(1.0, 0.0, None, T.BIAS_NONE, T.F32, -1)) == T.ERR_EPILOGUE
+    assert call(T.Epilogue(1.0, 0.0, FAKE + (3 << 36), 3, T.F32, T.ACT_NONE)) == T.ERR_EPILOGUE
+    assert call(T.Epilogue(1.0, 0.0, None, T.BIAS_COL, T.F32, T.ACT_NONE)) == T.ERR_EPILOGUE
+    assert call(T.Epilogue(1.0, 0.0, FAKE + (3 << 36), T.BIAS_COL, 7, T.ACT_NONE)) == T.ERR_EPILOGUE
+    # checked before the sizes: wrong whatever the sizes
+    assert call(T.Epilogue(1.0, 0.0, None, T.BIAS_NONE, T.F32, 9), M=0) == T.ERR_EPILOGUE
+    # a bias overlapping C
+    C = FAKE + (2 << 36)
+    assert call(T.Epilogue(1.0, 0.0, C + 16, T.BIAS_COL, T.F16, T.ACT_NONE), C=C) == T.ERR_ALIAS
+    assert call(T.Epilogue(1.0, 0.0, C - 64, T.BIAS_ROW, T.F32, T.ACT_NONE), C=C) == T.ERR_ALIAS
+    # the usual checks still apply
+    assert call(T.Epilogue(1.0, 0.0, None, T.BIAS_NONE, T.F32, T.ACT_RELU), M=-1) == T.ERR_DIM
+    assert T.gemm_strerror(T.ERR_EPILOGUE).startswith("epilogue")
+
+
+def test_fused_epilogue_struct_layout():
+    """The ctypes mirror of tgemm_epilogue: two floats, a pointer, three ints."""
+    assert ctypes.sizeof(T.Epilogue) == 32
+    assert T.Epilogue.bias.offset == 8 and T.Epilogue.activation.offset == 24

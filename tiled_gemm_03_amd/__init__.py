@@ -22,13 +22,17 @@ LIB_PATH = os.path.join(HERE, "libtgemm.so")
 
 F32, F16, BF16 = 0, 1, 2
 OK = 0
-ERR_DIM, ERR_NULL, ERR_LD, ERR_DTYPE, ERR_ALIAS, ERR_CONFIG, ERR_LAYOUT = -1, -2, -3, -4, -5, -6, -7
+ERR_DIM, ERR_NULL, ERR_LD, ERR_DTYPE, ERR_ALIAS, ERR_CONFIG, ERR_LAYOUT, ERR_EPILOGUE = -1, -2, -3, -4, -5, -6, -7, -8
 
-EXPORTED = ["gemm", "gemm_ex", "gemm_t", "gemm_strerror", "gemm_num_configs", "gemm_config_info",
+EXPORTED = ["gemm", "gemm_ex", "gemm_t", "gemm_fused", "gemm_strerror", "gemm_num_configs", "gemm_config_info",
             "gemm_select_config", "gemm_select_kernel", "gemm_select_kernel_t", "gemm_tile_map", "gemm_version"]
 
 # operand layouts (gemm_t)
 ROW_MAJOR, COL_MAJOR = 0, 1
+
+# fused epilogue (gemm_fused): activations and bias kinds
+ACT_NONE, ACT_RELU, ACT_GELU, ACT_GELU_TANH, ACT_SILU = 0, 1, 2, 3, 4
+BIAS_NONE, BIAS_ROW, BIAS_COL = 0, 1, 2
 
 # gemm_select_kernel results
 KERNEL_GENERAL, KERNEL_TILED, KERNEL_RING, KERNEL_DIRECT = 0, 1, 2, 3
@@ -47,6 +51,12 @@ class ConfigInfo(ctypes.Structure):
         d = {f: getattr(self, f) for f, _ in self._fields_}
         d["name"] = d["name"].decode()
         return d
+
+
+class Epilogue(ctypes.Structure):
+    """tgemm_epilogue: C := act(alpha * AB + beta * C + bias)."""
+    _fields_ = [("alpha", ctypes.c_float), ("beta", ctypes.c_float), ("bias", ctypes.c_void_p),
+                ("bias_kind", ctypes.c_int), ("bias_dtype", ctypes.c_int), ("activation", ctypes.c_int)]
 
 
 class TgemmError(RuntimeError):
@@ -82,6 +92,8 @@ def lib():
     L.gemm_select_config.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, i, i]
     L.gemm_t.restype = i
     L.gemm_t.argtypes = [i64, i64, i64, p, i64, i, p, i64, i, p, i64, i, i, i, p, i]
+    L.gemm_fused.restype = i
+    L.gemm_fused.argtypes = [i64, i64, i64, p, i64, i, p, i64, i, p, i64, i, i, i, ctypes.POINTER(Epilogue), p, i]
     L.gemm_select_kernel_t.restype = i
     L.gemm_select_kernel_t.argtypes = [i64, i64, i64, p, i64, i, p, i64, i, p, i64, i, i, i, i, ctypes.POINTER(i)]
     L.gemm_select_kernel.restype = i
@@ -126,6 +138,14 @@ def gemm_t(M, N, K, A, lda, layout_a, B, ldb, layout_b, C, ldc, layout_c, in_dty
            config_id=-1):
     return lib().gemm_t(M, N, K, A, lda, layout_a, B, ldb, layout_b, C, ldc, layout_c, in_dtype, out_dtype, stream,
                         config_id)
+
+
+def gemm_fused(M, N, K, A, lda, layout_a, B, ldb, layout_b, C, ldc, layout_c, in_dtype, out_dtype, epilogue=None,
+               stream=None, config_id=-1):
+    """gemm_t with the fused epilogue (an Epilogue, or None for none)."""
+    ep = ctypes.byref(epilogue) if epilogue is not None else None
+    return lib().gemm_fused(M, N, K, A, lda, layout_a, B, ldb, layout_b, C, ldc, layout_c, in_dtype, out_dtype, ep,
+                            stream, config_id)
 
 
 def gemm_select_kernel_t(M, N, K, A, lda, layout_a, B, ldb, layout_b, C, ldc, layout_c, in_dtype, out_dtype,
@@ -183,12 +203,17 @@ def _layout(t):
     raise ValueError("tensor needs contiguous rows or contiguous columns")
 
 
-def gemm_tensors(a, b, c, config_id=-1, stream=None, check=True):
+def gemm_tensors(a, b, c, config_id=-1, stream=None, check=True, alpha=None, beta=None, bias=None,
+                 bias_kind=None, activation=ACT_NONE):
     """c := a @ b on the device, through the C ABI.  a: M x K, b: K x N,
     c: M x N torch tensors on the GPU, each with contiguous rows (row-major,
     rows may be padded) or contiguous columns (column-major, e.g. a
-    transposed view).  Returns the library's return code (raises TgemmError
-    on failure if check)."""
+    transposed view).  With any of alpha, beta, bias or activation given, the
+    fused epilogue c := act(alpha * a @ b + beta * c + bias) runs
+    (gemm_fused); bias is a contiguous 1-D tensor of M values (one per row of
+    c, bias_kind BIAS_ROW) or N values (per column, BIAS_COL, the default for
+    a bias of N values).  Returns the library's return code (raises
+    TgemmError on failure if check)."""
     import torch
     M, K = a.shape
     K2, N = b.shape
@@ -201,8 +226,22 @@ def gemm_tensors(a, b, c, config_id=-1, stream=None, check=True):
     la, lda = _layout(a)
     lb, ldb = _layout(b)
     lc, ldc = _layout(c)
-    rc = gemm_t(M, N, K, a.data_ptr(), lda, la, b.data_ptr(), ldb, lb, c.data_ptr(), ldc, lc,
-                dtype_code(a), dtype_code(c), stream, config_id)
+    fused = alpha is not None or beta is not None or bias is not None or activation != ACT_NONE
+    if not fused:
+        rc = gemm_t(M, N, K, a.data_ptr(), lda, la, b.data_ptr(), ldb, lb, c.data_ptr(), ldc, lc,
+                    dtype_code(a), dtype_code(c), stream, config_id)
+    else:
+        ep = Epilogue(1.0 if alpha is None else float(alpha), 0.0 if beta is None else float(beta), None,
+                      BIAS_NONE, F32, int(activation))
+        if bias is not None:
+            if bias.dim() != 1 or not bias.is_contiguous():
+                raise ValueError("bias must be a contiguous 1-D tensor")
+            kind = bias_kind if bias_kind is not None else (BIAS_COL if bias.numel() == N else BIAS_ROW)
+            if bias.numel() != (M if kind == BIAS_ROW else N):
+                raise ValueError("bias length does not match its kind")
+            ep.bias, ep.bias_kind, ep.bias_dtype = bias.data_ptr(), kind, dtype_code(bias)
+        rc = gemm_fused(M, N, K, a.data_ptr(), lda, la, b.data_ptr(), ldb, lb, c.data_ptr(), ldc, lc,
+                        dtype_code(a), dtype_code(c), ep, stream, config_id)
     if check and rc != OK:
         raise TgemmError(rc)
     return rc

@@ -61,7 +61,15 @@ struct GemmArgs {
     int swz_mask;           // CPR-1: XOR-swizzled LDS; 0: plain row-major LDS
     int vec_ab;             // GENERAL kernels: A, B 16-byte aligned, lda, ldb whole chunks
     int vec_c;              // GENERAL kernels: C rows allow 4-element vector stores
+    // fused epilogue (epi != 0): C := act(alpha * AB + beta * C + bias)
+    int epi;
+    float alpha, beta;      // beta == 0: C is not read
+    const char* bias;       // bias_kind BIAS_ROW: M values, BIAS_COL: N values, of type bias_dt
+    int bias_kind, bias_dt, act;
 };
+
+enum { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU = 2, ACT_GELU_TANH = 3, ACT_SILU = 4 };
+enum { BIAS_NONE = 0, BIAS_ROW = 1, BIAS_COL = 2 };
 
 // Compile-time tile configuration.
 //   BM x BN   output tile of one workgroup
@@ -234,6 +242,94 @@ __device__ __forceinline__ void store_elem(char* p, float v) {
     else *(__bf16*)p = (__bf16)v;
 }
 
+// ------------------------------------------------------- fused epilogue
+// The operator fusion of page "企业官网建设流程全解析" §6.2 (further
+// operators merged into the product's kernel, so that the product makes no
+// round trip through memory), with the usual operators after a matrix
+// product: C := act(alpha * AB + beta * C + bias), bias one value per row or
+// per column of C, in fp32 before the output rounding.
+
+__device__ __forceinline__ float load_value(const char* p, int64_t i, int dt) {
+    if (dt == DT_F32) return ((const float*)p)[i];
+    if (dt == DT_F16) return (float)((const _Float16*)p)[i];
+    return (float)((const __bf16*)p)[i];
+}
+
+// relu(x) = max(x, 0); gelu(x) = x Phi(x) = x/2 (1 + erf(x / sqrt 2));
+// gelu_tanh(x) = x/2 (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))) (the tanh
+// approximation of gelu); silu(x) = x / (1 + exp(-x)).
+__device__ __forceinline__ float activate(float x, int act) {
+    switch (act) {
+        case ACT_RELU: return x > 0.f ? x : 0.f;
+        case ACT_GELU: return 0.5f * x * (1.f + erff(x * 0.70710678118654752f));
+        case ACT_GELU_TANH: return 0.5f * x * (1.f + tanhf(0.79788456080286536f * (x + 0.044715f * x * x * x)));
+        case ACT_SILU: return x / (1.f + expf(-x));
+        default: return x;
+    }
+}
+
+// Four consecutive outputs C[row][col .. col + 3], of which the first n lie
+// inside C, through the epilogue and stored (vec: 4-element vector store).
+template <int OUT>
+__device__ __forceinline__ void store4_fused(const GemmArgs& p, int row, int col, int n, bool vec, f32x4 v) {
+    constexpr int OB = OUT == DT_F32 ? 4 : 2;
+    char* dst = p.C + ((int64_t)row * p.ldc + col) * OB;
+    float o[4] = {v[0], v[1], v[2], v[3]};
+    const float brow = p.bias_kind == BIAS_ROW ? load_value(p.bias, row, p.bias_dt) : 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        if (e >= n) break;
+        float t = p.alpha * o[e];
+        if (p.beta != 0.f) t += p.beta * load_value(dst, e, OUT);
+        if (p.bias_kind == BIAS_ROW) t += brow;
+        else if (p.bias_kind == BIAS_COL) t += load_value(p.bias, col + e, p.bias_dt);
+        o[e] = activate(t, p.act);
+    }
+    if (n == 4) {
+        store4<OUT>(dst, o[0], o[1], o[2], o[3], vec);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 3; ++e)
+            if (e < n) store_elem<OUT>(dst + e * OB, o[e]);
+    }
+}
+
+// The fused epilogue of a wave's NB accumulator blocks of VPL fp32 values
+// per lane (VPL / 4 groups of 4 consecutive columns), through this wave's
+// LDS region (PB blocks at a time): the blocks are written out with
+// compile-time register indices, then read back in a run-time loop that
+// holds one copy of the epilogue code.  get(IntTag<b>): block b's values;
+// where(b, g, row, col, n, vec): the output position of group g of block b
+// (n = 0: nothing to store).  The caller has made sure that no wave still
+// reads the LDS it reuses.
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+
+template <int OUT, int NB, int VPL, int PB, class Get, class Where>
+__device__ __forceinline__ void fused_epilogue(const GemmArgs& p, lds_f32x4* region, Get&& get, Where&& where) {
+    static_assert(NB % PB == 0 && VPL % 4 == 0, "");
+    const int lane = threadIdx.x & 63;
+    static_for<0, NB / PB>([&](auto pass_t) {
+        constexpr int b0 = decltype(pass_t)::value * PB;
+        static_for<0, PB>([&](auto t_t) {
+            constexpr int t = decltype(t_t)::value;
+            const auto blk = get(IntTag<b0 + t>{});
+            static_for<0, VPL / 4>([&](auto g_t) {
+                constexpr int g = decltype(g_t)::value;
+                region[(t * 64 + lane) * (VPL / 4) + g] =
+                    f32x4{blk[4 * g + 0], blk[4 * g + 1], blk[4 * g + 2], blk[4 * g + 3]};
+            });
+        });
+        for (int t = 0; t < PB; ++t)
+            for (int g = 0; g < VPL / 4; ++g) {
+                int row, col, n;
+                bool vec;
+                where(b0 + t, g, row, col, n, vec);
+                if (n > 0) store4_fused<OUT>(p, row, col, n, vec, region[(t * 64 + lane) * (VPL / 4) + g]);
+            }
+    });
+}
+
 // ---------------------------------------------------------------- kernel
 // IN: input type, OUT: output type.
 // FAST: every tile is whole (M % BM == 0, N % BN == 0) and A, B, C are
@@ -241,7 +337,7 @@ __device__ __forceinline__ void store_elem(char* p, float v) {
 // the main loop has no bounds checks (only a ragged last K step is masked).
 // Otherwise (GENERAL) every load and store is checked; 16-byte accesses are
 // still used where p.vec_ab / p.vec_c allow them.
-template <class T, int IN, int OUT, bool FAST>
+template <class T, int IN, int OUT, bool FAST, bool EPI = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(T::THREADS, T::THREADS),
                           amdgpu_waves_per_eu(T::OCC * T::WAVES / 4 > 0 ? T::OCC * T::WAVES / 4 : 1)))
 void gemm_kernel(GemmArgs p) {
@@ -502,10 +598,34 @@ void gemm_kernel(GemmArgs p) {
 
     // a7: epilogue.  acc[i][j][4q + e] = C[row][col + e] with
     // row = m0 + wm*WTM + 32 i + lane%32, col = n0 + wn*WTN + 32 j + 8 q + 4 (lane/32).
-    // One 32x32 block at a time (fenced), so that only one block's values are
-    // moved out of the accumulator registers at once.
     constexpr int OB = OUT == DT_F32 ? 4 : 2;
     const int64_t ldc = p.ldc;
+    if constexpr (EPI) {
+        // fused epilogue through LDS, once no wave reads it any more
+        __syncthreads();
+        constexpr int REGION = T::LDS_BYTES / T::WAVES;                   // bytes per wave
+        constexpr int PB0 = REGION / (64 * 64) < T::FM * T::FN ? REGION / (64 * 64) : T::FM * T::FN;
+        constexpr int PB = (T::FM * T::FN) % PB0 == 0 ? PB0 : 1;
+        static_assert(PB >= 1, "the LDS holds a block of accumulators per wave");
+        lds_f32x4* region = (lds_f32x4*)(lds_void*)smem + wave * (REGION / 16);
+        fused_epilogue<OUT, T::FM * T::FN, 16, PB>(
+            p, region, [&](auto b_t) { constexpr int b = decltype(b_t)::value; return acc[b / T::FN][b % T::FN]; },
+            [&](int b, int q, int& row, int& col, int& n, bool& vec) {
+                const int i = b / T::FN, j = b % T::FN;
+                row = m0 + a_frow0 + 32 * i;
+                col = n0 + wn * T::WTN + 32 * j + 8 * q + 4 * fhalf;
+                if constexpr (FAST) {
+                    n = 4;
+                    vec = true;
+                } else {
+                    n = row < M ? (N - col >= 4 ? 4 : N - col > 0 ? N - col : 0) : 0;
+                    vec = p.vec_c && n == 4;
+                }
+            });
+        return;
+    }
+    // One 32x32 block at a time (fenced), so that only one block's values are
+    // moved out of the accumulator registers at once.
     static_for<0, T::FM * T::FN>([&](auto bt) {
         constexpr int i = decltype(bt)::value / T::FN, j = decltype(bt)::value % T::FN;
         const int row = m0 + a_frow0 + 32 * i;

@@ -48,7 +48,7 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 // elements below 2^31 bytes (buffer offsets, including the loads of the ring
 // past K); VA / VB only for a k-contiguous 16-bit operand that is 16-byte
 // aligned with ld % 8 == 0 and K % 8 == 0.  LA / LB: LAYOUT_ROW or LAYOUT_COL.
-template <int IN, int OUT, int LA, int LB, bool VA, bool VB>
+template <int IN, int OUT, int LA, int LB, bool VA, bool VB, bool EPI = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void gemm_kernel_direct(GemmArgs p) {
     constexpr int EB = IN == DT_F32 ? 4 : 2;
     constexpr bool KCA = LA == LAYOUT_ROW, KCB = LB == LAYOUT_COL;  // k contiguous
@@ -193,6 +193,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void gemm_kern
     // rounds to nearest even
     constexpr int OB = OUT == DT_F32 ? 4 : 2;
     const int row = m0 + l16, col = n0 + 4 * q;
+    if constexpr (EPI) {
+        // fused epilogue (one block per wave: no staging needed)
+        const int n = row < M ? (N - col >= 4 ? 4 : N - col > 0 ? N - col : 0) : 0;
+        if (n > 0) store4_fused<OUT>(p, row, col, n, p.vec_c && n == 4, acc);
+        return;
+    }
     if (row < M) {
         char* dst = p.C + ((int64_t)row * p.ldc + col) * OB;
         if (p.vec_c && col + 4 <= N) {

@@ -60,7 +60,6 @@ namespace tgemm {
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
@@ -212,7 +211,7 @@ struct RingCfg {
 // buffer offsets (a tile's rows or columns of each operand over
 // K + LOOKAHEAD * BK of K) below 2^31 bytes.  LA / LB: LAYOUT_ROW or
 // LAYOUT_COL; C is row-major.
-template <class T, int IN, int OUT, int LA, int LB>
+template <class T, int IN, int OUT, int LA, int LB, bool EPI = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(T::THREADS, T::THREADS),
                           amdgpu_waves_per_eu(T::OCC * T::WAVES / 4 > 0 ? T::OCC * T::WAVES / 4 : 1)))
 void gemm_kernel_ring(GemmArgs p) {
@@ -460,6 +459,33 @@ void gemm_kernel_ring(GemmArgs p) {
     // a7: epilogue.  acc[i][j] of lane l is C[row 16 i + l%16][columns
     // 16 j + 4 (l/16) .. +3] of the wave's block; fp32 -> fp16 / bf16 rounds
     // to nearest even.
+    if constexpr (EPI) {
+        // fused epilogue through the rings' LDS, once no wave reads it
+        __syncthreads();
+        constexpr int REGION = P::LDS_BYTES / T::WAVES;  // bytes per wave
+        constexpr int PB = REGION / 1024 < NMF ? REGION / 1024 : NMF;
+        static_assert(PB >= 1 && NMF % PB == 0, "");
+        lds_f32x4* region = (lds_f32x4*)(lds_void*)smem + wave * (REGION / 16);
+        // The blocks of the later passes wait in VGPRs (free once the loop
+        // is done): kept in the accumulator registers across the first
+        // pass's loop, they make the register allocator move accumulators
+        // around inside the main loop.
+        f32x4 held[NMF];
+        static_for<0, NMF>([&](auto b_t) __attribute__((always_inline)) {
+            constexpr int b = decltype(b_t)::value;
+            held[b] = acc[b / T::FN][b % T::FN];
+            if constexpr (b >= PB) asm volatile("" : "+v"(held[b]));
+        });
+        fused_epilogue<OUT, NMF, 4, PB>(
+            p, region, [&](auto b_t) { constexpr int b = decltype(b_t)::value; return held[b]; },
+            [&](int b, int, int& row, int& col, int& n, bool& vec) {
+                row = m0 + wm * T::WTM + 16 * (b / T::FN) + i16;
+                col = n0 + wn * T::WTN + 16 * (b % T::FN) + 4 * q;
+                n = 4;
+                vec = true;
+            });
+        return;
+    }
     constexpr int OB = OUT == DT_F32 ? 4 : 2;
     const int64_t ldc = p.ldc;
     static_for<0, NMF>([&](auto bt) __attribute__((always_inline)) {

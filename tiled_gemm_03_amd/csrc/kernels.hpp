@@ -29,21 +29,29 @@ enum { CFG_BIG = 0, CFG_MID = 1, CFG_SMALL = 2, CFG_TINY = 3, CFG_F32_MID = 4, C
 typedef void (*KernelFn)(GemmArgs);
 
 // Register-staged kernel of configuration cfg (CFG_BIG .. CFG_F32_TINY) for
-// (in, out) (DT_* values); fast: the unchecked whole-tile path.  nullptr if
-// the pair is not served.  One definition per configuration (k_tiled_<cfg>.hip).
-KernelFn tiled_kernel_big(int in, int out, bool fast);
-KernelFn tiled_kernel_mid(int in, int out, bool fast);
-KernelFn tiled_kernel_small(int in, int out, bool fast);
-KernelFn tiled_kernel_tiny(int in, int out, bool fast);
-KernelFn tiled_kernel_f32(int cfg, int in, int out, bool fast);
+// (in, out) (DT_* values); fast: the unchecked whole-tile path; epi: the
+// fused epilogue (GemmArgs::epi ... act).  nullptr if the pair is not served.
+// One definition per configuration (k_tiled_<cfg>.hip).
+KernelFn tiled_kernel_big(int in, int out, bool fast, bool epi);
+KernelFn tiled_kernel_mid(int in, int out, bool fast, bool epi);
+KernelFn tiled_kernel_small(int in, int out, bool fast, bool epi);
+KernelFn tiled_kernel_tiny(int in, int out, bool fast, bool epi);
+KernelFn tiled_kernel_f32(int cfg, int in, int out, bool fast, bool epi);
 
 // Ring kernel of CFG_BIG or CFG_MID for (in, out) and the layouts of A and B
 // (LAYOUT_ROW / LAYOUT_COL).  k_ring_big.hip, k_ring_mid.hip.
-KernelFn ring_kernel_big(int in, int out, int la, int lb);
-KernelFn ring_kernel_mid(int in, int out, int la, int lb);
+KernelFn ring_kernel_big(int in, int out, int la, int lb, bool epi);
+KernelFn ring_kernel_mid(int in, int out, int la, int lb, bool epi);
 
 // Direct kernel for (in, out), the layouts of A and B, and whether each
 // operand takes 16-byte loads.  k_direct.hip.
-KernelFn direct_kernel(int in, int out, int la, int lb, bool va, bool vb);
+KernelFn direct_kernel(int in, int out, int la, int lb, bool va, bool vb, bool epi);
+
+// The fused-epilogue halves of the largest families, compiled in units of
+// their own (k_*_fused.hip) so that the build runs them in parallel.
+KernelFn tiled_kernel_big_fused(int in, int out, bool fast);
+KernelFn ring_kernel_big_fused(int in, int out, int la, int lb);
+KernelFn ring_kernel_mid_fused(int in, int out, int la, int lb);
+KernelFn direct_kernel_fused(int in, int out, int la, int lb, bool va, bool vb);
 
 }  // namespace tgemm

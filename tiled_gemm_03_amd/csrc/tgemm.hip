@@ -24,18 +24,20 @@ struct ConfigEntry {
     bool direct;    // the direct kernel (32 x 32 per workgroup, no LDS)
     int bm, bn, bk, wm, wn, eb, lds_bytes, threads, cpr;
     // register-staged kernels (row-major operands only)
-    KernelFn (*tiled)(int in, int out, bool fast);
+    KernelFn (*tiled)(int in, int out, bool fast, bool epi);
     // direct-to-LDS ring kernels of the same output tile (whole tiles, K a
     // multiple of ring_k_mult; any operand layout), with their block_k,
     // stage count and LDS bytes
-    KernelFn (*ring)(int in, int out, int la, int lb);
+    KernelFn (*ring)(int in, int out, int la, int lb, bool epi);
     int ring_bk, ring_stages, ring_k_mult, ring_lds;
     int ring_lookahead;               // steps of ring_bk that the ring loads past K
     int ring_a_bk, ring_a_stages;     // the ring of a row-major A
 };
 
-KernelFn tiled_f32_mid(int in, int out, bool fast) { return tiled_kernel_f32(CFG_F32_MID, in, out, fast); }
-KernelFn tiled_f32_tiny(int in, int out, bool fast) { return tiled_kernel_f32(CFG_F32_TINY, in, out, fast); }
+KernelFn tiled_f32_mid(int in, int out, bool fast, bool epi) { return tiled_kernel_f32(CFG_F32_MID, in, out, fast, epi); }
+KernelFn tiled_f32_tiny(int in, int out, bool fast, bool epi) {
+    return tiled_kernel_f32(CFG_F32_TINY, in, out, fast, epi);
+}
 
 #define ENTRY(name, fam, T, sel)                                                                                \
     {name, fam, false, T::BM, T::BN, T::BK, T::WM, T::WN, T::EB, T::LDS_BYTES, T::THREADS, T::CPR, sel, nullptr, \
@@ -95,6 +97,14 @@ bool pair_supported(int in, int out) {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// The fused epilogue of a call (on = false: C := AB).
+struct Epi {
+    bool on = false;
+    float alpha = 1.f, beta = 0.f;
+    const void* bias = nullptr;
+    int bias_kind = TGEMM_BIAS_NONE, bias_dt = TGEMM_F32, act = TGEMM_ACT_NONE;
+};
+
 // One product after a column-major C has been turned into a row-major one
 // (C^T = B^T A^T): logical A is M x K, B is K x N, C row-major M x N.
 struct Problem {
@@ -108,6 +118,7 @@ struct Problem {
     void* C;
     int64_t ldc;
     int in, out;
+    Epi ep;
 };
 
 bool layout_ok(int l) { return l == TGEMM_ROW_MAJOR || l == TGEMM_COL_MAJOR; }
@@ -127,12 +138,31 @@ int validate(const Problem& p) {
     if (M == 0 || N == 0) return TGEMM_OK;
     if (p.C == nullptr) return TGEMM_ERR_NULL;
     if (K > 0 && (p.A == nullptr || p.B == nullptr)) return TGEMM_ERR_NULL;
+    const uintptr_t c0 = (uintptr_t)p.C, c1 = c0 + span(M, N, p.ldc, elem_bytes(p.out));
     if (K > 0) {
         const int ie = elem_bytes(p.in);
-        const uintptr_t c0 = (uintptr_t)p.C, c1 = c0 + span(M, N, p.ldc, elem_bytes(p.out));
         const uintptr_t a0 = (uintptr_t)p.A, a1 = a0 + span(a_rows, a_cols, p.lda, ie);
         const uintptr_t b0 = (uintptr_t)p.B, b1 = b0 + span(b_rows, b_cols, p.ldb, ie);
         if ((c0 < a1 && a0 < c1) || (c0 < b1 && b0 < c1)) return TGEMM_ERR_ALIAS;
+    }
+    if (p.ep.on && p.ep.bias_kind != TGEMM_BIAS_NONE) {
+        // the bias is read while C is written: it may not overlap C
+        const int64_t n = p.ep.bias_kind == TGEMM_BIAS_ROW ? M : N;
+        const uintptr_t x0 = (uintptr_t)p.ep.bias, x1 = x0 + (uintptr_t)n * elem_bytes(p.ep.bias_dt);
+        if (c0 < x1 && x0 < c1) return TGEMM_ERR_ALIAS;
+    }
+    return TGEMM_OK;
+}
+
+// The epilogue's own arguments (checked before the sizes: they are wrong
+// whatever the sizes).
+int validate_epi(const Epi& e) {
+    if (!e.on) return TGEMM_OK;
+    if (e.act < TGEMM_ACT_NONE || e.act > TGEMM_ACT_SILU) return TGEMM_ERR_EPILOGUE;
+    if (e.bias_kind < TGEMM_BIAS_NONE || e.bias_kind > TGEMM_BIAS_COL) return TGEMM_ERR_EPILOGUE;
+    if (e.bias_kind != TGEMM_BIAS_NONE) {
+        if (e.bias_dt != TGEMM_F32 && e.bias_dt != TGEMM_F16 && e.bias_dt != TGEMM_BF16) return TGEMM_ERR_EPILOGUE;
+        if (e.bias == nullptr) return TGEMM_ERR_EPILOGUE;
     }
     return TGEMM_OK;
 }
@@ -239,7 +269,7 @@ int plan_direct(const Problem& p, Plan& plan) {
     const bool va = half && kca && (uintptr_t)p.A % 16 == 0 && p.lda % 8 == 0 && p.K % 8 == 0;
     const bool vb = half && kcb && (uintptr_t)p.B % 16 == 0 && p.ldb % 8 == 0 && p.K % 8 == 0;
     plan.kind = TGEMM_KERNEL_DIRECT;
-    plan.fn = direct_kernel(p.in, p.out, p.la, p.lb, va, vb);
+    plan.fn = direct_kernel(p.in, p.out, p.la, p.lb, va, vb, p.ep.on);
     if (plan.fn == nullptr) return TGEMM_ERR_DTYPE;
     if (ceil_div(p.M, 32) * ceil_div(p.N, 32) > 0x7fffffff) return TGEMM_ERR_DIM;
     return TGEMM_OK;
@@ -248,6 +278,8 @@ int plan_direct(const Problem& p, Plan& plan) {
 // Validates the arguments and picks the kernel; returns TGEMM_OK (plan
 // filled; M == 0 or N == 0 leaves plan.fn null) or a negative error code.
 int make_plan(const Problem& p, int config_id, Plan& plan) {
+    const int ve = validate_epi(p.ep);
+    if (ve != TGEMM_OK) return ve;
     const int v = validate(p);
     if (v != TGEMM_OK) return v;
     if (config_id < -1 || config_id >= kNumConfigs) return TGEMM_ERR_CONFIG;
@@ -263,7 +295,7 @@ int make_plan(const Problem& p, int config_id, Plan& plan) {
     const ConfigEntry& c = kConfigs[plan.config];
     if (!c.direct && ring_applies(c, p)) {
         plan.kind = TGEMM_KERNEL_RING;
-        plan.fn = c.ring(p.in, p.out, p.la, p.lb);
+        plan.fn = c.ring(p.in, p.out, p.la, p.lb, p.ep.on);
         if (plan.fn == nullptr) return TGEMM_ERR_DTYPE;
         return ceil_div(p.M, c.bm) * ceil_div(p.N, c.bn) > 0x7fffffff ? TGEMM_ERR_DIM : TGEMM_OK;
     }
@@ -279,7 +311,7 @@ int make_plan(const Problem& p, int config_id, Plan& plan) {
     const ConfigEntry& t = kConfigs[plan.config];
     const bool fast = tiled_fast(t, p);
     plan.kind = fast ? TGEMM_KERNEL_TILED : TGEMM_KERNEL_GENERAL;
-    plan.fn = t.tiled(p.in, p.out, fast);
+    plan.fn = t.tiled(p.in, p.out, fast, p.ep.on);
     if (plan.fn == nullptr) return TGEMM_ERR_DTYPE;
     return ceil_div(p.M, t.bm) * ceil_div(p.N, t.bn) > 0x7fffffff ? TGEMM_ERR_DIM : TGEMM_OK;
 }
@@ -287,13 +319,27 @@ int make_plan(const Problem& p, int config_id, Plan& plan) {
 // The problem of a call: a column-major C is computed as the row-major
 // C^T = B^T A^T (M and N swapped, A and B swapped, each operand's layout
 // flipped: a row-major K x N B read as an N x K matrix is column-major).
+// A fused epilogue goes along; its bias per row of C becomes one per column
+// of C^T and the other way round.
 int make_problem(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int la, const void* B, int64_t ldb,
-                 int lb, void* C, int64_t ldc, int lc, int in, int out, Problem& p) {
+                 int lb, void* C, int64_t ldc, int lc, int in, int out, Problem& p,
+                 const tgemm_epilogue* ep = nullptr) {
     if (!layout_ok(la) || !layout_ok(lb) || !layout_ok(lc)) return TGEMM_ERR_LAYOUT;
     if (lc == TGEMM_ROW_MAJOR)
         p = Problem{M, N, K, A, lda, la, B, ldb, lb, C, ldc, in, out};
     else
         p = Problem{N, M, K, B, ldb, lb ^ 1, A, lda, la ^ 1, C, ldc, in, out};
+    if (ep != nullptr) {
+        p.ep.on = true;
+        p.ep.alpha = ep->alpha;
+        p.ep.beta = ep->beta;
+        p.ep.bias = ep->bias;
+        p.ep.bias_kind = ep->bias_kind;
+        p.ep.bias_dt = ep->bias_dtype;
+        p.ep.act = ep->activation;
+        if (lc == TGEMM_COL_MAJOR && ep->bias_kind == TGEMM_BIAS_ROW) p.ep.bias_kind = TGEMM_BIAS_COL;
+        else if (lc == TGEMM_COL_MAJOR && ep->bias_kind == TGEMM_BIAS_COL) p.ep.bias_kind = TGEMM_BIAS_ROW;
+    }
     return TGEMM_OK;
 }
 
@@ -320,6 +366,13 @@ int run(const Problem& p, void* stream, int config_id) {
     if (plan.kind == TGEMM_KERNEL_RING) args.swz_mask = tuning().swizzle ? 1 : 0;
     args.vec_ab = loads_aligned(c, p);
     args.vec_c = stores_aligned(p);
+    args.epi = p.ep.on ? 1 : 0;
+    args.alpha = p.ep.alpha;
+    args.beta = p.ep.beta;
+    args.bias = (const char*)p.ep.bias;
+    args.bias_kind = p.ep.on ? p.ep.bias_kind : TGEMM_BIAS_NONE;
+    args.bias_dt = p.ep.bias_dt;
+    args.act = p.ep.act;
     const int64_t grid = (int64_t)args.tiles_m * args.tiles_n;
 
     void* kargs[] = {&args};
@@ -354,6 +407,16 @@ int gemm_t(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int layo
     return run(p, stream, config_id);
 }
 
+int gemm_fused(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int layout_a, const void* B,
+               int64_t ldb, int layout_b, void* C, int64_t ldc, int layout_c, int in_dtype, int out_dtype,
+               const tgemm_epilogue* epilogue, void* stream, int config_id) {
+    Problem p;
+    const int v = make_problem(M, N, K, A, lda, layout_a, B, ldb, layout_b, C, ldc, layout_c, in_dtype, out_dtype, p,
+                               epilogue);
+    if (v != TGEMM_OK) return v;
+    return run(p, stream, config_id);
+}
+
 const char* gemm_strerror(int code) {
     switch (code) {
         case TGEMM_OK: return "success";
@@ -366,6 +429,8 @@ const char* gemm_strerror(int code) {
             return "unknown tile configuration, configuration for another input type, or one without a kernel for "
                    "column-major operands";
         case TGEMM_ERR_LAYOUT: return "layout is neither TGEMM_ROW_MAJOR nor TGEMM_COL_MAJOR";
+        case TGEMM_ERR_EPILOGUE:
+            return "epilogue: unknown activation, bias kind or bias type, or a bias kind without a bias pointer";
         default: break;
     }
     if (code > 0) return hipGetErrorString((hipError_t)code);
