@@ -165,6 +165,14 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 __device__ __forceinline__ u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
 
+// 16 bytes from any element-aligned address: gfx950 runs in unaligned-access
+// mode, so this is one global_load_dwordx4 whatever the alignment.
+__device__ __forceinline__ u32x4 load16(const char* p) {
+    u32x4 v;
+    __builtin_memcpy(&v, p, 16);
+    return v;
+}
+
 // One 16-byte chunk holding VE consecutive elements starting at `p`, of which
 // only the first `valid` exist (the rest read as zero).  Element-wise loads:
 // used for ragged edges and for operands that are not 16-byte aligned.
@@ -215,7 +223,8 @@ __device__ __forceinline__ void store4(char* p, float a, float b, float c, float
         if (vec) {
             *(f32x4*)p = f32x4{a, b, c, d};
         } else {
-            ((float*)p)[0] = a; ((float*)p)[1] = b; ((float*)p)[2] = c; ((float*)p)[3] = d;
+            const f32x4 v = f32x4{a, b, c, d};
+            __builtin_memcpy(p, &v, 16);  // one unaligned store (unaligned-access mode)
         }
     } else {
         uint32_t lo, hi;
@@ -229,8 +238,8 @@ __device__ __forceinline__ void store4(char* p, float a, float b, float c, float
         if (vec) {
             *(u32x2*)p = u32x2{lo, hi};
         } else {
-            ((uint16_t*)p)[0] = (uint16_t)lo; ((uint16_t*)p)[1] = (uint16_t)(lo >> 16);
-            ((uint16_t*)p)[2] = (uint16_t)hi; ((uint16_t*)p)[3] = (uint16_t)(hi >> 16);
+            const u32x2 v = u32x2{lo, hi};
+            __builtin_memcpy(p, &v, 8);
         }
     }
 }
@@ -335,8 +344,9 @@ __device__ __forceinline__ void fused_epilogue(const GemmArgs& p, lds_f32x4* reg
 // FAST: every tile is whole (M % BM == 0, N % BN == 0) and A, B, C are
 // 16-byte aligned with lda, ldb whole 16-byte chunks and ldc a multiple of 4:
 // the main loop has no bounds checks (only a ragged last K step is masked).
-// Otherwise (GENERAL) every load and store is checked; 16-byte accesses are
-// still used where p.vec_ab / p.vec_c allow them.
+// Otherwise (GENERAL) every load and store is checked; whole 16-byte chunks
+// and 4-element stores still take one access each (unaligned where p.vec_ab /
+// p.vec_c say so).
 template <class T, int IN, int OUT, bool FAST, bool EPI = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(T::THREADS, T::THREADS),
                           amdgpu_waves_per_eu(T::OCC * T::WAVES / 4 > 0 ? T::OCC * T::WAVES / 4 : 1)))
@@ -404,7 +414,7 @@ void gemm_kernel(GemmArgs p) {
                 const int gm = m0 + r, gk = k0 + a_c * VE;
                 const char* src = Ab + ((int64_t)gm * lda + gk) * EB;
                 const int valid = gm < M ? (K - gk < VE ? K - gk : VE) : 0;
-                if (vec_ab && valid == VE) ra[w] = *(const u32x4*)src;
+                if (valid == VE) ra[w] = vec_ab ? *(const u32x4*)src : load16(src);
                 else ra[w] = valid > 0 ? load_chunk_partial<EB>(src, valid) : zero4();
             }
         } else {
@@ -422,7 +432,7 @@ void gemm_kernel(GemmArgs p) {
                 const int gk = k0 + kb * VE + j;
                 const char* src = Bb + ((int64_t)gk * ldb + gn) * EB;
                 const int valid = (live && gk < K) ? (N - gn < VE ? N - gn : VE) : 0;
-                if (vec_ab && valid == VE) rb[i][j] = *(const u32x4*)src;
+                if (valid == VE) rb[i][j] = vec_ab ? *(const u32x4*)src : load16(src);
                 else rb[i][j] = valid > 0 ? load_chunk_partial<EB>(src, valid) : zero4();
             }
         }
@@ -619,7 +629,7 @@ void gemm_kernel(GemmArgs p) {
                     vec = true;
                 } else {
                     n = row < M ? (N - col >= 4 ? 4 : N - col > 0 ? N - col : 0) : 0;
-                    vec = p.vec_c && n == 4;
+                    vec = p.vec_c != 0;
                 }
             });
         return;
@@ -638,8 +648,8 @@ void gemm_kernel(GemmArgs p) {
             if constexpr (FAST) {
                 store4<OUT>(dst, v0, v1, v2, v3, true);
             } else if (row < M) {
-                if (p.vec_c && col + 4 <= N) {
-                    store4<OUT>(dst, v0, v1, v2, v3, true);
+                if (col + 4 <= N) {
+                    store4<OUT>(dst, v0, v1, v2, v3, p.vec_c);
                 } else {
                     if (col + 0 < N) store_elem<OUT>(dst + 0 * OB, v0);
                     if (col + 1 < N) store_elem<OUT>(dst + 1 * OB, v1);

@@ -196,13 +196,13 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void gemm_kern
     if constexpr (EPI) {
         // fused epilogue (one block per wave: no staging needed)
         const int n = row < M ? (N - col >= 4 ? 4 : N - col > 0 ? N - col : 0) : 0;
-        if (n > 0) store4_fused<OUT>(p, row, col, n, p.vec_c && n == 4, acc);
+        if (n > 0) store4_fused<OUT>(p, row, col, n, p.vec_c != 0, acc);
         return;
     }
     if (row < M) {
         char* dst = p.C + ((int64_t)row * p.ldc + col) * OB;
-        if (p.vec_c && col + 4 <= N) {
-            store4<OUT>(dst, acc[0], acc[1], acc[2], acc[3], true);
+        if (col + 4 <= N) {
+            store4<OUT>(dst, acc[0], acc[1], acc[2], acc[3], p.vec_c != 0);
         } else {
             if (col + 0 < N) store_elem<OUT>(dst + 0 * OB, acc[0]);
             if (col + 1 < N) store_elem<OUT>(dst + 1 * OB, acc[1]);
