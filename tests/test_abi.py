@@ -297,3 +297,39 @@ def test_fused_epilogue_struct_layout():
     """The ctypes mirror of tgemm_epilogue: two floats, a pointer, three ints."""
     assert ctypes.sizeof(T.Epilogue) == 32
     assert T.Epilogue.bias.offset == 8 and T.Epilogue.activation.offset == 24
+
+
+def _read_tuned_table(path):
+    rows = []
+    for line in open(path):
+        line = line.strip()
+        if not line or line.startswith("//"):
+            continue
+        m = re.fullmatch(r"\{([-0-9, ]+)\},", line)
+        assert m, f"unexpected line in the tuned table: {line!r}"
+        rows.append(tuple(int(x) for x in m.group(1).split(",")))
+    return rows
+
+
+def test_tuned_table_entries_are_valid():
+    """Every entry of the committed table names a configuration of its input
+    type's family and a supported type pair."""
+    from tiled_gemm_03_amd import tune
+    for M, N, K, lda, ldb, ldc, i, o, cfg in _read_tuned_table(tune.TABLE):
+        assert min(M, N, K) >= 0 and lda >= K and ldb >= N and ldc >= N
+        assert (i, o) in ((T.F32, T.F32), (T.F16, T.F16), (T.F16, T.F32), (T.BF16, T.BF16), (T.BF16, T.F32))
+        fam = T.F32 if i == T.F32 else T.F16
+        assert T.gemm_config_info(cfg)["in_dtype"] == fam
+        # the library picks that configuration for exactly that call
+        FAKE = 1 << 40
+        assert T.gemm_select_config(M, N, K, FAKE, lda, FAKE + (1 << 36), ldb, FAKE + (2 << 36), ldc, i, o) == cfg
+
+
+def test_tuner_emits_a_table_the_parser_reads(tmp_path):
+    from tiled_gemm_03_amd import tune
+    entries = [(8192, 8192, 8192, T.F16, T.F16, 8192, 8192, 8192, 0), (127, 255, 512, T.F16, T.F32, 512, 255, 255, 6)]
+    path = str(tmp_path / "t.inc")
+    tune.emit(entries, path=path, note="test")
+    assert _read_tuned_table(path) == [(8192, 8192, 8192, 8192, 8192, 8192, 1, 1, 0), (127, 255, 512, 512, 255, 255, 1, 0, 6)]
+    assert tune.parse_spec("1,2,3,1,0") == (1, 2, 3, 1, 0, 3, 2, 2)
+    assert tune.parse_spec("1,2,3,1,0,8,9,10") == (1, 2, 3, 1, 0, 8, 9, 10)

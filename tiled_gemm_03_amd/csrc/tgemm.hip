@@ -232,7 +232,31 @@ bool direct_fits(const Problem& p) {
 //    set the time.
 // Column-major operands have no register-staged kernel: the ring kernels
 // where they apply, the direct kernel elsewhere.
+// Exact calls timed by the configuration search (tune.py): the measured
+// winner, before the rule.  Row-major operands and C only; the last entry is
+// a sentinel that matches nothing.
+struct TunedEntry {
+    int64_t M, N, K, lda, ldb, ldc;
+    int in, out, config;
+};
+const TunedEntry kTuned[] = {
+#include "tuned_table.inc"
+    {-1, -1, -1, -1, -1, -1, -1, -1, -1},
+};
+
+int tuned_choice(const Problem& p) {
+    if (!row_row(p)) return -1;
+    for (const TunedEntry& e : kTuned)
+        if (e.M == p.M && e.N == p.N && e.K == p.K && e.lda == p.lda && e.ldb == p.ldb && e.ldc == p.ldc &&
+            e.in == p.in && e.out == p.out && e.config >= 0 && e.config < kNumConfigs &&
+            kConfigs[e.config].in_family == (p.in == TGEMM_F32 ? TGEMM_F32 : TGEMM_F16))
+            return e.config;
+    return -1;
+}
+
 int table_choice(const Problem& p) {
+    const int tuned = tuned_choice(p);
+    if (tuned >= 0) return tuned;
     const int64_t M = p.M, N = p.N;
     const bool small = M * N <= (1LL << 18);
     if (p.in == TGEMM_F32) {
