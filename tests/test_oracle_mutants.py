@@ -82,3 +82,40 @@ def test_unmutated_copy_passes(tmp_path):
     code = RUNNER.format(root=ROOT, tests=HERE, lib=lib)
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stdout + r.stderr
+
+
+# Planted mistakes in the attention oracle (oracle/attention.py): a mutated
+# copy is loaded as a module of its own and must fail one of the attention
+# pins.
+ATTENTION_MUTANTS = [
+    ("scores_use_v", "np.swapaxes(K, 2, 3)", "np.swapaxes(V, 2, 3)"),
+    ("scale_dropped", "S = scale * np.matmul", "S = np.matmul"),
+    ("causal_hides_diagonal", "np.arange(Nk)[None, :] > ri[:, None]", "np.arange(Nk)[None, :] >= ri[:, None]"),
+    ("causal_upper_triangle", "np.arange(Nk)[None, :] > ri[:, None]", "np.arange(Nk)[None, :] < ri[:, None]"),
+    ("max_over_queries", "m = np.max(S, axis=3, keepdims=True)", "m = np.max(S, axis=2, keepdims=True)"),
+    ("normalised_over_queries", "np.sum(E, axis=3, keepdims=True)", "np.sum(E, axis=2, keepdims=True)"),
+    ("weights_times_k", "return np.matmul(P, V)", "return np.matmul(P, K)"),
+    ("sampled_rows_ignored", "Qr = Q[:, :, ri, :]", "Qr = Q[:, :, :len(ri), :]"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", ATTENTION_MUTANTS, ids=[m[0] for m in ATTENTION_MUTANTS])
+def test_planted_attention_mistake_is_caught(name, old, new, tmp_path):
+    import importlib.util
+    import attention_pins as AP
+    import oracle.attention as OA
+    src = open(OA.__file__, encoding="utf-8").read()
+    assert src.count(old) >= 1, f"mutation site for {name} not found"
+    path = tmp_path / "attention_mut.py"
+    path.write_text(src.replace(old, new, 1).replace("from . import decode", "from oracle import decode"),
+                    encoding="utf-8")
+    spec = importlib.util.spec_from_file_location("attention_mut", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    failed = []
+    for pin in AP.ATTENTION_PINS:
+        try:
+            pin(mod.attention)
+        except Exception:
+            failed.append(pin.__name__)
+    assert failed, f"mutant {name} passed every attention pin"
