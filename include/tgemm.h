@@ -64,6 +64,7 @@ extern "C" {
 #define TGEMM_ERR_LAYOUT (-7)      /* gemm_t: layout not ROW_MAJOR / COL_MAJOR  */
 #define TGEMM_ERR_EPILOGUE (-8)    /* gemm_fused: bad activation, bias kind or
                                       bias type, or a bias kind without bias  */
+#define TGEMM_ERR_HEAD_DIM (-9)    /* attention_fwd: head_dim not 64 or 128     */
 
 /* Operand layouts (gemm_t): the row-major default and the column-major option
  * of page "TileLang实战：用Python DSL自动生成高性能GPU计算内核", §5.1. */

@@ -1,5 +1,5 @@
 """Host-side checks of libtgemm.so (no GPU needed): it loads, exports every
-function include/tgemm.h declares, rejects invalid arguments with the
+function include/*.h declares, rejects invalid arguments with the
 documented codes before touching the GPU, picks the table's configuration,
 and its workgroup -> tile map is a bijection."""
 import ctypes
@@ -12,11 +12,12 @@ import tiled_gemm_03_amd as T
 from tiled_gemm_03_amd import workloads as W
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "tgemm.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 
 def declared_functions():
-    text = open(HEADER, encoding="utf-8").read()
+    text = "\n".join(open(h, encoding="utf-8").read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
     return sorted(set(names))

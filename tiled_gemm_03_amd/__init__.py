@@ -9,10 +9,13 @@ built, loading fails with an error that says so.
     gemm_ex(..., config_id)
     gemm_strerror(code), gemm_num_configs(), gemm_config_info(id),
     gemm_select_config(...), gemm_tile_map(...), gemm_version()
+    attention_fwd(B, H, n_q, n_k, d, Q, q_stride, K, k_stride, V, v_stride,
+                  O, o_stride, in_dtype, out_dtype, scale, causal, stream)
+        (include/tgemm_attention.h)
 
-`gemm_tensors(a, b, c)` takes torch device tensors (row-major, unit column
-stride) and passes their pointers, leading dimensions and the current HIP
-stream; torch provides only the memory and the stream.
+`gemm_tensors(a, b, c)` and `attention_tensors(q, k, v, o)` take torch device
+tensors and pass their pointers, strides and the current HIP stream; torch
+provides only the memory and the stream.
 """
 import ctypes
 import os
@@ -23,9 +26,11 @@ LIB_PATH = os.path.join(HERE, "libtgemm.so")
 F32, F16, BF16 = 0, 1, 2
 OK = 0
 ERR_DIM, ERR_NULL, ERR_LD, ERR_DTYPE, ERR_ALIAS, ERR_CONFIG, ERR_LAYOUT, ERR_EPILOGUE = -1, -2, -3, -4, -5, -6, -7, -8
+ERR_HEAD_DIM = -9
 
 EXPORTED = ["gemm", "gemm_ex", "gemm_t", "gemm_fused", "gemm_strerror", "gemm_num_configs", "gemm_config_info",
-            "gemm_select_config", "gemm_select_kernel", "gemm_select_kernel_t", "gemm_tile_map", "gemm_version"]
+            "gemm_select_config", "gemm_select_kernel", "gemm_select_kernel_t", "gemm_tile_map", "gemm_version",
+            "attention_fwd"]
 
 # operand layouts (gemm_t)
 ROW_MAJOR, COL_MAJOR = 0, 1
@@ -102,6 +107,9 @@ def lib():
     L.gemm_tile_map.argtypes = [i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i)]
     L.gemm_version.restype = ctypes.c_char_p
     L.gemm_version.argtypes = []
+    s3 = ctypes.POINTER(i64)
+    L.attention_fwd.restype = i
+    L.attention_fwd.argtypes = [i64, i64, i64, i64, i64, p, s3, p, s3, p, s3, p, s3, i, i, ctypes.c_float, i, p]
     _lib = L
     return L
 
@@ -173,6 +181,22 @@ def gemm_version():
     return lib().gemm_version().decode()
 
 
+def _strides(st):
+    """A host array of three int64 strides (batch, head, row), or None."""
+    if st is None:
+        return None
+    return (ctypes.c_int64 * 3)(*[int(x) for x in st])
+
+
+def attention_fwd(B, H, n_q, n_k, d, Q, q_stride, K, k_stride, V, v_stride, O, o_stride, in_dtype, out_dtype,
+                  scale, causal, stream=None):
+    """O := softmax(scale Q K^T [causal]) V; strides are 3-sequences or None
+    (packed)."""
+    return lib().attention_fwd(B, H, n_q, n_k, d, Q, _strides(q_stride), K, _strides(k_stride), V,
+                               _strides(v_stride), O, _strides(o_stride), in_dtype, out_dtype, float(scale),
+                               int(bool(causal)), stream)
+
+
 # ------------------------------------------------------------ torch marshalling
 def dtype_code(t):
     import torch
@@ -242,6 +266,36 @@ def gemm_tensors(a, b, c, config_id=-1, stream=None, check=True, alpha=None, bet
             ep.bias, ep.bias_kind, ep.bias_dtype = bias.data_ptr(), kind, dtype_code(bias)
         rc = gemm_fused(M, N, K, a.data_ptr(), lda, la, b.data_ptr(), ldb, lb, c.data_ptr(), ldc, lc,
                         dtype_code(a), dtype_code(c), ep, stream, config_id)
+    if check and rc != OK:
+        raise TgemmError(rc)
+    return rc
+
+
+def _bhnd(t, name):
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be a 4-D [batch, heads, n, d] tensor")
+    if t.numel() > 0 and t.stride(3) != 1:
+        raise ValueError(f"{name}: the last dimension must be contiguous")
+    return (t.stride(0), t.stride(1), t.stride(2))
+
+
+def attention_tensors(q, k, v, o, scale=1.0, causal=False, stream=None, check=True):
+    """o := softmax(scale q k^T) v on the device, through the C ABI.  q, o:
+    [B, H, n_q, d]; k, v: [B, H, n_k, d] torch tensors on the GPU (any
+    strides with a contiguous last dimension).  Returns the return code
+    (raises TgemmError on failure if check)."""
+    import torch
+    B, H, nq, d = q.shape
+    if k.shape != v.shape or k.shape[:2] != (B, H) or k.shape[3] != d or tuple(o.shape) != (B, H, nq, d):
+        raise ValueError(f"shape mismatch q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}, "
+                         f"o {tuple(o.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must have one dtype")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = attention_fwd(B, H, nq, k.shape[2], d, q.data_ptr(), _bhnd(q, "q"), k.data_ptr(), _bhnd(k, "k"),
+                       v.data_ptr(), _bhnd(v, "v"), o.data_ptr(), _bhnd(o, "o"), dtype_code(q), dtype_code(o),
+                       scale, causal, stream)
     if check and rc != OK:
         raise TgemmError(rc)
     return rc

@@ -1,0 +1,132 @@
+// attention.hip -- C ABI of the attention forward (include/tgemm_attention.h):
+// argument checks, kernel choice and launch.  The kernel is in
+// attention_kernel.hpp.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "attention_kernel.hpp"
+#include "tgemm_attention.h"
+
+using namespace tgemm;
+
+namespace {
+
+typedef void (*AttnFn)(AttnArgs);
+
+template <int D, int IN, bool CAUSAL>
+AttnFn attn_pick_out(int out) {
+    if (out == DT_F32) return attention_kernel<D, IN, DT_F32, CAUSAL>;
+    return attention_kernel<D, IN, IN, CAUSAL>;
+}
+
+template <int D>
+AttnFn attn_pick(int in, int out, bool causal) {
+    if (in == DT_F16) return causal ? attn_pick_out<D, DT_F16, true>(out) : attn_pick_out<D, DT_F16, false>(out);
+    return causal ? attn_pick_out<D, DT_BF16, true>(out) : attn_pick_out<D, DT_BF16, false>(out);
+}
+
+struct Tensor4 {
+    const void* p;
+    int64_t s[3];  // batch, head, row strides (elements); the last dimension is contiguous
+};
+
+// Strides of a [B, H, n, d] operand: the given ones or the packed layout.
+bool strides_of(const int64_t* given, int64_t H, int64_t n, int64_t d, int64_t out[3]) {
+    if (given == nullptr) {
+        out[0] = H * n * d;
+        out[1] = n * d;
+        out[2] = d;
+        return true;
+    }
+    for (int i = 0; i < 3; ++i) {
+        if (given[i] < 0 || given[i] > ((int64_t)1 << 40)) return false;
+        out[i] = given[i];
+    }
+    return true;
+}
+
+// [first, last] byte range touched by a [B, H, n, d] operand (all sizes > 0).
+void byte_range(const Tensor4& t, int64_t B, int64_t H, int64_t n, int64_t d, int eb, uintptr_t& lo,
+                uintptr_t& hi) {
+    const int64_t last = (B - 1) * t.s[0] + (H - 1) * t.s[1] + (n - 1) * t.s[2] + (d - 1);
+    lo = (uintptr_t)t.p;
+    hi = (uintptr_t)t.p + (uintptr_t)(last + 1) * eb;
+}
+
+// No two elements of the output coincide: ordered by stride, every dimension
+// of extent > 1 steps over everything the smaller ones span.
+bool non_overlapping(const int64_t s[3], int64_t B, int64_t H, int64_t n, int64_t d) {
+    int64_t st[4] = {1, s[2], s[1], s[0]};
+    int64_t ex[4] = {d, n, H, B};
+    // insertion sort by stride (ties keep the inner dimension first)
+    for (int i = 1; i < 4; ++i)
+        for (int j = i; j > 0 && st[j] < st[j - 1]; --j) {
+            int64_t t = st[j]; st[j] = st[j - 1]; st[j - 1] = t;
+            t = ex[j]; ex[j] = ex[j - 1]; ex[j - 1] = t;
+        }
+    int64_t span = 1;  // elements spanned by the dimensions so far, as an extent
+    for (int i = 0; i < 4; ++i) {
+        if (ex[i] <= 1) continue;
+        if (st[i] < span) return false;
+        span = st[i] * (ex[i] - 1) + span;
+    }
+    return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attention_fwd(int64_t batch, int64_t heads, int64_t n_q, int64_t n_k, int64_t head_dim, const void* Q,
+                  const int64_t* q_stride, const void* K, const int64_t* k_stride, const void* V,
+                  const int64_t* v_stride, void* O, const int64_t* o_stride, int in_dtype, int out_dtype,
+                  float scale, int causal, void* stream) {
+    if (batch < 0 || heads < 0 || n_q < 0 || n_k < 0 || batch > 65535 || heads > 65535 || n_q > TGEMM_MAX_DIM ||
+        n_k > TGEMM_MAX_DIM)
+        return TGEMM_ERR_DIM;
+    if (head_dim != 64 && head_dim != 128) return TGEMM_ERR_HEAD_DIM;
+    if (in_dtype != TGEMM_F16 && in_dtype != TGEMM_BF16) return TGEMM_ERR_DTYPE;
+    if (out_dtype != in_dtype && out_dtype != TGEMM_F32) return TGEMM_ERR_DTYPE;
+    if (!isfinite(scale)) return TGEMM_ERR_DIM;
+    if (batch == 0 || heads == 0 || n_q == 0) return TGEMM_OK;
+    if (n_k == 0) return TGEMM_ERR_DIM;
+    const int64_t d = head_dim;
+    Tensor4 q{Q, {}}, k{K, {}}, v{V, {}}, o{O, {}};
+    if (!strides_of(q_stride, heads, n_q, d, q.s) || !strides_of(k_stride, heads, n_k, d, k.s) ||
+        !strides_of(v_stride, heads, n_k, d, v.s) || !strides_of(o_stride, heads, n_q, d, o.s))
+        return TGEMM_ERR_LD;
+    if (Q == nullptr || K == nullptr || V == nullptr || O == nullptr) return TGEMM_ERR_NULL;
+    if (!non_overlapping(o.s, batch, heads, n_q, d)) return TGEMM_ERR_LD;
+    const int ob = out_dtype == TGEMM_F32 ? 4 : 2;
+    uintptr_t o0, o1;
+    byte_range(o, batch, heads, n_q, d, ob, o0, o1);
+    const Tensor4* ins[3] = {&q, &k, &v};
+    const int64_t ns[3] = {n_q, n_k, n_k};
+    for (int i = 0; i < 3; ++i) {
+        uintptr_t a0, a1;
+        byte_range(*ins[i], batch, heads, ns[i], d, 2, a0, a1);
+        if (o0 < a1 && a0 < o1) return TGEMM_ERR_ALIAS;
+    }
+
+    AttnArgs a;
+    a.Q = (const char*)Q;
+    a.K = (const char*)K;
+    a.V = (const char*)V;
+    a.O = (char*)O;
+    a.q_sb = q.s[0]; a.q_sh = q.s[1]; a.q_sn = q.s[2];
+    a.k_sb = k.s[0]; a.k_sh = k.s[1]; a.k_sn = k.s[2];
+    a.v_sb = v.s[0]; a.v_sh = v.s[1]; a.v_sn = v.s[2];
+    a.o_sb = o.s[0]; a.o_sh = o.s[1]; a.o_sn = o.s[2];
+    a.Nq = (int)n_q;
+    a.Nk = (int)n_k;
+    a.scale_log2e = scale * 1.4426950408889634f;
+    const int in = in_dtype == TGEMM_F16 ? DT_F16 : DT_BF16;
+    const int out = out_dtype == TGEMM_F32 ? DT_F32 : in;
+    const AttnFn fn = d == 64 ? attn_pick<64>(in, out, causal != 0) : attn_pick<128>(in, out, causal != 0);
+    const dim3 grid((unsigned)((n_q + 63) / 64), (unsigned)heads, (unsigned)batch);
+    hipLaunchKernelGGL(fn, grid, dim3(256), 0, (hipStream_t)stream, a);
+    return (int)hipGetLastError();
+}
+
+}  // extern "C"

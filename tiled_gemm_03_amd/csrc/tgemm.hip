@@ -444,17 +444,18 @@ int gemm_fused(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int 
 const char* gemm_strerror(int code) {
     switch (code) {
         case TGEMM_OK: return "success";
-        case TGEMM_ERR_DIM: return "M, N or K negative or too large";
+        case TGEMM_ERR_DIM: return "a size negative or too large (attention: also keys = 0 with queries)";
         case TGEMM_ERR_NULL: return "NULL pointer for a non-empty operand";
-        case TGEMM_ERR_LD: return "leading dimension smaller than the stored row width";
+        case TGEMM_ERR_LD: return "leading dimension smaller than the stored row width (attention: output elements overlap)";
         case TGEMM_ERR_DTYPE: return "unsupported (in_dtype, out_dtype) pair";
-        case TGEMM_ERR_ALIAS: return "C overlaps A or B";
+        case TGEMM_ERR_ALIAS: return "output overlaps an input";
         case TGEMM_ERR_CONFIG:
             return "unknown tile configuration, configuration for another input type, or one without a kernel for "
                    "column-major operands";
         case TGEMM_ERR_LAYOUT: return "layout is neither TGEMM_ROW_MAJOR nor TGEMM_COL_MAJOR";
         case TGEMM_ERR_EPILOGUE:
             return "epilogue: unknown activation, bias kind or bias type, or a bias kind without a bias pointer";
+        case TGEMM_ERR_HEAD_DIM: return "attention: head dimension is neither 64 nor 128";
         default: break;
     }
     if (code > 0) return hipGetErrorString((hipError_t)code);

@@ -1,7 +1,7 @@
-"""Seeded synthetic inputs for the five GEMM workloads.
+"""Seeded synthetic inputs for the five GEMM workloads and the attention forward.
 
 This module draws random matrices and stores them in the input element type;
-it holds none of the matrix-product arithmetic.  Both the GPU tests and the
+it holds none of the matrix-product or attention arithmetic.  Both the GPU tests and the
 oracle tests take their inputs from here, so the two sides see the same bits.
 
 The workloads are the pages' own kind of input: random dense matrices drawn
@@ -111,3 +111,36 @@ def sample_indices(n: int, count: int, seed: int) -> np.ndarray:
     rng = np.random.default_rng(seed)
     inner = rng.choice(np.arange(1, n - 1), size=count - 2, replace=False)
     return np.sort(np.concatenate([[0, n - 1], inner]).astype(np.int64))
+
+
+# ------------------------------------------------------------------ attention
+# Q, K, V for the attention forward: N(0, 1) entries rounded to the input
+# type, drawn Q then K then V from numpy.random.default_rng(seed), each
+# [B, H, n, d] (row-major, packed).
+def attention_inputs(B, H, Nq, Nk, d, dtype, seed):
+    rng = np.random.default_rng(seed)
+    mk = lambda n: to_storage(rng.standard_normal((B, H, n, d), dtype=np.float32), dtype)
+    return mk(Nq), mk(Nk), mk(Nk)
+
+
+class AttnWorkload:
+    def __init__(self, name, B, H, N, d, causal, scale, dtype=F16):
+        self.name, self.B, self.H, self.N, self.d = name, B, H, N, d
+        self.causal, self.scale, self.dtype = causal, scale, dtype
+
+    def flops(self):
+        """4 B H N^2 d for the two products (half of it with the causal mask,
+        counted over the visible keys only: N (N + 1) / 2 per head)."""
+        pairs = self.N * (self.N + 1) // 2 if self.causal else self.N * self.N
+        return 4.0 * self.B * self.H * pairs * self.d
+
+
+# The sequence of page "TileLang实战" §4.3 (1024 positions, model width 768,
+# read as 12 heads of 64, no score scale as in its §4.2), and a long-sequence
+# case (4096 positions, the length its §4.1 names) with 128-wide heads, plain
+# and causal.
+ATTN_WORKLOADS = [
+    AttnWorkload("attn_b1_h12_n1024_d64", 1, 12, 1024, 64, False, 1.0),
+    AttnWorkload("attn_b4_h16_n4096_d128", 4, 16, 4096, 128, False, 128 ** -0.5),
+    AttnWorkload("attn_b4_h16_n4096_d128_causal", 4, 16, 4096, 128, True, 128 ** -0.5),
+]
