@@ -9,11 +9,13 @@ method with these precisions meets (fp32 scores and softmax, probabilities
 rounded to the input type before the product with V, fp32 accumulation,
 output rounded once):
 
-    |o - r| <= u_out |r| + (1 + u_out) ((u_in + 2 rho) (P|V|) + n_k eta_in max_j |v_j|)
+    |o - r| <= u_out |r| + (1 + u_out) ((2 u_in / (1 - u_in) + 2 rho) (P|V|) + 2 n_k eta_in max_j |v_j|)
 
 with r the oracle's output, P|V| the oracle's attention of |V| (the same
 weights applied to the absolute values), u_in / u_out the unit roundoffs of
-the input / output types (2^-11 fp16, 2^-8 bf16, 0 fp32), eta_in half the
+the input / output types (2^-11 fp16, 2^-8 bf16, 0 fp32; a weight p_j / L
+with p_j rounded to the input type and L the sum of the rounded or of the
+unrounded p is off by at most 2 u_in / (1 - u_in) relative), eta_in half the
 smallest subnormal spacing of the input type (probabilities below the normal
 range lose relative precision: 2^-25 fp16, negligible for bf16), and rho the
 fp32 part: the relative error of each weight from the rounded scores
@@ -116,7 +118,8 @@ def _bound(q, k, v, ref, dtype, out, scale, causal, rows=None):
     pv = oracle_attention(q, k, _abs_stored(v, dtype), dtype, scale=scale, causal=causal, rows=rows)
     vmax = np.abs(oracle.decode(np.ascontiguousarray(v), dtype)).max(axis=2, keepdims=True)
     uo = U[out]
-    return uo * np.abs(ref) + (1 + uo) * ((U[dtype] + 2 * rho) * pv + nk * ETA[dtype] * vmax)
+    ui = U[dtype]
+    return uo * np.abs(ref) + (1 + uo) * ((2 * ui / (1 - ui) + 2 * rho) * pv + 2 * nk * ETA[dtype] * vmax)
 
 
 def _run(q, k, v, dtype, out, scale, causal, layout="bhnd", tail=0):

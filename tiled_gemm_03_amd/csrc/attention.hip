@@ -14,10 +14,13 @@ namespace {
 
 typedef void (*AttnFn)(AttnArgs);
 
+// waves per workgroup (32 query rows each)
+constexpr int kWaves = 4;
+
 template <int D, int IN, bool CAUSAL>
 AttnFn attn_pick_out(int out) {
-    if (out == DT_F32) return attention_kernel<D, IN, DT_F32, CAUSAL>;
-    return attention_kernel<D, IN, IN, CAUSAL>;
+    if (out == DT_F32) return attention_kernel<D, IN, DT_F32, CAUSAL, kWaves>;
+    return attention_kernel<D, IN, IN, CAUSAL, kWaves>;
 }
 
 template <int D>
@@ -120,12 +123,18 @@ int attention_fwd(int64_t batch, int64_t heads, int64_t n_q, int64_t n_k, int64_
     a.o_sb = o.s[0]; a.o_sh = o.s[1]; a.o_sn = o.s[2];
     a.Nq = (int)n_q;
     a.Nk = (int)n_k;
-    a.scale_log2e = scale * 1.4426950408889634f;
+    a.H = (int)heads;
+    const int64_t bq = 32 * kWaves;
+    const int64_t tiles = (n_q + bq - 1) / bq;
+    if (batch * heads * tiles >= ((int64_t)1 << 24)) return TGEMM_ERR_DIM;  // grid limit
+    a.tiles = (int)tiles;
+    a.total = (int)(batch * heads * tiles);
+    a.c = fabsf(scale) * 1.4426950408889634f;
+    a.qsign = scale < 0.f ? 0x80008000u : 0u;
     const int in = in_dtype == TGEMM_F16 ? DT_F16 : DT_BF16;
     const int out = out_dtype == TGEMM_F32 ? DT_F32 : in;
     const AttnFn fn = d == 64 ? attn_pick<64>(in, out, causal != 0) : attn_pick<128>(in, out, causal != 0);
-    const dim3 grid((unsigned)((n_q + 63) / 64), (unsigned)heads, (unsigned)batch);
-    hipLaunchKernelGGL(fn, grid, dim3(256), 0, (hipStream_t)stream, a);
+    hipLaunchKernelGGL(fn, dim3((unsigned)a.total), dim3(64 * kWaves), 0, (hipStream_t)stream, a);
     return (int)hipGetLastError();
 }
 

@@ -6,34 +6,44 @@
 // the normaliser L and the output, so that the Nq x Nk score matrix never
 // exists in memory).
 //
-// One workgroup (4 waves) per 64 query rows of one (batch, head); wave w
-// owns rows 16 w .. 16 w + 15.  Per block of 64 keys:
+// One workgroup of NW waves per 32 NW query rows of one (batch, head); wave w
+// owns rows 32 w .. 32 w + 31 of the tile as two sets of 16 (every fragment
+// read from LDS feeds two MFMAs).  Per block of 64 keys:
 //   S = Q K^T      v_mfma_f32_16x16x32 with K (first operand) and Q (second):
 //                  lane l holds S[row l % 16][keys 4 (l/16) .. +3] of each
 //                  16-key group (Q stays in registers for the whole loop);
-//   online softmax in fp32 with exp2 (the scale is folded into log2 e):
-//                  m = max(m, rowmax), p = 2^(s - m), l = l 2^(m_old - m) +
-//                  rowsum, O *= 2^(m_old - m); row reductions over the 4
-//                  lanes that share a row;
+//   online softmax in fp32 with exp2 (c = |scale| log2 e; a negative scale
+//                  flips the signs of Q, which is exact): p = 2^(c s - m).
+//                  The reference point m of a row moves only when a score
+//                  exceeds it by more than 2^8 (then m := the row maximum,
+//                  O and L scaled by 2^(m_old - m)); in between p <= 2^8 and
+//                  O, L keep accumulating against the old m.  The result
+//                  O / L does not depend on m; p stays within the input
+//                  type's range.  L is the sum of the probabilities as
+//                  rounded for the product with V (so the weights sum to 1
+//                  exactly), accumulated on the MFMA against ones;
 //   O += P V       the same MFMA with V (first operand) and P (second).  The
 //                  8 k-values a lane feeds per 32 keys are the keys it holds
 //                  in S, 4 (l/16) .. +3 and 16 + 4 (l/16) .. +3, so P goes
 //                  from the S registers straight into the MFMA; V is read in
 //                  that key order with two transposing LDS reads (4 key rows
 //                  each).
-// K and V blocks go global -> registers -> LDS, the next block's loads in
-// flight while the current one is computed.  LDS layouts (XOR swizzles, as
-// the matrix-product kernels): K as [32 d][64 keys][64 bytes] with chunk
-// c ^ ((key / 2) % 4) (a K fragment read is then the conflict-free read of
-// the k-contiguous ring stage); V as [64 keys][d] with its 32-byte groups of
-// row r at group g ^ f(r), f spreading the 8 rows of a half-wave's
-// transposing read over the 8 bank groups.
+// K and V blocks go global -> LDS directly (no registers) through two LDS
+// buffers: block j + 1 lands while block j is computed, one barrier per
+// block.  LDS layouts (XOR swizzles, as the
+// matrix-product kernels): K as [d / 32][64 keys][64 bytes] with chunk
+// c ^ ((key / 2) % 4) (a K fragment read is the conflict-free read of the
+// k-contiguous ring stage); V as [64 keys][d] with its 32-byte groups of row
+// r at group g ^ f(r), f spreading the 8 rows of a half-wave's transposing
+// read over the 8 bank groups.
 //
-// Masks: keys >= Nk (and, causal, keys > query) get score -inf; rows >= Nq
-// are neither read nor written.  Rows with every key masked cannot occur
-// (key 0 is visible to every query).
+// Masks (only in the blocks after those that every row of the tile sees
+// whole: a separate loop): keys >= Nk, and keys > query when causal, get
+// p = 0.  Rows >= Nq are computed on zero queries and not written.  Every row sees key 0, so
+// the first block sets every row's reference point.
 #pragma once
 #include "gemm_kernel.hpp"
+#include "gemm_kernel_ring.hpp"
 
 namespace tgemm {
 
@@ -46,8 +56,11 @@ struct AttnArgs {
     int64_t k_sb, k_sh, k_sn;
     int64_t v_sb, v_sh, v_sn;
     int64_t o_sb, o_sh, o_sn;
-    int Nq, Nk;
-    float scale_log2e;         // scale * log2(e)
+    int Nq, Nk, H;
+    int tiles;                 // query tiles per (batch, head)
+    int total;                 // B H tiles workgroups
+    float c;                   // |scale| log2(e)
+    uint32_t qsign;            // 0x80008000 when the scale is negative, else 0
 };
 
 typedef short attn_i16x4 __attribute__((ext_vector_type(4)));
@@ -63,180 +76,300 @@ __device__ __forceinline__ uint32_t attn_pack2(float a, float b) {
     else return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
-// D: head dimension (64 or 128); IN: DT_F16 / DT_BF16; OUT: IN or DT_F32.
-template <int D, int IN, int OUT, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2)))
+template <int IN>
+__device__ __forceinline__ f32x4 attn_mfma(attn_i16x8 a, attn_i16x8 b, f32x4 c) {
+    if constexpr (IN == DT_F16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                      0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                       0, 0, 0);
+}
+
+// Workgroup g -> (batch-head, query tile).  Workgroups are dispatched to the
+// 8 XCDs in turn (g % 8); the map gives each XCD a contiguous run of tiles,
+// so that the tiles of one head share that XCD's L2 for K and V.  Causal:
+// the tiles of a head are taken last to first (the longest first).
+__device__ __forceinline__ void attn_tile_of(int g, int total, int tiles, bool reverse, int& bh, int& qt) {
+    const int full = total & ~7;
+    int lin = g;
+    if (g < full) lin = (g & 7) * (full >> 3) + (g >> 3);
+    bh = lin / tiles;
+    qt = lin - bh * tiles;
+    if (reverse) qt = tiles - 1 - qt;
+}
+
+// D: head dimension (64 or 128); IN: DT_F16 / DT_BF16; OUT: IN or DT_F32;
+// NW: waves per workgroup (32 NW query rows).
+template <int D, int IN, int OUT, bool CAUSAL, int NW>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2)))
 void attention_kernel(AttnArgs p) {
     static_assert(D == 64 || D == 128, "");
-    constexpr int BQ = 64, BKV = 64;
-    constexpr int KS = D / 32;          // k-steps of the score product
-    constexpr int DB = D / 16;          // 16-column blocks of the output
-    constexpr int CPR = D / 8;          // 16-byte chunks per K / V row
-    constexpr int LOADS = BKV * CPR / 256;  // chunks of K (and of V) per thread and block
-    constexpr int K_BYTES = BKV * D * 2, V_BYTES = BKV * D * 2;
-    __shared__ __attribute__((aligned(1024))) char smem[K_BYTES + V_BYTES];
+    constexpr int NT = 64 * NW;
+    constexpr int BQ = 32 * NW, BKV = 64;
+    constexpr int KS = D / 32;              // k-steps of the score product
+    constexpr int DB = D / 16;              // 16-column blocks of the output
+    constexpr int CPR = D / 8;              // 16-byte chunks per K / V row
+    constexpr int LOADS = BKV * CPR / NT;   // chunks of K (and of V) per thread and block
+    static_assert(LOADS * NT == BKV * CPR, "");
+    constexpr int K_BYTES = BKV * D * 2, V_BYTES = BKV * D * 2, BUF = K_BYTES + V_BYTES;
+    constexpr float TH = 8.f;               // reference-point slack (log2 units)
+    __shared__ __attribute__((aligned(1024))) char smem[2 * BUF];
     lds_attn_char* const lds = (lds_attn_char*)smem;
-    lds_attn_char* const ks = lds;
-    lds_attn_char* const vs = lds + K_BYTES;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int q = lane >> 4, i16 = lane & 15;
-    const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    int bh, qt;
+    attn_tile_of(blockIdx.x, p.total, p.tiles, CAUSAL, bh, qt);
+    const int b = bh / p.H, h = bh - b * p.H;
     const int q0 = qt * BQ;
     const int Nq = p.Nq, Nk = p.Nk;
     const char* Qh = p.Q + (b * p.q_sb + h * p.q_sh) * 2;
     const char* Kh = p.K + (b * p.k_sb + h * p.k_sh) * 2;
     const char* Vh = p.V + (b * p.v_sb + h * p.v_sh) * 2;
 
-    // Q fragments of this lane's row (zeros past Nq): d = 32 s + 8 q .. +7
-    const int my_row = q0 + 16 * wave + i16;
-    attn_i16x8 qf[KS];
+    // Q fragments of this lane's rows (zeros past Nq): d = 32 s + 8 q .. +7
+    const int w_row0 = q0 + 32 * wave;  // first row of the wave
+    int my_row[2];
+    attn_i16x8 qf[2][KS];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-        u32x4 v = zero4();
-        if (my_row < Nq) v = load16(Qh + ((int64_t)my_row * p.q_sn + 32 * s + 8 * q) * 2);
-        qf[s] = __builtin_bit_cast(attn_i16x8, v);
+    for (int rs = 0; rs < 2; ++rs) {
+        my_row[rs] = w_row0 + 16 * rs + i16;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            u32x4 v = zero4();
+            if (my_row[rs] < Nq) v = load16(Qh + ((int64_t)my_row[rs] * p.q_sn + 32 * s + 8 * q) * 2);
+            v ^= p.qsign;
+            qf[rs][s] = __builtin_bit_cast(attn_i16x8, v);
+        }
     }
 
     // keys this workgroup needs: all, or (causal) up to its last row
     const int kmax = CAUSAL ? (q0 + BQ < Nk ? q0 + BQ : Nk) : Nk;
     const int nblocks = (kmax + BKV - 1) / BKV;
 
-    // global -> registers: chunk x of this thread is row (tid + 256 x) / CPR,
-    // chunk (tid + 256 x) % CPR of the block; zeros past Nk
-    u32x4 kr[LOADS], vr[LOADS];
-    auto load_block = [&](int kb) {
+    // global -> LDS without registers: buffer_load_dwordx4 ... lds writes the
+    // 16 bytes of lane l at LDS byte M0 + 16 l, so each lane loads the chunk
+    // that the swizzled layout puts at its position.  A buffer resource per
+    // block starts at the block's first key and ends at the head's last
+    // element, so keys past Nk read as zeros (range check).  K: 1 KiB block j
+    // holds d-step j / 4, keys 16 (j % 4) + l / 4, slot l % 4 = chunk
+    // (l % 4) ^ ((key / 2) % 4).  V: block j holds rows RPB j + l / LPR, slot
+    // l % LPR = 32-byte group (slot / 2) ^ f(row), half slot % 2.
+    constexpr int NKB = BKV * D * 2 / 1024;  // 1 KiB blocks of K (and of V) per key block
+    constexpr int PW = NKB / NW;              // of them per wave
+    static_assert(PW * NW == NKB, "");
+    constexpr int LPR = D / 8, RPB = 64 / LPR;  // V: lanes per row, rows per 1 KiB
+    const int smem_base = (int)(uintptr_t)(lds_void*)smem;
+    int voff_k[PW], voff_v[PW];
 #pragma unroll
-        for (int x = 0; x < LOADS; ++x) {
-            const int idx = tid + 256 * x, r = idx / CPR, c = idx % CPR;
-            const int key = kb * BKV + r;
-            kr[x] = key < Nk ? load16(Kh + ((int64_t)key * p.k_sn + 8 * c) * 2) : zero4();
-            vr[x] = key < Nk ? load16(Vh + ((int64_t)key * p.v_sn + 8 * c) * 2) : zero4();
+    for (int x = 0; x < PW; ++x) {
+        const int j = wave * PW + x;
+        {
+            const int s = j >> 2, key = 16 * (j & 3) + (lane >> 2);
+            const int chunk = (lane & 3) ^ ((key >> 1) & 3);
+            voff_k[x] = (int)((int64_t)key * p.k_sn * 2) + (32 * s + 8 * chunk) * 2;
         }
+        {
+            const int row = RPB * j + lane / LPR, slot = lane % LPR;
+            const int f = D == 128 ? (row & 7) : ((row >> 1) & 3);
+            voff_v[x] = (int)((int64_t)row * p.v_sn * 2) + ((slot >> 1) ^ f) * 32 + (slot & 1) * 16;
+        }
+    }
+    auto make_rsrc = [&](const char* base, int64_t bytes) __attribute__((always_inline)) {
+        const uint64_t a = (uint64_t)base;
+        const uint32_t n = bytes <= 0 ? 0u : bytes > 0xffffffffLL ? 0xffffffffu : (uint32_t)bytes;
+        return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+                     __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)),
+                     __builtin_amdgcn_readfirstlane((int)n), 0x00020000};
     };
-    // registers -> LDS (swizzled)
-    auto store_block = [&]() {
+    // issued through inline asm: the compiler then adds no waits for these
+    // loads before LDS reads; the kernel waits for them itself (vmcnt) before
+    // the barrier that publishes a buffer
+    auto dma = [&](int lds_addr, int vo, i32x4 rs) __attribute__((always_inline)) {
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                     :
+                     : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(vo), "s"(rs), "s"(0)
+                     : "memory");
+    };
+    auto issue_block = [&](int kb, int buf) __attribute__((always_inline)) {
+        const int64_t k_rows = (int64_t)kb * BKV;
+        const i32x4 rk = make_rsrc(Kh + k_rows * p.k_sn * 2, ((Nk - 1 - k_rows) * p.k_sn + D) * 2);
+        const i32x4 rv = make_rsrc(Vh + k_rows * p.v_sn * 2, ((Nk - 1 - k_rows) * p.v_sn + D) * 2);
+        const int base = smem_base + buf * BUF;
 #pragma unroll
-        for (int x = 0; x < LOADS; ++x) {
-            const int idx = tid + 256 * x, r = idx / CPR, c = idx % CPR;
-            // K: [d-step c/4][key r][chunk (c%4) ^ ((r/2)%4)]
-            *(lds_attn_u32x4*)(ks + (c >> 2) * (BKV * 64) + r * 64 + (((c & 3) ^ ((r >> 1) & 3)) * 16)) = kr[x];
-            // V: row r, 32-byte group (c/2) ^ f(r), half c % 2
-            const int f = D == 128 ? (r & 7) : ((r >> 1) & 3);
-            *(lds_attn_u32x4*)(vs + r * (D * 2) + (((c >> 1) ^ f) * 32) + (c & 1) * 16) = vr[x];
-        }
+        for (int x = 0; x < PW; ++x) dma(base + (wave * PW + x) * 1024, voff_k[x], rk);
+#pragma unroll
+        for (int x = 0; x < PW; ++x) dma(base + K_BYTES + (wave * PW + x) * 1024, voff_v[x], rv);
     };
 
-    // per-lane LDS bases of the fragment reads
-    // K fragment (keys 16 g + l%16, d-step s, chunk q): ks + s*4096 + (16 g + l%16)*64 + (q ^ key)*16
-    lds_attn_char* const kbase = ks + i16 * 64 + ((q ^ ((i16 >> 1) & 3)) * 16);
-    // V fragment (keys 32 t + 4 q + i/4 [+16], columns 16 db + 4 (i%4) ..): one base per column block
-    auto vaddr = [&](int t, int half, int db) __attribute__((always_inline)) {
+    // per-lane LDS offsets of the fragment reads (within a buffer)
+    // K fragment (keys 16 g + l%16, d-step s, chunk q): s*4096 + (16 g + l%16)*64 + (q ^ key)*16
+    const int koff = i16 * 64 + ((q ^ ((i16 >> 1) & 3)) * 16);
+    // V fragment (keys 32 t + 4 q + i/4 [+16], columns 16 db + 4 (i%4) ..)
+    auto voff = [&](int t, int half, int db) __attribute__((always_inline)) {
         const int r = 32 * t + 16 * half + 4 * q + (i16 >> 2);
         const int c = 4 * db + (i16 & 3);  // 8-byte unit of the row: 16 db + 4 (i%4) columns
         const int g = c >> 2, f = D == 128 ? (r & 7) : ((r >> 1) & 3);
-        return vs + r * (D * 2) + ((g ^ f) * 32) + (c & 3) * 8;
+        return K_BYTES + r * (D * 2) + ((g ^ f) * 32) + (c & 3) * 8;
     };
 
-    f32x4 o[DB];
+    f32x4 o[2][DB];
 #pragma unroll
-    for (int j = 0; j < DB; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.f;
-    const float sl2 = p.scale_log2e;
+    for (int rs = 0; rs < 2; ++rs)
+#pragma unroll
+        for (int j = 0; j < DB; ++j) o[rs][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run[2] = {-INFINITY, -INFINITY};  // reference point (scaled, log2 units) of the lane's row
+    // normaliser L = sum of the rounded probabilities, on the MFMA against a
+    // fragment of ones (every element of the result is the row's sum)
+    f32x4 lacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    const uint32_t one2 = IN == DT_F16 ? 0x3C003C00u : 0x3F803F80u;
+    const attn_i16x8 ones = __builtin_bit_cast(attn_i16x8, u32x4{one2, one2, one2, one2});
+    const float c = p.c;
 
-    if (nblocks > 0) load_block(0);
-    for (int kb = 0; kb < nblocks; ++kb) {
-        __syncthreads();  // every wave is done with the previous block's LDS
-        store_block();
-        __syncthreads();
-        if (kb + 1 < nblocks) load_block(kb + 1);  // in flight during this block
+    // one block: the next block's loads, S, the softmax, O += P V, then the
+    // barrier that publishes the next block.  MASKED: keys past Nk and (causal)
+    // keys past a row are hidden; compile-time variants in separate loops, so
+    // that the main loop carries no mask code and no merge of its registers.
+    auto block_step = [&](int kb, auto masked_t) __attribute__((always_inline)) {
+        constexpr bool MASKED = decltype(masked_t)::value;
+        // the next block into the other buffer (its readers finished before
+        // the previous barrier), landing while this one is computed
+        if (kb + 1 < nblocks) issue_block(kb + 1, (kb + 1) & 1);
+        lds_attn_char* const cur = lds + (kb & 1) * BUF;
+        const int key0 = kb * BKV;
 
-        // S = Q K^T for the 4 key groups of 16
-        f32x4 sc[4];
+        // S = Q K^T for the 4 key groups of 16, both row sets
+        f32x4 sc[2][4];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            sc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+            sc[0][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+            sc[1][g] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
                 const attn_i16x8 kf =
-                    __builtin_bit_cast(attn_i16x8, *(const lds_attn_u32x4*)(kbase + s * (BKV * 64) + g * 1024));
-                if constexpr (IN == DT_F16)
-                    sc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, kf),
-                                                                   __builtin_bit_cast(f16x8, qf[s]), sc[g], 0, 0, 0);
-                else
-                    sc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf),
-                                                                    __builtin_bit_cast(bf16x8, qf[s]), sc[g], 0, 0, 0);
+                    __builtin_bit_cast(attn_i16x8, *(const lds_attn_u32x4*)(cur + koff + s * (BKV * 64) + g * 1024));
+                sc[0][g] = attn_mfma<IN>(kf, qf[0][s], sc[0][g]);
+                sc[1][g] = attn_mfma<IN>(kf, qf[1][s], sc[1][g]);
             }
         }
-        // scale (in log2 units) and masks: key 16 g + 4 q + e of this block
-        float mx = -INFINITY;
+        // row maxima of this lane's scores (hidden ones -inf)
+        float mx[2];
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
+        for (int rs = 0; rs < 2; ++rs) {
+            mx[rs] = -INFINITY;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int key = kb * BKV + 16 * g + 4 * q + e;
-                bool hide = key >= Nk;
-                if constexpr (CAUSAL) hide = hide || key > my_row;
-                const float v = hide ? -INFINITY : sc[g][e] * sl2;
-                sc[g][e] = v;
-                mx = fmaxf(mx, v);
+            for (int g = 0; g < 4; ++g)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if constexpr (MASKED) {
+                        const int key = key0 + 16 * g + 4 * q + e;  // key of score e of group g
+                        bool hide = key >= Nk;
+                        if constexpr (CAUSAL) hide = hide || key > my_row[rs];
+                        sc[rs][g][e] = hide ? -INFINITY : sc[rs][g][e];
+                    }
+                    mx[rs] = fmaxf(mx[rs], sc[rs][g][e]);
+                }
+        }
+        // move the reference point when a score passes it by more than TH
+        float mxc[2];
+#pragma unroll
+        for (int rs = 0; rs < 2; ++rs) mxc[rs] = mx[rs] == -INFINITY ? -INFINITY : mx[rs] * c;
+        const bool up = mxc[0] > m_run[0] + TH || mxc[1] > m_run[1] + TH;
+        if (__builtin_amdgcn_ballot_w64(up) != 0) {
+#pragma unroll
+            for (int rs = 0; rs < 2; ++rs) {
+                float rm = mxc[rs];
+                rm = fmaxf(rm, __shfl_xor(rm, 16));
+                rm = fmaxf(rm, __shfl_xor(rm, 32));
+                const float m_new = fmaxf(m_run[rs], rm);
+                const float alpha = __builtin_amdgcn_exp2f(m_run[rs] - m_new);  // 0 on the first block
+                m_run[rs] = m_new;
+                // in place (tied asm operands): a plain multiply lets the
+                // register allocator keep a second copy of O for the path
+                // without rescaling and copy it every block
+#pragma unroll
+                for (int j = 0; j <= DB; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        float x = j < DB ? o[rs][j][e] : lacc[rs][e];
+                        asm volatile("v_mul_f32 %0, %0, %1" : "+v"(x) : "v"(alpha));
+                        if (j < DB) o[rs][j][e] = x;
+                        else lacc[rs][e] = x;
+                    }
             }
-        // row maximum over the 4 lanes of the row (lanes l, l ^ 16, l ^ 32, l ^ 48)
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;  // a row with nothing visible yet
-        const float alpha = exp2f(m_run - m_use);               // 0 while m_run = -inf
-        float rs = 0.f;
+        }
+        // p = 2^(c s - m); hidden entries -> 0
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
+        for (int rs = 0; rs < 2; ++rs) {
+            const float nm = -m_run[rs];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float pv = exp2f(sc[g][e] - m_use);
-                sc[g][e] = pv;
-                rs += pv;
-            }
-        rs += __shfl_xor(rs, 16);
-        rs += __shfl_xor(rs, 32);
-        l_run = l_run * alpha + rs;
-        m_run = m_new;
+            for (int g = 0; g < 4; ++g)
 #pragma unroll
-        for (int j = 0; j < DB; ++j) o[j] *= alpha;
+                for (int e = 0; e < 4; ++e) {
+                    const float sv = sc[rs][g][e];
+                    float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c, nm));
+                    if constexpr (MASKED) pv = sv == -INFINITY ? 0.f : pv;
+                    sc[rs][g][e] = pv;
+                }
+        }
 
         // O += P V, 32 keys at a time: P = this lane's keys 4q..4q+3 of
         // groups 2t and 2t+1
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            const uint32_t w0 = attn_pack2<IN>(sc[2 * t][0], sc[2 * t][1]);
-            const uint32_t w1 = attn_pack2<IN>(sc[2 * t][2], sc[2 * t][3]);
-            const uint32_t w2 = attn_pack2<IN>(sc[2 * t + 1][0], sc[2 * t + 1][1]);
-            const uint32_t w3 = attn_pack2<IN>(sc[2 * t + 1][2], sc[2 * t + 1][3]);
-            const attn_i16x8 pf = __builtin_bit_cast(attn_i16x8, u32x4{w0, w1, w2, w3});
+            attn_i16x8 pf[2];
+#pragma unroll
+            for (int rs = 0; rs < 2; ++rs) {
+                const uint32_t w0 = attn_pack2<IN>(sc[rs][2 * t][0], sc[rs][2 * t][1]);
+                const uint32_t w1 = attn_pack2<IN>(sc[rs][2 * t][2], sc[rs][2 * t][3]);
+                const uint32_t w2 = attn_pack2<IN>(sc[rs][2 * t + 1][0], sc[rs][2 * t + 1][1]);
+                const uint32_t w3 = attn_pack2<IN>(sc[rs][2 * t + 1][2], sc[rs][2 * t + 1][3]);
+                pf[rs] = __builtin_bit_cast(attn_i16x8, u32x4{w0, w1, w2, w3});
+            }
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                const attn_i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_attn_i16x4*)vaddr(t, 0, db));
-                const attn_i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_attn_i16x4*)vaddr(t, 1, db));
+                const attn_i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_attn_i16x4*)(cur + voff(t, 0, db)));
+                const attn_i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_attn_i16x4*)(cur + voff(t, 1, db)));
                 const attn_i16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                if constexpr (IN == DT_F16)
-                    o[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, vf),
-                                                                   __builtin_bit_cast(f16x8, pf), o[db], 0, 0, 0);
-                else
-                    o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf),
-                                                                    __builtin_bit_cast(bf16x8, pf), o[db], 0, 0, 0);
+                o[0][db] = attn_mfma<IN>(vf, pf[0], o[0][db]);
+                o[1][db] = attn_mfma<IN>(vf, pf[1], o[1][db]);
             }
+            lacc[0] = attn_mfma<IN>(ones, pf[0], lacc[0]);
+            lacc[1] = attn_mfma<IN>(ones, pf[1], lacc[1]);
         }
-    }
+        wait_vmcnt<0>();
+        __syncthreads();
+    };
 
-    // epilogue: O / l, row my_row, columns 16 db + 4 q .. +3
-    if (my_row < Nq) {
-        const float inv = 1.f / l_run;
-        constexpr int OB = OUT == DT_F32 ? 4 : 2;
-        char* orow = p.O + ((b * p.o_sb + h * p.o_sh) + (int64_t)my_row * p.o_sn) * OB;
+    // blocks that need no mask for any row of the workgroup: every key
+    // exists and (causal) is at most the tile's first row
+    int plain = Nk / BKV;
+    if (CAUSAL && (q0 + 1) / BKV < plain) plain = (q0 + 1) / BKV;
+    if (plain > nblocks) plain = nblocks;
+    if (nblocks > 0) {
+        issue_block(0, 0);
+        wait_vmcnt<0>();
+        __syncthreads();
+    }
+    int kb = 0;
+    for (; kb < plain; ++kb) block_step(kb, BoolTag<false>{});
+    for (; kb < nblocks; ++kb) block_step(kb, BoolTag<true>{});
+
+    // epilogue: O / L, row my_row, columns 16 db + 4 q .. +3
+    constexpr int OB = OUT == DT_F32 ? 4 : 2;
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-            store4<OUT>(orow + (16 * db + 4 * q) * OB, o[db][0] * inv, o[db][1] * inv, o[db][2] * inv,
-                        o[db][3] * inv, false);
+    for (int rs = 0; rs < 2; ++rs) {
+        const float l = lacc[rs][0];
+        if (my_row[rs] < Nq) {
+            const float inv = 1.f / l;
+            char* orow = p.O + ((b * p.o_sb + h * p.o_sh) + (int64_t)my_row[rs] * p.o_sn) * OB;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+                store4<OUT>(orow + (16 * db + 4 * q) * OB, o[rs][db][0] * inv, o[rs][db][1] * inv,
+                            o[rs][db][2] * inv, o[rs][db][3] * inv, false);
+        }
     }
 }
 
