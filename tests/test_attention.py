@@ -78,6 +78,19 @@ def test_attention_interleaved_heads_are_not_an_overlap():
     assert _call(H=2, os_=(512, 64, 128), o=FAKE + 8) == T.ERR_ALIAS
 
 
+def test_attention_workgroup_shape():
+    # 4 waves (128 query rows) while that gives every CU a workgroup, then 2, then 1
+    assert T.attention_waves(4, 16, 4096, 128) == 4
+    assert T.attention_waves(1, 256, 1, 64) == 4
+    assert T.attention_waves(1, 255, 128, 64) == 2
+    assert T.attention_waves(1, 12, 1024, 64) == 1
+    assert T.attention_waves(1, 1, 1, 64) == 1
+    assert T.attention_waves(1, 1, 1, 128) == 4   # head_dim 128: always 4
+    assert T.attention_waves(0, 1, 1, 64) == T.ERR_DIM
+    assert T.attention_waves(1, 1 << 20, 1, 64) == T.ERR_DIM
+    assert T.attention_waves(1, 1, 1, 96) == T.ERR_HEAD_DIM
+
+
 def test_attention_empty_problems_are_noops():
     # nothing to compute: success, even with NULL pointers and no keys
     assert _call(nq=0, nk=0, q=None, k=None, v=None, o=None) == T.OK
@@ -168,25 +181,32 @@ def _check(o, ref, bound, label):
 
 
 CASES = [
-    # B, H, n_q, n_k, d, in, out, scale, causal, layout, tail
-    (1, 2, 200, 300, 64, W.F16, W.F16, 0.125, False, "bhnd", 0),
-    (2, 1, 130, 130, 128, W.BF16, W.F32, 128 ** -0.5, True, "bhnd", 3),
-    (1, 1, 64, 64, 64, W.F16, W.F32, 1.0, True, "bhnd", 0),
-    (1, 3, 1, 1, 64, W.F16, W.F16, 1.0, False, "bhnd", 5),
-    (1, 2, 100, 40, 128, W.F16, W.F32, 0.1, True, "bnhd", 7),     # more queries than keys, causal
-    (1, 2, 40, 200, 64, W.BF16, W.BF16, 0.125, True, "bnhd", 0),  # fewer queries than keys, causal
-    (2, 2, 65, 1, 64, W.BF16, W.F32, 2.0, False, "bhnd", 64),     # one key: o = v_0
-    (1, 1, 257, 513, 128, W.F16, W.F16, 128 ** -0.5, False, "bnhd", 1),
-    (1, 4, 192, 192, 64, W.BF16, W.F32, 1.0, False, "bhnd", 0),   # the pages' unscaled softmax(QK^T)V
+    # B, H, n_q, n_k, d, in, out, scale, causal, layout, tail, waves per workgroup
+    (1, 2, 200, 300, 64, W.F16, W.F16, 0.125, False, "bhnd", 0, 1),
+    (2, 1, 130, 130, 128, W.BF16, W.F32, 128 ** -0.5, True, "bhnd", 3, 4),
+    (1, 1, 64, 64, 64, W.F16, W.F32, 1.0, True, "bhnd", 0, 1),
+    (1, 3, 1, 1, 64, W.F16, W.F16, 1.0, False, "bhnd", 5, 1),
+    (1, 2, 100, 40, 128, W.F16, W.F32, 0.1, True, "bnhd", 7, 4),     # more queries than keys, causal
+    (1, 2, 40, 200, 64, W.BF16, W.BF16, 0.125, True, "bnhd", 0, 1),  # fewer queries than keys, causal
+    (2, 2, 65, 1, 64, W.BF16, W.F32, 2.0, False, "bhnd", 64, 1),     # one key: o = v_0
+    (1, 1, 257, 513, 128, W.F16, W.F16, 128 ** -0.5, False, "bnhd", 1, 4),
+    (1, 4, 192, 192, 64, W.BF16, W.F32, 1.0, False, "bhnd", 0, 1),   # the pages' unscaled softmax(QK^T)V
+    (1, 4, 130, 140, 64, W.F16, W.F32, -0.3, False, "bhnd", 0, 1),   # negative scale
+    (1, 130, 100, 77, 128, W.F16, W.F16, 0.2, True, "bhnd", 0, 4),   # head_dim 128: always 4 waves
+    (1, 130, 100, 77, 64, W.F16, W.F16, 0.2, True, "bhnd", 0, 2),
+    (2, 65, 100, 300, 64, W.BF16, W.BF16, 0.125, False, "bnhd", 1, 2),
+    (1, 256, 65, 70, 64, W.F16, W.F16, 0.125, True, "bhnd", 0, 4),
+    (2, 128, 130, 129, 128, W.BF16, W.F32, 128 ** -0.5, False, "bnhd", 2, 4),
 ]
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("case", CASES, ids=lambda c: "b%d_h%d_q%d_k%d_d%d_in%d_out%d_%s%s" % (
-    c[0], c[1], c[2], c[3], c[4], c[5], c[6], "causal" if c[8] else "full", "_" + c[9]))
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "b%d_h%d_q%d_k%d_d%d_in%d_out%d_%s%s_w%d" % (
+    c[0], c[1], c[2], c[3], c[4], c[5], c[6], "causal" if c[8] else "full", "_" + c[9], c[11]))
 def test_attention_parity_full(case):
     from gpu_helpers import say
-    B, H, nq, nk, d, dt, out, scale, causal, layout, tail = case
+    B, H, nq, nk, d, dt, out, scale, causal, layout, tail, waves = case
+    assert T.attention_waves(B, H, nq, d) == waves  # the case runs the workgroup shape it is meant to cover
     say(f"[attention] case {case}")
     q, k, v = W.attention_inputs(B, H, nq, nk, d, dt, seed=1000 + nq + nk + d)
     o, untouched = _run(q, k, v, dt, out, scale, causal, layout, tail)

@@ -30,7 +30,7 @@ ERR_HEAD_DIM = -9
 
 EXPORTED = ["gemm", "gemm_ex", "gemm_t", "gemm_fused", "gemm_strerror", "gemm_num_configs", "gemm_config_info",
             "gemm_select_config", "gemm_select_kernel", "gemm_select_kernel_t", "gemm_tile_map", "gemm_version",
-            "attention_fwd"]
+            "attention_fwd", "attention_waves"]
 
 # operand layouts (gemm_t)
 ROW_MAJOR, COL_MAJOR = 0, 1
@@ -110,6 +110,8 @@ def lib():
     s3 = ctypes.POINTER(i64)
     L.attention_fwd.restype = i
     L.attention_fwd.argtypes = [i64, i64, i64, i64, i64, p, s3, p, s3, p, s3, p, s3, i, i, ctypes.c_float, i, p]
+    L.attention_waves.restype = i
+    L.attention_waves.argtypes = [i64, i64, i64, i64]
     _lib = L
     return L
 
@@ -195,6 +197,11 @@ def attention_fwd(B, H, n_q, n_k, d, Q, q_stride, K, k_stride, V, v_stride, O, o
     return lib().attention_fwd(B, H, n_q, n_k, d, Q, _strides(q_stride), K, _strides(k_stride), V,
                                _strides(v_stride), O, _strides(o_stride), in_dtype, out_dtype, float(scale),
                                int(bool(causal)), stream)
+
+
+def attention_waves(B, H, n_q, d):
+    """Waves per workgroup that attention_fwd launches (4, 2 or 1)."""
+    return lib().attention_waves(B, H, n_q, d)
 
 
 # ------------------------------------------------------------ torch marshalling

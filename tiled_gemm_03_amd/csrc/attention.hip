@@ -14,19 +14,48 @@ namespace {
 
 typedef void (*AttnFn)(AttnArgs);
 
-// waves per workgroup (32 query rows each)
-constexpr int kWaves = 4;
-
-template <int D, int IN, bool CAUSAL>
+template <int D, int IN, bool CAUSAL, int NW>
 AttnFn attn_pick_out(int out) {
-    if (out == DT_F32) return attention_kernel<D, IN, DT_F32, CAUSAL, kWaves>;
-    return attention_kernel<D, IN, IN, CAUSAL, kWaves>;
+    if (out == DT_F32) return attention_kernel<D, IN, DT_F32, CAUSAL, NW>;
+    return attention_kernel<D, IN, IN, CAUSAL, NW>;
 }
 
-template <int D>
-AttnFn attn_pick(int in, int out, bool causal) {
-    if (in == DT_F16) return causal ? attn_pick_out<D, DT_F16, true>(out) : attn_pick_out<D, DT_F16, false>(out);
-    return causal ? attn_pick_out<D, DT_BF16, true>(out) : attn_pick_out<D, DT_BF16, false>(out);
+template <int D, int NW>
+AttnFn attn_pick_nw(int in, int out, bool causal) {
+    if (in == DT_F16)
+        return causal ? attn_pick_out<D, DT_F16, true, NW>(out) : attn_pick_out<D, DT_F16, false, NW>(out);
+    return causal ? attn_pick_out<D, DT_BF16, true, NW>(out) : attn_pick_out<D, DT_BF16, false, NW>(out);
+}
+
+AttnFn attn_pick(int d, int nw, int in, int out, bool causal, int& lds) {
+    if (d == 128) {
+        lds = attn_lds_bytes<128, 4>();
+        return attn_pick_nw<128, 4>(in, out, causal);
+    }
+    if (nw == 4) {
+        lds = attn_lds_bytes<64, 4>();
+        return attn_pick_nw<64, 4>(in, out, causal);
+    }
+    if (nw == 2) {
+        lds = attn_lds_bytes<64, 2>();
+        return attn_pick_nw<64, 2>(in, out, causal);
+    }
+    lds = attn_lds_bytes<64, 1>();
+    return attn_pick_nw<64, 1>(in, out, causal);
+}
+
+int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Waves per workgroup (32 query rows each): 4 unless that leaves CUs idle
+// (fewer workgroups than the 256 CUs), then 2, then 1; head dimension 128
+// always 4 (its 64 KiB of LDS would hold a smaller workgroup to one wave per
+// SIMD, and the compiler then moves the accumulators through AGPRs).
+int waves_for(int64_t batch, int64_t heads, int64_t n_q, int64_t d) {
+    const int64_t bh = batch * heads;
+    if (d == 128) return 4;
+    if (bh * ceil_div64(n_q, 128) >= 256) return 4;
+    if (bh * ceil_div64(n_q, 64) >= 256) return 2;
+    return 1;
 }
 
 struct Tensor4 {
@@ -124,7 +153,8 @@ int attention_fwd(int64_t batch, int64_t heads, int64_t n_q, int64_t n_k, int64_
     a.Nq = (int)n_q;
     a.Nk = (int)n_k;
     a.H = (int)heads;
-    const int64_t bq = 32 * kWaves;
+    const int nw = waves_for(batch, heads, n_q, d);
+    const int64_t bq = 32 * nw;
     const int64_t tiles = (n_q + bq - 1) / bq;
     if (batch * heads * tiles >= ((int64_t)1 << 24)) return TGEMM_ERR_DIM;  // grid limit
     a.tiles = (int)tiles;
@@ -133,9 +163,17 @@ int attention_fwd(int64_t batch, int64_t heads, int64_t n_q, int64_t n_k, int64_
     a.qsign = scale < 0.f ? 0x80008000u : 0u;
     const int in = in_dtype == TGEMM_F16 ? DT_F16 : DT_BF16;
     const int out = out_dtype == TGEMM_F32 ? DT_F32 : in;
-    const AttnFn fn = d == 64 ? attn_pick<64>(in, out, causal != 0) : attn_pick<128>(in, out, causal != 0);
-    hipLaunchKernelGGL(fn, dim3((unsigned)a.total), dim3(64 * kWaves), 0, (hipStream_t)stream, a);
+    int lds = 0;
+    const AttnFn fn = attn_pick((int)d, nw, in, out, causal != 0, lds);
+    hipLaunchKernelGGL(fn, dim3((unsigned)a.total), dim3(64 * nw), (unsigned)lds, (hipStream_t)stream, a);
     return (int)hipGetLastError();
+}
+
+int attention_waves(int64_t batch, int64_t heads, int64_t n_q, int64_t head_dim) {
+    if (batch <= 0 || heads <= 0 || n_q <= 0 || batch > 65535 || heads > 65535 || n_q > TGEMM_MAX_DIM)
+        return TGEMM_ERR_DIM;
+    if (head_dim != 64 && head_dim != 128) return TGEMM_ERR_HEAD_DIM;
+    return waves_for(batch, heads, n_q, head_dim);
 }
 
 }  // extern "C"

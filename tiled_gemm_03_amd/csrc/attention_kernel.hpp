@@ -13,13 +13,9 @@
 //                  lane l holds S[row l % 16][keys 4 (l/16) .. +3] of each
 //                  16-key group (Q stays in registers for the whole loop);
 //   online softmax in fp32 with exp2 (c = |scale| log2 e; a negative scale
-//                  flips the signs of Q, which is exact): p = 2^(c s - m).
-//                  The reference point m of a row moves only when a score
-//                  exceeds it by more than 2^8 (then m := the row maximum,
-//                  O and L scaled by 2^(m_old - m)); in between p <= 2^8 and
-//                  O, L keep accumulating against the old m.  The result
-//                  O / L does not depend on m; p stays within the input
-//                  type's range.  L is the sum of the probabilities as
+//                  flips the signs of Q, which is exact): p = 2^(c s - m)
+//                  with m the running row maximum; O and L are scaled by
+//                  2^(m_old - m) every block.  L is the sum of the probabilities as
 //                  rounded for the product with V (so the weights sum to 1
 //                  exactly), accumulated on the MFMA against ones;
 //   O += P V       the same MFMA with V (first operand) and P (second).  The
@@ -28,9 +24,9 @@
 //                  from the S registers straight into the MFMA; V is read in
 //                  that key order with two transposing LDS reads (4 key rows
 //                  each).
-// K and V blocks go global -> LDS directly (no registers) through two LDS
-// buffers: block j + 1 lands while block j is computed, one barrier per
-// block.  LDS layouts (XOR swizzles, as the
+// K and V blocks go global -> LDS directly (no registers) through a ring of
+// LDS buffers (2, or 4 for workgroups of 1 or 2 waves): the next blocks land
+// while block j is computed, one barrier per block.  LDS layouts (XOR swizzles, as the
 // matrix-product kernels): K as [d / 32][64 keys][64 bytes] with chunk
 // c ^ ((key / 2) % 4) (a K fragment read is the conflict-free read of the
 // k-contiguous ring stage); V as [64 keys][d] with its 32-byte groups of row
@@ -99,6 +95,10 @@ __device__ __forceinline__ void attn_tile_of(int g, int total, int tiles, bool r
     if (reverse) qt = tiles - 1 - qt;
 }
 
+// LDS bytes of a workgroup: NBUF buffers of 64 keys of K and of V.
+template <int D, int NW>
+constexpr int attn_lds_bytes() { return (NW == 4 ? 2 : 4) * 2 * 64 * D * 2; }
+
 // D: head dimension (64 or 128); IN: DT_F16 / DT_BF16; OUT: IN or DT_F32;
 // NW: waves per workgroup (32 NW query rows).
 template <int D, int IN, int OUT, bool CAUSAL, int NW>
@@ -113,8 +113,17 @@ void attention_kernel(AttnArgs p) {
     constexpr int LOADS = BKV * CPR / NT;   // chunks of K (and of V) per thread and block
     static_assert(LOADS * NT == BKV * CPR, "");
     constexpr int K_BYTES = BKV * D * 2, V_BYTES = BKV * D * 2, BUF = K_BYTES + V_BYTES;
+    // LDS buffers: blocks j + 1 .. j + NBUF - 1 in flight while block j is
+    // computed; 4 for the small workgroups (few waves per CU to hide the
+    // latency of a load), 2 for 4 waves
+    constexpr int NBUF = NW == 4 ? 2 : 4;
+    static_assert(NBUF * BUF == attn_lds_bytes<D, NW>(), "");
     constexpr float TH = 8.f;               // reference-point slack (log2 units)
-    __shared__ __attribute__((aligned(1024))) char smem[2 * BUF];
+    // dynamic LDS of attn_lds_bytes<D, NW>() bytes (declared at launch: a
+    // static array this size would make the compiler budget registers for
+    // the one wave per SIMD that it leaves room for, and move the
+    // accumulators through AGPRs)
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
     lds_attn_char* const lds = (lds_attn_char*)smem;
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -234,10 +243,10 @@ void attention_kernel(AttnArgs p) {
     // that the main loop carries no mask code and no merge of its registers.
     auto block_step = [&](int kb, auto masked_t) __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(masked_t)::value;
-        // the next block into the other buffer (its readers finished before
-        // the previous barrier), landing while this one is computed
-        if (kb + 1 < nblocks) issue_block(kb + 1, (kb + 1) & 1);
-        lds_attn_char* const cur = lds + (kb & 1) * BUF;
+        // block kb + NBUF - 1 into the buffer that block kb - 1 used (its
+        // readers finished before the previous barrier)
+        if (kb + NBUF - 1 < nblocks) issue_block(kb + NBUF - 1, (kb + NBUF - 1) % NBUF);
+        lds_attn_char* const cur = lds + (kb % NBUF) * BUF;
         const int key0 = kb * BKV;
 
         // S = Q K^T for the 4 key groups of 16, both row sets
@@ -278,6 +287,9 @@ void attention_kernel(AttnArgs p) {
         for (int rs = 0; rs < 2; ++rs) mxc[rs] = mx[rs] == -INFINITY ? -INFINITY : mx[rs] * c;
         const bool up = mxc[0] > m_run[0] + TH || mxc[1] > m_run[1] + TH;
         if (__builtin_amdgcn_ballot_w64(up) != 0) {
+            // a real branch (the volatile no-op cannot be speculated): the
+            // rescale runs only when the reference point moves
+            asm volatile("s_nop 0");
 #pragma unroll
             for (int rs = 0; rs < 2; ++rs) {
                 float rm = mxc[rs];
@@ -286,18 +298,9 @@ void attention_kernel(AttnArgs p) {
                 const float m_new = fmaxf(m_run[rs], rm);
                 const float alpha = __builtin_amdgcn_exp2f(m_run[rs] - m_new);  // 0 on the first block
                 m_run[rs] = m_new;
-                // in place (tied asm operands): a plain multiply lets the
-                // register allocator keep a second copy of O for the path
-                // without rescaling and copy it every block
 #pragma unroll
-                for (int j = 0; j <= DB; ++j)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        float x = j < DB ? o[rs][j][e] : lacc[rs][e];
-                        asm volatile("v_mul_f32 %0, %0, %1" : "+v"(x) : "v"(alpha));
-                        if (j < DB) o[rs][j][e] = x;
-                        else lacc[rs][e] = x;
-                    }
+                for (int j = 0; j < DB; ++j) o[rs][j] *= alpha;
+                lacc[rs] *= alpha;
             }
         }
         // p = 2^(c s - m); hidden entries -> 0
@@ -339,7 +342,12 @@ void attention_kernel(AttnArgs p) {
             lacc[0] = attn_mfma<IN>(ones, pf[0], lacc[0]);
             lacc[1] = attn_mfma<IN>(ones, pf[1], lacc[1]);
         }
-        wait_vmcnt<0>();
+        // block kb + 1 has landed: later blocks' loads may still be in flight
+        // (2 PW per block, in issue order), all of them at the tail
+        if (kb + NBUF - 1 < nblocks)
+            wait_vmcnt<(NBUF - 2) * 2 * PW>();
+        else
+            wait_vmcnt<0>();
         __syncthreads();
     };
 
@@ -349,8 +357,13 @@ void attention_kernel(AttnArgs p) {
     if (CAUSAL && (q0 + 1) / BKV < plain) plain = (q0 + 1) / BKV;
     if (plain > nblocks) plain = nblocks;
     if (nblocks > 0) {
-        issue_block(0, 0);
-        wait_vmcnt<0>();
+#pragma unroll
+        for (int j = 0; j < NBUF - 1; ++j)
+            if (j < nblocks) issue_block(j, j);
+        if (NBUF - 1 <= nblocks)
+            wait_vmcnt<(NBUF - 2) * 2 * PW>();  // block 0 has landed
+        else
+            wait_vmcnt<0>();
         __syncthreads();
     }
     int kb = 0;
