@@ -13,7 +13,10 @@ Printed: ONE JSON line with the contract's keys plus
                 null;
   cpu_baseline  the oracle (test infrastructure) timed on this host on a
                 bounded sample of the same workload (whole rows of C);
-  per_config    the four smaller workloads, each timed the same way (context).
+  per_config    the four smaller workloads, each timed the same way (context);
+  attention     the attention forward on its workloads (the sequence of page
+                "TileLang实战" §4.3 and a long-sequence case), timed the same
+                way, with torch's scaled_dot_product_attention as context.
 """
 import argparse
 import hashlib
@@ -114,6 +117,7 @@ def main():
     ap.add_argument("--config", type=int, default=-1, help="force a tile configuration (gemm_ex)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-config", action="store_true")
+    ap.add_argument("--no-attention", action="store_true")
     ap.add_argument("--mfma-ceiling", action="store_true",
                     help="only run the MFMA ceiling program (issue rate and clock of both fp16 MFMA shapes on "
                          "every SIMD, N(0,1) and all-ones operands) and print its JSON lines")
@@ -251,6 +255,41 @@ def main():
             fused.append({"epilogue": name, "us_median": med * 1e3, "tflops": flops / (med * 1e-3) / 1e12})
         del bias
 
+    # the attention forward (attention_fwd) on its workloads: O = softmax(scale
+    # Q K^T) V per head, fp16, inputs resident; FLOPs of the two products over
+    # the visible (query, key) pairs, HBM bytes of Q, K, V and O once
+    attention = []
+    if not args.no_attention:
+        for aw in W.ATTN_WORKLOADS:
+            g = torch.Generator(device="cpu").manual_seed(11)
+            shape = (aw.B, aw.H, aw.N, aw.d)
+            q_ = torch.randn(shape, generator=g).half().to(dev)
+            k_ = torch.randn(shape, generator=g).half().to(dev)
+            v_ = torch.randn(shape, generator=g).half().to(dev)
+            o_ = torch.empty_like(q_)
+            call = lambda: T.attention_tensors(q_, k_, v_, o_, scale=aw.scale, causal=aw.causal,
+                                               stream=stream.cuda_stream)
+            reps = 200 if aw.N <= 1024 else 20
+            _, aev = time_calls(call, reps, max(3, reps // 10), stream)
+            med = float(np.median(aev))
+            af = aw.flops()
+            abytes = 4 * aw.B * aw.H * aw.N * aw.d * 2
+            entry = {"workload": aw.name, "B": aw.B, "H": aw.H, "N": aw.N, "d": aw.d, "causal": aw.causal,
+                     "scale": aw.scale, "waves_per_workgroup": T.attention_waves(aw.B, aw.H, aw.N, aw.d),
+                     "us_median": med * 1e3, "tflops": af / (med * 1e-3) / 1e12,
+                     "frac_of_mfma_peak": af / (med * 1e-3) / 1e12 / PEAK_F16_TFLOPS,
+                     "gbs": abytes / (med * 1e-3) / 1e9, "algorithmic_flop": af, "algorithmic_bytes": abytes}
+            # context: torch's own scaled_dot_product_attention on the same tensors
+            sdpa = lambda: torch.nn.functional.scaled_dot_product_attention(q_, k_, v_, is_causal=aw.causal,
+                                                                            scale=aw.scale)
+            try:
+                _, sev = time_calls(sdpa, reps, max(3, reps // 10), stream)
+                entry["torch_sdpa_us_median"] = float(np.median(sev)) * 1e3
+            except Exception as e:  # noqa: BLE001 - context only
+                entry["torch_sdpa_us_median"] = None
+            attention.append(entry)
+            del q_, k_, v_, o_
+
     if args.calibrate_copy:
         src = torch.ones(128 << 20, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -285,6 +324,7 @@ def main():
         "per_config": per_config,
         "layouts_8192": layouts,
         "fused_8192": fused,
+        "attention": attention,
         "sclk": sclk_mhz(),
         "kernel_source_hash": kernel_source_hash(),
     }

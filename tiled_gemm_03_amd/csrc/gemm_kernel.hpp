@@ -266,34 +266,79 @@ __device__ __forceinline__ float load_value(const char* p, int64_t i, int dt) {
 
 // relu(x) = max(x, 0); gelu(x) = x Phi(x) = x/2 (1 + erf(x / sqrt 2));
 // gelu_tanh(x) = x/2 (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))) (the tanh
-// approximation of gelu); silu(x) = x / (1 + exp(-x)).
+// approximation of gelu); silu(x) = x / (1 + exp(-x)).  Since
+// (1 + tanh u) / 2 = 1 / (1 + exp(-2u)), gelu_tanh and silu are both x times
+// a logistic function, evaluated with the hardware exp2 and reciprocal
+// (a few ulp; exp2 overflowing to +inf gives the limit 0).
+__device__ __forceinline__ float logistic_times(float x, float z) {  // x / (1 + exp(-z))
+    return x * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
+}
 __device__ __forceinline__ float activate(float x, int act) {
     switch (act) {
         case ACT_RELU: return x > 0.f ? x : 0.f;
         case ACT_GELU: return 0.5f * x * (1.f + erff(x * 0.70710678118654752f));
-        case ACT_GELU_TANH: return 0.5f * x * (1.f + tanhf(0.79788456080286536f * (x + 0.044715f * x * x * x)));
-        case ACT_SILU: return x / (1.f + expf(-x));
+        case ACT_GELU_TANH: return logistic_times(x, 1.5957691216057308f * (x + 0.044715f * x * x * x));
+        case ACT_SILU: return logistic_times(x, x);
         default: return x;
     }
 }
 
-// Four consecutive outputs C[row][col .. col + 3], of which the first n lie
-// inside C, through the epilogue and stored (vec: 4-element vector store).
+// Four consecutive elements of type dt from any element-aligned address, as
+// fp32 (one load: unaligned-access mode).
+__device__ __forceinline__ f32x4 load4_values(const char* p, int dt) {
+    if (dt == DT_F32) {
+        f32x4 v;
+        __builtin_memcpy(&v, p, 16);
+        return v;
+    }
+    // one 64-bit scalar split by shifts: a memcpy into a two-dword vector
+    // followed by an element read loads only the first dword (hipcc 7.2)
+    uint64_t w;
+    __builtin_memcpy(&w, p, 8);
+    const uint32_t lo = (uint32_t)w, hi = (uint32_t)(w >> 32);
+    if (dt == DT_F16) {
+        const f16x2 a = __builtin_bit_cast(f16x2, lo), b = __builtin_bit_cast(f16x2, hi);
+        return f32x4{(float)a[0], (float)a[1], (float)b[0], (float)b[1]};
+    }
+    const bf16x2 a = __builtin_bit_cast(bf16x2, lo), b = __builtin_bit_cast(bf16x2, hi);
+    return f32x4{(float)a[0], (float)a[1], (float)b[0], (float)b[1]};
+}
+
+// The epilogue of four consecutive outputs C[row][col .. col + 3], of which
+// the first n (> 0) lie inside C, in two halves: fused_pre forms
+// alpha * AB + beta * C + bias (whole groups with one load of C and one of
+// the bias), fused_post applies the activation and stores (vec: 4-element
+// vector store).  Kernels with many groups per lane run the first half for
+// a whole batch of groups before the second, so that the loads of the batch
+// are in flight together.
 template <int OUT>
-__device__ __forceinline__ void store4_fused(const GemmArgs& p, int row, int col, int n, bool vec, f32x4 v) {
+__device__ __forceinline__ f32x4 fused_pre(const GemmArgs& p, int row, int col, int n, f32x4 v) {
+    constexpr int OB = OUT == DT_F32 ? 4 : 2;
+    const char* src = p.C + ((int64_t)row * p.ldc + col) * OB;
+    const int beb = p.bias_dt == DT_F32 ? 4 : 2;
+    f32x4 t = v * p.alpha;
+    if (n == 4) {
+        if (p.beta != 0.f) t += p.beta * load4_values(src, OUT);
+        if (p.bias_kind == BIAS_COL) t += load4_values(p.bias + (int64_t)col * beb, p.bias_dt);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 3; ++e) {
+            if (e >= n) break;
+            if (p.beta != 0.f) t[e] += p.beta * load_value(src, e, OUT);
+            if (p.bias_kind == BIAS_COL) t[e] += load_value(p.bias, col + e, p.bias_dt);
+        }
+    }
+    if (p.bias_kind == BIAS_ROW) t += load_value(p.bias, row, p.bias_dt);
+    return t;
+}
+
+template <int OUT>
+__device__ __forceinline__ void fused_post(const GemmArgs& p, int row, int col, int n, bool vec, f32x4 t) {
     constexpr int OB = OUT == DT_F32 ? 4 : 2;
     char* dst = p.C + ((int64_t)row * p.ldc + col) * OB;
-    float o[4] = {v[0], v[1], v[2], v[3]};
-    const float brow = p.bias_kind == BIAS_ROW ? load_value(p.bias, row, p.bias_dt) : 0.f;
+    float o[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        if (e >= n) break;
-        float t = p.alpha * o[e];
-        if (p.beta != 0.f) t += p.beta * load_value(dst, e, OUT);
-        if (p.bias_kind == BIAS_ROW) t += brow;
-        else if (p.bias_kind == BIAS_COL) t += load_value(p.bias, col + e, p.bias_dt);
-        o[e] = activate(t, p.act);
-    }
+    for (int e = 0; e < 4; ++e) o[e] = activate(t[e], p.act);
     if (n == 4) {
         store4<OUT>(dst, o[0], o[1], o[2], o[3], vec);
     } else {
@@ -303,11 +348,17 @@ __device__ __forceinline__ void store4_fused(const GemmArgs& p, int row, int col
     }
 }
 
+template <int OUT>
+__device__ __forceinline__ void store4_fused(const GemmArgs& p, int row, int col, int n, bool vec, f32x4 v) {
+    fused_post<OUT>(p, row, col, n, vec, fused_pre<OUT>(p, row, col, n, v));
+}
+
 // The fused epilogue of a wave's NB accumulator blocks of VPL fp32 values
 // per lane (VPL / 4 groups of 4 consecutive columns), through this wave's
-// LDS region (PB blocks at a time): the blocks are written out with
-// compile-time register indices, then read back in a run-time loop that
-// holds one copy of the epilogue code.  get(IntTag<b>): block b's values;
+// LDS region (PB blocks at a time): the blocks go through fused_pre with
+// compile-time register indices (every load of C and of the bias of the
+// pass issued together) into the region, then are read back in a run-time
+// loop that holds one copy of the activation code.  get(IntTag<b>): block b's values;
 // where(b, g, row, col, n, vec): the output position of group g of block b
 // (n = 0: nothing to store).  The caller has made sure that no wave still
 // reads the LDS it reuses.
@@ -325,8 +376,11 @@ __device__ __forceinline__ void fused_epilogue(const GemmArgs& p, lds_f32x4* reg
             const auto blk = get(IntTag<b0 + t>{});
             static_for<0, VPL / 4>([&](auto g_t) {
                 constexpr int g = decltype(g_t)::value;
-                region[(t * 64 + lane) * (VPL / 4) + g] =
-                    f32x4{blk[4 * g + 0], blk[4 * g + 1], blk[4 * g + 2], blk[4 * g + 3]};
+                int row, col, n;
+                bool vec;
+                where(b0 + t, g, row, col, n, vec);
+                const f32x4 v = f32x4{blk[4 * g + 0], blk[4 * g + 1], blk[4 * g + 2], blk[4 * g + 3]};
+                region[(t * 64 + lane) * (VPL / 4) + g] = n > 0 ? fused_pre<OUT>(p, row, col, n, v) : v;
             });
         });
         for (int t = 0; t < PB; ++t)
@@ -334,7 +388,7 @@ __device__ __forceinline__ void fused_epilogue(const GemmArgs& p, lds_f32x4* reg
                 int row, col, n;
                 bool vec;
                 where(b0 + t, g, row, col, n, vec);
-                if (n > 0) store4_fused<OUT>(p, row, col, n, vec, region[(t * 64 + lane) * (VPL / 4) + g]);
+                if (n > 0) fused_post<OUT>(p, row, col, n, vec, region[(t * 64 + lane) * (VPL / 4) + g]);
             }
     });
 }
