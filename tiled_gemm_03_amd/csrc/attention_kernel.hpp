@@ -24,9 +24,9 @@
 //                  from the S registers straight into the MFMA; V is read in
 //                  that key order with two transposing LDS reads (4 key rows
 //                  each).
-// K and V blocks go global -> LDS directly (no registers) through a ring of
-// LDS buffers (2, or 4 for workgroups of 1 or 2 waves): the next blocks land
-// while block j is computed, one barrier per block.  LDS layouts (XOR swizzles, as the
+// K and V blocks go global -> LDS directly (no registers) into rings of two
+// LDS slots each, K two blocks ahead and V one (S of the next block is
+// computed during this block's softmax), one barrier per block.  LDS layouts (XOR swizzles, as the
 // matrix-product kernels): K as [d / 32][64 keys][64 bytes] with chunk
 // c ^ ((key / 2) % 4) (a K fragment read is the conflict-free read of the
 // k-contiguous ring stage); V as [64 keys][d] with its 32-byte groups of row
@@ -95,9 +95,9 @@ __device__ __forceinline__ void attn_tile_of(int g, int total, int tiles, bool r
     if (reverse) qt = tiles - 1 - qt;
 }
 
-// LDS bytes of a workgroup: NBUF buffers of 64 keys of K and of V.
+// LDS bytes of a workgroup: two blocks of 64 keys of K and two of V.
 template <int D, int NW>
-constexpr int attn_lds_bytes() { return (NW == 4 ? 2 : 4) * 2 * 64 * D * 2; }
+constexpr int attn_lds_bytes() { return 4 * 64 * D * 2; }
 
 // D: head dimension (64 or 128); IN: DT_F16 / DT_BF16; OUT: IN or DT_F32;
 // NW: waves per workgroup (32 NW query rows).
@@ -113,11 +113,7 @@ void attention_kernel(AttnArgs p) {
     constexpr int LOADS = BKV * CPR / NT;   // chunks of K (and of V) per thread and block
     static_assert(LOADS * NT == BKV * CPR, "");
     constexpr int K_BYTES = BKV * D * 2, V_BYTES = BKV * D * 2, BUF = K_BYTES + V_BYTES;
-    // LDS buffers: blocks j + 1 .. j + NBUF - 1 in flight while block j is
-    // computed; 4 for the small workgroups (few waves per CU to hide the
-    // latency of a load), 2 for 4 waves
-    constexpr int NBUF = NW == 4 ? 2 : 4;
-    static_assert(NBUF * BUF == attn_lds_bytes<D, NW>(), "");
+    static_assert(2 * BUF == attn_lds_bytes<D, NW>(), "");
     constexpr float TH = 8.f;               // reference-point slack (log2 units)
     // dynamic LDS of attn_lds_bytes<D, NW>() bytes (declared at launch: a
     // static array this size would make the compiler budget registers for
@@ -202,18 +198,24 @@ void attention_kernel(AttnArgs p) {
                      : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(vo), "s"(rs), "s"(0)
                      : "memory");
     };
-    auto issue_block = [&](int kb, int buf) __attribute__((always_inline)) {
+    // LDS: K of blocks j, j + 1 at (j % 2) K_BYTES, V of blocks j, j + 1 at
+    // 2 K_BYTES + (j % 2) V_BYTES
+    auto issue_k = [&](int kb) __attribute__((always_inline)) {
         const int64_t k_rows = (int64_t)kb * BKV;
         const i32x4 rk = make_rsrc(Kh + k_rows * p.k_sn * 2, ((Nk - 1 - k_rows) * p.k_sn + D) * 2);
-        const i32x4 rv = make_rsrc(Vh + k_rows * p.v_sn * 2, ((Nk - 1 - k_rows) * p.v_sn + D) * 2);
-        const int base = smem_base + buf * BUF;
+        const int base = smem_base + (kb & 1) * K_BYTES;
 #pragma unroll
         for (int x = 0; x < PW; ++x) dma(base + (wave * PW + x) * 1024, voff_k[x], rk);
+    };
+    auto issue_v = [&](int kb) __attribute__((always_inline)) {
+        const int64_t k_rows = (int64_t)kb * BKV;
+        const i32x4 rv = make_rsrc(Vh + k_rows * p.v_sn * 2, ((Nk - 1 - k_rows) * p.v_sn + D) * 2);
+        const int base = smem_base + 2 * K_BYTES + (kb & 1) * V_BYTES;
 #pragma unroll
-        for (int x = 0; x < PW; ++x) dma(base + K_BYTES + (wave * PW + x) * 1024, voff_v[x], rv);
+        for (int x = 0; x < PW; ++x) dma(base + (wave * PW + x) * 1024, voff_v[x], rv);
     };
 
-    // per-lane LDS offsets of the fragment reads (within a buffer)
+    // per-lane LDS offsets of the fragment reads (within a block's K or V)
     // K fragment (keys 16 g + l%16, d-step s, chunk q): s*4096 + (16 g + l%16)*64 + (q ^ key)*16
     const int koff = i16 * 64 + ((q ^ ((i16 >> 1) & 3)) * 16);
     // V fragment (keys 32 t + 4 q + i/4 [+16], columns 16 db + 4 (i%4) ..)
@@ -221,7 +223,7 @@ void attention_kernel(AttnArgs p) {
         const int r = 32 * t + 16 * half + 4 * q + (i16 >> 2);
         const int c = 4 * db + (i16 & 3);  // 8-byte unit of the row: 16 db + 4 (i%4) columns
         const int g = c >> 2, f = D == 128 ? (r & 7) : ((r >> 1) & 3);
-        return K_BYTES + r * (D * 2) + ((g ^ f) * 32) + (c & 3) * 8;
+        return r * (D * 2) + ((g ^ f) * 32) + (c & 3) * 8;
     };
 
     f32x4 o[2][DB];
@@ -237,20 +239,9 @@ void attention_kernel(AttnArgs p) {
     const attn_i16x8 ones = __builtin_bit_cast(attn_i16x8, u32x4{one2, one2, one2, one2});
     const float c = p.c;
 
-    // one block: the next block's loads, S, the softmax, O += P V, then the
-    // barrier that publishes the next block.  MASKED: keys past Nk and (causal)
-    // keys past a row are hidden; compile-time variants in separate loops, so
-    // that the main loop carries no mask code and no merge of its registers.
-    auto block_step = [&](int kb, auto masked_t) __attribute__((always_inline)) {
-        constexpr bool MASKED = decltype(masked_t)::value;
-        // block kb + NBUF - 1 into the buffer that block kb - 1 used (its
-        // readers finished before the previous barrier)
-        if (kb + NBUF - 1 < nblocks) issue_block(kb + NBUF - 1, (kb + NBUF - 1) % NBUF);
-        lds_attn_char* const cur = lds + (kb % NBUF) * BUF;
-        const int key0 = kb * BKV;
-
-        // S = Q K^T for the 4 key groups of 16, both row sets
-        f32x4 sc[2][4];
+    // S = Q K^T of block kb (K from its ring slot) into sc, both row sets
+    auto scores = [&](int kb, f32x4 (&sc)[2][4]) __attribute__((always_inline)) {
+        lds_attn_char* const kbase = lds + (kb & 1) * K_BYTES + koff;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             sc[0][g] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -258,11 +249,27 @@ void attention_kernel(AttnArgs p) {
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
                 const attn_i16x8 kf =
-                    __builtin_bit_cast(attn_i16x8, *(const lds_attn_u32x4*)(cur + koff + s * (BKV * 64) + g * 1024));
+                    __builtin_bit_cast(attn_i16x8, *(const lds_attn_u32x4*)(kbase + s * (BKV * 64) + g * 1024));
                 sc[0][g] = attn_mfma<IN>(kf, qf[0][s], sc[0][g]);
                 sc[1][g] = attn_mfma<IN>(kf, qf[1][s], sc[1][g]);
             }
         }
+    };
+
+    // Iteration kb: sc holds S(kb); the MFMAs of S(kb + 1) into nx run
+    // beside the softmax of block kb (independent work for the matrix cores
+    // while the SIMD computes exponentials), then O += P(kb) V(kb).  Loads:
+    // K(kb + 2) into the slot S(kb) used, V(kb + 1) into the slot PV(kb - 1)
+    // used (both finished before the previous barrier); the barrier at the
+    // end publishes K(kb + 2) and V(kb + 1).  MASKED: keys past Nk and
+    // (causal) keys past a row are hidden; compile-time variants in separate
+    // loops, so that the main loop carries no mask code and no merge of its
+    // registers.
+    auto step = [&](int kb, f32x4 (&sc)[2][4], f32x4 (&nx)[2][4], auto masked_t) __attribute__((always_inline)) {
+        constexpr bool MASKED = decltype(masked_t)::value;
+        if (kb + 2 < nblocks) issue_k(kb + 2);
+        if (kb + 1 < nblocks) issue_v(kb + 1);
+        const int key0 = kb * BKV;
         // row maxima of this lane's scores (hidden ones -inf)
         float mx[2];
 #pragma unroll
@@ -303,23 +310,36 @@ void attention_kernel(AttnArgs p) {
                 lacc[rs] *= alpha;
             }
         }
-        // p = 2^(c s - m); hidden entries -> 0
+        // S(kb + 1) on the matrix cores and p = 2^(c s - m) on the SIMD, one
+        // key group at a time (each group's 2 KS MFMAs beside its 8 exp2).
+        // On the last block the next scores come from a stale LDS slot and
+        // are not used: no branch splits the interleaved code.
+        lds_attn_char* const knext = lds + ((kb + 1) & 1) * K_BYTES + koff;
 #pragma unroll
-        for (int rs = 0; rs < 2; ++rs) {
-            const float nm = -m_run[rs];
+        for (int g = 0; g < 4; ++g) {
+            nx[0][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+            nx[1][g] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int g = 0; g < 4; ++g)
+            for (int s = 0; s < KS; ++s) {
+                const attn_i16x8 kf =
+                    __builtin_bit_cast(attn_i16x8, *(const lds_attn_u32x4*)(knext + s * (BKV * 64) + g * 1024));
+                nx[0][g] = attn_mfma<IN>(kf, qf[0][s], nx[0][g]);
+                nx[1][g] = attn_mfma<IN>(kf, qf[1][s], nx[1][g]);
+            }
+#pragma unroll
+            for (int rs = 0; rs < 2; ++rs)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float sv = sc[rs][g][e];
-                    float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c, nm));
+                    float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c, -m_run[rs]));
                     if constexpr (MASKED) pv = sv == -INFINITY ? 0.f : pv;
                     sc[rs][g][e] = pv;
                 }
+            if constexpr (D == 128) __builtin_amdgcn_sched_barrier(0);
         }
-
         // O += P V, 32 keys at a time: P = this lane's keys 4q..4q+3 of
         // groups 2t and 2t+1
+        lds_attn_char* const vbase = lds + 2 * K_BYTES + (kb & 1) * V_BYTES;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             attn_i16x8 pf[2];
@@ -333,21 +353,17 @@ void attention_kernel(AttnArgs p) {
             }
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                const attn_i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_attn_i16x4*)(cur + voff(t, 0, db)));
-                const attn_i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_attn_i16x4*)(cur + voff(t, 1, db)));
+                const attn_i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_attn_i16x4*)(vbase + voff(t, 0, db)));
+                const attn_i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_attn_i16x4*)(vbase + voff(t, 1, db)));
                 const attn_i16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
                 o[0][db] = attn_mfma<IN>(vf, pf[0], o[0][db]);
                 o[1][db] = attn_mfma<IN>(vf, pf[1], o[1][db]);
             }
             lacc[0] = attn_mfma<IN>(ones, pf[0], lacc[0]);
             lacc[1] = attn_mfma<IN>(ones, pf[1], lacc[1]);
+            if constexpr (D == 128) __builtin_amdgcn_sched_barrier(0);
         }
-        // block kb + 1 has landed: later blocks' loads may still be in flight
-        // (2 PW per block, in issue order), all of them at the tail
-        if (kb + NBUF - 1 < nblocks)
-            wait_vmcnt<(NBUF - 2) * 2 * PW>();
-        else
-            wait_vmcnt<0>();
+        wait_vmcnt<0>();
         __syncthreads();
     };
 
@@ -356,19 +372,38 @@ void attention_kernel(AttnArgs p) {
     int plain = Nk / BKV;
     if (CAUSAL && (q0 + 1) / BKV < plain) plain = (q0 + 1) / BKV;
     if (plain > nblocks) plain = nblocks;
+    // two score buffers, alternating (the loops run two blocks per trip so
+    // that each buffer keeps its registers)
+    f32x4 sa[2][4], sb[2][4];
     if (nblocks > 0) {
-#pragma unroll
-        for (int j = 0; j < NBUF - 1; ++j)
-            if (j < nblocks) issue_block(j, j);
-        if (NBUF - 1 <= nblocks)
-            wait_vmcnt<(NBUF - 2) * 2 * PW>();  // block 0 has landed
-        else
-            wait_vmcnt<0>();
+        issue_k(0);
+        issue_v(0);
+        if (nblocks > 1) issue_k(1);
+        wait_vmcnt<0>();
         __syncthreads();
+        scores(0, sa);
+        __syncthreads();  // every wave has read K(0) before K(2) replaces it
     }
+    // S(kb) is in sa for even kb, in sb for odd kb: every call below has its
+    // buffers fixed at compile time
     int kb = 0;
-    for (; kb < plain; ++kb) block_step(kb, BoolTag<false>{});
-    for (; kb < nblocks; ++kb) block_step(kb, BoolTag<true>{});
+    for (; kb + 1 < plain; kb += 2) {
+        step(kb, sa, sb, BoolTag<false>{});
+        step(kb + 1, sb, sa, BoolTag<false>{});
+    }
+    if (kb < plain) {
+        step(kb, sa, sb, BoolTag<false>{});
+        ++kb;
+    }
+    if (kb < nblocks && (kb & 1)) {
+        step(kb, sb, sa, BoolTag<true>{});
+        ++kb;
+    }
+    for (; kb + 1 < nblocks; kb += 2) {
+        step(kb, sa, sb, BoolTag<true>{});
+        step(kb + 1, sb, sa, BoolTag<true>{});
+    }
+    if (kb < nblocks) step(kb, sa, sb, BoolTag<true>{});
 
     // epilogue: O / L, row my_row, columns 16 db + 4 q .. +3
     constexpr int OB = OUT == DT_F32 ? 4 : 2;
