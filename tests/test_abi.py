@@ -177,9 +177,10 @@ def _kernel(M, N, K, lda=None, ldb=None, ldc=None, in_dt=T.F16, out_dt=T.F16, ci
 
 
 def test_kernel_choice_ring_path():
-    """The direct-to-LDS ring kernel runs exactly for whole tiles of 16-bit
-    inputs with K a multiple of 128 and 16-byte aligned operands; anything
-    else falls back to a register-staged kernel of the same tile."""
+    """The direct-to-LDS ring kernel runs exactly for 16-bit inputs with K a
+    multiple of 128, 16-byte aligned operands and 4-element aligned C rows,
+    whatever M and N (edge tiles store masked); anything else falls back to
+    a register-staged kernel of the same tile."""
     R, TI, GE = T.KERNEL_RING, T.KERNEL_TILED, T.KERNEL_GENERAL
     assert _kernel(8192, 8192, 8192) == R
     assert _kernel(8192, 8192, 8192, in_dt=T.BF16, out_dt=T.F32) == R
@@ -189,7 +190,10 @@ def test_kernel_choice_ring_path():
     assert _kernel(8192, 8192, 8192 + 64) == TI          # K not a multiple of 128
     assert _kernel(8192, 8192, 8192 - 32) == TI
     assert _kernel(8192 - 256, 8192, 8192) == R          # still whole tiles
-    assert _kernel(8191, 8192, 8192) == GE               # ragged M
+    assert _kernel(8191, 8192, 8192) == R                # ragged M: masked edge tiles
+    assert _kernel(8191, 8000, 8192) == R                # ragged M and N
+    assert _kernel(8192, 8190, 8192) == GE               # B rows not whole 16-byte chunks
+    assert _kernel(8192, 8192, 8192, ldc=8194) == GE     # C rows not 4-element aligned
     assert _kernel(8192, 8192, 8192, lda=8196) == GE     # rows not whole 16-byte chunks
     assert _kernel(8192, 8192, 8192, lda=8192 + 8) == R  # padded, still aligned
     assert _kernel(8192, 8192, 8192, offs=(1, 0, 0)) == GE

@@ -102,8 +102,9 @@ def check_bound(d, o, z, a, b, in_dt, out_dt, c_old, bias, bias_dt, bias_kind, a
 
 # shapes that take each kernel (table's choice): ring 256x256 tiles, ring
 # 128x128 tiles, register-staged whole tiles, direct
-SHAPES = [((256, 512, 384), "ring big"), ((1024, 2048, 512), "ring mid"), ((128, 256, 512), "tiled"),
-          ((127, 255, 512), "direct"), ((33, 47, 255), "direct ragged")]
+SHAPES = [((256, 512, 384), "ring big", 0), ((1024, 2048, 512), "ring mid", 1), ((128, 256, 512), "tiled", -1),
+          ((127, 255, 512), "direct", -1), ((33, 47, 255), "direct ragged", -1),
+          ((1000, 1200, 512), "ring big ragged", 0), ((777, 1000, 256), "ring mid ragged", 1)]
 EPILOGUES = [
     (1.0, 0.0, None, None, oracle.ACT_RELU),
     (0.5, 2.0, W.F32, oracle.BIAS_COL, oracle.ACT_NONE),
@@ -116,7 +117,7 @@ EPILOGUES = [
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: s[1].replace(" ", "_"))
 @pytest.mark.parametrize("pair", [(W.F16, W.F16), (W.BF16, W.F32)], ids=["f16-f16", "bf16-f32"])
 def test_fused_against_oracle(shape, pair):
-    (M, N, K), name = shape
+    (M, N, K), name, cid = shape
     in_dt, out_dt = pair
     a, b = W.random_inputs(M, N, K, in_dt, seed=M + N + K)
     c_old = W.to_storage(np.random.default_rng(8).standard_normal((M, N)).astype(np.float32), out_dt)
@@ -125,7 +126,10 @@ def test_fused_against_oracle(shape, pair):
         if bias_kind is not None:
             n = M if bias_kind == oracle.BIAS_ROW else N
             bias = W.to_storage(np.random.default_rng(9).standard_normal(n).astype(np.float32), bias_dt)
-        d, kind = run_fused(a, b, in_dt, out_dt, c_old, bias, bias_dt, bias_kind, alpha, beta, act, label=name)
+        d, kind = run_fused(a, b, in_dt, out_dt, c_old, bias, bias_dt, bias_kind, alpha, beta, act, cid=cid,
+                            label=name)
+        if name.startswith("ring"):
+            assert kind == T.KERNEL_RING
         o, z = expected(a, b, in_dt, out_dt, c_old, bias, bias_dt, bias_kind, alpha, beta, act)
         r = check_bound(d, o, z, a, b, in_dt, out_dt, c_old, bias, bias_dt, bias_kind, alpha, beta, name)
         G.say(f"    ok, worst bound ratio {r:.3f}")

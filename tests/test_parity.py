@@ -304,6 +304,32 @@ def test_ring_path_against_oracle(shape):
         run_case(a, b, in_dt, out_dt, config=cid, label=f"ring {shape}")
 
 
+# M and N not multiples of the tile: the ring kernel with masked edge tiles
+RING_RAGGED = [(1000, 1200, 512, 0), (1000, 1200, 512, 1), (777, 1000, 256, 0), (129, 136, 128, 1),
+               (255, 264, 384, 0), (1, 8, 128, 0), (300, 1000, 128, 1)]
+
+
+@pytest.mark.parametrize("shape", RING_RAGGED, ids=lambda s: "x".join(map(str, s[:3])) + f"_cfg{s[3]}")
+def test_ring_path_ragged_edges(shape):
+    """Ragged M and N through the ring kernel (the path asserted): every
+    element inside C against the oracle, the 8 padding columns of every row
+    and the memory after C untouched (NaN-prefilled guard)."""
+    M, N, K, cid = shape
+    for in_dt, out_dt in ((W.F16, W.F16), (W.BF16, W.F32)):
+        a, b = W.random_inputs(M, N, K, in_dt, seed=M + 5 * N + 9 * K + cid)
+        ad, bd = G.to_device(a, in_dt), G.to_device(b, in_dt)
+        flat, cd = G.out_tensor(M, N, out_dt, pad_cols=8)
+        assert T.gemm_select_kernel(M, N, K, ad.data_ptr(), K, bd.data_ptr(), N, cd.data_ptr(), N + 8, in_dt,
+                                    out_dt, cid) == T.KERNEL_RING
+        G.say(f"[case] ring ragged {M}x{N}x{K} cfg{cid} in={in_dt} out={out_dt}")
+        G.run(ad, bd, cd, cid)
+        c = G.values(cd, out_dt)
+        G.check(c, G.oracle_values(a, b, in_dt), a, b, in_dt, out_dt, K, label=f"ring ragged {shape}")
+        whole = flat[:M * (N + 8)].view(M, N + 8)
+        assert torch.isnan(whole[:, N:].float()).all(), "padding columns written"
+        assert torch.isnan(flat[M * (N + 8):].float()).all(), "memory after C written"
+
+
 @pytest.mark.parametrize("cid", [0, 1])
 def test_ring_path_ignores_data_past_k(cid):
     """The ring kernel's loads run up to 4 steps of 32 past the end of K.  A

@@ -1,5 +1,6 @@
 // gemm_kernel_ring.hpp -- the gfx950 fast path of the tiled matrix product
-// for 16-bit inputs (fp16 / bf16) on whole tiles: direct-to-LDS loads into
+// for 16-bit inputs (fp16 / bf16), aligned operands, K a multiple of the
+// ring's step (any M and N: edge tiles store masked): direct-to-LDS loads into
 // multi-stage LDS rings and v_mfma_f32_16x16x32_{f16,bf16}.
 //
 // The method is the tiled kernel of page "企业官网建设流程全解析" §3.3 (one
@@ -481,20 +482,42 @@ void gemm_kernel_ring(GemmArgs p) {
             [&](int b, int, int& row, int& col, int& n, bool& vec) {
                 row = m0 + wm * T::WTM + 16 * (b / T::FN) + i16;
                 col = n0 + wn * T::WTN + 16 * (b % T::FN) + 4 * q;
-                n = 4;
+                n = row < p.M ? (p.N - col >= 4 ? 4 : p.N - col > 0 ? p.N - col : 0) : 0;
                 vec = true;
             });
         return;
     }
     constexpr int OB = OUT == DT_F32 ? 4 : 2;
     const int64_t ldc = p.ldc;
-    static_for<0, NMF>([&](auto bt) __attribute__((always_inline)) {
-        constexpr int i = decltype(bt)::value / T::FN, j = decltype(bt)::value % T::FN;
-        const int row = m0 + wm * T::WTM + 16 * i + i16;
-        const int col = n0 + wn * T::WTN + 16 * j + 4 * q;
-        store4<OUT>(p.C + ((int64_t)row * ldc + col) * OB, acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3],
-                    true);
-    });
+    // a tile on the bottom or right edge of C (M or N not a multiple of the
+    // tile) stores only its elements inside C: its other rows and columns hold
+    // products of zeros or of elements outside the tile's operand rows and
+    // columns, never mixed into the stored ones
+    if (m0 + T::BM <= p.M && n0 + T::BN <= p.N) {
+        static_for<0, NMF>([&](auto bt) __attribute__((always_inline)) {
+            constexpr int i = decltype(bt)::value / T::FN, j = decltype(bt)::value % T::FN;
+            const int row = m0 + wm * T::WTM + 16 * i + i16;
+            const int col = n0 + wn * T::WTN + 16 * j + 4 * q;
+            store4<OUT>(p.C + ((int64_t)row * ldc + col) * OB, acc[i][j][0], acc[i][j][1], acc[i][j][2],
+                        acc[i][j][3], true);
+        });
+    } else {
+        static_for<0, NMF>([&](auto bt) __attribute__((always_inline)) {
+            constexpr int i = decltype(bt)::value / T::FN, j = decltype(bt)::value % T::FN;
+            const int row = m0 + wm * T::WTM + 16 * i + i16;
+            const int col = n0 + wn * T::WTN + 16 * j + 4 * q;
+            if (row < p.M) {
+                char* dst = p.C + ((int64_t)row * ldc + col) * OB;
+                if (col + 4 <= p.N) {
+                    store4<OUT>(dst, acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3], true);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 3; ++e)
+                        if (col + e < p.N) store_elem<OUT>(dst + e * OB, acc[i][j][e]);
+                }
+            }
+        });
+    }
 }
 
 }  // namespace tgemm

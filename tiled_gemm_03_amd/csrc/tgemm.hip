@@ -1,8 +1,8 @@
 // tgemm.hip -- C ABI of libtgemm.so: argument checks, the per-shape tile
 // configuration table and the kernel launch.  The kernels are in
 // gemm_kernel.hpp (register-staged; every shape, type and alignment, both
-// operands row-major), gemm_kernel_ring.hpp (direct-to-LDS rings; whole tiles
-// of 16-bit inputs, any operand layout) and gemm_kernel_direct.hpp (operands
+// operands row-major), gemm_kernel_ring.hpp (direct-to-LDS rings; 16-bit
+// inputs, aligned, K a multiple of the ring's step, any operand layout) and gemm_kernel_direct.hpp (operands
 // straight to registers; small, ragged or unaligned products, any operand
 // layout), compiled in units of their own (k_*.hip) behind the selectors of
 // kernels.hpp; the ABI is declared (and documented) in include/tgemm.h.
@@ -25,8 +25,8 @@ struct ConfigEntry {
     int bm, bn, bk, wm, wn, eb, lds_bytes, threads, cpr;
     // register-staged kernels (row-major operands only)
     KernelFn (*tiled)(int in, int out, bool fast, bool epi);
-    // direct-to-LDS ring kernels of the same output tile (whole tiles, K a
-    // multiple of ring_k_mult; any operand layout), with their block_k,
+    // direct-to-LDS ring kernels of the same output tile (K a multiple of
+    // ring_k_mult, aligned operands, any M and N, any operand layout), with their block_k,
     // stage count and LDS bytes
     KernelFn (*ring)(int in, int out, int la, int lb, bool epi);
     int ring_bk, ring_stages, ring_k_mult, ring_lds;
@@ -203,8 +203,7 @@ int64_t operand_reach(bool kcontig, int64_t ext, int64_t ld, int64_t K, int64_t 
 bool ring_applies(const ConfigEntry& c, const Problem& p) {
     if (c.ring == nullptr || !tuning().direct_lds) return false;
     const int64_t extra = (int64_t)c.ring_lookahead * c.ring_bk;
-    return loads_aligned(c, p) && stores_aligned(p) && p.M % c.bm == 0 && p.N % c.bn == 0 &&
-           p.K % c.ring_k_mult == 0 &&
+    return loads_aligned(c, p) && stores_aligned(p) && p.K % c.ring_k_mult == 0 &&
            operand_reach(p.la == LAYOUT_ROW, c.bm, p.lda, p.K, extra, c.eb) < (1LL << 31) &&
            operand_reach(p.lb == LAYOUT_COL, c.bn, p.ldb, p.K, extra, c.eb) < (1LL << 31);
 }
