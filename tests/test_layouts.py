@@ -89,7 +89,8 @@ SHAPES = [(256, 256, 128), (512, 768, 384), (1024, 2048, 512), (127, 255, 512), 
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_layouts_against_oracle(lay, shape):
     """Random inputs; whole tiles with K a multiple of 128 take the ring
-    kernel whenever the call does not reduce to row-major operands."""
+    kernel whenever the call does not reduce to row-major operands, other
+    shapes the ring or the direct kernel."""
     M, N, K = shape
     for in_dt, out_dt in ((W.F16, W.F16), (W.BF16, W.F32)):
         a, b = W.random_inputs(M, N, K, in_dt, seed=M + 5 * N + 11 * K + 3 * lay[0] + 7 * lay[1] + 13 * lay[2])
@@ -97,8 +98,10 @@ def test_layouts_against_oracle(lay, shape):
         G.check(c, o, a, b, in_dt, out_dt, K, label=f"{lid(lay)} {shape}")
         if not effective_row_row(lay) and M % 128 == 0 and N % 128 == 0 and K % 128 == 0:
             assert kind == T.KERNEL_RING
-        if not effective_row_row(lay) and (M % 128 or N % 128 or K % 128):
-            assert kind == T.KERNEL_DIRECT
+        if not effective_row_row(lay):
+            # column-major operands run the ring kernel where it applies
+            # (alignment, K % 8, N % 4: pinned in test_abi) and else direct
+            assert kind in (T.KERNEL_RING, T.KERNEL_DIRECT)
 
 
 @pytest.mark.parametrize("lay", LAYOUTS, ids=lid)
@@ -183,3 +186,24 @@ def test_layouts_8192_sampled(lay):
     c, o, kind = run_layout(a, b, w.in_dtype, w.out_dtype, lay, rows=rows, cols=cols, label=w.name)
     assert kind == T.KERNEL_RING
     G.check(c, o, a, b, w.in_dtype, w.out_dtype, w.K, rows=rows, cols=cols, label=f"{w.name} {lid(lay)}")
+
+
+@pytest.mark.parametrize("lay", LAYOUTS, ids=lid)
+@pytest.mark.parametrize("cid", [0, 1])
+def test_layouts_ring_odd_edges(lay, cid):
+    """The ring kernel (forced, path asserted) on an odd M and N a multiple
+    of 4 but not of 8: leading dimensions padded to the alignment the ring
+    needs, the padding NaN (it reaches only outputs past M or N, never
+    stored; a k-strided A's last element must not be lost to the dword that
+    straddles the end of its range)."""
+    # an odd size in the role of M of the row-major product the call runs
+    # (a column-major C swaps M and N); its N a multiple of 4, not of 8
+    M, N, K = (1001, 1004, 512) if lay[2] == ROW else (1004, 1001, 512)
+    ext = {"a": (K, M), "b": (N, K), "c": (N, M)}  # stored row length for (row-major, column-major)
+    pad = lambda e, mult: (-e) % mult or mult
+    pads = (pad(ext["a"][lay[0]], 8), pad(ext["b"][lay[1]], 8), pad(ext["c"][lay[2]], 4))
+    for in_dt, out_dt in ((W.F16, W.F16), (W.BF16, W.F32)):
+        a, b = W.random_inputs(M, N, K, in_dt, seed=17 + cid + 3 * lay[0] + 5 * lay[1] + 7 * lay[2])
+        c, o, kind = run_layout(a, b, in_dt, out_dt, lay, cid=cid, pads=pads, label="ring odd")
+        assert kind == T.KERNEL_RING, kind
+        G.check(c, o, a, b, in_dt, out_dt, K, label=f"ring odd {lid(lay)} cfg{cid}")

@@ -304,9 +304,10 @@ def test_ring_path_against_oracle(shape):
         run_case(a, b, in_dt, out_dt, config=cid, label=f"ring {shape}")
 
 
-# M and N not multiples of the tile: the ring kernel with masked edge tiles
+# M and N not multiples of the tile (N a multiple of 4): the ring kernel with
+# masked edge tiles
 RING_RAGGED = [(1000, 1200, 512, 0), (1000, 1200, 512, 1), (777, 1000, 256, 0), (129, 136, 128, 1),
-               (255, 264, 384, 0), (1, 8, 128, 0), (300, 1000, 128, 1)]
+               (255, 264, 384, 0), (1, 8, 128, 0), (300, 1000, 128, 1), (1000, 1200, 640, 0), (513, 264, 1024, 1)]
 
 
 @pytest.mark.parametrize("shape", RING_RAGGED, ids=lambda s: "x".join(map(str, s[:3])) + f"_cfg{s[3]}")

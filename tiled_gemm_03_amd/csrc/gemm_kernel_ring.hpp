@@ -1,6 +1,7 @@
 // gemm_kernel_ring.hpp -- the gfx950 fast path of the tiled matrix product
-// for 16-bit inputs (fp16 / bf16), aligned operands, K a multiple of the
-// ring's step (any M and N: edge tiles store masked): direct-to-LDS loads into
+// for 16-bit inputs (fp16 / bf16), aligned operands, K a multiple of 128,
+// N % 4 == 0 (any M and N otherwise: edge tiles store masked): direct-to-LDS
+// loads into
 // multi-stage LDS rings and v_mfma_f32_16x16x32_{f16,bf16}.
 //
 // The method is the tiled kernel of page "企业官网建设流程全解析" §3.3 (one
@@ -206,11 +207,11 @@ struct RingCfg {
     static_assert(WTM % 16 == 0 && WTN % 16 == 0, "");
 };
 
-// Preconditions (checked by the host): 16-bit inputs; M % BM == 0,
-// N % BN == 0, K % K_MULT == 0; A and B 16-byte aligned with lda and ldb
-// multiples of 8; C aligned for 4-element stores with ldc % 4 == 0; the
-// buffer offsets (a tile's rows or columns of each operand over
-// K + LOOKAHEAD * BK of K) below 2^31 bytes.  LA / LB: LAYOUT_ROW or
+// Preconditions (checked by the host): 16-bit inputs; K % K_MULT == 0 and
+// N % 4 == 0 (any M and N otherwise: edge tiles store masked);
+// A and B 16-byte aligned with lda and ldb multiples of 8; C aligned for
+// 4-element stores with ldc % 4 == 0; the buffer offsets (a tile's rows or
+// columns of each operand over K + LOOKAHEAD * BK of K) below 2^31 bytes.  LA / LB: LAYOUT_ROW or
 // LAYOUT_COL; C is row-major.
 template <class T, int IN, int OUT, int LA, int LB, bool EPI = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(T::THREADS, T::THREADS),
@@ -240,8 +241,14 @@ void gemm_kernel_ring(GemmArgs p) {
     const int swz = p.swz_mask != 0 ? 1 : 0;
 
     // ---------------------------------------------------------- a2: loads
+    // The range is rounded up to whole dwords: the range check zeroes a dword
+    // that straddles the end, which would drop the operand's last element
+    // when a k-strided tile row ends at an odd M or N.  The element after it
+    // is row padding (ld is a multiple of 8, so an odd row length leaves at
+    // least one), and it only reaches outputs past M or N, never stored.
     auto make_rsrc = [&](const char* base, int64_t bytes) __attribute__((always_inline)) {
         const uint64_t a = (uint64_t)base;
+        bytes = (bytes + 3) & ~(int64_t)3;
         const uint32_t n = bytes <= 0 ? 0u : bytes > 0xffffffffLL ? 0xffffffffu : (uint32_t)bytes;
         return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
                      __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)),
@@ -490,34 +497,20 @@ void gemm_kernel_ring(GemmArgs p) {
     constexpr int OB = OUT == DT_F32 ? 4 : 2;
     const int64_t ldc = p.ldc;
     // a tile on the bottom or right edge of C (M or N not a multiple of the
-    // tile) stores only its elements inside C: its other rows and columns hold
+    // tile) stores only its groups inside C (N % 4 == 0: a group of four
+    // columns is wholly inside or outside); its other rows and columns hold
     // products of zeros or of elements outside the tile's operand rows and
-    // columns, never mixed into the stored ones
-    if (m0 + T::BM <= p.M && n0 + T::BN <= p.N) {
-        static_for<0, NMF>([&](auto bt) __attribute__((always_inline)) {
-            constexpr int i = decltype(bt)::value / T::FN, j = decltype(bt)::value % T::FN;
-            const int row = m0 + wm * T::WTM + 16 * i + i16;
-            const int col = n0 + wn * T::WTN + 16 * j + 4 * q;
+    // columns, never mixed into the stored ones.  (Element stores for a
+    // partial group make the compiler move every accumulator to VGPRs ahead
+    // of the stores, and spill.)
+    static_for<0, NMF>([&](auto bt) __attribute__((always_inline)) {
+        constexpr int i = decltype(bt)::value / T::FN, j = decltype(bt)::value % T::FN;
+        const int row = m0 + wm * T::WTM + 16 * i + i16;
+        const int col = n0 + wn * T::WTN + 16 * j + 4 * q;
+        if (row < p.M && col < p.N)
             store4<OUT>(p.C + ((int64_t)row * ldc + col) * OB, acc[i][j][0], acc[i][j][1], acc[i][j][2],
                         acc[i][j][3], true);
-        });
-    } else {
-        static_for<0, NMF>([&](auto bt) __attribute__((always_inline)) {
-            constexpr int i = decltype(bt)::value / T::FN, j = decltype(bt)::value % T::FN;
-            const int row = m0 + wm * T::WTM + 16 * i + i16;
-            const int col = n0 + wn * T::WTN + 16 * j + 4 * q;
-            if (row < p.M) {
-                char* dst = p.C + ((int64_t)row * ldc + col) * OB;
-                if (col + 4 <= p.N) {
-                    store4<OUT>(dst, acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3], true);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 3; ++e)
-                        if (col + e < p.N) store_elem<OUT>(dst + e * OB, acc[i][j][e]);
-                }
-            }
-        });
-    }
+    });
 }
 
 }  // namespace tgemm

@@ -2,7 +2,7 @@
 // configuration table and the kernel launch.  The kernels are in
 // gemm_kernel.hpp (register-staged; every shape, type and alignment, both
 // operands row-major), gemm_kernel_ring.hpp (direct-to-LDS rings; 16-bit
-// inputs, aligned, K a multiple of the ring's step, any operand layout) and gemm_kernel_direct.hpp (operands
+// inputs, aligned, K a multiple of 128, N % 4 == 0, any operand layout) and gemm_kernel_direct.hpp (operands
 // straight to registers; small, ragged or unaligned products, any operand
 // layout), compiled in units of their own (k_*.hip) behind the selectors of
 // kernels.hpp; the ABI is declared (and documented) in include/tgemm.h.
@@ -25,8 +25,9 @@ struct ConfigEntry {
     int bm, bn, bk, wm, wn, eb, lds_bytes, threads, cpr;
     // register-staged kernels (row-major operands only)
     KernelFn (*tiled)(int in, int out, bool fast, bool epi);
-    // direct-to-LDS ring kernels of the same output tile (K a multiple of
-    // ring_k_mult, aligned operands, any M and N, any operand layout), with their block_k,
+    // direct-to-LDS ring kernels of the same output tile (aligned operands,
+    // K a multiple of ring_k_mult, N % 4 == 0, any M, any operand layout),
+    // with their block_k,
     // stage count and LDS bytes
     KernelFn (*ring)(int in, int out, int la, int lb, bool epi);
     int ring_bk, ring_stages, ring_k_mult, ring_lds;
@@ -202,8 +203,9 @@ int64_t operand_reach(bool kcontig, int64_t ext, int64_t ld, int64_t K, int64_t 
 // Whether a configuration with a ring kernel runs it.
 bool ring_applies(const ConfigEntry& c, const Problem& p) {
     if (c.ring == nullptr || !tuning().direct_lds) return false;
+    // the ring loads ring_lookahead steps past K
     const int64_t extra = (int64_t)c.ring_lookahead * c.ring_bk;
-    return loads_aligned(c, p) && stores_aligned(p) && p.K % c.ring_k_mult == 0 &&
+    return loads_aligned(c, p) && stores_aligned(p) && p.K % c.ring_k_mult == 0 && p.N % 4 == 0 &&
            operand_reach(p.la == LAYOUT_ROW, c.bm, p.lda, p.K, extra, c.eb) < (1LL << 31) &&
            operand_reach(p.lb == LAYOUT_COL, c.bn, p.ldb, p.K, extra, c.eb) < (1LL << 31);
 }
