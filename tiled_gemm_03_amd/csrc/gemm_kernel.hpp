@@ -365,7 +365,9 @@ __device__ __forceinline__ void store4_fused(const GemmArgs& p, int row, int col
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 
-template <int OUT, int NB, int VPL, int PB, class Get, class Where>
+// WHOLE: every group is wholly inside C or wholly outside (n is 4 or 0), so
+// the partial-group code is not compiled.
+template <int OUT, int NB, int VPL, int PB, bool WHOLE, class Get, class Where>
 __device__ __forceinline__ void fused_epilogue(const GemmArgs& p, lds_f32x4* region, Get&& get, Where&& where) {
     static_assert(NB % PB == 0 && VPL % 4 == 0, "");
     const int lane = threadIdx.x & 63;
@@ -380,7 +382,7 @@ __device__ __forceinline__ void fused_epilogue(const GemmArgs& p, lds_f32x4* reg
                 bool vec;
                 where(b0 + t, g, row, col, n, vec);
                 const f32x4 v = f32x4{blk[4 * g + 0], blk[4 * g + 1], blk[4 * g + 2], blk[4 * g + 3]};
-                region[(t * 64 + lane) * (VPL / 4) + g] = n > 0 ? fused_pre<OUT>(p, row, col, n, v) : v;
+                region[(t * 64 + lane) * (VPL / 4) + g] = n > 0 ? fused_pre<OUT>(p, row, col, WHOLE ? 4 : n, v) : v;
             });
         });
         for (int t = 0; t < PB; ++t)
@@ -388,7 +390,7 @@ __device__ __forceinline__ void fused_epilogue(const GemmArgs& p, lds_f32x4* reg
                 int row, col, n;
                 bool vec;
                 where(b0 + t, g, row, col, n, vec);
-                if (n > 0) fused_post<OUT>(p, row, col, n, vec, region[(t * 64 + lane) * (VPL / 4) + g]);
+                if (n > 0) fused_post<OUT>(p, row, col, WHOLE ? 4 : n, vec, region[(t * 64 + lane) * (VPL / 4) + g]);
             }
     });
 }
@@ -672,7 +674,7 @@ void gemm_kernel(GemmArgs p) {
         constexpr int PB = (T::FM * T::FN) % PB0 == 0 ? PB0 : 1;
         static_assert(PB >= 1, "the LDS holds a block of accumulators per wave");
         lds_f32x4* region = (lds_f32x4*)(lds_void*)smem + wave * (REGION / 16);
-        fused_epilogue<OUT, T::FM * T::FN, 16, PB>(
+        fused_epilogue<OUT, T::FM * T::FN, 16, PB, FAST>(
             p, region, [&](auto b_t) { constexpr int b = decltype(b_t)::value; return acc[b / T::FN][b % T::FN]; },
             [&](int b, int q, int& row, int& col, int& n, bool& vec) {
                 const int i = b / T::FN, j = b % T::FN;

@@ -484,12 +484,12 @@ void gemm_kernel_ring(GemmArgs p) {
             held[b] = acc[b / T::FN][b % T::FN];
             if constexpr (b >= PB) asm volatile("" : "+v"(held[b]));
         });
-        fused_epilogue<OUT, NMF, 4, PB>(
+        fused_epilogue<OUT, NMF, 4, PB, true>(
             p, region, [&](auto b_t) { constexpr int b = decltype(b_t)::value; return held[b]; },
             [&](int b, int, int& row, int& col, int& n, bool& vec) {
                 row = m0 + wm * T::WTM + 16 * (b / T::FN) + i16;
                 col = n0 + wn * T::WTN + 16 * (b % T::FN) + 4 * q;
-                n = row < p.M ? (p.N - col >= 4 ? 4 : p.N - col > 0 ? p.N - col : 0) : 0;
+                n = row < p.M && col < p.N ? 4 : 0;  // N % 4 == 0: whole groups
                 vec = true;
             });
         return;
