@@ -197,6 +197,9 @@ CASES = [
     (2, 65, 100, 300, 64, W.BF16, W.BF16, 0.125, False, "bnhd", 1, 2),
     (1, 256, 65, 70, 64, W.F16, W.F16, 0.125, True, "bhnd", 0, 4),
     (2, 128, 130, 129, 128, W.BF16, W.F32, 128 ** -0.5, False, "bnhd", 2, 4),
+    (1, 3, 100, 77, 64, W.F16, W.F32, 0.0, False, "bhnd", 0, 1),     # scale 0: the mean of V
+    (1, 3, 100, 77, 64, W.F16, W.F32, 0.0, True, "bhnd", 0, 1),      # scale 0, causal: running means
+    (2, 2, 300, 300, 128, W.BF16, W.BF16, 128 ** -0.5, True, "bnhd", 3, 4),
 ]
 
 

@@ -13,11 +13,15 @@
 //                  lane l holds S[row l % 16][keys 4 (l/16) .. +3] of each
 //                  16-key group (Q stays in registers for the whole loop);
 //   online softmax in fp32 with exp2 (c = |scale| log2 e; a negative scale
-//                  flips the signs of Q, which is exact): p = 2^(c s - m)
-//                  with m the running row maximum; O and L are scaled by
-//                  2^(m_old - m) every block.  L is the sum of the probabilities as
-//                  rounded for the product with V (so the weights sum to 1
-//                  exactly), accumulated on the MFMA against ones;
+//                  flips the signs of Q, which is exact): p = 2^(c s - m).
+//                  The reference point m of a row moves only when a score
+//                  passes it by more than 2^8 (then m := the row maximum and
+//                  O, L are scaled by 2^(m_old - m), in a branch of its own);
+//                  in between p <= 2^8 and O, L keep accumulating against the
+//                  old m (O / L does not depend on m).  L is the sum of the
+//                  probabilities as rounded for the product with V (so the
+//                  weights sum to 1 exactly), accumulated on the MFMA
+//                  against a fragment of ones;
 //   O += P V       the same MFMA with V (first operand) and P (second).  The
 //                  8 k-values a lane feeds per 32 keys are the keys it holds
 //                  in S, 4 (l/16) .. +3 and 16 + 4 (l/16) .. +3, so P goes
@@ -26,17 +30,17 @@
 //                  each).
 // K and V blocks go global -> LDS directly (no registers) into rings of two
 // LDS slots each, K two blocks ahead and V one (S of the next block is
-// computed during this block's softmax), one barrier per block.  LDS layouts (XOR swizzles, as the
-// matrix-product kernels): K as [d / 32][64 keys][64 bytes] with chunk
-// c ^ ((key / 2) % 4) (a K fragment read is the conflict-free read of the
-// k-contiguous ring stage); V as [64 keys][d] with its 32-byte groups of row
-// r at group g ^ f(r), f spreading the 8 rows of a half-wave's transposing
-// read over the 8 bank groups.
+// computed during this block's softmax), one barrier per block.  LDS layouts
+// (XOR swizzles, as the matrix-product kernels): K as [d / 32][64 keys][64
+// bytes] with chunk c ^ ((key / 2) % 4) (a K fragment read is the
+// conflict-free read of the k-contiguous ring stage); V as [64 keys][d] with
+// its 32-byte groups of row r at group g ^ f(r), f spreading the 8 rows of a
+// half-wave's transposing read over the 8 bank groups.
 //
 // Masks (only in the blocks after those that every row of the tile sees
 // whole: a separate loop): keys >= Nk, and keys > query when causal, get
-// p = 0.  Rows >= Nq are computed on zero queries and not written.  Every row sees key 0, so
-// the first block sets every row's reference point.
+// p = 0.  Rows >= Nq are computed on zero queries and not written.  Every row
+// sees key 0, so the first block sets every row's reference point.
 #pragma once
 #include "gemm_kernel.hpp"
 #include "gemm_kernel_ring.hpp"
