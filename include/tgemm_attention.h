@@ -59,10 +59,11 @@ int attention_fwd(int64_t batch, int64_t heads, int64_t n_q, int64_t n_k, int64_
                   int in_dtype, int out_dtype, float scale, int causal, void* stream);
 
 /*
- * attention_waves: the workgroup shape attention_fwd launches for these
- * sizes: 32 query rows per wave and 4 waves per workgroup, or (head_dim 64)
- * 2 or 1 when 4 would leave some of the 256 CUs without a workgroup.
- * Returns 4, 2 or 1; TGEMM_ERR_DIM for sizes outside attention_fwd's range
+ * attention_waves: the query tile attention_fwd launches for these sizes, in
+ * units of 32 rows: 4 (128 rows, four waves with 32 rows each) or, for
+ * head_dim 64 when 128-row tiles would leave some of the 256 CUs without a
+ * workgroup, 1 (32 rows, two waves splitting the keys and combining their
+ * partial results).  TGEMM_ERR_DIM for sizes outside attention_fwd's range
  * or with nothing to compute, TGEMM_ERR_HEAD_DIM for a head_dim other than
  * 64 and 128.  Host-only; enqueues nothing.
  */

@@ -79,10 +79,11 @@ def test_attention_interleaved_heads_are_not_an_overlap():
 
 
 def test_attention_workgroup_shape():
-    # 4 waves (128 query rows) while that gives every CU a workgroup, then 2, then 1
+    # 128-row tiles while that gives every CU a workgroup, else (head dim
+    # 64) 32-row tiles with the keys split over two waves
     assert T.attention_waves(4, 16, 4096, 128) == 4
     assert T.attention_waves(1, 256, 1, 64) == 4
-    assert T.attention_waves(1, 255, 128, 64) == 2
+    assert T.attention_waves(1, 255, 128, 64) == 1
     assert T.attention_waves(1, 12, 1024, 64) == 1
     assert T.attention_waves(1, 1, 1, 64) == 1
     assert T.attention_waves(1, 1, 1, 128) == 4   # head_dim 128: always 4
@@ -181,7 +182,7 @@ def _check(o, ref, bound, label):
 
 
 CASES = [
-    # B, H, n_q, n_k, d, in, out, scale, causal, layout, tail, waves per workgroup
+    # B, H, n_q, n_k, d, in, out, scale, causal, layout, tail, tile rows / 32 (1: keys split over waves)
     (1, 2, 200, 300, 64, W.F16, W.F16, 0.125, False, "bhnd", 0, 1),
     (2, 1, 130, 130, 128, W.BF16, W.F32, 128 ** -0.5, True, "bhnd", 3, 4),
     (1, 1, 64, 64, 64, W.F16, W.F32, 1.0, True, "bhnd", 0, 1),
@@ -193,13 +194,15 @@ CASES = [
     (1, 4, 192, 192, 64, W.BF16, W.F32, 1.0, False, "bhnd", 0, 1),   # the pages' unscaled softmax(QK^T)V
     (1, 4, 130, 140, 64, W.F16, W.F32, -0.3, False, "bhnd", 0, 1),   # negative scale
     (1, 130, 100, 77, 128, W.F16, W.F16, 0.2, True, "bhnd", 0, 4),   # head_dim 128: always 4 waves
-    (1, 130, 100, 77, 64, W.F16, W.F16, 0.2, True, "bhnd", 0, 2),
-    (2, 65, 100, 300, 64, W.BF16, W.BF16, 0.125, False, "bnhd", 1, 2),
+    (1, 130, 100, 77, 64, W.F16, W.F16, 0.2, True, "bhnd", 0, 1),
+    (2, 65, 100, 300, 64, W.BF16, W.BF16, 0.125, False, "bnhd", 1, 1),
     (1, 256, 65, 70, 64, W.F16, W.F16, 0.125, True, "bhnd", 0, 4),
     (2, 128, 130, 129, 128, W.BF16, W.F32, 128 ** -0.5, False, "bnhd", 2, 4),
     (1, 3, 100, 77, 64, W.F16, W.F32, 0.0, False, "bhnd", 0, 1),     # scale 0: the mean of V
     (1, 3, 100, 77, 64, W.F16, W.F32, 0.0, True, "bhnd", 0, 1),      # scale 0, causal: running means
     (2, 2, 300, 300, 128, W.BF16, W.BF16, 128 ** -0.5, True, "bnhd", 3, 4),
+    (1, 2, 97, 449, 64, W.F16, W.F16, 0.125, False, "bhnd", 2, 1),   # 8 key blocks split over two waves
+    (1, 2, 300, 300, 64, W.BF16, W.F32, 0.125, True, "bnhd", 0, 1),  # split, causal, tiles along the diagonal
 ]
 
 

@@ -200,7 +200,8 @@ def attention_fwd(B, H, n_q, n_k, d, Q, q_stride, K, k_stride, V, v_stride, O, o
 
 
 def attention_waves(B, H, n_q, d):
-    """Waves per workgroup that attention_fwd launches (4, 2 or 1)."""
+    """Query rows per workgroup that attention_fwd launches, in units of 32:
+    4, or 1 (two waves splitting the keys of 32 rows)."""
     return lib().attention_waves(B, H, n_q, d)
 
 

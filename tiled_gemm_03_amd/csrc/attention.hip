@@ -14,48 +14,49 @@ namespace {
 
 typedef void (*AttnFn)(AttnArgs);
 
-template <int D, int IN, bool CAUSAL, int NW>
+template <int D, int IN, bool CAUSAL, int NW, bool SPLIT>
 AttnFn attn_pick_out(int out) {
-    if (out == DT_F32) return attention_kernel<D, IN, DT_F32, CAUSAL, NW>;
-    return attention_kernel<D, IN, IN, CAUSAL, NW>;
+    if (out == DT_F32) return attention_kernel<D, IN, DT_F32, CAUSAL, NW, SPLIT>;
+    return attention_kernel<D, IN, IN, CAUSAL, NW, SPLIT>;
 }
 
-template <int D, int NW>
+template <int D, int NW, bool SPLIT>
 AttnFn attn_pick_nw(int in, int out, bool causal) {
     if (in == DT_F16)
-        return causal ? attn_pick_out<D, DT_F16, true, NW>(out) : attn_pick_out<D, DT_F16, false, NW>(out);
-    return causal ? attn_pick_out<D, DT_BF16, true, NW>(out) : attn_pick_out<D, DT_BF16, false, NW>(out);
+        return causal ? attn_pick_out<D, DT_F16, true, NW, SPLIT>(out) : attn_pick_out<D, DT_F16, false, NW, SPLIT>(out);
+    return causal ? attn_pick_out<D, DT_BF16, true, NW, SPLIT>(out) : attn_pick_out<D, DT_BF16, false, NW, SPLIT>(out);
 }
 
-AttnFn attn_pick(int d, int nw, int in, int out, bool causal, int& lds) {
+// The kernel for head dimension d and tile rows / 32 (4: four waves with 32
+// rows each; 1: two waves splitting the keys of 32 rows), its threads and LDS.
+constexpr int kSplitWaves = 2;
+AttnFn attn_pick(int d, int row_waves, int in, int out, bool causal, int& threads, int& lds) {
     if (d == 128) {
-        lds = attn_lds_bytes<128, 4>();
-        return attn_pick_nw<128, 4>(in, out, causal);
+        threads = 256;
+        lds = attn_lds_bytes<128, 4, false>();
+        return attn_pick_nw<128, 4, false>(in, out, causal);
     }
-    if (nw == 4) {
-        lds = attn_lds_bytes<64, 4>();
-        return attn_pick_nw<64, 4>(in, out, causal);
+    if (row_waves == 4) {
+        threads = 256;
+        lds = attn_lds_bytes<64, 4, false>();
+        return attn_pick_nw<64, 4, false>(in, out, causal);
     }
-    if (nw == 2) {
-        lds = attn_lds_bytes<64, 2>();
-        return attn_pick_nw<64, 2>(in, out, causal);
-    }
-    lds = attn_lds_bytes<64, 1>();
-    return attn_pick_nw<64, 1>(in, out, causal);
+    threads = 64 * kSplitWaves;
+    lds = attn_lds_bytes<64, kSplitWaves, true>();
+    return attn_pick_nw<64, kSplitWaves, true>(in, out, causal);
 }
 
 int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Waves per workgroup (32 query rows each): 4 unless that leaves CUs idle
-// (fewer workgroups than the 256 CUs), then 2, then 1; head dimension 128
-// always 4 (its 64 KiB of LDS would hold a smaller workgroup to one wave per
-// SIMD, and the compiler then moves the accumulators through AGPRs).
+// Query rows per workgroup, in units of 32: 4 (four waves, 32 rows each)
+// unless that leaves CUs idle (fewer workgroups than the 256 CUs) with head
+// dimension 64, then 1 (32 rows, two waves splitting the keys: half the
+// chain of dependent key blocks per wave).  Head dimension 128 always 4: its
+// registers leave no room for the split's second ring beside two workgroups
+// per CU.
 int waves_for(int64_t batch, int64_t heads, int64_t n_q, int64_t d) {
-    const int64_t bh = batch * heads;
     if (d == 128) return 4;
-    if (bh * ceil_div64(n_q, 128) >= 256) return 4;
-    if (bh * ceil_div64(n_q, 64) >= 256) return 2;
-    return 1;
+    return batch * heads * ceil_div64(n_q, 128) >= 256 ? 4 : 1;
 }
 
 struct Tensor4 {
@@ -163,9 +164,9 @@ int attention_fwd(int64_t batch, int64_t heads, int64_t n_q, int64_t n_k, int64_
     a.qsign = scale < 0.f ? 0x80008000u : 0u;
     const int in = in_dtype == TGEMM_F16 ? DT_F16 : DT_BF16;
     const int out = out_dtype == TGEMM_F32 ? DT_F32 : in;
-    int lds = 0;
-    const AttnFn fn = attn_pick((int)d, nw, in, out, causal != 0, lds);
-    hipLaunchKernelGGL(fn, dim3((unsigned)a.total), dim3(64 * nw), (unsigned)lds, (hipStream_t)stream, a);
+    int lds = 0, threads = 0;
+    const AttnFn fn = attn_pick((int)d, nw, in, out, causal != 0, threads, lds);
+    hipLaunchKernelGGL(fn, dim3((unsigned)a.total), dim3(threads), (unsigned)lds, (hipStream_t)stream, a);
     return (int)hipGetLastError();
 }
 

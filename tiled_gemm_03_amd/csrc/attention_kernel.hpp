@@ -99,25 +99,32 @@ __device__ __forceinline__ void attn_tile_of(int g, int total, int tiles, bool r
     if (reverse) qt = tiles - 1 - qt;
 }
 
-// LDS bytes of a workgroup: two blocks of 64 keys of K and two of V.
-template <int D, int NW>
-constexpr int attn_lds_bytes() { return 4 * 64 * D * 2; }
+// LDS bytes of a workgroup: two blocks of 64 keys of K and two of V (per
+// wave when the waves split the keys).
+template <int D, int NW, bool SPLIT>
+constexpr int attn_lds_bytes() { return (SPLIT ? NW : 1) * 4 * 64 * D * 2; }
+
+typedef __attribute__((address_space(3))) float lds_attn_float;
 
 // D: head dimension (64 or 128); IN: DT_F16 / DT_BF16; OUT: IN or DT_F32;
-// NW: waves per workgroup (32 NW query rows).
-template <int D, int IN, int OUT, bool CAUSAL, int NW>
+// NW: waves per workgroup, each with 32 query rows of its own (32 NW rows),
+// or (SPLIT) all on the same 32 rows, wave w taking key blocks w, w + NW,
+// w + 2 NW, ... through an LDS ring of its own, the partial results combined
+// through LDS at the end (for grids too small to fill the CUs: the chain of
+// key blocks a wave walks in sequence is NW times shorter).
+template <int D, int IN, int OUT, bool CAUSAL, int NW, bool SPLIT>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2)))
 void attention_kernel(AttnArgs p) {
     static_assert(D == 64 || D == 128, "");
     constexpr int NT = 64 * NW;
-    constexpr int BQ = 32 * NW, BKV = 64;
+    constexpr int BQ = SPLIT ? 32 : 32 * NW, BKV = 64;
     constexpr int KS = D / 32;              // k-steps of the score product
     constexpr int DB = D / 16;              // 16-column blocks of the output
     constexpr int CPR = D / 8;              // 16-byte chunks per K / V row
     constexpr int LOADS = BKV * CPR / NT;   // chunks of K (and of V) per thread and block
     static_assert(LOADS * NT == BKV * CPR, "");
     constexpr int K_BYTES = BKV * D * 2, V_BYTES = BKV * D * 2, BUF = K_BYTES + V_BYTES;
-    static_assert(2 * BUF == attn_lds_bytes<D, NW>(), "");
+    static_assert((SPLIT ? NW : 1) * 2 * BUF == attn_lds_bytes<D, NW, SPLIT>(), "");
     constexpr float TH = 8.f;               // reference-point slack (log2 units)
     // dynamic LDS of attn_lds_bytes<D, NW>() bytes (declared at launch: a
     // static array this size would make the compiler budget registers for
@@ -139,7 +146,7 @@ void attention_kernel(AttnArgs p) {
     const char* Vh = p.V + (b * p.v_sb + h * p.v_sh) * 2;
 
     // Q fragments of this lane's rows (zeros past Nq): d = 32 s + 8 q .. +7
-    const int w_row0 = q0 + 32 * wave;  // first row of the wave
+    const int w_row0 = SPLIT ? q0 : q0 + 32 * wave;  // first row of the wave
     int my_row[2];
     attn_i16x8 qf[2][KS];
 #pragma unroll
@@ -167,14 +174,16 @@ void attention_kernel(AttnArgs p) {
     // (l % 4) ^ ((key / 2) % 4).  V: block j holds rows RPB j + l / LPR, slot
     // l % LPR = 32-byte group (slot / 2) ^ f(row), half slot % 2.
     constexpr int NKB = BKV * D * 2 / 1024;  // 1 KiB blocks of K (and of V) per key block
-    constexpr int PW = NKB / NW;              // of them per wave
-    static_assert(PW * NW == NKB, "");
+    constexpr int PW = SPLIT ? NKB : NKB / NW;  // of them per wave
+    static_assert(SPLIT || PW * NW == NKB, "");
     constexpr int LPR = D / 8, RPB = 64 / LPR;  // V: lanes per row, rows per 1 KiB
-    const int smem_base = (int)(uintptr_t)(lds_void*)smem;
+    // SPLIT: each wave's ring in its own part of the LDS
+    const int ring0 = SPLIT ? wave * 2 * BUF : 0;
+    const int smem_base = (int)(uintptr_t)(lds_void*)smem + ring0;
     int voff_k[PW], voff_v[PW];
 #pragma unroll
     for (int x = 0; x < PW; ++x) {
-        const int j = wave * PW + x;
+        const int j = SPLIT ? x : wave * PW + x;
         {
             const int s = j >> 2, key = 16 * (j & 3) + (lane >> 2);
             const int chunk = (lane & 3) ^ ((key >> 1) & 3);
@@ -202,22 +211,26 @@ void attention_kernel(AttnArgs p) {
                      : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(vo), "s"(rs), "s"(0)
                      : "memory");
     };
-    // LDS: K of blocks j, j + 1 at (j % 2) K_BYTES, V of blocks j, j + 1 at
-    // 2 K_BYTES + (j % 2) V_BYTES
-    auto issue_k = [&](int kb) __attribute__((always_inline)) {
-        const int64_t k_rows = (int64_t)kb * BKV;
+    // The i-th key block a wave walks: block i, or (SPLIT) wave + NW i.  LDS:
+    // K of walk positions i, i + 1 at (i % 2) K_BYTES, V at 2 K_BYTES +
+    // (i % 2) V_BYTES (from the wave's ring)
+    auto kb_of = [&](int i) __attribute__((always_inline)) { return SPLIT ? wave + NW * i : i; };
+    const int blk0 = SPLIT ? 0 : wave * PW;  // first of this wave's 1 KiB blocks
+    auto issue_k = [&](int i) __attribute__((always_inline)) {
+        const int64_t k_rows = (int64_t)kb_of(i) * BKV;
         const i32x4 rk = make_rsrc(Kh + k_rows * p.k_sn * 2, ((Nk - 1 - k_rows) * p.k_sn + D) * 2);
-        const int base = smem_base + (kb & 1) * K_BYTES;
+        const int base = smem_base + (i & 1) * K_BYTES;
 #pragma unroll
-        for (int x = 0; x < PW; ++x) dma(base + (wave * PW + x) * 1024, voff_k[x], rk);
+        for (int x = 0; x < PW; ++x) dma(base + (blk0 + x) * 1024, voff_k[x], rk);
     };
-    auto issue_v = [&](int kb) __attribute__((always_inline)) {
-        const int64_t k_rows = (int64_t)kb * BKV;
+    auto issue_v = [&](int i) __attribute__((always_inline)) {
+        const int64_t k_rows = (int64_t)kb_of(i) * BKV;
         const i32x4 rv = make_rsrc(Vh + k_rows * p.v_sn * 2, ((Nk - 1 - k_rows) * p.v_sn + D) * 2);
-        const int base = smem_base + 2 * K_BYTES + (kb & 1) * V_BYTES;
+        const int base = smem_base + 2 * K_BYTES + (i & 1) * V_BYTES;
 #pragma unroll
-        for (int x = 0; x < PW; ++x) dma(base + (wave * PW + x) * 1024, voff_v[x], rv);
+        for (int x = 0; x < PW; ++x) dma(base + (blk0 + x) * 1024, voff_v[x], rv);
     };
+    lds_attn_char* const ring = lds + ring0;
 
     // per-lane LDS offsets of the fragment reads (within a block's K or V)
     // K fragment (keys 16 g + l%16, d-step s, chunk q): s*4096 + (16 g + l%16)*64 + (q ^ key)*16
@@ -243,9 +256,18 @@ void attention_kernel(AttnArgs p) {
     const attn_i16x8 ones = __builtin_bit_cast(attn_i16x8, u32x4{one2, one2, one2, one2});
     const float c = p.c;
 
-    // S = Q K^T of block kb (K from its ring slot) into sc, both row sets
+    // blocks that need no mask for any row of the workgroup: every key
+    // exists and (causal) is at most the tile's first row
+    int plain = Nk / BKV;
+    if (CAUSAL && (q0 + 1) / BKV < plain) plain = (q0 + 1) / BKV;
+    if (plain > nblocks) plain = nblocks;
+    // the blocks this wave walks, and how many of them are plain
+    const int nwalk = SPLIT ? (nblocks > wave ? (nblocks - wave + NW - 1) / NW : 0) : nblocks;
+    const int pwalk = SPLIT ? (plain > wave ? (plain - wave + NW - 1) / NW : 0) : plain;
+
+    // S = Q K^T of walk position kb (K from its ring slot) into sc, both row sets
     auto scores = [&](int kb, f32x4 (&sc)[2][4]) __attribute__((always_inline)) {
-        lds_attn_char* const kbase = lds + (kb & 1) * K_BYTES + koff;
+        lds_attn_char* const kbase = ring + (kb & 1) * K_BYTES + koff;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             sc[0][g] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -271,9 +293,9 @@ void attention_kernel(AttnArgs p) {
     // registers.
     auto step = [&](int kb, f32x4 (&sc)[2][4], f32x4 (&nx)[2][4], auto masked_t) __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(masked_t)::value;
-        if (kb + 2 < nblocks) issue_k(kb + 2);
-        if (kb + 1 < nblocks) issue_v(kb + 1);
-        const int key0 = kb * BKV;
+        if (kb + 2 < nwalk) issue_k(kb + 2);
+        if (kb + 1 < nwalk) issue_v(kb + 1);
+        const int key0 = kb_of(kb) * BKV;
         // row maxima of this lane's scores (hidden ones -inf)
         float mx[2];
 #pragma unroll
@@ -318,7 +340,7 @@ void attention_kernel(AttnArgs p) {
         // key group at a time (each group's 2 KS MFMAs beside its 8 exp2).
         // On the last block the next scores come from a stale LDS slot and
         // are not used: no branch splits the interleaved code.
-        lds_attn_char* const knext = lds + ((kb + 1) & 1) * K_BYTES + koff;
+        lds_attn_char* const knext = ring + ((kb + 1) & 1) * K_BYTES + koff;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             nx[0][g] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -343,7 +365,7 @@ void attention_kernel(AttnArgs p) {
         }
         // O += P V, 32 keys at a time: P = this lane's keys 4q..4q+3 of
         // groups 2t and 2t+1
-        lds_attn_char* const vbase = lds + 2 * K_BYTES + (kb & 1) * V_BYTES;
+        lds_attn_char* const vbase = ring + 2 * K_BYTES + (kb & 1) * V_BYTES;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             attn_i16x8 pf[2];
@@ -368,49 +390,92 @@ void attention_kernel(AttnArgs p) {
             if constexpr (D == 128) __builtin_amdgcn_sched_barrier(0);
         }
         wait_vmcnt<0>();
-        __syncthreads();
+        if constexpr (!SPLIT) __syncthreads();  // SPLIT: the ring is the wave's own
     };
 
-    // blocks that need no mask for any row of the workgroup: every key
-    // exists and (causal) is at most the tile's first row
-    int plain = Nk / BKV;
-    if (CAUSAL && (q0 + 1) / BKV < plain) plain = (q0 + 1) / BKV;
-    if (plain > nblocks) plain = nblocks;
     // two score buffers, alternating (the loops run two blocks per trip so
     // that each buffer keeps its registers)
     f32x4 sa[2][4], sb[2][4];
-    if (nblocks > 0) {
+    if (nwalk > 0) {
         issue_k(0);
         issue_v(0);
-        if (nblocks > 1) issue_k(1);
+        if (nwalk > 1) issue_k(1);
         wait_vmcnt<0>();
-        __syncthreads();
+        if constexpr (!SPLIT) __syncthreads();
         scores(0, sa);
-        __syncthreads();  // every wave has read K(0) before K(2) replaces it
+        if constexpr (!SPLIT) __syncthreads();  // every wave has read K(0) before K(2) replaces it
     }
     // S(kb) is in sa for even kb, in sb for odd kb: every call below has its
     // buffers fixed at compile time
-    int kb = 0;
-    for (; kb + 1 < plain; kb += 2) {
+    int kb = 0;  // walk position
+    for (; kb + 1 < pwalk; kb += 2) {
         step(kb, sa, sb, BoolTag<false>{});
         step(kb + 1, sb, sa, BoolTag<false>{});
     }
-    if (kb < plain) {
+    if (kb < pwalk) {
         step(kb, sa, sb, BoolTag<false>{});
         ++kb;
     }
-    if (kb < nblocks && (kb & 1)) {
+    if (kb < nwalk && (kb & 1)) {
         step(kb, sb, sa, BoolTag<true>{});
         ++kb;
     }
-    for (; kb + 1 < nblocks; kb += 2) {
+    for (; kb + 1 < nwalk; kb += 2) {
         step(kb, sa, sb, BoolTag<true>{});
         step(kb + 1, sb, sa, BoolTag<true>{});
     }
-    if (kb < nblocks) step(kb, sa, sb, BoolTag<true>{});
+    if (kb < nwalk) step(kb, sa, sb, BoolTag<true>{});
 
     // epilogue: O / L, row my_row, columns 16 db + 4 q .. +3
     constexpr int OB = OUT == DT_F32 ? 4 : 2;
+    if constexpr (SPLIT) {
+        // combine the waves' partial results: each wave's O, reference point
+        // m and L (relative to m) through the LDS its ring used, then wave w
+        // finishes column blocks w DB / NW ..: O = sum_w 2^(m_w - M) O_w over
+        // sum_w 2^(m_w - M) L_w with M = max_w m_w (finite: wave 0 walks
+        // block 0, whose key 0 every row sees; a wave that walked nothing
+        // has m = -inf and weight 0)
+        static_assert(DB % NW == 0, "");
+        __syncthreads();  // every wave is done with its ring
+        lds_f32x4* const co = (lds_f32x4*)(lds_void*)smem;  // [NW][2][DB][64]
+        lds_attn_float* const cm = (lds_attn_float*)(lds + NW * 2 * DB * 64 * 16);  // [NW][2][64]
+        lds_attn_float* const cl = cm + NW * 2 * 64;                               // [NW][2][64]
+#pragma unroll
+        for (int rs = 0; rs < 2; ++rs) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db) co[((wave * 2 + rs) * DB + db) * 64 + lane] = o[rs][db];
+            cm[(wave * 2 + rs) * 64 + lane] = m_run[rs];
+            cl[(wave * 2 + rs) * 64 + lane] = lacc[rs][0];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int rs = 0; rs < 2; ++rs) {
+            float M = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) M = fmaxf(M, cm[(w * 2 + rs) * 64 + lane]);
+            float wt[NW], L = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                const float mw = cm[(w * 2 + rs) * 64 + lane];
+                wt[w] = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+                L += wt[w] * cl[(w * 2 + rs) * 64 + lane];
+            }
+            if (my_row[rs] < Nq) {
+                const float inv = 1.f / L;
+                char* orow = p.O + ((b * p.o_sb + h * p.o_sh) + (int64_t)my_row[rs] * p.o_sn) * OB;
+#pragma unroll
+                for (int c = 0; c < DB / NW; ++c) {
+                    const int db = wave * (DB / NW) + c;
+                    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int w = 0; w < NW; ++w) acc += wt[w] * co[((w * 2 + rs) * DB + db) * 64 + lane];
+                    store4<OUT>(orow + (16 * db + 4 * q) * OB, acc[0] * inv, acc[1] * inv, acc[2] * inv,
+                                acc[3] * inv, false);
+                }
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int rs = 0; rs < 2; ++rs) {
         const float l = lacc[rs][0];
