@@ -275,7 +275,7 @@ def main():
             af = aw.flops()
             abytes = 4 * aw.B * aw.H * aw.N * aw.d * 2
             entry = {"workload": aw.name, "B": aw.B, "H": aw.H, "N": aw.N, "d": aw.d, "causal": aw.causal,
-                     "scale": aw.scale, "waves_per_workgroup": T.attention_waves(aw.B, aw.H, aw.N, aw.d),
+                     "scale": aw.scale, "tile_rows_over_32": T.attention_waves(aw.B, aw.H, aw.N, aw.d),
                      "us_median": med * 1e3, "tflops": af / (med * 1e-3) / 1e12,
                      "frac_of_mfma_peak": af / (med * 1e-3) / 1e12 / PEAK_F16_TFLOPS,
                      "gbs": abytes / (med * 1e-3) / 1e9, "algorithmic_flop": af, "algorithmic_bytes": abytes}

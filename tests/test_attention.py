@@ -212,7 +212,7 @@ CASES = [
 def test_attention_parity_full(case):
     from gpu_helpers import say
     B, H, nq, nk, d, dt, out, scale, causal, layout, tail, waves = case
-    assert T.attention_waves(B, H, nq, d) == waves  # the case runs the workgroup shape it is meant to cover
+    assert T.attention_waves(B, H, nq, d) == waves  # the case runs the tile shape it is meant to cover
     say(f"[attention] case {case}")
     q, k, v = W.attention_inputs(B, H, nq, nk, d, dt, seed=1000 + nq + nk + d)
     o, untouched = _run(q, k, v, dt, out, scale, causal, layout, tail)
