@@ -137,9 +137,10 @@ def _bound(q, k, v, ref, dtype, out, scale, causal, rows=None):
 
 
 def _run(q, k, v, dtype, out, scale, causal, layout="bhnd", tail=0):
-    """Device copies in the given layout (bhnd packed, or bnhd: [B, n, H, d]
-    memory seen through a permuted view), `tail` NaN rows after every head's
-    n_q / n_k rows, a NaN-filled output; returns (o, untouched-guard ok)."""
+    """Device copies in the given layout (bhnd packed; bhnd_odd: rows d + 1
+    elements apart, the extra element NaN; bnhd: [B, n, H, d] memory seen
+    through a permuted view), `tail` NaN rows after every head's n_q / n_k
+    rows, a NaN-filled output; returns (o, untouched-guard ok)."""
     import torch
     from gpu_helpers import TORCH
     B, H, nq, d = q.shape
@@ -149,6 +150,9 @@ def _run(q, k, v, dtype, out, scale, causal, layout="bhnd", tail=0):
         if layout == "bhnd":
             buf = torch.full((B, H, n + tail, d), fill, dtype=TORCH[dt], device="cuda:0")
             view = buf[:, :, :n, :]
+        elif layout == "bhnd_odd":  # rows d + 1 elements apart: odd strides, rows 2-byte aligned
+            buf = torch.full((B, H, n + tail, d + 1), fill, dtype=TORCH[dt], device="cuda:0")
+            view = buf[:, :, :n, :d]
         else:
             buf = torch.full((B, n + tail, H, d), fill, dtype=TORCH[dt], device="cuda:0")
             view = buf[:, :n, :, :].permute(0, 2, 1, 3)
@@ -165,6 +169,8 @@ def _run(q, k, v, dtype, out, scale, causal, layout="bhnd", tail=0):
     # the tail rows of the output buffer are never written
     if layout == "bhnd":
         guard = obuf[:, :, nq:, :]
+    elif layout == "bhnd_odd":
+        guard = torch.cat([obuf[:, :, nq:, :].flatten(), obuf[:, :, :nq, d:].flatten()])
     else:
         guard = obuf[:, nq:, :, :]
     untouched = bool(torch.all(guard == 12345.0).item()) if guard.numel() else True
@@ -203,6 +209,8 @@ CASES = [
     (2, 2, 300, 300, 128, W.BF16, W.BF16, 128 ** -0.5, True, "bnhd", 3, 4),
     (1, 2, 97, 449, 64, W.F16, W.F16, 0.125, False, "bhnd", 2, 1),   # 8 key blocks split over two waves
     (1, 2, 300, 300, 64, W.BF16, W.F32, 0.125, True, "bnhd", 0, 1),  # split, causal, tiles along the diagonal
+    (1, 2, 130, 140, 64, W.F16, W.F16, 0.125, False, "bhnd_odd", 1, 1),         # odd row strides (65)
+    (1, 3, 200, 333, 128, W.BF16, W.F32, 128 ** -0.5, True, "bhnd_odd", 2, 4),  # odd row strides (129)
 ]
 
 

@@ -116,17 +116,13 @@ template <int D, int IN, int OUT, bool CAUSAL, int NW, bool SPLIT>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2)))
 void attention_kernel(AttnArgs p) {
     static_assert(D == 64 || D == 128, "");
-    constexpr int NT = 64 * NW;
     constexpr int BQ = SPLIT ? 32 : 32 * NW, BKV = 64;
     constexpr int KS = D / 32;              // k-steps of the score product
     constexpr int DB = D / 16;              // 16-column blocks of the output
-    constexpr int CPR = D / 8;              // 16-byte chunks per K / V row
-    constexpr int LOADS = BKV * CPR / NT;   // chunks of K (and of V) per thread and block
-    static_assert(LOADS * NT == BKV * CPR, "");
     constexpr int K_BYTES = BKV * D * 2, V_BYTES = BKV * D * 2, BUF = K_BYTES + V_BYTES;
     static_assert((SPLIT ? NW : 1) * 2 * BUF == attn_lds_bytes<D, NW, SPLIT>(), "");
     constexpr float TH = 8.f;               // reference-point slack (log2 units)
-    // dynamic LDS of attn_lds_bytes<D, NW>() bytes (declared at launch: a
+    // dynamic LDS of attn_lds_bytes<D, NW, SPLIT>() bytes (declared at launch: a
     // static array this size would make the compiler budget registers for
     // the one wave per SIMD that it leaves room for, and move the
     // accumulators through AGPRs)
