@@ -217,7 +217,7 @@ int gemm_select_config(int64_t M, int64_t N, int64_t K,
 #define TGEMM_KERNEL_GENERAL 0 /* register-staged, every access checked (ragged or unaligned) */
 #define TGEMM_KERNEL_TILED 1   /* register-staged, whole tiles, aligned operands              */
 #define TGEMM_KERNEL_RING 2    /* direct-to-LDS rings: 16-bit inputs, aligned, K a multiple
-                                  of 128, N % 4 == 0 (configurations 0 and 1)               */
+                                  of 128 or above 128, N % 4 == 0 (configurations 0, 1)     */
 #define TGEMM_KERNEL_DIRECT 3  /* operands straight from memory to registers, no LDS: small,
                                   ragged or unaligned products (configurations 6 and 7)     */
 

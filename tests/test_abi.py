@@ -178,17 +178,21 @@ def _kernel(M, N, K, lda=None, ldb=None, ldc=None, in_dt=T.F16, out_dt=T.F16, ci
 
 def test_kernel_choice_ring_path():
     """The direct-to-LDS ring kernel runs exactly for 16-bit inputs with K a
-    multiple of 128, N % 4 == 0, 16-byte aligned operands and 4-element
-    aligned C rows, whatever M and N (edge tiles store masked); anything else
-    falls back to a register-staged kernel of the same tile."""
+    multiple of 128 or above 128 (the K-tail variant), N % 4 == 0, 16-byte
+    aligned operands and 4-element aligned C rows, whatever M and N (edge
+    tiles store masked); anything else falls back to a register-staged
+    kernel of the same tile."""
     R, TI, GE = T.KERNEL_RING, T.KERNEL_TILED, T.KERNEL_GENERAL
     assert _kernel(8192, 8192, 8192) == R
     assert _kernel(8192, 8192, 8192, in_dt=T.BF16, out_dt=T.F32) == R
     assert _kernel(1024, 2048, 512, out_dt=T.F32, cid=0) == R
     assert _kernel(1024, 2048, 512, out_dt=T.F32, cid=1) == R
     assert _kernel(256, 256, 128, cid=0) == R
-    assert _kernel(8192, 8192, 8192 + 64) == TI          # K not a multiple of 128
-    assert _kernel(8192, 8192, 8192 - 32) == TI
+    assert _kernel(8192, 8192, 8192 + 64) == R           # K not a multiple of 128: the K tail
+    assert _kernel(8192, 8192, 8192 - 32) == R
+    assert _kernel(256, 256, 129, lda=136, cid=0) == R   # K just above 128
+    assert _kernel(256, 256, 120, cid=0) == TI           # K below 128 and not a multiple of it
+    assert _kernel(256, 256, 64, cid=1) == TI
     assert _kernel(8192 - 256, 8192, 8192) == R          # still whole tiles
     assert _kernel(8191, 8192, 8192) == R                # ragged M: masked edge tiles
     assert _kernel(8191, 8000, 8192) == R                # ragged M and N

@@ -104,7 +104,8 @@ def check_bound(d, o, z, a, b, in_dt, out_dt, c_old, bias, bias_dt, bias_kind, a
 # 128x128 tiles, register-staged whole tiles, direct
 SHAPES = [((256, 512, 384), "ring big", 0), ((1024, 2048, 512), "ring mid", 1), ((128, 256, 512), "tiled", -1),
           ((127, 255, 512), "direct", -1), ((33, 47, 255), "direct ragged", -1),
-          ((1000, 1200, 512), "ring big ragged", 0), ((777, 1000, 256), "ring mid ragged", 1)]
+          ((1000, 1200, 512), "ring big ragged", 0), ((777, 1000, 256), "ring mid ragged", 1),
+          ((1000, 1208, 1000), "ring big k tail", 0), ((300, 264, 200), "ring mid k tail", 1)]
 EPILOGUES = [
     (1.0, 0.0, None, None, oracle.ACT_RELU),
     (0.5, 2.0, W.F32, oracle.BIAS_COL, oracle.ACT_NONE),

@@ -105,6 +105,43 @@ def test_layouts_against_oracle(lay, shape):
 
 
 @pytest.mark.parametrize("lay", LAYOUTS, ids=lid)
+@pytest.mark.parametrize("cid", [0, 1])
+def test_layouts_ring_k_tail(lay, cid):
+    """K not a multiple of 128: the ring kernel walks the largest multiple
+    and adds the rest in 32-wide steps from registers (forced, path
+    asserted).  Tails of 1, 72, 127 and 104 elements, K odd and K % 8 != 0;
+    leading dimensions padded to 16-byte rows with NaN, so a k-contiguous
+    operand has NaN right after its K-th element: it must be masked, not
+    multiplied by zero."""
+    cases = (((1001, 1004, 129), W.F16, W.F16), ((260, 516, 200), W.BF16, W.F32),
+             ((513, 260, 1023), W.F16, W.F32), ((256, 256, 1000), W.BF16, W.BF16))
+    pad = lambda e, mult: (-e) % mult or mult
+    for (M, N, K), in_dt, out_dt in cases:
+        if lay[2] == COL:
+            M, N = N, M  # keep the odd size in the role of M of the product the call runs
+        ext = {"a": (K, M), "b": (N, K), "c": (N, M)}
+        pads = (pad(ext["a"][lay[0]], 8), pad(ext["b"][lay[1]], 8), pad(ext["c"][lay[2]], 4))
+        a, b = W.random_inputs(M, N, K, in_dt, seed=K + cid + 3 * lay[0] + 5 * lay[1] + 7 * lay[2])
+        c, o, kind = run_layout(a, b, in_dt, out_dt, lay, cid=cid, pads=pads, label="ring k tail")
+        assert kind == T.KERNEL_RING, kind
+        G.check(c, o, a, b, in_dt, out_dt, K, label=f"ring k tail {M}x{N}x{K} {lid(lay)} cfg{cid}")
+
+
+@pytest.mark.parametrize("lay", [(ROW, ROW, ROW), (COL, ROW, ROW), (ROW, COL, ROW)], ids=lid)
+def test_ring_k_tail_large_sampled(lay):
+    """8192 x 8192 x 8000 fp16 (a K tail of 64 after 62 ring trips of 128),
+    the launch configuration of the large products, checked on 64 x 64
+    sampled outputs."""
+    M, N, K = 8192, 8192, 8000
+    a, b = W.random_inputs(M, N, K, W.F16, seed=8000)
+    rows = W.sample_indices(M, 64, 8001)
+    cols = W.sample_indices(N, 64, 8002)
+    c, o, kind = run_layout(a, b, W.F16, W.F16, lay, rows=rows, cols=cols, label="ring k tail 8192^2x8000")
+    assert kind == T.KERNEL_RING
+    G.check(c, o, a, b, W.F16, W.F16, K, rows=rows, cols=cols, label=f"8192^2x8000 {lid(lay)}")
+
+
+@pytest.mark.parametrize("lay", LAYOUTS, ids=lid)
 def test_layouts_integer_bitwise(lay):
     """Small-integer inputs: every sum is exact in fp32 whatever its order,
     so C must equal the oracle rounded to the output type bit for bit, for

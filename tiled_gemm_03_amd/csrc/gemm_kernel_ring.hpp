@@ -1,8 +1,9 @@
 // gemm_kernel_ring.hpp -- the gfx950 fast path of the tiled matrix product
-// for 16-bit inputs (fp16 / bf16), aligned operands, K a multiple of 128,
-// N % 4 == 0 (any M and N otherwise: edge tiles store masked): direct-to-LDS
-// loads into
-// multi-stage LDS rings and v_mfma_f32_16x16x32_{f16,bf16}.
+// for 16-bit inputs (fp16 / bf16), aligned operands, N % 4 == 0 (any M and N
+// otherwise: edge tiles store masked): direct-to-LDS loads into multi-stage
+// LDS rings and v_mfma_f32_16x16x32_{f16,bf16}.  K a multiple of 128, or
+// (variant KT) any K above 128: the rings walk the largest multiple of 128 and
+// the rest takes a few steps from registers.
 //
 // The method is the tiled kernel of page "企业官网建设流程全解析" §3.3 (one
 // workgroup per BM x BN tile of C, K walked in steps, A and B tiles staged in
@@ -163,7 +164,7 @@ struct RingCfg {
     static constexpr int THREADS = 64 * WM * WN, WAVES = WM * WN;
     static constexpr int WTM = BM / WM, WTN = BN / WN;
     static constexpr int FM = WTM / 16, FN = WTN / 16;
-    static constexpr int K_MULT = 4 * BK;          // K must be a multiple of this
+    static constexpr int K_MULT = 4 * BK;          // the rings walk K in multiples of this
     // Ring of each operand for the layouts of A and B.  A k-contiguous
     // operand reads 64 bytes of every row per step, half a 128-byte line, and
     // such loads run at about 60% of the rate of whole lines: a k-contiguous
@@ -207,13 +208,21 @@ struct RingCfg {
     static_assert(WTM % 16 == 0 && WTN % 16 == 0, "");
 };
 
-// Preconditions (checked by the host): 16-bit inputs; K % K_MULT == 0 and
-// N % 4 == 0 (any M and N otherwise: edge tiles store masked);
+// Preconditions (checked by the host): 16-bit inputs; K % K_MULT == 0, or
+// K > K_MULT with KT; N % 4 == 0 (any M and N otherwise: edge tiles store
+// masked);
 // A and B 16-byte aligned with lda and ldb multiples of 8; C aligned for
 // 4-element stores with ldc % 4 == 0; the buffer offsets (a tile's rows or
 // columns of each operand over K + LOOKAHEAD * BK of K) below 2^31 bytes.  LA / LB: LAYOUT_ROW or
 // LAYOUT_COL; C is row-major.
-template <class T, int IN, int OUT, int LA, int LB, bool EPI = false>
+//
+// KT (K tail): the rings walk the largest multiple of K_MULT below K; the
+// remaining K % K_MULT values take steps of 32 whose fragments are loaded
+// from global memory straight into registers (no LDS, no barrier), with the
+// elements at k >= K zeroed (inside the buffer range they are other elements
+// of the operand or row padding, which may hold anything).  The main loop is
+// the same code as without KT.
+template <class T, int IN, int OUT, int LA, int LB, bool EPI = false, bool KT = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(T::THREADS, T::THREADS),
                           amdgpu_waves_per_eu(T::OCC * T::WAVES / 4 > 0 ? T::OCC * T::WAVES / 4 : 1)))
 void gemm_kernel_ring(GemmArgs p) {
@@ -257,16 +266,24 @@ void gemm_kernel_ring(GemmArgs p) {
     // Buffer resource of one operand: it starts at the tile's corner and ends
     // at the operand's last element (empty when K = 0: no load is issued
     // then).  outer0: the tile's first row (A) / column (B); outer: M / N.
-    auto operand_rsrc = [&](auto op_t, const char* X, int64_t ld, int outer0, int outer) __attribute__((always_inline)) {
+    auto operand_start = [&](auto op_t, const char* X, int64_t ld, int outer0) __attribute__((always_inline)) {
         using O = decltype(op_t);
-        if (K <= 0) return make_rsrc(X, 0);
-        if constexpr (O::KC)  // element (o, k) at o * ld + k
-            return make_rsrc(X + (int64_t)outer0 * ld * 2, ((int64_t)(outer - 1 - outer0) * ld + K) * 2);
-        else                  // element (o, k) at k * ld + o
-            return make_rsrc(X + (int64_t)outer0 * 2, ((int64_t)(K - 1) * ld + outer - outer0) * 2);
+        return O::KC ? X + (int64_t)outer0 * ld * 2 : X + (int64_t)outer0 * 2;
     };
-    const i32x4 rs_a = operand_rsrc(OA{}, p.A, lda, m0, p.M);
-    const i32x4 rs_b = operand_rsrc(OB_{}, p.B, ldb, n0, p.N);
+    auto operand_bytes = [&](auto op_t, int64_t ld, int outer0, int outer) __attribute__((always_inline)) {
+        using O = decltype(op_t);
+        if (K <= 0) return (int64_t)0;
+        if constexpr (O::KC)  // element (o, k) at o * ld + k
+            return ((int64_t)(outer - 1 - outer0) * ld + K) * 2;
+        else                  // element (o, k) at k * ld + o
+            return ((int64_t)(K - 1) * ld + outer - outer0) * 2;
+    };
+    const char* const a_start = operand_start(OA{}, p.A, lda, m0);
+    const char* const b_start = operand_start(OB_{}, p.B, ldb, n0);
+    const int64_t a_bytes = operand_bytes(OA{}, lda, m0, p.M);
+    const int64_t b_bytes = operand_bytes(OB_{}, ldb, n0, p.N);
+    const i32x4 rs_a = make_rsrc(a_start, a_bytes);
+    const i32x4 rs_b = make_rsrc(b_start, b_bytes);
     // per-lane byte offset of a load (block blk of a stage): lane l fills
     // byte 16 l of the block with the chunk the layout puts there
     auto load_voff = [&](auto op_t, int blk, int64_t ld) __attribute__((always_inline)) {
@@ -438,7 +455,8 @@ void gemm_kernel_ring(GemmArgs p) {
         });
     };
 
-    const int nk = K / T::BK;  // a multiple of U (host precondition)
+    // steps of the rings: a multiple of U (without KT, K % K_MULT == 0)
+    const int nk = K / (T::BK * P::U) * P::U;
     if (nk > 0) {
         // prologue: the loads of the virtual steps before step 0, then the
         // fragments of step 0
@@ -462,6 +480,45 @@ void gemm_kernel_ring(GemmArgs p) {
         for (int s = 0; s < nk; s += P::U) static_for<0, P::U>([&](auto u) __attribute__((always_inline)) { step(u); });
         // no load may still be writing LDS when the workgroup ends
         wait_vmcnt<0>();
+    }
+    if constexpr (KT) {
+        // the K tail: steps of 32 from k = 32 nk, fragments from global
+        // memory through buffer loads over the same ranges as the rings'
+        auto tail_rsrc = [&](const char* base, int64_t bytes) __attribute__((always_inline)) {
+            bytes = (bytes + 3) & ~(int64_t)3;
+            const int n = bytes <= 0 ? 0 : bytes > 0x7fffffffLL ? 0x7fffffff : (int)bytes;
+            return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, n, 0x00020000);
+        };
+        const auto ta = tail_rsrc(a_start, a_bytes);
+        const auto tb = tail_rsrc(b_start, b_bytes);
+        // lane's 8 k (k ..) of row / column o (from the tile's corner)
+        auto tail_frag = [&](auto op_t, const auto& rs, int o, int64_t ld, int k) __attribute__((always_inline)) {
+            using O = decltype(op_t);
+            i16x8 v;
+            if constexpr (O::KC) {
+                v = __builtin_bit_cast(i16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(((int64_t)o * ld + k) * 2), 0, 0));
+            } else {
+#pragma unroll
+                for (int t = 0; t < 8; ++t)
+                    v[t] = (short)__builtin_amdgcn_raw_buffer_load_b16(rs, (int)(((int64_t)(k + t) * ld + o) * 2), 0, 0);
+            }
+            const int kv = K - k;  // elements of the 8 below K
+#pragma unroll
+            for (int t = 0; t < 8; ++t) v[t] = t < kv ? v[t] : (short)0;
+            return v;
+        };
+        for (int k0 = nk * T::BK; k0 < K; k0 += T::BK) {
+            const int k = k0 + 8 * q;
+            static_for<0, T::FN>([&](auto j_t) __attribute__((always_inline)) {
+                constexpr int j = decltype(j_t)::value;
+                fb[0][j] = tail_frag(OB_{}, tb, wn * T::WTN + 16 * j + i16, ldb, k);
+            });
+            static_for<0, T::FM>([&](auto i_t) __attribute__((always_inline)) {
+                constexpr int i = decltype(i_t)::value;
+                fa[0][i] = tail_frag(OA{}, ta, wm * T::WTM + 16 * i + i16, lda, k);
+            });
+            static_for<0, NMF>([&](auto mt) __attribute__((always_inline)) { mfma_one(0, decltype(mt)::value); });
+        }
     }
 
     // a7: epilogue.  acc[i][j] of lane l is C[row 16 i + l%16][columns

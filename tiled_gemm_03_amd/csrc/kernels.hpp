@@ -39,9 +39,10 @@ KernelFn tiled_kernel_tiny(int in, int out, bool fast, bool epi);
 KernelFn tiled_kernel_f32(int cfg, int in, int out, bool fast, bool epi);
 
 // Ring kernel of CFG_BIG or CFG_MID for (in, out) and the layouts of A and B
-// (LAYOUT_ROW / LAYOUT_COL).  k_ring_big.hip, k_ring_mid.hip.
-KernelFn ring_kernel_big(int in, int out, int la, int lb, bool epi);
-KernelFn ring_kernel_mid(int in, int out, int la, int lb, bool epi);
+// (LAYOUT_ROW / LAYOUT_COL); kt: the variant with the K tail (K not a
+// multiple of 128).  k_ring_big.hip, k_ring_mid.hip.
+KernelFn ring_kernel_big(int in, int out, int la, int lb, bool epi, bool kt);
+KernelFn ring_kernel_mid(int in, int out, int la, int lb, bool epi, bool kt);
 
 // Direct kernel for (in, out), the layouts of A and B, and whether each
 // operand takes 16-byte loads.  k_direct.hip.
@@ -50,8 +51,12 @@ KernelFn direct_kernel(int in, int out, int la, int lb, bool va, bool vb, bool e
 // The fused-epilogue halves of the largest families, compiled in units of
 // their own (k_*_fused.hip) so that the build runs them in parallel.
 KernelFn tiled_kernel_big_fused(int in, int out, bool fast);
-KernelFn ring_kernel_big_fused(int in, int out, int la, int lb);
-KernelFn ring_kernel_mid_fused(int in, int out, int la, int lb);
+KernelFn ring_kernel_big_fused(int in, int out, int la, int lb, bool kt);
+KernelFn ring_kernel_mid_fused(int in, int out, int la, int lb, bool kt);
+KernelFn ring_kernel_big_kt(int in, int out, int la, int lb);
+KernelFn ring_kernel_mid_kt(int in, int out, int la, int lb);
+KernelFn ring_kernel_big_fused_kt(int in, int out, int la, int lb);
+KernelFn ring_kernel_mid_fused_kt(int in, int out, int la, int lb);
 KernelFn direct_kernel_fused(int in, int out, int la, int lb, bool va, bool vb);
 
 }  // namespace tgemm

@@ -26,10 +26,10 @@ struct ConfigEntry {
     // register-staged kernels (row-major operands only)
     KernelFn (*tiled)(int in, int out, bool fast, bool epi);
     // direct-to-LDS ring kernels of the same output tile (aligned operands,
-    // K a multiple of ring_k_mult, N % 4 == 0, any M, any operand layout),
-    // with their block_k,
-    // stage count and LDS bytes
-    KernelFn (*ring)(int in, int out, int la, int lb, bool epi);
+    // N % 4 == 0, any M, any operand layout; the rings walk K in multiples of
+    // ring_k_mult, kt: the variant that adds the rest of K), with their
+    // block_k, stage count and LDS bytes
+    KernelFn (*ring)(int in, int out, int la, int lb, bool epi, bool kt);
     int ring_bk, ring_stages, ring_k_mult, ring_lds;
     int ring_lookahead;               // steps of ring_bk that the ring loads past K
     int ring_a_bk, ring_a_stages;     // the ring of a row-major A
@@ -205,7 +205,9 @@ bool ring_applies(const ConfigEntry& c, const Problem& p) {
     if (c.ring == nullptr || !tuning().direct_lds) return false;
     // the ring loads ring_lookahead steps past K
     const int64_t extra = (int64_t)c.ring_lookahead * c.ring_bk;
-    return loads_aligned(c, p) && stores_aligned(p) && p.K % c.ring_k_mult == 0 && p.N % 4 == 0 &&
+    // K a multiple of ring_k_mult, or above it (the K-tail variant)
+    return loads_aligned(c, p) && stores_aligned(p) && (p.K % c.ring_k_mult == 0 || p.K > c.ring_k_mult) &&
+           p.N % 4 == 0 &&
            operand_reach(p.la == LAYOUT_ROW, c.bm, p.lda, p.K, extra, c.eb) < (1LL << 31) &&
            operand_reach(p.lb == LAYOUT_COL, c.bn, p.ldb, p.K, extra, c.eb) < (1LL << 31);
 }
@@ -320,7 +322,7 @@ int make_plan(const Problem& p, int config_id, Plan& plan) {
     const ConfigEntry& c = kConfigs[plan.config];
     if (!c.direct && ring_applies(c, p)) {
         plan.kind = TGEMM_KERNEL_RING;
-        plan.fn = c.ring(p.in, p.out, p.la, p.lb, p.ep.on);
+        plan.fn = c.ring(p.in, p.out, p.la, p.lb, p.ep.on, p.K % c.ring_k_mult != 0);
         if (plan.fn == nullptr) return TGEMM_ERR_DTYPE;
         return ceil_div(p.M, c.bm) * ceil_div(p.N, c.bn) > 0x7fffffff ? TGEMM_ERR_DIM : TGEMM_OK;
     }
