@@ -178,10 +178,11 @@ def _kernel(M, N, K, lda=None, ldb=None, ldc=None, in_dt=T.F16, out_dt=T.F16, ci
 
 def test_kernel_choice_ring_path():
     """The direct-to-LDS ring kernel runs exactly for 16-bit inputs with K a
-    multiple of 128 or above 128 (the K-tail variant), N % 4 == 0, 16-byte
-    aligned operands and 4-element aligned C rows, whatever M and N (edge
-    tiles store masked); anything else falls back to a register-staged
-    kernel of the same tile."""
+    multiple of 128 or above 128 (the K-tail variant) and 16-byte aligned
+    operands, whatever M, N and the alignment of C (edge tiles store masked;
+    partial column groups and unaligned C rows through the fused epilogue's
+    stores); anything else falls back to a register-staged kernel of the same
+    tile."""
     R, TI, GE = T.KERNEL_RING, T.KERNEL_TILED, T.KERNEL_GENERAL
     assert _kernel(8192, 8192, 8192) == R
     assert _kernel(8192, 8192, 8192, in_dt=T.BF16, out_dt=T.F32) == R
@@ -197,8 +198,9 @@ def test_kernel_choice_ring_path():
     assert _kernel(8191, 8192, 8192) == R                # ragged M: masked edge tiles
     assert _kernel(8191, 8000, 8192) == R                # ragged M and N
     assert _kernel(8192, 8190, 8192) == GE               # B rows not whole 16-byte chunks
-    assert _kernel(8192, 8192, 8192, ldc=8194) == GE     # C rows not 4-element aligned
-    assert _kernel(8192, 8190, 8192, ldb=8192, ldc=8192) == GE  # N % 4 != 0: partial column groups
+    assert _kernel(8192, 8192, 8192, ldc=8194) == R      # C rows not 4-element aligned
+    assert _kernel(8192, 8192, 8192, offs=(0, 0, 1)) == R  # C base not 4-element aligned
+    assert _kernel(8192, 8190, 8192, ldb=8192, ldc=8192) == R   # N % 4 != 0: partial column groups
     assert _kernel(8192, 8192, 8192, lda=8196) == GE     # rows not whole 16-byte chunks
     assert _kernel(8192, 8192, 8192, lda=8192 + 8) == R  # padded, still aligned
     assert _kernel(8192, 8192, 8192, offs=(1, 0, 0)) == GE

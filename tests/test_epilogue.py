@@ -155,6 +155,26 @@ def test_fused_layouts_bitwise(lay, shape):
             assert np.array_equal(d, o), f"{int((d != o).sum())} entries differ"
 
 
+@pytest.mark.parametrize("shape", [((300, 1030, 512), 1), ((1000, 1202, 1000), 0)], ids=["mid", "big_k_tail"])
+def test_fused_ring_partial_groups(shape):
+    """The fused epilogue on the ring kernel (forced, path asserted) with N %
+    4 == 2 (a column-major B keeps the operands aligned) and ldc = N: the
+    last group of each row is partial and the C rows are not 4-element
+    aligned, in loads of the old C and in stores; exact integer case."""
+    (M, N, K), cid = shape
+    lay = (ROW, COL, ROW)
+    a, b = W.integer_inputs(M, N, K, W.F16, seed=N)
+    rng = np.random.default_rng(5)
+    c_old = rng.integers(-8, 9, size=(M, N)).astype(np.float32)
+    for bias_kind, act in ((oracle.BIAS_COL, oracle.ACT_RELU), (oracle.BIAS_ROW, oracle.ACT_NONE)):
+        bias = rng.integers(-50, 51, size=M if bias_kind == oracle.BIAS_ROW else N).astype(np.float32)
+        d, kind = run_fused(a, b, W.F16, W.F32, c_old, bias, W.F32, bias_kind, 2.0, -0.5, act, lay=lay, cid=cid,
+                            label="ring partial groups")
+        assert kind == T.KERNEL_RING
+        o, _ = expected(a, b, W.F16, W.F32, c_old, bias, W.F32, bias_kind, 2.0, -0.5, act)
+        assert np.array_equal(d, o), f"{int((d != o).sum())} entries differ"
+
+
 @pytest.mark.parametrize("cid", range(8))
 def test_fused_every_configuration_bitwise(cid):
     """Every configuration (forced), exact integer case, fp16 output."""

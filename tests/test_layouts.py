@@ -202,6 +202,42 @@ def test_layouts_write_only_c(lay):
     G.check(G.values(c, W.F16), G.oracle_values(a, b, W.F16), a, b, W.F16, W.F16, K, label="canary")
 
 
+@pytest.mark.parametrize("lay", LAYOUTS, ids=lid)
+@pytest.mark.parametrize("cid", [0, 1])
+def test_layouts_ring_partial_groups_unaligned_c(lay, cid):
+    """The ring kernel (forced, path asserted) with M and N both 2 mod 4 and
+    C rows 3 elements longer than C (ldc odd: no 4-element aligned store),
+    operands padded to 16-byte rows: the last column group of every row is
+    partial and every store unaligned, through the fused epilogue's stores
+    with the identity epilogue.  C starts as NaN, its padding and the memory
+    after it hold sentinels: every entry of C is written and nothing else,
+    and with small-integer inputs the values are exact."""
+    M, N, K = 302, 1030, 384 if cid == 1 else 520
+    pad = lambda e, mult: (-e) % mult or mult
+    stored = {"a": (K, M), "b": (N, K)}  # stored row length for (row-major, column-major)
+    for in_dt, out_dt in ((W.F16, W.F16), (W.BF16, W.F32)):
+        a, b = W.integer_inputs(M, N, K, in_dt, seed=cid + 3 * lay[0] + 5 * lay[1] + 7 * lay[2])
+        ad = place(a, in_dt, lay[0], pad(stored["a"][lay[0]], 8))
+        bd = place(b, in_dt, lay[1], pad(stored["b"][lay[1]], 8))
+        rows, cols = (M, N) if lay[2] == ROW else (N, M)
+        tdt = G.TORCH[out_dt]
+        flat = torch.full((rows * (cols + 3) + 64,), float("nan"), dtype=tdt, device=G.DEV)
+        store = flat[:rows * (cols + 3)].view(rows, cols + 3)
+        store[:, cols:] = 12345.0
+        flat[rows * (cols + 3):] = -777.0
+        c = store[:, :cols] if lay[2] == ROW else store[:, :cols].t()
+        kind, _ = kernel_of(ad, bd, c, in_dt, out_dt, cid)
+        G.say(f"[case] ring partial groups {M}x{N}x{K} {lid(lay)} cfg{cid} in={in_dt} out={out_dt} kind={kind}")
+        assert kind == T.KERNEL_RING, kind
+        G.run(ad, bd, c, config=cid)
+        assert not bool(torch.isnan(c).any()), "some entries of C were not written"
+        assert bool((store[:, cols:] == 12345.0).all()), "padding was written"
+        assert bool((flat[rows * (cols + 3):] == -777.0).all()), "memory after C was written"
+        got = G.values(c, out_dt)
+        want = G.round_to(G.oracle_values(a, b, in_dt), out_dt)
+        assert np.array_equal(got, want), f"{int((got != want).sum())} entries differ"
+
+
 def test_layouts_k_zero():
     for lay in LAYOUTS:
         G.say(f"[case] layout K=0 {lid(lay)}")

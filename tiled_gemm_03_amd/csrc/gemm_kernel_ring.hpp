@@ -1,7 +1,7 @@
 // gemm_kernel_ring.hpp -- the gfx950 fast path of the tiled matrix product
-// for 16-bit inputs (fp16 / bf16), aligned operands, N % 4 == 0 (any M and N
-// otherwise: edge tiles store masked): direct-to-LDS loads into multi-stage
-// LDS rings and v_mfma_f32_16x16x32_{f16,bf16}.  K a multiple of 128, or
+// for 16-bit inputs (fp16 / bf16), aligned operands, any M and N (edge tiles
+// store masked): direct-to-LDS loads into multi-stage LDS rings and
+// v_mfma_f32_16x16x32_{f16,bf16}.  K a multiple of 128, or
 // (variant KT) any K above 128: the rings walk the largest multiple of 128 and
 // the rest takes a few steps from registers.
 //
@@ -209,10 +209,11 @@ struct RingCfg {
 };
 
 // Preconditions (checked by the host): 16-bit inputs; K % K_MULT == 0, or
-// K > K_MULT with KT; N % 4 == 0 (any M and N otherwise: edge tiles store
-// masked);
-// A and B 16-byte aligned with lda and ldb multiples of 8; C aligned for
-// 4-element stores with ldc % 4 == 0; the buffer offsets (a tile's rows or
+// K > K_MULT with KT; A and B 16-byte aligned with lda and ldb multiples of
+// 8; without EPI, N % 4 == 0 and C aligned for 4-element stores with
+// ldc % 4 == 0 (the fused epilogue, EPI, takes any N and C alignment; a plain
+// product that needs it runs EPI with alpha 1, beta 0, no bias and no
+// activation, which store the product unchanged); the buffer offsets (a tile's rows or
 // columns of each operand over K + LOOKAHEAD * BK of K) below 2^31 bytes.  LA / LB: LAYOUT_ROW or
 // LAYOUT_COL; C is row-major.
 //
@@ -541,13 +542,17 @@ void gemm_kernel_ring(GemmArgs p) {
             held[b] = acc[b / T::FN][b % T::FN];
             if constexpr (b >= PB) asm volatile("" : "+v"(held[b]));
         });
-        fused_epilogue<OUT, NMF, 4, PB, true>(
+        // any N and C alignment: the last group of a row may be partial
+        // (element stores, in the run-time loop of values read back from
+        // LDS, away from the accumulators) and C rows need not be aligned
+        // for 4-element stores (p.vec_c)
+        fused_epilogue<OUT, NMF, 4, PB, false>(
             p, region, [&](auto b_t) { constexpr int b = decltype(b_t)::value; return held[b]; },
             [&](int b, int, int& row, int& col, int& n, bool& vec) {
                 row = m0 + wm * T::WTM + 16 * (b / T::FN) + i16;
                 col = n0 + wn * T::WTN + 16 * (b % T::FN) + 4 * q;
-                n = row < p.M && col < p.N ? 4 : 0;  // N % 4 == 0: whole groups
-                vec = true;
+                n = row < p.M && col < p.N ? (p.N - col < 4 ? p.N - col : 4) : 0;
+                vec = p.vec_c;
             });
         return;
     }

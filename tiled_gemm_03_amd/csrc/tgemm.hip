@@ -26,8 +26,9 @@ struct ConfigEntry {
     // register-staged kernels (row-major operands only)
     KernelFn (*tiled)(int in, int out, bool fast, bool epi);
     // direct-to-LDS ring kernels of the same output tile (aligned operands,
-    // N % 4 == 0, any M, any operand layout; the rings walk K in multiples of
-    // ring_k_mult, kt: the variant that adds the rest of K), with their
+    // any M and N, any operand layout; the rings walk K in multiples of
+    // ring_k_mult, kt: the variant that adds the rest of K; epi: the fused
+    // epilogue, also taken when the plain one cannot store C), with their
     // block_k, stage count and LDS bytes
     KernelFn (*ring)(int in, int out, int la, int lb, bool epi, bool kt);
     int ring_bk, ring_stages, ring_k_mult, ring_lds;
@@ -205,12 +206,17 @@ bool ring_applies(const ConfigEntry& c, const Problem& p) {
     if (c.ring == nullptr || !tuning().direct_lds) return false;
     // the ring loads ring_lookahead steps past K
     const int64_t extra = (int64_t)c.ring_lookahead * c.ring_bk;
-    // K a multiple of ring_k_mult, or above it (the K-tail variant)
-    return loads_aligned(c, p) && stores_aligned(p) && (p.K % c.ring_k_mult == 0 || p.K > c.ring_k_mult) &&
-           p.N % 4 == 0 &&
+    // K a multiple of ring_k_mult, or above it (the K-tail variant); any N
+    // and C alignment (ring_plain_stores)
+    return loads_aligned(c, p) && (p.K % c.ring_k_mult == 0 || p.K > c.ring_k_mult) &&
            operand_reach(p.la == LAYOUT_ROW, c.bm, p.lda, p.K, extra, c.eb) < (1LL << 31) &&
            operand_reach(p.lb == LAYOUT_COL, c.bn, p.ldb, p.K, extra, c.eb) < (1LL << 31);
 }
+
+// Whether the ring kernel's plain epilogue can store C: whole groups of four
+// columns (N % 4 == 0) in rows aligned for 4-element stores.  Otherwise the
+// fused epilogue runs, with the identity epilogue when none was asked for.
+bool ring_plain_stores(const Problem& p) { return stores_aligned(p) && p.N % 4 == 0; }
 
 // Whether the direct kernel's buffer offsets fit (32 rows / columns of each
 // operand over K + 320 of K).
@@ -270,7 +276,9 @@ int table_choice(const Problem& p) {
     }
     if (!row_row(p)) {
         if (tiles_for(kConfigs[CFG_BIG], M, N) >= 256 && ring_applies(kConfigs[CFG_BIG], p)) return CFG_BIG;
-        if (ring_applies(kConfigs[CFG_MID], p)) return CFG_MID;
+        // small products whose C the ring could store only through the fused
+        // epilogue stay on the direct kernel
+        if (ring_applies(kConfigs[CFG_MID], p) && (ring_plain_stores(p) || !small)) return CFG_MID;
         return CFG_DIRECT;
     }
     if (tiles_for(kConfigs[CFG_BIG], M, N) >= 256) return CFG_BIG;
@@ -322,7 +330,7 @@ int make_plan(const Problem& p, int config_id, Plan& plan) {
     const ConfigEntry& c = kConfigs[plan.config];
     if (!c.direct && ring_applies(c, p)) {
         plan.kind = TGEMM_KERNEL_RING;
-        plan.fn = c.ring(p.in, p.out, p.la, p.lb, p.ep.on, p.K % c.ring_k_mult != 0);
+        plan.fn = c.ring(p.in, p.out, p.la, p.lb, p.ep.on || !ring_plain_stores(p), p.K % c.ring_k_mult != 0);
         if (plan.fn == nullptr) return TGEMM_ERR_DTYPE;
         return ceil_div(p.M, c.bm) * ceil_div(p.N, c.bn) > 0x7fffffff ? TGEMM_ERR_DIM : TGEMM_OK;
     }
