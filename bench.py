@@ -255,6 +255,30 @@ def main():
             fused.append({"epilogue": name, "us_median": med * 1e3, "tflops": flops / (med * 1e-3) / 1e12})
         del bias
 
+    # the ring kernel's edge paths on sub-views of the same operands: a K
+    # tail (K not a multiple of 128) and partial column groups with C rows
+    # not 4-element aligned (the fused epilogue's stores with the identity
+    # epilogue); torch.matmul on the same views for context
+    edges = []
+    if not args.no_per_config:
+        kinds = {0: "general", 1: "tiled", 2: "ring", 3: "direct"}
+        for name, m_, n_, k_ in (("K tail: K = 8000", w.M, w.N, 8000),
+                                 ("N = 8190, ldc = 8190 (partial groups, unaligned C rows)", w.M, 8190, w.K)):
+            ea, eb = a[:m_, :k_], b[:k_, :n_]
+            ec = torch.empty((m_, n_), dtype=torch.float16, device=dev)
+            call = lambda: T.gemm_tensors(ea, eb, ec, stream=stream.cuda_stream)
+            _, eev = time_calls(call, 20, 3, stream)
+            _, tev = time_calls(lambda: torch.matmul(ea, eb, out=ec), 20, 3, stream)
+            (xa, lda_), (xb, ldb_), (xc, ldc_) = T._layout(ea), T._layout(eb), T._layout(ec)
+            kind, ecfg = T.gemm_select_kernel_t(m_, n_, k_, ea.data_ptr(), lda_, xa, eb.data_ptr(), ldb_, xb,
+                                                ec.data_ptr(), ldc_, xc, w.in_dtype, w.out_dtype)
+            med, tmed = float(np.median(eev)), float(np.median(tev))
+            ef = 2.0 * m_ * n_ * k_
+            edges.append({"case": name, "M": m_, "N": n_, "K": k_, "config": T.gemm_config_info(ecfg)["name"],
+                          "kernel": kinds.get(kind, str(kind)), "us_median": med * 1e3,
+                          "tflops": ef / (med * 1e-3) / 1e12, "torch_matmul_us_median": tmed * 1e3})
+            del ec
+
     # the attention forward (attention_fwd) on its workloads: O = softmax(scale
     # Q K^T) V per head, fp16, inputs resident; FLOPs of the two products over
     # the visible (query, key) pairs, HBM bytes of Q, K, V and O once
@@ -324,6 +348,7 @@ def main():
         "per_config": per_config,
         "layouts_8192": layouts,
         "fused_8192": fused,
+        "edges_8192": edges,
         "attention": attention,
         "sclk": sclk_mhz(),
         "kernel_source_hash": kernel_source_hash(),
