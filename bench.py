@@ -11,12 +11,24 @@ Printed: ONE JSON line with the contract's keys plus
                 fp16 MFMA peak; `traffic` comes from the committed counter
                 summary when it was taken on the current kernel source, else
                 null;
+  clock         shader clock, socket power, hotspot temperature and energy
+                sampled by a child process (amdsmi, started before this
+                process touches the GPU) during the timed steps, and the
+                TFLOP/s per GHz and per watt they imply;
   cpu_baseline  the oracle (test infrastructure) timed on this host on a
                 bounded sample of the same workload (whole rows of C);
-  per_config    the four smaller workloads, each timed the same way (context);
-  attention     the attention forward on its workloads (the sequence of page
-                "TileLang实战" §4.3 and a long-sequence case), timed the same
-                way, with torch's scaled_dot_product_attention as context.
+  per_config    all five workloads: warm timing (back-to-back calls on the
+                same inputs) and flushed timing (a 512 MiB buffer written
+                between calls, so that no input or output line stays in L2 or
+                the 256 MB Infinity Cache), kernel chosen, TFLOP/s, GB/s, and,
+                from the CPU-baseline leg after all GPU timing, the oracle's
+                GFLOP/s on the same workload and the GPU result's error
+                against it (normalised as the tolerance is, plus max and mean
+                absolute error);
+  layouts_8192 / fused_8192 / edges_8192   the same product with column-major
+                operands, the fused epilogue, and the ring kernel's edge paths;
+  attention     the attention forward on its workloads, with torch's
+                scaled_dot_product_attention as context.
 """
 import argparse
 import hashlib
@@ -33,11 +45,13 @@ sys.path.insert(0, ROOT)
 PEAK_F16_TFLOPS = 2516.6   # 256 CU x 4096 FLOP/clk x 2.4 GHz, dense
 PEAK_F32_TFLOPS = 157.3    # dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0
+FLUSH_BYTES = 512 << 20    # written between flushed calls (2x the Infinity Cache)
 # the sources of the kernel the 8192^3 workload runs (the ring kernel and the
 # helpers it includes): the committed counter record is valid while they are
 # unchanged
 KERNEL_SOURCES = ["tiled_gemm_03_amd/csrc/gemm_kernel.hpp", "tiled_gemm_03_amd/csrc/gemm_kernel_ring.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_f16_8192x8192x8192.json")
+KINDS = {0: "general", 1: "tiled", 2: "ring", 3: "direct"}
 
 
 def kernel_source_hash():
@@ -48,46 +62,205 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def sclk_mhz():
-    # rocm-smi starts through an `env python3` shebang; under a profiler's
-    # preload that is an exec after GPU initialisation, so skip it there
-    if "rocprof" in os.environ.get("LD_PRELOAD", "") or os.environ.get("TGEMM_NO_SCLK"):
-        return None
+# ---------------------------------------------------------------- clock sampler
+def clock_sampler_child():
+    """Child process: reads the GPU's power-management metrics table (amdsmi)
+    in a loop.  Protocol on stdin: first line the PCI address of the GPU to
+    sample (domain:bus:device.function, or empty when only one GPU is
+    visible), then any line to stop; it then prints one JSON object with the
+    samples: (monotonic seconds, current gfxclk MHz, mean of the per-XCD
+    current gfxclks, average gfxclk MHz, socket power W, hotspot C, energy
+    counter in microjoules, throttle status)."""
+    import ctypes
+    import threading
+    out = {"samples": [], "error": None, "bdf": None}
     try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
-        d = json.loads(r.stdout)
-        for v in d.values():
-            for k, s in v.items():
-                if "sclk" in k.lower():
-                    return s
-    except Exception:
-        return None
-    return None
+        import amdsmi
+        from amdsmi import amdsmi_wrapper as AW
+        amdsmi.amdsmi_init(amdsmi.AmdSmiInitFlags.INIT_AMD_GPUS)
+        handles = amdsmi.amdsmi_get_processor_handles()
+        bdfs = [amdsmi.amdsmi_get_gpu_device_bdf(h).lower() for h in handles]
+    except Exception as e:  # noqa: BLE001 - reported, not fatal
+        out["error"] = f"amdsmi unavailable: {e}"
+        sys.stdin.readline()
+        print(json.dumps(out), flush=True)
+        return
+    want = sys.stdin.readline().strip().lower()
+    # match domain:bus:device.function, else bus:device.function
+    pick = [i for i, b in enumerate(bdfs) if want and b == want]
+    pick = pick or [i for i, b in enumerate(bdfs) if want and b.split(":", 1)[-1] == want.split(":", 1)[-1]]
+    if not pick and len(handles) == 1:
+        pick = [0]
+    if not pick:
+        out["error"] = f"GPU {want!r} not among {bdfs}"
+        sys.stdin.readline()
+        print(json.dumps(out), flush=True)
+        return
+    h = handles[pick[0]]
+    out["bdf"] = bdfs[pick[0]]
+    stop = threading.Event()
+
+    def waiter():
+        sys.stdin.readline()
+        stop.set()
+
+    threading.Thread(target=waiter, daemon=True).start()
+    gm = AW.amdsmi_gpu_metrics_t()
+    acc, res, ts = ctypes.c_uint64(), ctypes.c_float(), ctypes.c_uint64()
+    samples = out["samples"]
+    while not stop.is_set() and len(samples) < 400000:
+        t = time.monotonic()
+        if AW.amdsmi_get_gpu_metrics_info(h, ctypes.byref(gm)) == 0:
+            xcd = [int(c) for c in gm.current_gfxclks if 0 < c < 0xFFFF]
+            e_uj = None
+            if AW.amdsmi_get_energy_count(h, ctypes.byref(acc), ctypes.byref(res), ctypes.byref(ts)) == 0:
+                e_uj = acc.value * float(res.value)
+            samples.append((t, int(gm.current_gfxclk), sum(xcd) / len(xcd) if xcd else None,
+                            int(gm.average_gfxclk_frequency), int(gm.current_socket_power),
+                            int(gm.temperature_hotspot), e_uj, int(gm.throttle_status)))
+        time.sleep(0.0005)
+    print(json.dumps(out), flush=True)
 
 
-def time_calls(fn, steps, warmup, stream):
+def _valid(x, hi=0xFFFF):
+    return x is not None and 0 < x < hi
+
+
+def clock_window(samples, t0, t1):
+    """Statistics of the sampler's samples taken in [t0, t1] (monotonic
+    seconds): mean / min / max of the per-XCD gfxclk (else the current
+    gfxclk), mean socket power, hotspot temperature, and the average power
+    from the energy counter between the first and last sample of the window
+    (None where the table did not hold the value)."""
+    win = [s for s in samples if t0 <= s[0] <= t1]
+    r = {"samples": len(win), "window_ms": (t1 - t0) * 1e3}
+    if not win:
+        return r
+
+    def stats(vals, key):
+        vals = [v for v in vals if v is not None]
+        if vals:
+            r[key + "_mean"] = sum(vals) / len(vals)
+            r[key + "_min"] = min(vals)
+            r[key + "_max"] = max(vals)
+
+    stats([s[2] if s[2] is not None else (s[1] if _valid(s[1]) else None) for s in win], "gfxclk_mhz")
+    stats([s[3] if _valid(s[3]) else None for s in win], "avg_gfxclk_mhz")
+    stats([s[4] if _valid(s[4]) else None for s in win], "socket_power_w")
+    stats([s[5] if _valid(s[5]) else None for s in win], "hotspot_c")
+    e = [(s[0], s[6]) for s in win if s[6] is not None]
+    if len(e) >= 2 and e[-1][0] > e[0][0] and e[-1][1] >= e[0][1]:
+        r["energy_power_w"] = (e[-1][1] - e[0][1]) * 1e-6 / (e[-1][0] - e[0][0])
+    r["throttle_status_any"] = any(s[7] not in (0, 0xFFFFFFFF) for s in win)
+    return r
+
+
+class ClockSampler:
+    """Parent side of clock_sampler_child.  Start it before this process
+    makes any GPU call; under a profiler's preloaded library (which has
+    already initialised the GPU in this process) it is not started."""
+
+    def __init__(self, enabled=True):
+        self.proc = None
+        self.reason = None
+        if not enabled:
+            self.reason = "disabled"
+        elif "rocprof" in os.environ.get("LD_PRELOAD", ""):
+            self.reason = "not started under a profiler"
+        else:
+            try:
+                self.proc = subprocess.Popen([sys.executable, os.path.abspath(__file__), "--clock-sampler"],
+                                             stdin=subprocess.PIPE, stdout=subprocess.PIPE,
+                                             stderr=subprocess.DEVNULL, text=True)
+            except OSError as e:
+                self.reason = f"could not start: {e}"
+        self.data = None
+
+    def select(self, bdf):
+        if self.proc is not None:
+            self.proc.stdin.write((bdf or "") + "\n")
+            self.proc.stdin.flush()
+
+    def finish(self):
+        if self.proc is None:
+            return {"samples": [], "error": self.reason}
+        try:
+            o, _ = self.proc.communicate("stop\n", timeout=60)
+            self.data = json.loads(o.strip().splitlines()[-1])
+        except Exception as e:  # noqa: BLE001 - reported, not fatal
+            self.proc.kill()
+            self.data = {"samples": [], "error": f"sampler: {e}"}
+        return self.data
+
+
+def device_bdf(dev_index=0):
+    """PCI address of a torch device as domain:bus:device.function."""
+    import torch
+    p = torch.cuda.get_device_properties(dev_index)
+    if all(hasattr(p, f) for f in ("pci_domain_id", "pci_bus_id", "pci_device_id")):
+        return f"{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:{p.pci_device_id:02x}.0"
+    return ""
+
+
+# ---------------------------------------------------------------- timing
+def time_calls(fn, steps, warmup, stream, flush=None):
+    """Per-call HIP-event times (ms) of `steps` calls after `warmup` calls, the
+    wall time per call, and the monotonic bounds of the timed region.  With
+    `flush`, it runs between calls, outside the events."""
     import torch
     for _ in range(warmup):
+        if flush is not None:
+            flush()
         fn()
     torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     torch.cuda.synchronize()
+    m0 = time.monotonic()
     t0 = time.perf_counter()
     for i in range(steps):
+        if flush is not None:
+            flush()
         starts[i].record(stream)
         fn()
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ev = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
-    return wall * 1e3 / steps, ev
+    m1 = time.monotonic()
+    ev = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return {"wall_ms_per_call": wall * 1e3 / steps, "events_ms": ev, "t0": m0, "t1": m1}
+
+
+def summary_us(ev):
+    import numpy as np
+    return {"us_median": float(np.median(ev)) * 1e3, "us_p10": float(np.percentile(ev, 10)) * 1e3,
+            "us_p90": float(np.percentile(ev, 90)) * 1e3}
+
+
+def gemm_error(c, o, a, b, in_dtype):
+    """The tolerance's error measure of a GPU result c against the oracle o
+    (binary64, same entries): fp16 / bf16 inputs max|c - o| / (sqrt(K) max|a|
+    max|b|) over the whole stored inputs (tolerance 1e-2); fp32 inputs the
+    normwise max|c - o| / max|o| (tolerance 1e-4); with the absolute max and
+    mean error."""
+    import numpy as np
+    import oracle
+    from tiled_gemm_03_amd import workloads as W
+    d = np.abs(c.astype(np.float64) - o)
+    K = a.shape[1]
+    if in_dtype == W.F32:
+        e, tol = float(d.max() / max(np.abs(o).max(), 1e-300)), 1e-4
+    else:
+        av = np.abs(oracle.decode(a.view(np.uint16), in_dtype)).max()
+        bv = np.abs(oracle.decode(b.view(np.uint16), in_dtype)).max()
+        e, tol = float(d.max() / (math.sqrt(K) * av * bv)), 1e-2
+    return {"normalised_max": e, "tolerance": tol, "within": bool(e <= tol and np.isfinite(c).all()),
+            "max_abs": float(d.max()), "mean_abs": float(d.mean())}
 
 
 def cpu_baseline(a, b, budget_s=12.0):
     """The oracle on whole rows of C (all N columns, the full K), doubling the
     row count until the run takes budget_s seconds or more."""
-    import numpy as np
     import oracle
     from tiled_gemm_03_amd import workloads as W
     threads = max(1, min(16, len(os.sched_getaffinity(0))))
@@ -109,6 +282,35 @@ def cpu_baseline(a, b, budget_s=12.0):
             "seconds": dt}
 
 
+def oracle_per_config(results):
+    """The oracle on every workload's own inputs (full C for the four small
+    ones, the 64 x 64 sampled entries of the 8192^3 one), timed on this host
+    (T threads; 1 thread too on 128 x 256 x 512), and the error of the GPU
+    result captured after its timing."""
+    import oracle
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    for r in results:
+        a, b, c_gpu = r.pop("_a"), r.pop("_b"), r.pop("_c")
+        rows, cols = r.pop("_rows", None), r.pop("_cols", None)
+        n_r = a.shape[0] if rows is None else len(rows)
+        n_c = b.shape[1] if cols is None else len(cols)
+        flops = 2.0 * n_r * n_c * a.shape[1]
+        reps = max(1, int(2e8 // flops))   # repeat tiny cases to time more than a few ms
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            o = oracle.gemm(a, b, r["_in"], rows=rows, cols=cols, nthreads=threads)
+        dt = (time.perf_counter() - t0) / reps
+        r["oracle"] = {"gflops": flops / dt / 1e9, "threads": threads, "ms": dt * 1e3,
+                       "entries": "full C" if rows is None else f"{n_r} seeded rows x {n_c} seeded columns"}
+        if r["workload"] == "f16_128x256x512":
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                oracle.gemm(a, b, r["_in"], rows=rows, cols=cols, nthreads=1)
+            d1 = (time.perf_counter() - t0) / reps
+            r["oracle"]["gflops_1_thread"] = flops / d1 / 1e9
+        r["error"] = gemm_error(c_gpu, o, a, b, r.pop("_in"))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -118,30 +320,23 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-config", action="store_true")
     ap.add_argument("--no-attention", action="store_true")
-    ap.add_argument("--mfma-ceiling", action="store_true",
-                    help="only run the MFMA ceiling program (issue rate and clock of both fp16 MFMA shapes on "
-                         "every SIMD, N(0,1) and all-ones operands) and print its JSON lines")
-    ap.add_argument("--lds-probes", action="store_true",
-                    help="only run the LDS probe program (read rate of each candidate LDS layout, direct-to-LDS "
-                         "load rate of each global footprint) and print its JSON lines")
+    ap.add_argument("--no-clock", action="store_true", help="do not start the clock sampler")
+    ap.add_argument("--clock-sampler", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one elementwise kernel that reads and writes 512 MiB "
                          "(scale reference for the HBM byte counters)")
     args = ap.parse_args()
+    if args.clock_sampler:
+        clock_sampler_child()
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
               "(a row-sharded multi-GPU product needs no collective; it is described, not built)",
               file=sys.stderr)
         sys.exit(2)
 
-    if args.mfma_ceiling or args.lds_probes:
-        # a child process of its own, started before this process touches the GPU
-        from tiled_gemm_03_amd import build as B
-        prog = B.CEILING_BIN if args.mfma_ceiling else B.PROBES_BIN
-        if not os.path.exists(prog):
-            print(f"bench.py: {prog} is not built (run __graft_entry__.build())", file=sys.stderr)
-            sys.exit(1)
-        sys.exit(subprocess.run([prog]).returncode)
+    # before anything touches the GPU
+    sampler = ClockSampler(enabled=not args.no_clock)
 
     import numpy as np
     import torch
@@ -150,6 +345,7 @@ def main():
 
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
+    sampler.select(device_bdf(0))
     w = W.BY_NAME["f16_8192x8192x8192"]
     print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
     a_np, b_np = W.make_inputs(w)
@@ -162,11 +358,19 @@ def main():
         T.gemm_tensors(a, b, c, config_id=args.config, stream=stream.cuda_stream)
 
     print(f"[bench] timing {args.steps} steps after {args.warmup} warmup", file=sys.stderr, flush=True)
-    ms_per_step, ev = time_calls(step, args.steps, args.warmup, stream)
+    mw0 = time.monotonic()
+    main_t = time_calls(step, args.steps, args.warmup, stream)
+    ms_per_step = main_t["wall_ms_per_call"]
+    ev = main_t["events_ms"]
     flops = 2.0 * w.M * w.N * w.K
     value = flops / (ms_per_step * 1e-3) / 1e12
     kern_ms = float(np.mean(ev))
     achieved = flops / (kern_ms * 1e-3) / 1e12
+    print(f"[bench] {value:.1f} TFLOP/s ({ms_per_step:.4f} ms per step), kernel {achieved:.1f} TFLOP/s",
+          file=sys.stderr, flush=True)
+    # the sampled entries of the timed product's output, for the error check
+    rows5, cols5 = W.sample_indices(w.M, 64, w.seed + 100), W.sample_indices(w.N, 64, w.seed + 200)
+    c5 = c[torch.from_numpy(rows5).to(dev)][:, torch.from_numpy(cols5).to(dev)].cpu().numpy()
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -182,16 +386,24 @@ def main():
                                   w.in_dtype, w.out_dtype) if args.config < 0 else args.config
     info = T.gemm_config_info(cfg_id)
 
+    flush_buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
+    flush_val = [0]
+
+    def flush():
+        flush_val[0] += 1
+        flush_buf.fill_(flush_val[0])
+
     per_config = []
     if not args.no_per_config:
+        tdt = {W.F16: torch.float16, W.F32: torch.float32}
         for pw in W.WORKLOADS[:4]:
             pa, pb = W.make_inputs(pw)
-            tdt = {W.F16: torch.float16, W.F32: torch.float32}
             pad = torch.from_numpy(pa).to(dev)
             pbd = torch.from_numpy(pb).to(dev)
             pc = torch.empty((pw.M, pw.N), dtype=tdt[pw.out_dtype], device=dev)
             call = lambda: T.gemm_tensors(pad, pbd, pc, stream=stream.cuda_stream)
-            pms, pev = time_calls(call, 200, 20, stream)
+            warm = time_calls(call, 200, 20, stream)
+            cold = time_calls(call, 100, 5, stream, flush=flush)
             # back to back: events around 200 launches in a row (the launch
             # latency of one call overlaps the previous kernel)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -203,7 +415,6 @@ def main():
             torch.cuda.synchronize()
             b2b_ms = e0.elapsed_time(e1) / 200
             pf = 2.0 * pw.M * pw.N * pw.K
-            med = float(np.median(pev))
             peak = PEAK_F32_TFLOPS if pw.in_dtype == W.F32 else PEAK_F16_TFLOPS
             algo_bytes = (pw.M * pw.K + pw.K * pw.N) * (4 if pw.in_dtype == W.F32 else 2) + \
                 pw.M * pw.N * (4 if pw.out_dtype == W.F32 else 2)
@@ -211,16 +422,36 @@ def main():
                                        pc.data_ptr(), pw.N, pw.in_dtype, pw.out_dtype)
             kind = T.gemm_select_kernel(pw.M, pw.N, pw.K, pad.data_ptr(), pw.K, pbd.data_ptr(), pw.N,
                                         pc.data_ptr(), pw.N, pw.in_dtype, pw.out_dtype)
-            per_config.append({
-                "workload": pw.name, "config": T.gemm_config_info(pid)["name"],
-                "kernel": {0: "general", 1: "tiled", 2: "ring", 3: "direct"}.get(kind, str(kind)),
-                "us_median": med * 1e3, "us_p10": float(np.percentile(pev, 10)) * 1e3,
-                "us_p90": float(np.percentile(pev, 90)) * 1e3, "us_per_call_wall": pms * 1e3,
-                "us_back_to_back": b2b_ms * 1e3,
-                "tflops": pf / (med * 1e-3) / 1e12, "frac_of_mfma_peak": pf / (med * 1e-3) / 1e12 / peak,
-                "gbs": algo_bytes / (med * 1e-3) / 1e9,
-                "tflops_back_to_back": pf / (b2b_ms * 1e-3) / 1e12,
-                "gbs_back_to_back": algo_bytes / (b2b_ms * 1e-3) / 1e9})
+            entry = {"workload": pw.name, "config": T.gemm_config_info(pid)["name"], "kernel": KINDS.get(kind, kind),
+                     "algorithmic_flop": pf, "algorithmic_bytes": algo_bytes,
+                     "us_per_call_wall": warm["wall_ms_per_call"] * 1e3, "us_back_to_back": b2b_ms * 1e3}
+            for mode, t in (("warm", warm), ("flushed", cold)):
+                s = summary_us(t["events_ms"])
+                sec = s["us_median"] * 1e-6
+                s.update({"tflops": pf / sec / 1e12, "frac_of_mfma_peak": pf / sec / 1e12 / peak,
+                          "gbs": algo_bytes / sec / 1e9, "frac_of_hbm_peak": algo_bytes / sec / 1e9 / PEAK_HBM_GBS})
+                entry[mode] = s
+            entry["tflops_back_to_back"] = pf / (b2b_ms * 1e-3) / 1e12
+            entry.update({"_a": pa, "_b": pb, "_c": pc.cpu().numpy(), "_in": pw.in_dtype})
+            per_config.append(entry)
+            del pad, pbd, pc
+        # the 8192^3 workload itself: its warm figures are the main timing's;
+        # flushed: 20 calls with the flush between them
+        cold = time_calls(step, 20, 3, stream, flush=flush)
+        s_w = summary_us(ev)
+        s_c = summary_us(cold["events_ms"])
+        entry = {"workload": w.name, "config": info["name"], "kernel": "ring", "algorithmic_flop": flops,
+                 "algorithmic_bytes": (w.M * w.K + w.K * w.N + w.M * w.N) * 2}
+        for mode, s in (("warm", s_w), ("flushed", s_c)):
+            sec = s["us_median"] * 1e-6
+            s.update({"tflops": flops / sec / 1e12, "frac_of_mfma_peak": flops / sec / 1e12 / PEAK_F16_TFLOPS})
+            entry[mode] = s
+        entry.update({"_a": a_np, "_b": b_np, "_c": c5, "_rows": rows5, "_cols": cols5, "_in": w.in_dtype})
+        per_config.append(entry)
+    else:
+        per_config.append({"workload": w.name, "_a": a_np, "_b": b_np, "_c": c5, "_rows": rows5, "_cols": cols5,
+                           "_in": w.in_dtype})
+    del flush_buf
 
     # the same 8192^3 product with column-major operands or output (gemm_t):
     # each matrix holds the same values, stored transposed
@@ -229,17 +460,16 @@ def main():
         a_col = a.t().contiguous().t()
         b_col = b.t().contiguous().t()
         c_col = torch.empty((w.N, w.M), dtype=torch.float16, device=dev).t()
-        kinds = {0: "general", 1: "tiled", 2: "ring", 3: "direct"}
         for name, la_, lb_, lc_ in (("A col-major", a_col, b, c), ("B col-major", a, b_col, c),
                                     ("A, B col-major", a_col, b_col, c), ("C col-major", a, b, c_col)):
             call = lambda: T.gemm_tensors(la_, lb_, lc_, stream=stream.cuda_stream)
-            _, lev = time_calls(call, 20, 3, stream)
+            lev = time_calls(call, 20, 3, stream)["events_ms"]
             (xa, lda_), (xb, ldb_), (xc, ldc_) = T._layout(la_), T._layout(lb_), T._layout(lc_)
             kind, lcfg = T.gemm_select_kernel_t(w.M, w.N, w.K, la_.data_ptr(), lda_, xa, lb_.data_ptr(), ldb_, xb,
                                                 lc_.data_ptr(), ldc_, xc, w.in_dtype, w.out_dtype)
             med = float(np.median(lev))
             layouts.append({"layouts": name, "config": T.gemm_config_info(lcfg)["name"],
-                            "kernel": kinds.get(kind, str(kind)), "us_median": med * 1e3,
+                            "kernel": KINDS.get(kind, kind), "us_median": med * 1e3,
                             "tflops": flops / (med * 1e-3) / 1e12})
         del a_col, b_col, c_col
 
@@ -250,9 +480,14 @@ def main():
         for name, kw in (("column bias + gelu (tanh form)", dict(bias=bias, activation=T.ACT_GELU_TANH)),
                          ("alpha 0.5, beta 1 (C read) + relu", dict(alpha=0.5, beta=1.0, activation=T.ACT_RELU))):
             call = lambda: T.gemm_tensors(a, b, c, stream=stream.cuda_stream, **kw)
-            _, fev = time_calls(call, 20, 3, stream)
+            fev = time_calls(call, 20, 3, stream)["events_ms"]
             med = float(np.median(fev))
             fused.append({"epilogue": name, "us_median": med * 1e3, "tflops": flops / (med * 1e-3) / 1e12})
+        # the plain product again, right after, for the comparison at the same clock
+        pev = time_calls(step, 20, 3, stream)["events_ms"]
+        med = float(np.median(pev))
+        fused.append({"epilogue": "none (plain, same run)", "us_median": med * 1e3,
+                      "tflops": flops / (med * 1e-3) / 1e12})
         del bias
 
     # the ring kernel's edge paths on sub-views of the same operands: a K
@@ -261,21 +496,20 @@ def main():
     # epilogue); torch.matmul on the same views for context
     edges = []
     if not args.no_per_config:
-        kinds = {0: "general", 1: "tiled", 2: "ring", 3: "direct"}
         for name, m_, n_, k_ in (("K tail: K = 8000", w.M, w.N, 8000),
                                  ("N = 8190, ldc = 8190 (partial groups, unaligned C rows)", w.M, 8190, w.K)):
             ea, eb = a[:m_, :k_], b[:k_, :n_]
             ec = torch.empty((m_, n_), dtype=torch.float16, device=dev)
             call = lambda: T.gemm_tensors(ea, eb, ec, stream=stream.cuda_stream)
-            _, eev = time_calls(call, 20, 3, stream)
-            _, tev = time_calls(lambda: torch.matmul(ea, eb, out=ec), 20, 3, stream)
+            eev = time_calls(call, 20, 3, stream)["events_ms"]
+            tev = time_calls(lambda: torch.matmul(ea, eb, out=ec), 20, 3, stream)["events_ms"]
             (xa, lda_), (xb, ldb_), (xc, ldc_) = T._layout(ea), T._layout(eb), T._layout(ec)
             kind, ecfg = T.gemm_select_kernel_t(m_, n_, k_, ea.data_ptr(), lda_, xa, eb.data_ptr(), ldb_, xb,
                                                 ec.data_ptr(), ldc_, xc, w.in_dtype, w.out_dtype)
             med, tmed = float(np.median(eev)), float(np.median(tev))
             ef = 2.0 * m_ * n_ * k_
             edges.append({"case": name, "M": m_, "N": n_, "K": k_, "config": T.gemm_config_info(ecfg)["name"],
-                          "kernel": kinds.get(kind, str(kind)), "us_median": med * 1e3,
+                          "kernel": KINDS.get(kind, kind), "us_median": med * 1e3,
                           "tflops": ef / (med * 1e-3) / 1e12, "torch_matmul_us_median": tmed * 1e3})
             del ec
 
@@ -294,7 +528,7 @@ def main():
             call = lambda: T.attention_tensors(q_, k_, v_, o_, scale=aw.scale, causal=aw.causal,
                                                stream=stream.cuda_stream)
             reps = 200 if aw.N <= 1024 else 20
-            _, aev = time_calls(call, reps, max(3, reps // 10), stream)
+            aev = time_calls(call, reps, max(3, reps // 10), stream)["events_ms"]
             med = float(np.median(aev))
             af = aw.flops()
             abytes = 4 * aw.B * aw.H * aw.N * aw.d * 2
@@ -307,9 +541,9 @@ def main():
             sdpa = lambda: torch.nn.functional.scaled_dot_product_attention(q_, k_, v_, is_causal=aw.causal,
                                                                             scale=aw.scale)
             try:
-                _, sev = time_calls(sdpa, reps, max(3, reps // 10), stream)
+                sev = time_calls(sdpa, reps, max(3, reps // 10), stream)["events_ms"]
                 entry["torch_sdpa_us_median"] = float(np.median(sev)) * 1e3
-            except Exception as e:  # noqa: BLE001 - context only
+            except Exception:  # noqa: BLE001 - context only
                 entry["torch_sdpa_us_median"] = None
             attention.append(entry)
             del q_, k_, v_, o_
@@ -323,10 +557,36 @@ def main():
         print("[bench] calibration: neg over 512 MiB in, 512 MiB out", file=sys.stderr, flush=True)
         del src, dst
 
+    # every GPU measurement is done: the clock record, then the CPU leg
+    sd = sampler.finish()
+    clock = {"source": "amdsmi GPU metrics table, read by a child process every ~0.5 ms",
+             "bdf": sd.get("bdf"), "error": sd.get("error")}
+    if sd.get("samples"):
+        tw = clock_window(sd["samples"], main_t["t0"], main_t["t1"])
+        clock["timed_steps"] = tw
+        clock["warmup_and_timed"] = clock_window(sd["samples"], mw0, main_t["t1"])
+        g = tw.get("gfxclk_mhz_mean")
+        if g:
+            # the dense fp16 rate at the clock the timed steps ran at
+            dense = 256 * 4096 * g * 1e6 / 1e12
+            clock["dense_fp16_tflops_at_clock"] = dense
+            clock["kernel_frac_of_dense_at_clock"] = achieved / dense
+        pw_ = tw.get("energy_power_w") or tw.get("socket_power_w_mean")
+        if pw_:
+            clock["kernel_tflops_per_watt"] = achieved / pw_
+
     cpu = None
     if not args.no_cpu_baseline:
+        print("[bench] oracle on every workload (errors, GFLOP/s)", file=sys.stderr, flush=True)
+        oracle_per_config(per_config)
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         cpu = cpu_baseline(a_np, b_np)
+    for r in per_config:
+        for k in [k for k in r if k.startswith("_")]:
+            del r[k]
+    if args.no_per_config:
+        per_config = [r for r in per_config if len(r) > 1]
+    err5 = next((r.get("error") for r in per_config if r.get("workload") == w.name), None)
 
     line = {
         "metric": "GEMM TFLOP/s (fp16 in, fp32 acc) at 8192^3 and % of MI355X MFMA peak",
@@ -344,13 +604,14 @@ def main():
                      "kernel_ms_p90": float(np.percentile(ev, 90)),
                      "algorithmic_flop_per_launch": flops,
                      "algorithmic_bytes_per_launch": (w.M * w.K + w.K * w.N + w.M * w.N) * 2},
+        "clock": clock,
+        "error_8192_sampled": err5,
         "cpu_baseline": cpu,
         "per_config": per_config,
         "layouts_8192": layouts,
         "fused_8192": fused,
         "edges_8192": edges,
         "attention": attention,
-        "sclk": sclk_mhz(),
         "kernel_source_hash": kernel_source_hash(),
     }
     print(json.dumps(line), flush=True)

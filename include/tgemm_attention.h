@@ -36,6 +36,9 @@ extern "C" {
  *                     layout {H n d, n d, d}.  The stride arrays are read on
  *                     the host during the call.  Elements need only be
  *                     aligned to their size; overlapping inputs are fine.
+ *                     The row strides of K and V must keep 64 rows within
+ *                     32-bit byte offsets: (64 max(k_stride[2], v_stride[2])
+ *                     + d) * 2 < 2^31 (else TGEMM_ERR_LD).
  *   O                 device output [B, H, n_q, d] of type out_dtype, strides
  *                     as above; its elements must not overlap one another
  *                     (TGEMM_ERR_LD) nor Q, K or V (TGEMM_ERR_ALIAS).

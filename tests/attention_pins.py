@@ -1,8 +1,9 @@
 """Pins of the attention oracle (oracle/attention.py) against facts that do
 not come from it: torch.nn.functional.scaled_dot_product_attention in float64
-on the CPU (an independent library routine), the blockwise online-softmax
-algorithm of page "TileLang实战：用Python DSL自动生成高性能GPU计算内核" §4.2
-written out here on its own, and closed forms.
+on the CPU (an independent library routine), the block decomposition of the
+softmax that the blockwise method of page "TileLang实战：用Python DSL自动生成
+高性能GPU计算内核" §4.2 rests on (partial maxima, sums and weighted values per
+block of keys, merged associatively), and closed forms.
 
 Each pin takes the attention function to check, so that the same pins run
 against the oracle (tests/test_oracle.py) and against copies of it with a
@@ -38,34 +39,52 @@ def pin_attention_vs_torch(att):
         assert np.allclose(got, want, rtol=1e-12, atol=1e-13), (B, H, Nq, Nk, d, causal, np.abs(got - want).max())
 
 
-def _online_blocks(Q, K, V, scale, causal, block):
-    """The page's blockwise algorithm: walk K, V in blocks, keep per query the
-    running maximum M, normaliser L and normalised output O."""
+def _block_partials(Q, K, V, scale, causal, block):
+    """Softmax attention over keys split into blocks, from the identity
+    behind the blockwise method of page "TileLang实战：用Python DSL自动生成高性能
+    GPU计算内核" §4.2: for any partition of the visible keys of a query into
+    blocks, with m_b the block's largest score, s_b = sum exp(score - m_b)
+    and u_b = sum exp(score - m_b) v over the block, the attention output is
+    sum_b e^(m_b - m) u_b / sum_b e^(m_b - m) s_b for any m.  Each block's
+    triple (m_b, s_b, u_b) is formed for all queries at once; the triples are
+    merged two at a time in a balanced tree, each merge rescaling both sides
+    to the larger of the two maxima; one division at the end."""
     Nq, d = Q.shape
     Nk = K.shape[0]
-    O = np.zeros((Nq, d))
-    L = np.zeros(Nq)
-    M = np.full(Nq, -np.inf)
-    for s in range(0, Nk, block):
-        Kb, Vb = K[s:s + block], V[s:s + block]
-        for i in range(Nq):
-            sc = scale * (Kb @ Q[i])
-            if causal:
-                sc = np.where(np.arange(s, s + len(sc)) > i, -np.inf, sc)
-            if np.all(np.isneginf(sc)):
-                continue
-            m_new = max(M[i], np.max(sc))
-            l_new = L[i] * np.exp(M[i] - m_new) + np.sum(np.exp(sc - m_new))
-            O[i] = (O[i] * L[i] * np.exp(M[i] - m_new) + np.exp(sc - m_new) @ Vb) / l_new
-            L[i], M[i] = l_new, m_new
-    return O
+    parts = []
+    for lo in range(0, Nk, block):
+        hi = min(lo + block, Nk)
+        S = scale * (Q @ K[lo:hi].T)                       # Nq x (hi - lo)
+        if causal:
+            S = np.where(np.arange(lo, hi)[None, :] > np.arange(Nq)[:, None], -np.inf, S)
+        m = S.max(axis=1)                                  # -inf where no key of the block is visible
+        safe = np.where(np.isneginf(m), 0.0, m)
+        E = np.exp(S - safe[:, None])                      # exp(-inf) = 0 for hidden keys
+        parts.append((m, E.sum(axis=1), E @ V[lo:hi]))
+
+    def merge(x, y):
+        (mx, sx, ux), (my, sy, uy) = x, y
+        m = np.maximum(mx, my)
+        safe = np.where(np.isneginf(m), 0.0, m)
+        fx = np.where(np.isneginf(mx), 0.0, np.exp(mx - safe))
+        fy = np.where(np.isneginf(my), 0.0, np.exp(my - safe))
+        return m, fx * sx + fy * sy, fx[:, None] * ux + fy[:, None] * uy
+
+    while len(parts) > 1:
+        nxt = [merge(parts[t], parts[t + 1]) for t in range(0, len(parts) - 1, 2)]
+        if len(parts) % 2:
+            nxt.append(parts[-1])
+        parts = nxt
+    _, s_all, u_all = parts[0]
+    return u_all / s_all[:, None]
 
 
-def pin_attention_vs_online_blocks(att):
+def pin_attention_vs_block_partials(att):
     for (Nq, Nk, d, causal, block, seed) in ((6, 11, 8, False, 4, 6), (10, 10, 16, True, 3, 7), (5, 13, 4, True, 5, 8)):
         q, k, v = _qkv(1, 1, Nq, Nk, d, W.F16, seed)
         got = att(q, k, v, W.F16, scale=0.3, causal=causal)[0, 0]
-        want = _online_blocks(_vals(q, W.F16)[0, 0], _vals(k, W.F16)[0, 0], _vals(v, W.F16)[0, 0], 0.3, causal, block)
+        want = _block_partials(_vals(q, W.F16)[0, 0], _vals(k, W.F16)[0, 0], _vals(v, W.F16)[0, 0], 0.3, causal,
+                               block)
         assert np.allclose(got, want, rtol=1e-12, atol=1e-13), (Nq, Nk, causal, np.abs(got - want).max())
 
 
@@ -100,5 +119,5 @@ def pin_attention_sampled_rows(att):
     assert np.array_equal(att(q, k, v, W.BF16, scale=0.5, causal=True, rows=rows), full[:, :, rows, :])
 
 
-ATTENTION_PINS = [pin_attention_vs_torch, pin_attention_vs_online_blocks, pin_attention_closed_forms,
+ATTENTION_PINS = [pin_attention_vs_torch, pin_attention_vs_block_partials, pin_attention_closed_forms,
                   pin_attention_sampled_rows]

@@ -61,6 +61,9 @@ def _call(B=1, H=1, nq=4, nk=4, d=64, q=FAKE, qs=None, k=FAKE + (1 << 30), ks=No
     (dict(o=None), T.ERR_NULL),
     (dict(qs=(256, 256, -64)), T.ERR_LD),
     (dict(os_=(256, 256, 32)), T.ERR_LD),            # output rows overlap
+    (dict(ks=(1 << 26, 1 << 26, 1 << 24)), T.ERR_LD),  # 64 K rows beyond 32-bit byte offsets
+    (dict(vs=(1 << 26, 1 << 26, 1 << 24)), T.ERR_LD),  # the same for V
+    (dict(ks=(1 << 26, 1 << 26, (1 << 24) - 1)), T.ERR_LD),  # 64 rows + d elements just reach 2^31 bytes
     (dict(H=2, os_=(512, 32, 128)), T.ERR_LD),       # head 1 starts inside a row of head 0
     (dict(o=FAKE + 100), T.ERR_ALIAS),                # output overlaps Q
     (dict(o=FAKE + (2 << 30) + 510), T.ERR_ALIAS),   # output overlaps the end of V

@@ -100,9 +100,10 @@ def check_bound(d, o, z, a, b, in_dt, out_dt, c_old, bias, bias_dt, bias_kind, a
     return float((diff / bound).max())
 
 
-# shapes that take each kernel (table's choice): ring 256x256 tiles, ring
-# 128x128 tiles, register-staged whole tiles, direct
-SHAPES = [((256, 512, 384), "ring big", 0), ((1024, 2048, 512), "ring mid", 1), ((128, 256, 512), "tiled", -1),
+# shapes and the kernel each takes (-1: the table's choice; a forced
+# configuration otherwise, the path asserted): ring 256x256 tiles, ring
+# 128x128 tiles, register-staged whole tiles (the 32x32 configuration), direct
+SHAPES = [((256, 512, 384), "ring big", 0), ((1024, 2048, 512), "ring mid", 1), ((128, 256, 512), "tiled", 3),
           ((127, 255, 512), "direct", -1), ((33, 47, 255), "direct ragged", -1),
           ((1000, 1200, 512), "ring big ragged", 0), ((777, 1000, 256), "ring mid ragged", 1),
           ((1000, 1208, 1000), "ring big k tail", 0), ((300, 264, 200), "ring mid k tail", 1)]
@@ -131,6 +132,8 @@ def test_fused_against_oracle(shape, pair):
                             label=name)
         if name.startswith("ring"):
             assert kind == T.KERNEL_RING
+        if name == "tiled":
+            assert kind == T.KERNEL_TILED
         o, z = expected(a, b, in_dt, out_dt, c_old, bias, bias_dt, bias_kind, alpha, beta, act)
         r = check_bound(d, o, z, a, b, in_dt, out_dt, c_old, bias, bias_dt, bias_kind, alpha, beta, name)
         G.say(f"    ok, worst bound ratio {r:.3f}")

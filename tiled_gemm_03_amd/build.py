@@ -14,13 +14,6 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libtgemm.so")
-# measurement programs: MFMA issue rate and clock on every SIMD (bench.py
-# --mfma-ceiling); LDS read and direct-to-LDS load rates of the ring kernel's
-# layouts (bench.py --lds-probes)
-CEILING_SRC = os.path.join(CSRC, "mfma_ceiling.hip")
-CEILING_BIN = os.path.join(HERE, "mfma_ceiling")
-PROBES_SRC = os.path.join(CSRC, "lds_probes.hip")
-PROBES_BIN = os.path.join(HERE, "lds_probes")
 # the host code and the kernel units (compiled in parallel, then linked)
 SOURCES = [os.path.join(CSRC, f) for f in (
     "tgemm.hip", "k_tiled_big.hip", "k_tiled_mid.hip", "k_tiled_small.hip", "k_tiled_tiny.hip", "k_tiled_f32.hip",
@@ -80,28 +73,5 @@ def build(out: str = LIB, extra=(), verbose: bool = False, jobs: int = 0) -> str
     return out
 
 
-def build_program(src: str, out: str, verbose: bool = False) -> str:
-    tmp = out + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-O3", "-std=c++17",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", src, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    rc, msg = _hipcc(cmd)
-    if rc != 0:
-        raise RuntimeError(f"hipcc failed ({rc}) on {src}:\n{msg}")
-    os.replace(tmp, out)
-    return out
-
-
-def build_ceiling(out: str = CEILING_BIN, verbose: bool = False) -> str:
-    return build_program(CEILING_SRC, out, verbose)
-
-
-def build_probes(out: str = PROBES_BIN, verbose: bool = False) -> str:
-    return build_program(PROBES_SRC, out, verbose)
-
-
 if __name__ == "__main__":
     print(build(verbose=True))
-    print(build_ceiling(verbose=True))
-    print(build_probes(verbose=True))

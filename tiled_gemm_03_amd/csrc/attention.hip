@@ -129,6 +129,9 @@ int attention_fwd(int64_t batch, int64_t heads, int64_t n_q, int64_t n_k, int64_
     if (!strides_of(q_stride, heads, n_q, d, q.s) || !strides_of(k_stride, heads, n_k, d, k.s) ||
         !strides_of(v_stride, heads, n_k, d, v.s) || !strides_of(o_stride, heads, n_q, d, o.s))
         return TGEMM_ERR_LD;
+    // the kernel addresses the 64 rows of a key block from the block's first
+    // row with 32-bit byte offsets
+    if ((64 * (k.s[2] > v.s[2] ? k.s[2] : v.s[2]) + d) * 2 >= ((int64_t)1 << 31)) return TGEMM_ERR_LD;
     if (Q == nullptr || K == nullptr || V == nullptr || O == nullptr) return TGEMM_ERR_NULL;
     if (!non_overlapping(o.s, batch, heads, n_q, d)) return TGEMM_ERR_LD;
     const int ob = out_dtype == TGEMM_F32 ? 4 : 2;
