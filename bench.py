@@ -126,13 +126,24 @@ def _valid(x, hi=0xFFFF):
     return x is not None and 0 < x < hi
 
 
+def refreshes(samples):
+    """The samples at which the metrics table held new values (the firmware
+    refreshes it about once per second; the samples in between repeat it)."""
+    out, prev = [], None
+    for s in samples:
+        if tuple(s[1:]) != prev:
+            out.append(s)
+            prev = tuple(s[1:])
+    return out
+
+
 def clock_window(samples, t0, t1):
-    """Statistics of the sampler's samples taken in [t0, t1] (monotonic
+    """Statistics of the table refreshes seen in [t0, t1] (monotonic
     seconds): mean / min / max of the per-XCD gfxclk (else the current
-    gfxclk), mean socket power, hotspot temperature, and the average power
-    from the energy counter between the first and last sample of the window
-    (None where the table did not hold the value)."""
-    win = [s for s in samples if t0 <= s[0] <= t1]
+    gfxclk), socket power, hotspot temperature, and the average power from
+    the energy counter between the first and last refresh of the window
+    (absent where the table did not hold the value)."""
+    win = [s for s in refreshes(samples) if t0 <= s[0] <= t1]
     r = {"samples": len(win), "window_ms": (t1 - t0) * 1e3}
     if not win:
         return r
@@ -321,7 +332,16 @@ def main():
     ap.add_argument("--no-per-config", action="store_true")
     ap.add_argument("--no-attention", action="store_true")
     ap.add_argument("--no-clock", action="store_true", help="do not start the clock sampler")
+    ap.add_argument("--settle-ms", type=float, default=250.0,
+                    help="run the product for this long before the warmup steps, so that the timed steps see the "
+                         "clock of sustained use rather than the power controller's response to leaving idle")
+    ap.add_argument("--hold-ms", type=float, default=3000.0,
+                    help="after the timed steps, keep running the product this long while the clock sampler reads "
+                         "the metrics table (which the firmware refreshes about once per second)")
     ap.add_argument("--clock-sampler", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--dump", default=None,
+                    help="write the sampler's raw samples and the per-step event times of the timed steps to "
+                         "this JSON file")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one elementwise kernel that reads and writes 512 MiB "
                          "(scale reference for the HBM byte counters)")
@@ -357,9 +377,31 @@ def main():
     def step():
         T.gemm_tensors(a, b, c, config_id=args.config, stream=stream.cuda_stream)
 
-    print(f"[bench] timing {args.steps} steps after {args.warmup} warmup", file=sys.stderr, flush=True)
+    # settle: leave the idle clock state before the warmup steps (the power
+    # controller's response to a burst from idle makes steps 2-50 up to 40%
+    # slower than sustained use)
+    settle_steps = 0
+    load0 = time.monotonic()   # the product runs without pause from here to the end of the hold
+    ts0 = time.perf_counter()
+    while (time.perf_counter() - ts0) * 1e3 < args.settle_ms:
+        for _ in range(10):
+            step()
+        settle_steps += 10
+        torch.cuda.synchronize()
+    settle = {"ms": (time.perf_counter() - ts0) * 1e3, "steps": settle_steps}
+    print(f"[bench] settled for {settle['ms']:.0f} ms ({settle_steps} steps); timing {args.steps} steps after "
+          f"{args.warmup} warmup", file=sys.stderr, flush=True)
     mw0 = time.monotonic()
     main_t = time_calls(step, args.steps, args.warmup, stream)
+    # hold: the same product, untimed, while the sampler reads the table
+    th0 = time.monotonic()
+    hold_steps = 0
+    while (time.monotonic() - th0) * 1e3 < args.hold_ms:
+        for _ in range(10):
+            step()
+        hold_steps += 10
+        torch.cuda.synchronize()
+    th1 = time.monotonic()
     ms_per_step = main_t["wall_ms_per_call"]
     ev = main_t["events_ms"]
     flops = 2.0 * w.M * w.N * w.K
@@ -562,18 +604,35 @@ def main():
     clock = {"source": "amdsmi GPU metrics table, read by a child process every ~0.5 ms",
              "bdf": sd.get("bdf"), "error": sd.get("error")}
     if sd.get("samples"):
-        tw = clock_window(sd["samples"], main_t["t0"], main_t["t1"])
-        clock["timed_steps"] = tw
-        clock["warmup_and_timed"] = clock_window(sd["samples"], mw0, main_t["t1"])
+        clock["table_refresh_ms_median"] = None
+        rf = [x[0] for x in refreshes(sd["samples"])]
+        if len(rf) >= 3:
+            clock["table_refresh_ms_median"] = float(np.median(np.diff(rf))) * 1e3
+        clock["timed_steps"] = clock_window(sd["samples"], main_t["t0"], main_t["t1"])
+        # the product kept running right after the timed steps: the refreshes
+        # of that window give the clock and power of sustained use (the
+        # table lags: a refresh within about a period of the start of the
+        # load can still hold idle values, so those are left out)
+        tw = clock_window(sd["samples"], max(th0, load0 + 1.2), th1)
+        tw["steps"] = hold_steps
+        clock["hold_after_timed"] = tw
         g = tw.get("gfxclk_mhz_mean")
         if g:
             # the dense fp16 rate at the clock the timed steps ran at
             dense = 256 * 4096 * g * 1e6 / 1e12
             clock["dense_fp16_tflops_at_clock"] = dense
             clock["kernel_frac_of_dense_at_clock"] = achieved / dense
+            clock["note"] = ("the table refreshes about once per second, so the timed steps (tens of ms) see at "
+                             "most one refresh; the clock of the hold window (the same product, right after) stands "
+                             "for theirs")
         pw_ = tw.get("energy_power_w") or tw.get("socket_power_w_mean")
         if pw_:
             clock["kernel_tflops_per_watt"] = achieved / pw_
+
+    if args.dump:
+        with open(args.dump, "w") as f:
+            json.dump({"samples": sd.get("samples"), "t_warmup": mw0, "t0": main_t["t0"], "t1": main_t["t1"],
+                       "events_ms": ev}, f)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -604,6 +663,8 @@ def main():
                      "kernel_ms_p90": float(np.percentile(ev, 90)),
                      "algorithmic_flop_per_launch": flops,
                      "algorithmic_bytes_per_launch": (w.M * w.K + w.K * w.N + w.M * w.N) * 2},
+        "settle": settle,
+        "events_ms_first_last": [ev[0], ev[-1]],
         "clock": clock,
         "error_8192_sampled": err5,
         "cpu_baseline": cpu,

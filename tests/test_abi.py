@@ -220,11 +220,26 @@ def test_kernel_choice_ring_path():
 
 
 def test_ring_configs_report_their_ring_kernel():
-    for cid in (0, 1):
+    for cid in (0, 1, 8):
         c = T.gemm_config_info(cid)
         assert (c["block_k"], c["stages"]) == (32, 4)
         assert (c["a_block_k"], c["a_stages"]) == (64, 2)
         assert (c["mfma_m"], c["mfma_n"], c["mfma_k"]) == (16, 16, 32)
+    assert (T.gemm_config_info(8)["block_m"], T.gemm_config_info(8)["block_n"]) == (64, 128)
+
+
+def test_ring_only_configuration_falls_back_to_128x128():
+    """Configuration 8 (64 x 128 ring, row-major A) has no register-staged
+    kernel: calls its ring does not take run configuration 1 instead, and the
+    configuration reported is the one that runs."""
+    RING = T.KERNEL_RING
+    assert _kernel_t(1024, 2048, 512, R_, R_, R_, cid=8) == (RING, 8)
+    assert _kernel_t(1024, 2048, 512, R_, C_, R_, cid=8) == (RING, 8)      # column-major B: k-contiguous
+    assert _kernel_t(1024, 2048, 512, C_, R_, R_, cid=8) == (RING, 1)      # column-major A
+    assert _kernel_t(1024, 2048, 512, R_, R_, R_, lda=516, cid=8)[1] == 1  # A rows not whole chunks
+    assert _kernel_t(1024, 2048, 64, R_, R_, R_, cid=8) == (T.KERNEL_TILED, 1)  # K below the ring's multiple
+    assert _kernel_t(1000, 2000, 1000, R_, R_, R_, cid=8) == (RING, 8)     # ragged, K tail
+    assert _kernel_t(4, 4, 4, R_, R_, R_, in_dt=T.F32, out_dt=T.F32, cid=8)[0] == T.ERR_CONFIG
 
 
 R_, C_ = T.ROW_MAJOR, T.COL_MAJOR
@@ -262,7 +277,11 @@ def test_kernel_choice_for_layouts():
                 k, cfg = _kernel_t(8192, 8192, 8192, la, lb, lc)
                 assert (k, cfg) == (RING, 0), (la, lb, lc)
                 k, cfg = _kernel_t(1024, 2048, 512, la, lb, lc, out_dt=T.F32)
-                assert (k, cfg) == (RING, 1), (la, lb, lc)
+                # 128 tiles of 128 x 128: the 64 x 128 ring when both operands
+                # of the row-major product it runs are row-major (a column-major
+                # C swaps A and B and flips their layouts), else 128 x 128
+                row_row = (la, lb) == (R_, R_) if lc == R_ else (la, lb) == (C_, C_)
+                assert (k, cfg) == (RING, 8 if row_row else 1), (la, lb, lc)
                 k, cfg = _kernel_t(127, 255, 512, la, lb, lc, out_dt=T.F32)
                 if (la, lb, lc) == (R_, R_, R_):
                     assert k == DIRECT or k >= 0

@@ -16,6 +16,12 @@ def _sample(t, xcd=1500.0, cur=0xFFFF, avg=1490, power=1380, hot=80, e_uj=0.0, t
     return (t, cur, xcd, avg, power, hot, e_uj, thr)
 
 
+def test_refreshes_keep_the_samples_where_the_table_changed():
+    s = [_sample(0.0, xcd=100.0), _sample(0.001, xcd=100.0), _sample(0.9, xcd=1700.0), _sample(0.95, xcd=1700.0),
+         _sample(1.9, xcd=1650.0)]
+    assert [x[0] for x in bench.refreshes(s)] == [0.0, 0.9, 1.9]
+
+
 def test_clock_window_selects_the_window_and_averages():
     s = [_sample(0.9, xcd=2400.0, e_uj=0.0),
          _sample(1.0, xcd=1500.0, e_uj=1e6),
@@ -38,6 +44,8 @@ def test_clock_window_falls_back_to_the_current_clock_and_skips_missing_values()
     r = bench.clock_window(s, 0.0, 2.0)
     assert r["gfxclk_mhz_mean"] == 1650
     assert r["socket_power_w_mean"] == 1200
+    # a repeated table is one refresh
+    assert bench.clock_window(s[:1] * 3, 0.0, 2.0)["samples"] == 1
     assert "energy_power_w" not in r
     assert bench.clock_window(s, 5.0, 6.0) == {"samples": 0, "window_ms": 1000.0}
 

@@ -17,7 +17,7 @@ LIB = os.path.join(HERE, "libtgemm.so")
 # the host code and the kernel units (compiled in parallel, then linked)
 SOURCES = [os.path.join(CSRC, f) for f in (
     "tgemm.hip", "k_tiled_big.hip", "k_tiled_mid.hip", "k_tiled_small.hip", "k_tiled_tiny.hip", "k_tiled_f32.hip",
-    "k_ring_big.hip", "k_ring_mid.hip", "k_direct.hip",
+    "k_ring_big.hip", "k_ring_mid.hip", "k_ring_small.hip", "k_ring_small_fused.hip", "k_direct.hip",
     "k_tiled_big_fused.hip", "k_ring_big_fused.hip", "k_ring_mid_fused.hip", "k_direct_fused.hip",
     "k_ring_big_kt.hip", "k_ring_mid_kt.hip", "k_ring_big_fused_kt.hip", "k_ring_mid_fused_kt.hip",
     "attention.hip")]

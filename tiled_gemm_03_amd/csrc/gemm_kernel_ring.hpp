@@ -197,9 +197,13 @@ struct RingCfg {
         // every LDS read offset fits the 16-bit immediate of ds_read
         static_assert(OA::imm_ok(FM) && OB::imm_ok(FN), "");
     };
-    // LDS per workgroup (the same for every layout)
+    // LDS per workgroup (the same for every layout: a k-strided A ring of 4
+    // one-step stages and a k-contiguous one of 2 two-step stages both hold
+    // BM x 128 elements)
     static constexpr int LDS_BYTES = Plan<true, false>::LDS_BYTES;
-    static_assert(LDS_BYTES == Plan<false, false>::LDS_BYTES, "");
+    // a k-strided A stage needs rows of at least 16 chunks for its swizzle
+    // key: tiles narrower than 128 rows take row-major A only
+    static constexpr bool A_COL_OK = BM >= 128;
     // how far past K the ring loads (steps of 32)
     static constexpr int LOOKAHEAD = 4;
     // the rings of row-major A and B (the default layouts)

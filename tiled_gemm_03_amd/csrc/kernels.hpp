@@ -22,9 +22,13 @@ using CfgF32Tiny = TileCfg<32, 32, 32, 1, 1, 4, 4>;  // fp32 inputs, 1 wave
 // direct-to-LDS ring kernels of the two largest tiles
 using RingBig = RingCfg<256, 256, 2, 2, 1>;
 using RingMid = RingCfg<128, 128, 2, 2, 2>;
+// a ring-only configuration of 64 x 128 tiles (4 waves of 32 x 64): twice the
+// workgroups of RingMid for products that leave CUs idle at 128 x 128
+// (row-major A only)
+using RingSmall = RingCfg<64, 128, 2, 2, 2>;
 
 enum { CFG_BIG = 0, CFG_MID = 1, CFG_SMALL = 2, CFG_TINY = 3, CFG_F32_MID = 4, CFG_F32_TINY = 5,
-       CFG_DIRECT = 6, CFG_F32_DIRECT = 7, NUM_CONFIGS = 8 };
+       CFG_DIRECT = 6, CFG_F32_DIRECT = 7, CFG_RING_SMALL = 8, NUM_CONFIGS = 9 };
 
 typedef void (*KernelFn)(GemmArgs);
 
@@ -43,6 +47,9 @@ KernelFn tiled_kernel_f32(int cfg, int in, int out, bool fast, bool epi);
 // multiple of 128).  k_ring_big.hip, k_ring_mid.hip.
 KernelFn ring_kernel_big(int in, int out, int la, int lb, bool epi, bool kt);
 KernelFn ring_kernel_mid(int in, int out, int la, int lb, bool epi, bool kt);
+// RingSmall (k_ring_small.hip, k_ring_small_fused.hip): every variant
+KernelFn ring_kernel_small(int in, int out, int la, int lb, bool epi, bool kt);
+KernelFn ring_kernel_small_fused(int in, int out, int la, int lb, bool kt);
 
 // Direct kernel for (in, out), the layouts of A and B, and whether each
 // operand takes 16-byte loads.  k_direct.hip.

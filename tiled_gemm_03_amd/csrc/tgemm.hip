@@ -34,6 +34,7 @@ struct ConfigEntry {
     int ring_bk, ring_stages, ring_k_mult, ring_lds;
     int ring_lookahead;               // steps of ring_bk that the ring loads past K
     int ring_a_bk, ring_a_stages;     // the ring of a row-major A
+    bool ring_a_col;                  // whether the ring kernels take a column-major A
 };
 
 KernelFn tiled_f32_mid(int in, int out, bool fast, bool epi) { return tiled_kernel_f32(CFG_F32_MID, in, out, fast, epi); }
@@ -43,13 +44,18 @@ KernelFn tiled_f32_tiny(int in, int out, bool fast, bool epi) {
 
 #define ENTRY(name, fam, T, sel)                                                                                \
     {name, fam, false, T::BM, T::BN, T::BK, T::WM, T::WN, T::EB, T::LDS_BYTES, T::THREADS, T::CPR, sel, nullptr, \
-     0, 0, 0, 0, 0, 0, 0}
+     0, 0, 0, 0, 0, 0, 0, false}
 #define ENTRY_RING(name, fam, T, sel, R, rsel)                                                              \
     {name, fam, false, T::BM, T::BN, T::BK, T::WM, T::WN, T::EB, T::LDS_BYTES, T::THREADS, T::CPR, sel, rsel, \
-     R::B_BK, R::B_STAGES, R::K_MULT, R::LDS_BYTES, R::LOOKAHEAD, R::A_BK, R::A_STAGES}
+     R::B_BK, R::B_STAGES, R::K_MULT, R::LDS_BYTES, R::LOOKAHEAD, R::A_BK, R::A_STAGES, R::A_COL_OK}
+// a configuration with only a ring kernel (16-bit inputs; calls it does not
+// take run the 128 x 128 configuration)
+#define ENTRY_RING_ONLY(name, R, rsel)                                                                          \
+    {name, TGEMM_F16, false, R::BM, R::BN, R::BK, R::WM, R::WN, 2, R::LDS_BYTES, R::THREADS, 1, nullptr, rsel, \
+     R::B_BK, R::B_STAGES, R::K_MULT, R::LDS_BYTES, R::LOOKAHEAD, R::A_BK, R::A_STAGES, R::A_COL_OK}
 // direct kernel: 32 x 32 per workgroup of 2 x 2 waves, steps of 32 of K
 #define ENTRY_DIRECT(name, fam, eb) \
-    {name, fam, true, 32, 32, 32, 2, 2, eb, 0, 256, 1, nullptr, nullptr, 0, 0, 0, 0, 0, 0, 0}
+    {name, fam, true, 32, 32, 32, 2, 2, eb, 0, 256, 1, nullptr, nullptr, 0, 0, 0, 0, 0, 0, 0, false}
 
 const ConfigEntry kConfigs[] = {
     ENTRY_RING("h256x256_w2x2", TGEMM_F16, CfgBig, tiled_kernel_big, RingBig, ring_kernel_big),
@@ -60,6 +66,7 @@ const ConfigEntry kConfigs[] = {
     ENTRY("s32x32x32_w1x1", TGEMM_F32, CfgF32Tiny, tiled_f32_tiny),
     ENTRY_DIRECT("h32x32_direct", TGEMM_F16, 2),
     ENTRY_DIRECT("s32x32_direct", TGEMM_F32, 4),
+    ENTRY_RING_ONLY("h64x128_w2x2", RingSmall, ring_kernel_small),
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 static_assert(kNumConfigs == NUM_CONFIGS, "");
@@ -204,6 +211,7 @@ int64_t operand_reach(bool kcontig, int64_t ext, int64_t ld, int64_t K, int64_t 
 // Whether a configuration with a ring kernel runs it.
 bool ring_applies(const ConfigEntry& c, const Problem& p) {
     if (c.ring == nullptr || !tuning().direct_lds) return false;
+    if (p.la == LAYOUT_COL && !c.ring_a_col) return false;
     // the ring loads ring_lookahead steps past K
     const int64_t extra = (int64_t)c.ring_lookahead * c.ring_bk;
     // K a multiple of ring_k_mult, or above it (the K-tail variant); any N
@@ -282,6 +290,10 @@ int table_choice(const Problem& p) {
         return CFG_DIRECT;
     }
     if (tiles_for(kConfigs[CFG_BIG], M, N) >= 256) return CFG_BIG;
+    // fewer 128 x 128 tiles than CUs: 64 x 128 tiles (twice the workgroups)
+    if (tiles_for(kConfigs[CFG_MID], M, N) >= 64 && tiles_for(kConfigs[CFG_MID], M, N) < 256 &&
+        ring_applies(kConfigs[CFG_RING_SMALL], p))
+        return CFG_RING_SMALL;
     if (tiles_for(kConfigs[CFG_MID], M, N) >= 128 && ring_applies(kConfigs[CFG_MID], p)) return CFG_MID;
     if (tiles_for(kConfigs[CFG_MID], M, N) >= 256) return CFG_MID;
     if (tiles_for(kConfigs[CFG_SMALL], M, N) >= 256) return CFG_SMALL;
@@ -327,6 +339,12 @@ int make_plan(const Problem& p, int config_id, Plan& plan) {
     plan.fn = nullptr;
     plan.kind = TGEMM_KERNEL_GENERAL;
     if (p.M == 0 || p.N == 0) return TGEMM_OK;
+    // a ring-only configuration whose ring kernel does not take the call
+    // (unaligned operands, short K, a column-major A it has no kernel for)
+    // runs the 128 x 128 configuration instead
+    if (!kConfigs[plan.config].direct && kConfigs[plan.config].tiled == nullptr &&
+        !ring_applies(kConfigs[plan.config], p))
+        plan.config = CFG_MID;
     const ConfigEntry& c = kConfigs[plan.config];
     if (!c.direct && ring_applies(c, p)) {
         plan.kind = TGEMM_KERNEL_RING;

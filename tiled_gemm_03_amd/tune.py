@@ -82,6 +82,15 @@ def time_configs(spec, configs, reps):
     return out
 
 
+def current_choice(spec):
+    """The configuration the built library's table picks for a call spec
+    (host-only lookup, with distinct aligned stand-in addresses)."""
+    from . import gemm_select_config
+    M, N, K, in_dt, out_dt, lda, ldb, ldc = spec
+    base = 1 << 40
+    return gemm_select_config(M, N, K, base, lda, base + (1 << 36), ldb, base + (2 << 36), ldc, in_dt, out_dt)
+
+
 def tune(specs, reps=20, log=print):
     """Screen at 1024^3 per type pair, refine the best KEEP at each spec."""
     record = {"screen": {}, "refine": []}
@@ -97,7 +106,14 @@ def tune(specs, reps=20, log=print):
             record["screen"][f"{in_dt}-{out_dt}"] = {str(k): v * 1e3 for k, v in t.items()}  # us
             log(f"[tune] screen {in_dt}->{out_dt} at {SCREEN}: " +
                 ", ".join(f"cfg{k} {t[k] * 1e3:.1f} us" for k in sorted(t, key=t.get)))
-        t = time_configs(spec, screened[(in_dt, out_dt)], reps)
+        # the configuration the library picks now is always refined too: a
+        # tile that is slow at the screening size (the 256 x 256 tile has 16
+        # tiles at 1024^3) may still be the best at the real size
+        cands = list(screened[(in_dt, out_dt)])
+        cur = current_choice(spec)
+        if cur >= 0 and cur not in cands:
+            cands.append(cur)
+        t = time_configs(spec, cands, reps)
         best = min(t, key=t.get)
         record["refine"].append({"spec": list(spec), "us": {str(k): v * 1e3 for k, v in t.items()}, "best": best})
         entries.append((*spec, best))
@@ -109,7 +125,8 @@ def tune(specs, reps=20, log=print):
 def emit(entries, path=TABLE, note=""):
     """Writes the exact-call table included by tgemm.hip."""
     lines = ["// tuned_table.inc -- exact-call entries written by tiled_gemm_03_amd/tune.py (the",
-             "// configuration search: screen at M = N = K = 1024, refine the best five at the real size).",
+             "// configuration search: screen at M = N = K = 1024, refine the best five and the current choice",
+             "// at the real size).",
              f"// {note}".rstrip(),
              "// {M, N, K, lda, ldb, ldc, in_dtype, out_dtype, config}"]
     for M, N, K, in_dt, out_dt, lda, ldb, ldc, cfg in entries:
