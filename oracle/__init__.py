@@ -18,10 +18,10 @@ import numpy as np
 
 from . import build as _build
 
-BINARY32, BINARY16, BFLOAT16 = 0, 1, 2
+BINARY32, BINARY16, BFLOAT16, FP8_E4M3, FP8_E5M2 = 0, 1, 2, 3, 4
 ACT_NONE, ACT_RELU, ACT_GELU, ACT_GELU_TANH, ACT_SILU = 0, 1, 2, 3, 4
 BIAS_NONE, BIAS_ROW, BIAS_COL = 0, 1, 2
-_NAMES = {"f32": BINARY32, "f16": BINARY16, "bf16": BFLOAT16}
+_NAMES = {"f32": BINARY32, "f16": BINARY16, "bf16": BFLOAT16, "e4m3": FP8_E4M3, "e5m2": FP8_E5M2}
 
 _lib = None
 
@@ -42,6 +42,8 @@ def _load(path=None):
                                 p, i64, p, i64, p, i64, ctypes.c_int]
     lib.oracle_decode_array.restype = ctypes.c_int
     lib.oracle_decode_array.argtypes = [p, ctypes.c_int, i64, p]
+    lib.oracle_encode_fp8_array.restype = ctypes.c_int
+    lib.oracle_encode_fp8_array.argtypes = [p, ctypes.c_int, i64, p]
     d = ctypes.c_double
     lib.oracle_activation.restype = d
     lib.oracle_activation.argtypes = [d, ctypes.c_int]
@@ -105,7 +107,8 @@ def gemm(a: np.ndarray, b: np.ndarray, dtype, rows=None, cols=None,
 
 def decode(bits: np.ndarray, dtype, lib_path=None) -> np.ndarray:
     """binary64 values of stored elements (uint16 bits for binary16 and
-    bfloat16, uint32 bits or float32 for binary32)."""
+    bfloat16, uint32 bits or float32 for binary32, uint8 bits for the 8-bit
+    formats FP8_E4M3 and FP8_E5M2)."""
     code = dtype_code(dtype)
     lib = _load(lib_path)
     x = np.ascontiguousarray(bits)
@@ -113,6 +116,19 @@ def decode(bits: np.ndarray, dtype, lib_path=None) -> np.ndarray:
     if lib.oracle_decode_array(x.ctypes.data, code, x.size, out.ctypes.data) != 0:
         raise ValueError("bad dtype")
     return out.reshape(x.shape)
+
+
+def encode_fp8(values, fmt, lib_path=None) -> np.ndarray:
+    """uint8 patterns of binary64 values rounded to FP8_E4M3 or FP8_E5M2
+    (nearest, ties to even; beyond the largest finite value, infinities
+    included, the largest finite value of the sign; NaN stays NaN)."""
+    code = dtype_code(fmt)
+    lib = _load(lib_path)
+    x = np.ascontiguousarray(values, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint8)
+    if lib.oracle_encode_fp8_array(x.ctypes.data, code, x.size, out.ctypes.data) != 0:
+        raise ValueError("bad 8-bit format")
+    return out
 
 
 def activation(x, act: int, lib_path=None) -> np.ndarray:

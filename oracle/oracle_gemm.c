@@ -109,7 +109,89 @@ double oracle_decode_binary32(uint32_t w) {
     return s ? -v : v;
 }
 
+/*
+ * 8-bit floating-point formats of the OCP specification, the output types of
+ * the fused epilogue (their own codes in this file):
+ *   E4M3: 1 sign bit, 4 exponent bits (bias 7), 3 fraction bits.  No
+ *         infinity: S.1111.111 is NaN, so the largest finite value is
+ *         S.1111.110 = 1.75 * 2^8 = 448.
+ *   E5M2: 1 sign bit, 5 exponent bits (bias 15), 2 fraction bits, laid out
+ *         like IEEE: e == 31 is infinity (f == 0) or NaN; the largest finite
+ *         value is 1.75 * 2^15 = 57344.
+ * With F fraction bits and bias b:
+ *   e == 0      : (-1)^s * f * 2^(1-b-F)          (zero and subnormals)
+ *   otherwise   : (-1)^s * (2^F + f) * 2^(e-b-F)
+ */
+#define ORACLE_FP8_E4M3 3
+#define ORACLE_FP8_E5M2 4
+
+double oracle_decode_fp8(uint8_t x, int fmt) {
+    const int F = fmt == ORACLE_FP8_E4M3 ? 3 : 2;
+    const int bias = fmt == ORACLE_FP8_E4M3 ? 7 : 15;
+    const int emax = fmt == ORACLE_FP8_E4M3 ? 15 : 31;
+    int s = (x >> 7) & 1;
+    int e = (x >> F) & emax;
+    int f = x & ((1 << F) - 1);
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, 1 - bias - F);
+    else if (fmt == ORACLE_FP8_E4M3 && e == 15 && f == 7)
+        v = NAN;
+    else if (fmt == ORACLE_FP8_E5M2 && e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)((1 << F) + f), e - bias - F);
+    return s ? -v : v;
+}
+
+/*
+ * Rounding of a binary64 value to an 8-bit format, the conversion the fused
+ * epilogue applies to its fp32 result: to the nearest representable value,
+ * ties to the one with an even fraction; a magnitude beyond the largest
+ * finite value, infinity included, becomes the largest finite value of the
+ * same sign (the saturating conversion); NaN becomes the all-ones pattern
+ * with the input's sign.  Returns the 8-bit pattern.
+ *
+ * Steps: the representable values in [2^E, 2^(E+1)) (E >= 1-b) are the
+ * multiples of 2^(E-F); below 2^(1-b) they are the multiples of the
+ * subnormal spacing 2^(1-b-F).  |x| divided by that spacing is exact; its
+ * nearest integer (ties to even: rint in the default rounding mode) times the
+ * spacing is the rounded magnitude (at most the largest finite value, to
+ * which larger magnitudes were clamped first), which is then encoded.
+ */
+uint8_t oracle_encode_fp8(double x, int fmt) {
+    const int F = fmt == ORACLE_FP8_E4M3 ? 3 : 2;
+    const int bias = fmt == ORACLE_FP8_E4M3 ? 7 : 15;
+    const double maxfin = fmt == ORACLE_FP8_E4M3 ? 448.0 : 57344.0;
+    const uint8_t s = signbit(x) ? 0x80 : 0;
+    if (isnan(x)) return s | 0x7f;
+    double a = fabs(x);
+    if (a > maxfin) a = maxfin;          /* infinity included */
+    if (a == 0.0) return s;
+    int e2;
+    frexp(a, &e2);                       /* a in [2^(e2-1), 2^e2) */
+    int E = e2 - 1;
+    if (E < 1 - bias) E = 1 - bias;      /* subnormal range: one spacing */
+    const double q = ldexp(1.0, E - F);
+    const double v = rint(a / q) * q;    /* <= maxfin: the rounding of a value <= maxfin */
+    if (v < ldexp(1.0, 1 - bias))        /* zero or subnormal: the code is f */
+        return s | (uint8_t)(v / ldexp(1.0, 1 - bias - F));
+    frexp(v, &e2);
+    E = e2 - 1;                          /* v in [2^E, 2^(E+1)) */
+    const int f = (int)(v / ldexp(1.0, E - F)) - (1 << F);
+    return s | (uint8_t)(((E + bias) << F) | f);
+}
+
+/* Rounds n binary64 values to an 8-bit format (oracle_encode_fp8). */
+int oracle_encode_fp8_array(const double* src, int fmt, int64_t n, uint8_t* dst) {
+    if ((fmt != ORACLE_FP8_E4M3 && fmt != ORACLE_FP8_E5M2) || n < 0) return -1;
+    for (int64_t i = 0; i < n; ++i) dst[i] = oracle_encode_fp8(src[i], fmt);
+    return 0;
+}
+
 static double decode_one(const void* base, int64_t idx, int dtype) {
+    if (dtype == ORACLE_FP8_E4M3 || dtype == ORACLE_FP8_E5M2)
+        return oracle_decode_fp8(((const uint8_t*)base)[idx], dtype);
     if (dtype == ORACLE_BINARY32) {
         uint32_t w;
         memcpy(&w, (const char*)base + idx * 4, 4);
@@ -122,7 +204,7 @@ static double decode_one(const void* base, int64_t idx, int dtype) {
 
 /* Decode n consecutive stored elements of type dtype into binary64. */
 int oracle_decode_array(const void* src, int dtype, int64_t n, double* dst) {
-    if (dtype < ORACLE_BINARY32 || dtype > ORACLE_BFLOAT16 || n < 0) return -1;
+    if (dtype < ORACLE_BINARY32 || dtype > ORACLE_FP8_E5M2 || n < 0) return -1;
     for (int64_t i = 0; i < n; ++i) dst[i] = decode_one(src, i, dtype);
     return 0;
 }

@@ -88,6 +88,72 @@ def pin_decode_binary32_sampled(lib_path=None):
     assert np.array_equal(got[~nan], want[~nan]), "binary32 decode differs"
 
 
+# ------------------------------------------------- 8-bit output formats
+# The OCP 8-bit formats the fused epilogue can write (E4M3: largest finite
+# 448, no infinity; E5M2: largest finite 57344).  torch's float8_e4m3fn and
+# float8_e5m2 are the same formats and an independent implementation of
+# their decoding and of the nearest-even rounding of in-range values; above
+# the largest finite value torch does not saturate (NaN / infinity), which is
+# pinned separately against closed forms.
+FP8 = ((oracle.FP8_E4M3, "float8_e4m3fn", 448.0, 0x7E), (oracle.FP8_E5M2, "float8_e5m2", 57344.0, 0x7B))
+
+
+def pin_decode_fp8_exhaustive(lib_path=None):
+    import torch
+    bits = np.arange(256, dtype=np.uint8)
+    for fmt, tname, _, _ in FP8:
+        got = oracle.decode(bits, fmt, lib_path=lib_path)
+        want = torch.from_numpy(bits).view(getattr(torch, tname)).to(torch.float64).numpy()
+        nan = np.isnan(want)
+        assert np.array_equal(np.isnan(got), nan), f"{tname}: NaN set differs"
+        assert np.array_equal(got[~nan], want[~nan]), f"{tname}: decode differs"
+        assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan])), f"{tname}: sign of zero"
+
+
+def pin_encode_fp8_vs_torch(lib_path=None):
+    """Every finite pattern encodes back to itself; every midpoint between
+    neighbouring values, the binary32 values just either side of it, and
+    random binary32 values within the finite range round as torch rounds."""
+    import torch
+    bits = np.arange(256, dtype=np.uint8)
+    rng = np.random.default_rng(77)
+    for fmt, tname, mx, _ in FP8:
+        vals = oracle.decode(bits, fmt, lib_path=lib_path)
+        fin = np.isfinite(vals)
+        back = oracle.encode_fp8(vals[fin], fmt, lib_path=lib_path)
+        assert np.array_equal(back, bits[fin]), f"{tname}: a value does not encode to its own pattern"
+        pos = np.unique(vals[fin & (vals >= 0)])
+        mids = ((pos[1:] + pos[:-1]) / 2).astype(np.float32)
+        x = np.concatenate([mids, np.nextafter(mids, np.float32(np.inf)), np.nextafter(mids, np.float32(0)),
+                            rng.uniform(-mx, mx, 4000).astype(np.float32),
+                            (rng.standard_normal(2000) * 2.0 ** rng.integers(-20, 8, 2000)).astype(np.float32)])
+        x = x[np.abs(x) <= mx]
+        x = np.concatenate([x, -x])
+        want = torch.from_numpy(x).to(getattr(torch, tname)).view(torch.uint8).numpy()
+        got = oracle.encode_fp8(x.astype(np.float64), fmt, lib_path=lib_path)
+        bad = got != want
+        assert not bad.any(), f"{tname}: {int(bad.sum())} roundings differ, e.g. {x[bad][:4]}"
+
+
+def pin_encode_fp8_saturation_and_ties(lib_path=None):
+    """Closed forms: beyond the largest finite value (infinity included) the
+    largest finite value of the sign; NaN the all-ones pattern; ties to the
+    even fraction, in the subnormal range too."""
+    for fmt, tname, mx, top in FP8:
+        enc = lambda v: int(oracle.encode_fp8(np.array([v], dtype=np.float64), fmt, lib_path=lib_path)[0])
+        for v in (mx * 1.0001, mx * 1.5, 1e30, np.inf):
+            assert enc(v) == top and enc(-v) == 0x80 | top, (tname, v)
+        assert enc(np.nan) & 0x7F == 0x7F
+        assert enc(0.0) == 0 and enc(-0.0) == 0x80
+        # subnormal spacing 2^(1 - bias - F)
+        q = 2.0 ** (-9 if fmt == oracle.FP8_E4M3 else -16)
+        assert enc(0.5 * q) == 0 and enc(1.5 * q) == 2 and enc(2.5 * q) == 2 and enc(0.5000001 * q) == 1
+        # 1 + half a spacing of [1, 2) lies between 1 (even) and the next value
+        F = 3 if fmt == oracle.FP8_E4M3 else 2
+        one = enc(1.0)
+        assert enc(1.0 + 2.0 ** -(F + 1)) == one and enc(1.0 + 3 * 2.0 ** -(F + 1)) == one + 2
+
+
 # --------------------------------------------------------- product pins
 def pin_identity(lib_path=None):
     """I x B == B and A x I == A exactly (closed form), every input type,
@@ -339,6 +405,9 @@ FAST_PINS = [
     pin_decode_binary16_exhaustive,
     pin_decode_bfloat16_exhaustive,
     pin_decode_binary32_sampled,
+    pin_decode_fp8_exhaustive,
+    pin_encode_fp8_vs_torch,
+    pin_encode_fp8_saturation_and_ties,
     pin_identity,
     pin_all_ones,
     pin_golden_ones_8x8,

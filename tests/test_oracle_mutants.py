@@ -44,6 +44,17 @@ MUTANTS = [
     ("gelu_tanh_cubic_term", "0.044715 * x * x * x", "0.044715 * x * x"),
     ("silu_sign", "return x / (1.0 + exp(-x));", "return x / (1.0 + exp(x));"),
     ("relu_inverted", "return x > 0.0 ? x : 0.0;", "return x < 0.0 ? x : 0.0;"),
+    # the 8-bit output formats
+    ("fp8_e4m3_bias", "const int bias = fmt == ORACLE_FP8_E4M3 ? 7 : 15;",
+     "const int bias = fmt == ORACLE_FP8_E4M3 ? 8 : 15;"),
+    ("fp8_e4m3_nan_as_number", "else if (fmt == ORACLE_FP8_E4M3 && e == 15 && f == 7)\n        v = NAN;", ""),
+    ("fp8_subnormal_scale", "v = ldexp((double)f, 1 - bias - F);", "v = ldexp((double)f, -bias - F);"),
+    ("fp8_truncates", "const double v = rint(a / q) * q;", "const double v = floor(a / q) * q;"),
+    ("fp8_ties_away", "const double v = rint(a / q) * q;", "const double v = round(a / q) * q;"),
+    ("fp8_no_saturation", "if (a > maxfin) a = maxfin;", ""),
+    ("fp8_sign_dropped", "const uint8_t s = signbit(x) ? 0x80 : 0;", "const uint8_t s = 0;"),
+    ("fp8_e5m2_fraction_bits", "const int F = fmt == ORACLE_FP8_E4M3 ? 3 : 2;\n    const int bias = fmt == ORACLE_FP8_E4M3 ? 7 : 15;\n    const double maxfin",
+     "const int F = fmt == ORACLE_FP8_E4M3 ? 3 : 3;\n    const int bias = fmt == ORACLE_FP8_E4M3 ? 7 : 15;\n    const double maxfin"),
 ]
 
 RUNNER = r"""
