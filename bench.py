@@ -525,6 +525,20 @@ def main():
             fev = time_calls(call, 20, 3, stream)["events_ms"]
             med = float(np.median(fev))
             fused.append({"epilogue": name, "us_median": med * 1e3, "tflops": flops / (med * 1e-3) / 1e12})
+        # an 8-bit output (OCP E4M3) with the same epilogue
+        c8 = torch.empty((w.M, w.N), dtype=torch.float8_e4m3fn, device=dev)
+        call = lambda: T.gemm_tensors(a, b, c8, stream=stream.cuda_stream, alpha=1.0 / 64, bias=bias,
+                                      activation=T.ACT_GELU_TANH)
+        fev = time_calls(call, 20, 3, stream)["events_ms"]
+        med = float(np.median(fev))
+        fused.append({"epilogue": "alpha 1/64, column bias + gelu (tanh form), fp8 e4m3 output",
+                      "us_median": med * 1e3, "tflops": flops / (med * 1e-3) / 1e12})
+        del c8
+        # the identity epilogue (what an unaligned C or N % 4 != 0 runs)
+        call = lambda: T.gemm_tensors(a, b, c, stream=stream.cuda_stream, alpha=1.0)
+        fev = time_calls(call, 20, 3, stream)["events_ms"]
+        med = float(np.median(fev))
+        fused.append({"epilogue": "identity (alpha 1)", "us_median": med * 1e3, "tflops": flops / (med * 1e-3) / 1e12})
         # the plain product again, right after, for the comparison at the same clock
         pev = time_calls(step, 20, 3, stream)["events_ms"]
         med = float(np.median(pev))

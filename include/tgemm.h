@@ -45,11 +45,28 @@ extern "C" {
 #define TGEMM_F32 0  /* IEEE binary32 */
 #define TGEMM_F16 1  /* IEEE binary16 */
 #define TGEMM_BF16 2 /* bfloat16 (upper half of a binary32) */
+/* 8-bit floating-point outputs (OCP 8-bit floating point formats; output
+ * types only):
+ *   E4M3: 1 sign, 4 exponent (bias 7), 3 fraction bits; no infinity,
+ *         S.1111.111 is NaN; largest finite value 448.
+ *   E5M2: 1 sign, 5 exponent (bias 15), 2 fraction bits; IEEE-like
+ *         infinities and NaNs; largest finite value 57344.
+ * One byte per element; torch's float8_e4m3fn and float8_e5m2 hold the same
+ * formats. */
+#define TGEMM_FP8_E4M3 3
+#define TGEMM_FP8_E5M2 4
 
 /* Supported (in_dtype -> out_dtype) pairs:
- *   F32 -> F32, F16 -> F16, F16 -> F32, BF16 -> BF16, BF16 -> F32.
+ *   F32 -> F32, F16 -> F16, F16 -> F32, BF16 -> BF16, BF16 -> F32,
+ *   F16 or BF16 -> FP8_E4M3 or FP8_E5M2.
  * Conversion of the fp32 accumulator to F16 / BF16 rounds to nearest, ties to
- * even; values beyond the output range become +-Inf. */
+ * even; values beyond the output range become +-Inf.  Conversion to an 8-bit
+ * format rounds to nearest, ties to even, and saturates: magnitudes beyond
+ * the largest finite value, infinities included, become the largest finite
+ * value of their sign; NaN stays NaN (the all-ones pattern).  8-bit outputs
+ * are written by the fused epilogue's kernels (ring configurations where
+ * they apply, the direct kernel otherwise; TGEMM_ERR_DIM where neither
+ * does), with the identity epilogue when none is given. */
 
 /* Error codes. */
 #define TGEMM_OK 0
@@ -112,8 +129,9 @@ int gemm_ex(int64_t M, int64_t N, int64_t K,
  * gemm(...) is gemm_t(..., ROW_MAJOR, ..., ROW_MAJOR, ..., ROW_MAJOR, ..., -1).
  * A column-major C is computed as the row-major C^T = B^T x A^T.  Kernels:
  * row-major A and B take every configuration; with a column-major operand
- * the direct-to-LDS ring kernels of configurations 0 and 1 run whole aligned
- * tiles, the direct kernels of configurations 6 and 7 everything else
+ * the direct-to-LDS ring kernels of configurations 0 and 1 (8 with a
+ * row-major A) run whole aligned tiles, the direct kernels of
+ * configurations 6 and 7 everything else
  * (configurations 2 to 5 return TGEMM_ERR_CONFIG there, and products whose
  * 32-bit buffer offsets would overflow return TGEMM_ERR_DIM).  config_id -1:
  * the table's choice.  Other arguments, ownership and errors as gemm_ex.
@@ -133,8 +151,9 @@ int gemm_t(int64_t M, int64_t N, int64_t K,
  *   C := act(alpha * (A x B) + beta * C + bias)
  *
  * evaluated in fp32 on the fp32 accumulator, then rounded to the output type
- * (nearest even).  beta == 0: C is not read (it may hold anything, NaN
- * included).  bias: one value per row of C (bias_kind TGEMM_BIAS_ROW, M
+ * (nearest even; saturating for the 8-bit formats).  beta == 0: C is not read
+ * (it may hold anything, NaN included); otherwise C is read in the output
+ * type, an 8-bit C too.  bias: one value per row of C (bias_kind TGEMM_BIAS_ROW, M
  * values) or per column (TGEMM_BIAS_COL, N values, the bias of a linear
  * layer), contiguous, of type bias_dtype (TGEMM_F32 / F16 / BF16), device
  * memory owned by the caller, not overlapping C.  Activations:
@@ -217,7 +236,7 @@ int gemm_select_config(int64_t M, int64_t N, int64_t K,
 #define TGEMM_KERNEL_GENERAL 0 /* register-staged, every access checked (ragged or unaligned) */
 #define TGEMM_KERNEL_TILED 1   /* register-staged, whole tiles, aligned operands              */
 #define TGEMM_KERNEL_RING 2    /* direct-to-LDS rings: 16-bit inputs, aligned, K a multiple
-                                  of 128 or above 128, N % 4 == 0 (configurations 0, 1)     */
+                                  of 128 or above 128 (configurations 0, 1 and 8)           */
 #define TGEMM_KERNEL_DIRECT 3  /* operands straight from memory to registers, no LDS: small,
                                   ragged or unaligned products (configurations 6 and 7)     */
 

@@ -228,6 +228,31 @@ def test_ring_configs_report_their_ring_kernel():
     assert (T.gemm_config_info(8)["block_m"], T.gemm_config_info(8)["block_n"]) == (64, 128)
 
 
+def test_fp8_outputs_are_checked_and_routed():
+    """8-bit outputs: from 16-bit inputs only; written by the ring kernels
+    where they apply, by the direct kernel elsewhere (never a register-staged
+    kernel)."""
+    RING, DIRECT = T.KERNEL_RING, T.KERNEL_DIRECT
+    for fmt in (T.FP8_E4M3, T.FP8_E5M2):
+        for in_dt in (T.F16, T.BF16):
+            assert _kernel(8192, 8192, 8192, in_dt=in_dt, out_dt=fmt) == RING
+            assert _kernel_t(1024, 2048, 512, R_, R_, R_, in_dt=in_dt, out_dt=fmt) == (RING, 8)
+            assert _kernel_t(1000, 1000, 1000, C_, C_, C_, in_dt=in_dt, out_dt=fmt)[0] == RING
+            assert _kernel(127, 255, 512, ldb=255, ldc=255, in_dt=in_dt, out_dt=fmt) == DIRECT
+            # unaligned rows: the table's register-staged tile is replaced by the direct kernel
+            assert _kernel(1024, 1024, 301, lda=302, ldb=1027, in_dt=in_dt, out_dt=T.F32) == T.KERNEL_GENERAL
+            assert _kernel_t(1024, 1024, 301, R_, R_, R_, lda=302, ldb=1027, in_dt=in_dt, out_dt=fmt) == (DIRECT, 6)
+            assert _kernel(256, 256, 64, cid=2, in_dt=in_dt, out_dt=fmt) == DIRECT
+        assert _kernel(64, 64, 64, in_dt=T.F32, out_dt=fmt) == T.ERR_DTYPE
+        assert _kernel(64, 64, 64, in_dt=fmt, out_dt=fmt) == T.ERR_DTYPE
+        assert _kernel(64, 64, 64, in_dt=fmt, out_dt=T.F16) == T.ERR_DTYPE
+        # C holds one byte per element: its span for the overlap check
+        assert T.gemm(4, 4, 4, FAKE, 4, FAKE + 4096, 4, FAKE + 8, 4, T.F16, fmt, None) == T.ERR_ALIAS
+    # offsets beyond 31 bits for the direct kernel: no kernel for an 8-bit output
+    assert _kernel(64, 64, 1 << 20, ldb=1 << 12, out_dt=T.FP8_E4M3) == T.ERR_DIM
+    assert _kernel(64, 64, 64, out_dt=5) == T.ERR_DTYPE
+
+
 def test_ring_only_configuration_falls_back_to_128x128():
     """Configuration 8 (64 x 128 ring, row-major A) has no register-staged
     kernel: calls its ring does not take run configuration 1 instead, and the

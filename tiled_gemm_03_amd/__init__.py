@@ -23,7 +23,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libtgemm.so")
 
-F32, F16, BF16 = 0, 1, 2
+F32, F16, BF16, FP8_E4M3, FP8_E5M2 = 0, 1, 2, 3, 4
 OK = 0
 ERR_DIM, ERR_NULL, ERR_LD, ERR_DTYPE, ERR_ALIAS, ERR_CONFIG, ERR_LAYOUT, ERR_EPILOGUE = -1, -2, -3, -4, -5, -6, -7, -8
 ERR_HEAD_DIM = -9
@@ -208,7 +208,8 @@ def attention_waves(B, H, n_q, d):
 # ------------------------------------------------------------ torch marshalling
 def dtype_code(t):
     import torch
-    codes = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+    codes = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16,
+             torch.float8_e4m3fn: FP8_E4M3, torch.float8_e5m2: FP8_E5M2}
     if t.dtype not in codes:
         raise TypeError(f"unsupported tensor dtype {t.dtype}")
     return codes[t.dtype]

@@ -48,7 +48,16 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-enum { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+// element types; DT_FP8: an 8-bit floating-point output (output only, with
+// the fused epilogue's kernels), its format OCP E4M3 or E5M2 chosen at run
+// time by GemmArgs::fp8_e5m2
+enum { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_FP8 = 3 };
+
+// bytes per output element
+template <int OUT>
+__host__ __device__ constexpr int out_bytes() {
+    return OUT == DT_F32 ? 4 : OUT == DT_FP8 ? 1 : 2;
+}
 
 struct GemmArgs {
     const char* A;
@@ -66,6 +75,7 @@ struct GemmArgs {
     float alpha, beta;      // beta == 0: C is not read
     const char* bias;       // bias_kind BIAS_ROW: M values, BIAS_COL: N values, of type bias_dt
     int bias_kind, bias_dt, act;
+    int fp8_e5m2;           // DT_FP8 output: 0 = E4M3, 1 = E5M2
 };
 
 enum { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU = 2, ACT_GELU_TANH = 3, ACT_SILU = 4 };
@@ -216,10 +226,61 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-// Four consecutive outputs; fp32 -> fp16 / bf16 rounds to nearest even.
+// ------------------------------------------------------- 8-bit outputs
+// The OCP 8-bit floating-point formats.  E4M3: 1 sign, 4 exponent (bias 7)
+// and 3 fraction bits, no infinity, S.1111.111 NaN, largest finite value
+// 1.75 * 2^8 = 448.  E5M2: 1 sign, 5 exponent (bias 15) and 2 fraction bits,
+// IEEE-like (exponent 31: infinity or NaN), largest finite 1.75 * 2^15 =
+// 57344.  Below 2^(1 - bias) the values are multiples of the subnormal
+// spacing 2^(1 - bias - F).
+//
+// fp32 -> 8 bits: nearest, ties to even; magnitudes beyond the largest finite
+// value, infinities included, become the largest finite value of the sign
+// (the saturating conversion); NaN becomes the all-ones pattern with the sign.
+__device__ __forceinline__ uint32_t to_fp8(float x, int e5m2) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7fffffffu;
+    if (a > 0x7f800000u) return sign | 0x7fu;
+    const int F = e5m2 ? 2 : 3;
+    const uint32_t top = e5m2 ? 0x7bu : 0x7eu;   // largest finite pattern
+    uint32_t r;
+    if (a < (e5m2 ? 0x38800000u : 0x3c800000u)) {  // below 2^-14 / 2^-6: subnormal spacing
+        // |x| / spacing is exact (a power-of-two scale of a value below 2^F);
+        // rint rounds it to nearest even; 2^F is the smallest normal's pattern
+        r = (uint32_t)__builtin_rintf(__builtin_bit_cast(float, a) * (e5m2 ? 65536.f : 512.f));
+    } else {
+        // drop 23 - F fraction bits, nearest even, carrying into the
+        // exponent; then re-bias the exponent (127 -> 15 or 7)
+        const int drop = 23 - F;
+        const uint32_t rnd = a + ((1u << (drop - 1)) - 1u) + ((a >> drop) & 1u);
+        const uint32_t e = (rnd >> 23) - (e5m2 ? 112u : 120u);
+        r = (e << F) | ((rnd >> drop) & ((1u << F) - 1u));
+        r = r > top ? top : r;
+    }
+    return sign | r;
+}
+__device__ __forceinline__ float from_fp8(uint32_t b, int e5m2) {
+    if (e5m2) {
+        // an E5M2 pattern is the upper byte of the binary16 of the same value
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(b << 8));
+    }
+    const uint32_t sign = (b & 0x80u) << 24, e = (b >> 3) & 15u, m = b & 7u;
+    if (e == 15u && m == 7u) return __builtin_bit_cast(float, sign | 0x7fc00000u);
+    if (e == 0u) return __builtin_bit_cast(float, sign | __builtin_bit_cast(uint32_t, (float)m * 0.001953125f));
+    return __builtin_bit_cast(float, sign | ((e + 120u) << 23) | (m << 20));
+}
+
+// Four consecutive outputs; fp32 -> fp16 / bf16 rounds to nearest even, fp32
+// -> 8 bits as to_fp8 (fp8_e5m2 picks the format).
 template <int OUT>
-__device__ __forceinline__ void store4(char* p, float a, float b, float c, float d, bool vec) {
-    if constexpr (OUT == DT_F32) {
+__device__ __forceinline__ void store4(char* p, float a, float b, float c, float d, bool vec, int fp8_e5m2 = 0) {
+    if constexpr (OUT == DT_FP8) {
+        const uint32_t w = to_fp8(a, fp8_e5m2) | (to_fp8(b, fp8_e5m2) << 8) | (to_fp8(c, fp8_e5m2) << 16) |
+                           (to_fp8(d, fp8_e5m2) << 24);
+        if (vec) *(uint32_t*)p = w;
+        else __builtin_memcpy(p, &w, 4);
+    } else if constexpr (OUT == DT_F32) {
         if (vec) {
             *(f32x4*)p = f32x4{a, b, c, d};
         } else {
@@ -245,8 +306,9 @@ __device__ __forceinline__ void store4(char* p, float a, float b, float c, float
 }
 
 template <int OUT>
-__device__ __forceinline__ void store_elem(char* p, float v) {
-    if constexpr (OUT == DT_F32) *(float*)p = v;
+__device__ __forceinline__ void store_elem(char* p, float v, int fp8_e5m2 = 0) {
+    if constexpr (OUT == DT_FP8) *(uint8_t*)p = (uint8_t)to_fp8(v, fp8_e5m2);
+    else if constexpr (OUT == DT_F32) *(float*)p = v;
     else if constexpr (OUT == DT_F16) *(_Float16*)p = (_Float16)v;
     else *(__bf16*)p = (__bf16)v;
 }
@@ -258,7 +320,8 @@ __device__ __forceinline__ void store_elem(char* p, float v) {
 // product: C := act(alpha * AB + beta * C + bias), bias one value per row or
 // per column of C, in fp32 before the output rounding.
 
-__device__ __forceinline__ float load_value(const char* p, int64_t i, int dt) {
+__device__ __forceinline__ float load_value(const char* p, int64_t i, int dt, int fp8_e5m2 = 0) {
+    if (dt == DT_FP8) return from_fp8(((const uint8_t*)p)[i], fp8_e5m2);
     if (dt == DT_F32) return ((const float*)p)[i];
     if (dt == DT_F16) return (float)((const _Float16*)p)[i];
     return (float)((const __bf16*)p)[i];
@@ -285,7 +348,13 @@ __device__ __forceinline__ float activate(float x, int act) {
 
 // Four consecutive elements of type dt from any element-aligned address, as
 // fp32 (one load: unaligned-access mode).
-__device__ __forceinline__ f32x4 load4_values(const char* p, int dt) {
+__device__ __forceinline__ f32x4 load4_values(const char* p, int dt, int fp8_e5m2 = 0) {
+    if (dt == DT_FP8) {
+        uint32_t w;
+        __builtin_memcpy(&w, p, 4);
+        return f32x4{from_fp8(w & 0xffu, fp8_e5m2), from_fp8((w >> 8) & 0xffu, fp8_e5m2),
+                     from_fp8((w >> 16) & 0xffu, fp8_e5m2), from_fp8(w >> 24, fp8_e5m2)};
+    }
     if (dt == DT_F32) {
         f32x4 v;
         __builtin_memcpy(&v, p, 16);
@@ -313,18 +382,18 @@ __device__ __forceinline__ f32x4 load4_values(const char* p, int dt) {
 // are in flight together.
 template <int OUT>
 __device__ __forceinline__ f32x4 fused_pre(const GemmArgs& p, int row, int col, int n, f32x4 v) {
-    constexpr int OB = OUT == DT_F32 ? 4 : 2;
+    constexpr int OB = out_bytes<OUT>();
     const char* src = p.C + ((int64_t)row * p.ldc + col) * OB;
     const int beb = p.bias_dt == DT_F32 ? 4 : 2;
     f32x4 t = v * p.alpha;
     if (n == 4) {
-        if (p.beta != 0.f) t += p.beta * load4_values(src, OUT);
+        if (p.beta != 0.f) t += p.beta * load4_values(src, OUT, p.fp8_e5m2);
         if (p.bias_kind == BIAS_COL) t += load4_values(p.bias + (int64_t)col * beb, p.bias_dt);
     } else {
 #pragma unroll
         for (int e = 0; e < 3; ++e) {
             if (e >= n) break;
-            if (p.beta != 0.f) t[e] += p.beta * load_value(src, e, OUT);
+            if (p.beta != 0.f) t[e] += p.beta * load_value(src, e, OUT, p.fp8_e5m2);
             if (p.bias_kind == BIAS_COL) t[e] += load_value(p.bias, col + e, p.bias_dt);
         }
     }
@@ -334,17 +403,17 @@ __device__ __forceinline__ f32x4 fused_pre(const GemmArgs& p, int row, int col, 
 
 template <int OUT>
 __device__ __forceinline__ void fused_post(const GemmArgs& p, int row, int col, int n, bool vec, f32x4 t) {
-    constexpr int OB = OUT == DT_F32 ? 4 : 2;
+    constexpr int OB = out_bytes<OUT>();
     char* dst = p.C + ((int64_t)row * p.ldc + col) * OB;
     float o[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) o[e] = activate(t[e], p.act);
     if (n == 4) {
-        store4<OUT>(dst, o[0], o[1], o[2], o[3], vec);
+        store4<OUT>(dst, o[0], o[1], o[2], o[3], vec, p.fp8_e5m2);
     } else {
 #pragma unroll
         for (int e = 0; e < 3; ++e)
-            if (e < n) store_elem<OUT>(dst + e * OB, o[e]);
+            if (e < n) store_elem<OUT>(dst + e * OB, o[e], p.fp8_e5m2);
     }
 }
 
@@ -354,44 +423,164 @@ __device__ __forceinline__ void store4_fused(const GemmArgs& p, int row, int col
 }
 
 // The fused epilogue of a wave's NB accumulator blocks of VPL fp32 values
-// per lane (VPL / 4 groups of 4 consecutive columns), through this wave's
-// LDS region (PB blocks at a time): the blocks go through fused_pre with
-// compile-time register indices (every load of C and of the bias of the
-// pass issued together) into the region, then are read back in a run-time
-// loop that holds one copy of the activation code.  get(IntTag<b>): block b's values;
+// per lane (VPL / 4 groups of 4 consecutive columns), through this wave's LDS
+// region, PB blocks (a pass) at a time.  get(IntTag<b>): block b's values;
 // where(b, g, row, col, n, vec): the output position of group g of block b
-// (n = 0: nothing to store).  The caller has made sure that no wave still
-// reads the LDS it reuses.
+// (n outputs inside C, 0: nothing to store; vec: 4-element vector stores).
+// The caller has made sure that no wave still reads the LDS it reuses, and
+// has staged the workgroup tile's bias (stage_bias) in LDS.
+//
+// Every decision that depends on the epilogue's arguments (beta, the bias,
+// its kind and type, the activation) is taken at run time and is the same for
+// every lane; the code that takes it exists once per kernel, in loops, so
+// that the epilogue runs a few thousand instructions per wave rather than one
+// copy of every branch per group.  Per pass:
+//  1. the pass's accumulators go to the region (compile-time register
+//     indices, no loads), group i at region[64 i + lane];
+//  2. unless the epilogue is alpha and an activation only, the whole groups
+//     are taken EB at a time: the old C of all EB is loaded together (one
+//     wait), then each group's alpha * acc + beta * C + bias (the bias from
+//     LDS) is written back in place;
+//  3. one loop over the groups applies alpha (when step 2 did not run), the
+//     activation and the output rounding, and stores; a partial group (n <
+//     4) is formed there element by element.
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+typedef __attribute__((address_space(3))) float lds_float;
+
+// The bias of a workgroup tile (rows m0 .. m0 + BM - 1, columns n0 .. n0 +
+// BN - 1) as fp32 in LDS: bias_col[j] for column n0 + j (BIAS_COL), bias_row[i]
+// for row m0 + i (BIAS_ROW); the array of the other kind, and entries past M
+// or N, hold zeros.  Every thread of the workgroup takes part; a barrier must
+// follow before the values are read.
+template <int THREADS, int BM, int BN>
+__device__ __forceinline__ void stage_bias(const GemmArgs& p, lds_float* bias_col, lds_float* bias_row, int m0, int n0) {
+    for (int j = threadIdx.x; j < BN; j += THREADS)
+        bias_col[j] = p.bias_kind == BIAS_COL && n0 + j < p.N ? load_value(p.bias, n0 + j, p.bias_dt) : 0.f;
+    for (int i = threadIdx.x; i < BM; i += THREADS)
+        bias_row[i] = p.bias_kind == BIAS_ROW && m0 + i < p.M ? load_value(p.bias, m0 + i, p.bias_dt) : 0.f;
+}
+
+// The old C of one whole group (4 outputs), raw: one register of a type fixed
+// by the output type, so that several groups' loads can be in flight at once.
+template <int OUT>
+struct RawC {
+    typedef uint64_t type;   // 16-bit outputs: 4 x 16 bits
+};
+template <>
+struct RawC<DT_F32> {
+    typedef f32x4 type;
+};
+template <>
+struct RawC<DT_FP8> {
+    typedef uint32_t type;
+};
+
+template <int OUT>
+__device__ __forceinline__ typename RawC<OUT>::type load_raw_c(const char* src) {
+    typename RawC<OUT>::type v;
+    __builtin_memcpy(&v, src, sizeof(v));
+    return v;
+}
+
+template <int OUT>
+__device__ __forceinline__ f32x4 raw_c_values(typename RawC<OUT>::type w, int fp8_e5m2) {
+    if constexpr (OUT == DT_F32) {
+        return w;
+    } else if constexpr (OUT == DT_FP8) {
+        return f32x4{from_fp8(w & 0xffu, fp8_e5m2), from_fp8((w >> 8) & 0xffu, fp8_e5m2),
+                     from_fp8((w >> 16) & 0xffu, fp8_e5m2), from_fp8(w >> 24, fp8_e5m2)};
+    } else {
+        // the two halves of the 64-bit scalar by shifts (a two-dword vector
+        // read element by element is miscompiled by hipcc 7.2: the second
+        // dword is taken from the first)
+        const uint32_t lo = (uint32_t)w, hi = (uint32_t)(w >> 32);
+        if constexpr (OUT == DT_F16) {
+            const f16x2 a = __builtin_bit_cast(f16x2, lo), b = __builtin_bit_cast(f16x2, hi);
+            return f32x4{(float)a[0], (float)a[1], (float)b[0], (float)b[1]};
+        } else {
+            return f32x4{__builtin_bit_cast(float, lo << 16), __builtin_bit_cast(float, lo & 0xffff0000u),
+                         __builtin_bit_cast(float, hi << 16), __builtin_bit_cast(float, hi & 0xffff0000u)};
+        }
+    }
+}
 
 // WHOLE: every group is wholly inside C or wholly outside (n is 4 or 0), so
-// the partial-group code is not compiled.
+// the partial-group code is not compiled.  row0 / col0: the first row and
+// column of the workgroup tile (the origin of the staged bias).
 template <int OUT, int NB, int VPL, int PB, bool WHOLE, class Get, class Where>
-__device__ __forceinline__ void fused_epilogue(const GemmArgs& p, lds_f32x4* region, Get&& get, Where&& where) {
+__device__ __forceinline__ void fused_epilogue(const GemmArgs& p, lds_f32x4* region, const lds_float* bias_col,
+                                               const lds_float* bias_row, int row0, int col0, Get&& get,
+                                               Where&& where) {
     static_assert(NB % PB == 0 && VPL % 4 == 0, "");
+    constexpr int G = VPL / 4;   // groups per block
+    constexpr int NG = PB * G;   // groups per pass
+    constexpr int EB = NG < 8 ? NG : 8;  // groups whose loads of C are in flight together
+    static_assert(NG % EB == 0, "");
+    constexpr int OB = out_bytes<OUT>();
     const int lane = threadIdx.x & 63;
+    const bool rd_c = p.beta != 0.f;
+    const bool has_bias = p.bias_kind != BIAS_NONE;
+    const bool combine = rd_c || has_bias;
     static_for<0, NB / PB>([&](auto pass_t) {
         constexpr int b0 = decltype(pass_t)::value * PB;
+        // 1: the pass's accumulators into the region
         static_for<0, PB>([&](auto t_t) {
             constexpr int t = decltype(t_t)::value;
             const auto blk = get(IntTag<b0 + t>{});
-            static_for<0, VPL / 4>([&](auto g_t) {
+            static_for<0, G>([&](auto g_t) {
                 constexpr int g = decltype(g_t)::value;
-                int row, col, n;
-                bool vec;
-                where(b0 + t, g, row, col, n, vec);
-                const f32x4 v = f32x4{blk[4 * g + 0], blk[4 * g + 1], blk[4 * g + 2], blk[4 * g + 3]};
-                region[(t * 64 + lane) * (VPL / 4) + g] = n > 0 ? fused_pre<OUT>(p, row, col, WHOLE ? 4 : n, v) : v;
+                region[(t * G + g) * 64 + lane] = f32x4{blk[4 * g + 0], blk[4 * g + 1], blk[4 * g + 2], blk[4 * g + 3]};
             });
         });
-        for (int t = 0; t < PB; ++t)
-            for (int g = 0; g < VPL / 4; ++g) {
-                int row, col, n;
-                bool vec;
-                where(b0 + t, g, row, col, n, vec);
-                if (n > 0) fused_post<OUT>(p, row, col, WHOLE ? 4 : n, vec, region[(t * 64 + lane) * (VPL / 4) + g]);
+        auto at = [&](int i, int& row, int& col, int& n, bool& vec) __attribute__((always_inline)) {
+            where(b0 + i / G, i % G, row, col, n, vec);
+        };
+        // 2: alpha * acc + beta * C + bias of the whole groups, EB at a time
+        if (combine) {
+            // not unrolled: with the batches unrolled the register allocator
+            // moves accumulators inside the main loop of the ring kernel
+#pragma unroll 1
+            for (int i0 = 0; i0 < NG; i0 += EB) {
+                typename RawC<OUT>::type cw[EB];
+                int ns[EB], rows[EB], cols[EB];
+                static_for<0, EB>([&](auto d_t) {
+                    constexpr int d = decltype(d_t)::value;
+                    bool vec;
+                    at(i0 + d, rows[d], cols[d], ns[d], vec);
+                    if (rd_c && ns[d] == 4) cw[d] = load_raw_c<OUT>(p.C + ((int64_t)rows[d] * p.ldc + cols[d]) * OB);
+                });
+                static_for<0, EB>([&](auto d_t) {
+                    constexpr int d = decltype(d_t)::value;
+                    if (ns[d] == 4) {
+                        lds_f32x4* slot = region + (i0 + d) * 64 + lane;
+                        // both bias arrays are read (the one of the other
+                        // kind holds zeros); only the bias of the call's kind
+                        // is added
+                        const f32x4 bc = *(const lds_f32x4*)(bias_col + (cols[d] - col0));
+                        const float br = bias_row[rows[d] - row0];
+                        f32x4 t = *slot * p.alpha;
+                        if (rd_c) t += p.beta * raw_c_values<OUT>(cw[d], p.fp8_e5m2);
+                        if (has_bias) t += p.bias_kind == BIAS_COL ? bc : f32x4{br, br, br, br};
+                        *slot = t;
+                    }
+                });
             }
+        }
+        // 3: activation, output rounding and stores
+        for (int i = 0; i < NG; ++i) {
+            int row, col, n;
+            bool vec;
+            at(i, row, col, n, vec);
+            if (n <= 0) continue;
+            f32x4 t = region[i * 64 + lane];
+            if (WHOLE || n == 4) {
+                if (!combine) t *= p.alpha;
+            } else {
+                t = fused_pre<OUT>(p, row, col, n, t);
+            }
+            fused_post<OUT>(p, row, col, WHOLE ? 4 : n, vec, t);
+        }
     });
 }
 
@@ -664,10 +853,14 @@ void gemm_kernel(GemmArgs p) {
 
     // a7: epilogue.  acc[i][j][4q + e] = C[row][col + e] with
     // row = m0 + wm*WTM + 32 i + lane%32, col = n0 + wn*WTN + 32 j + 8 q + 4 (lane/32).
-    constexpr int OB = OUT == DT_F32 ? 4 : 2;
+    constexpr int OB = out_bytes<OUT>();
     const int64_t ldc = p.ldc;
     if constexpr (EPI) {
-        // fused epilogue through LDS, once no wave reads it any more
+        // fused epilogue through LDS, once no wave reads it any more; the
+        // tile's bias in an LDS array of its own
+        __shared__ __attribute__((aligned(16))) float ebias_[T::BM + T::BN];
+        lds_float* const ebias = (lds_float*)(lds_void*)ebias_;
+        stage_bias<T::THREADS, T::BM, T::BN>(p, ebias, ebias + T::BN, m0, n0);
         __syncthreads();
         constexpr int REGION = T::LDS_BYTES / T::WAVES;                   // bytes per wave
         constexpr int PB0 = REGION / (64 * 64) < T::FM * T::FN ? REGION / (64 * 64) : T::FM * T::FN;
@@ -675,7 +868,8 @@ void gemm_kernel(GemmArgs p) {
         static_assert(PB >= 1, "the LDS holds a block of accumulators per wave");
         lds_f32x4* region = (lds_f32x4*)(lds_void*)smem + wave * (REGION / 16);
         fused_epilogue<OUT, T::FM * T::FN, 16, PB, FAST>(
-            p, region, [&](auto b_t) { constexpr int b = decltype(b_t)::value; return acc[b / T::FN][b % T::FN]; },
+            p, region, ebias, ebias + T::BN, m0, n0,
+            [&](auto b_t) { constexpr int b = decltype(b_t)::value; return acc[b / T::FN][b % T::FN]; },
             [&](int b, int q, int& row, int& col, int& n, bool& vec) {
                 const int i = b / T::FN, j = b % T::FN;
                 row = m0 + a_frow0 + 32 * i;

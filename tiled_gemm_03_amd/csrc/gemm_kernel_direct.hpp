@@ -191,7 +191,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void gemm_kern
 
     // epilogue: row m0 + l%16, columns n0 + 4q .. +3; fp32 -> fp16 / bf16
     // rounds to nearest even
-    constexpr int OB = OUT == DT_F32 ? 4 : 2;
+    constexpr int OB = out_bytes<OUT>();
     const int row = m0 + l16, col = n0 + 4 * q;
     if constexpr (EPI) {
         // fused epilogue (one block per wave: no staging needed)

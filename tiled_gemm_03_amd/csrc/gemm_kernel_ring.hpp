@@ -530,7 +530,11 @@ void gemm_kernel_ring(GemmArgs p) {
     // 16 j + 4 (l/16) .. +3] of the wave's block; fp32 -> fp16 / bf16 rounds
     // to nearest even.
     if constexpr (EPI) {
-        // fused epilogue through the rings' LDS, once no wave reads it
+        // fused epilogue through the rings' LDS, once no wave reads it; the
+        // tile's bias in an LDS array of its own
+        __shared__ __attribute__((aligned(16))) float ebias_[T::BM + T::BN];
+        lds_float* const ebias = (lds_float*)(lds_void*)ebias_;
+        stage_bias<T::THREADS, T::BM, T::BN>(p, ebias, ebias + T::BN, m0, n0);
         __syncthreads();
         constexpr int REGION = P::LDS_BYTES / T::WAVES;  // bytes per wave
         constexpr int PB = REGION / 1024 < NMF ? REGION / 1024 : NMF;
@@ -551,7 +555,8 @@ void gemm_kernel_ring(GemmArgs p) {
         // LDS, away from the accumulators) and C rows need not be aligned
         // for 4-element stores (p.vec_c)
         fused_epilogue<OUT, NMF, 4, PB, false>(
-            p, region, [&](auto b_t) { constexpr int b = decltype(b_t)::value; return held[b]; },
+            p, region, ebias, ebias + T::BN, m0, n0,
+            [&](auto b_t) { constexpr int b = decltype(b_t)::value; return held[b]; },
             [&](int b, int, int& row, int& col, int& n, bool& vec) {
                 row = m0 + wm * T::WTM + 16 * (b / T::FN) + i16;
                 col = n0 + wn * T::WTN + 16 * (b % T::FN) + 4 * q;
@@ -560,7 +565,7 @@ void gemm_kernel_ring(GemmArgs p) {
             });
         return;
     }
-    constexpr int OB = OUT == DT_F32 ? 4 : 2;
+    constexpr int OB = out_bytes<OUT>();
     const int64_t ldc = p.ldc;
     // a tile on the bottom or right edge of C (M or N not a multiple of the
     // tile) stores only its groups inside C (N % 4 == 0: a group of four

@@ -6,6 +6,7 @@
 
 namespace tgemm {
 KernelFn ring_kernel_mid(int in, int out, int la, int lb, bool epi, bool kt) {
+    if (out == DT_FP8) return ring_kernel_mid_fp8(in, la, lb, kt);
     if (epi) return ring_kernel_mid_fused(in, out, la, lb, kt);
     if (kt) return ring_kernel_mid_kt(in, out, la, lb);
     return ring_pick<RingMid, false, false>(in, out, la, lb);

@@ -65,5 +65,13 @@ KernelFn ring_kernel_mid_kt(int in, int out, int la, int lb);
 KernelFn ring_kernel_big_fused_kt(int in, int out, int la, int lb);
 KernelFn ring_kernel_mid_fused_kt(int in, int out, int la, int lb);
 KernelFn direct_kernel_fused(int in, int out, int la, int lb, bool va, bool vb);
+// 8-bit float output (out == DT_FP8; always the fused epilogue's kernels):
+// k_ring_big_fp8(_kt).hip, k_ring_mid_fp8.hip, k_ring_small_fp8.hip,
+// k_direct_fp8.hip.  The selectors above forward to these.
+KernelFn ring_kernel_big_fp8(int in, int la, int lb);
+KernelFn ring_kernel_big_fp8_kt(int in, int la, int lb);
+KernelFn ring_kernel_mid_fp8(int in, int la, int lb, bool kt);
+KernelFn ring_kernel_small_fp8(int in, int la, int lb, bool kt);
+KernelFn direct_kernel_fp8(int in, int la, int lb, bool va, bool vb);
 
 }  // namespace tgemm

@@ -93,16 +93,22 @@ const Tuning& tuning() {
     return t;
 }
 
-int elem_bytes(int dt) { return dt == TGEMM_F32 ? 4 : 2; }
+bool is_fp8(int dt) { return dt == TGEMM_FP8_E4M3 || dt == TGEMM_FP8_E5M2; }
+
+int elem_bytes(int dt) { return dt == TGEMM_F32 ? 4 : is_fp8(dt) ? 1 : 2; }
 
 bool pair_supported(int in, int out) {
     switch (in) {
         case TGEMM_F32: return out == TGEMM_F32;
-        case TGEMM_F16: return out == TGEMM_F16 || out == TGEMM_F32;
-        case TGEMM_BF16: return out == TGEMM_BF16 || out == TGEMM_F32;
+        case TGEMM_F16: return out == TGEMM_F16 || out == TGEMM_F32 || is_fp8(out);
+        case TGEMM_BF16: return out == TGEMM_BF16 || out == TGEMM_F32 || is_fp8(out);
         default: return false;
     }
 }
+
+// The kernels' output type: an 8-bit format is one kernel type (DT_FP8), its
+// format a kernel argument.
+int kernel_out(int out) { return is_fp8(out) ? DT_FP8 : out; }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -316,7 +322,7 @@ int plan_direct(const Problem& p, Plan& plan) {
     const bool va = half && kca && (uintptr_t)p.A % 16 == 0 && p.lda % 8 == 0 && p.K % 8 == 0;
     const bool vb = half && kcb && (uintptr_t)p.B % 16 == 0 && p.ldb % 8 == 0 && p.K % 8 == 0;
     plan.kind = TGEMM_KERNEL_DIRECT;
-    plan.fn = direct_kernel(p.in, p.out, p.la, p.lb, va, vb, p.ep.on);
+    plan.fn = direct_kernel(p.in, kernel_out(p.out), p.la, p.lb, va, vb, p.ep.on || is_fp8(p.out));
     if (plan.fn == nullptr) return TGEMM_ERR_DTYPE;
     if (ceil_div(p.M, 32) * ceil_div(p.N, 32) > 0x7fffffff) return TGEMM_ERR_DIM;
     return TGEMM_OK;
@@ -348,17 +354,21 @@ int make_plan(const Problem& p, int config_id, Plan& plan) {
     const ConfigEntry& c = kConfigs[plan.config];
     if (!c.direct && ring_applies(c, p)) {
         plan.kind = TGEMM_KERNEL_RING;
-        plan.fn = c.ring(p.in, p.out, p.la, p.lb, p.ep.on || !ring_plain_stores(p), p.K % c.ring_k_mult != 0);
+        // 8-bit outputs are written by the fused epilogue's kernels
+        plan.fn = c.ring(p.in, kernel_out(p.out), p.la, p.lb, p.ep.on || is_fp8(p.out) || !ring_plain_stores(p),
+                         p.K % c.ring_k_mult != 0);
         if (plan.fn == nullptr) return TGEMM_ERR_DTYPE;
         return ceil_div(p.M, c.bm) * ceil_div(p.N, c.bn) > 0x7fffffff ? TGEMM_ERR_DIM : TGEMM_OK;
     }
-    if (c.direct || !row_row(p)) {
-        // column-major operands outside the ring kernel's cases run direct
+    if (c.direct || !row_row(p) || is_fp8(p.out)) {
+        // column-major operands outside the ring kernel's cases run direct,
+        // and so do 8-bit outputs (the register-staged kernels write 16- and
+        // 32-bit outputs only)
         if (direct_fits(p)) {
             if (!c.direct) plan.config = p.in == TGEMM_F32 ? CFG_F32_DIRECT : CFG_DIRECT;
             return plan_direct(p, plan);
         }
-        if (!row_row(p)) return TGEMM_ERR_DIM;  // offsets beyond 31 bits: no kernel
+        if (!row_row(p) || is_fp8(p.out)) return TGEMM_ERR_DIM;  // offsets beyond 31 bits: no kernel
         plan.config = p.in == TGEMM_F32 ? CFG_F32_TINY : CFG_TINY;  // the checked kernel instead
     }
     const ConfigEntry& t = kConfigs[plan.config];
@@ -426,6 +436,7 @@ int run(const Problem& p, void* stream, int config_id) {
     args.bias_kind = p.ep.on ? p.ep.bias_kind : TGEMM_BIAS_NONE;
     args.bias_dt = p.ep.bias_dt;
     args.act = p.ep.act;
+    args.fp8_e5m2 = p.out == TGEMM_FP8_E5M2 ? 1 : 0;
     const int64_t grid = (int64_t)args.tiles_m * args.tiles_n;
 
     void* kargs[] = {&args};
