@@ -156,15 +156,22 @@ struct RingOperand {
     }
 };
 
+constexpr int ring_gcd(int a, int b) { return b == 0 ? a : ring_gcd(b, a % b); }
+constexpr int ring_lcm(int a, int b) { return a / ring_gcd(a, b) * b; }
+
 // Tile configuration of the ring kernel: BM x BN output tile, WM x WN waves,
 // OCC workgroups per CU the registers and LDS are sized for; steps of BK = 32.
-template <int BM_, int BN_, int WM_, int WN_, int OCC_>
+// BNS: stages of B's ring (one step each); ANS: stages of a k-contiguous A's
+// ring (two steps each; a k-strided A takes 2 ANS stages of one step).
+template <int BM_, int BN_, int WM_, int WN_, int OCC_, int BNS_ = 4, int ANS_ = 2>
 struct RingCfg {
     static constexpr int BM = BM_, BN = BN_, BK = 32, WM = WM_, WN = WN_, OCC = OCC_;
+    static_assert(BNS_ >= 2 && ANS_ >= 2, "a stage is refilled while the other stages are read");
     static constexpr int THREADS = 64 * WM * WN, WAVES = WM * WN;
     static constexpr int WTM = BM / WM, WTN = BN / WN;
     static constexpr int FM = WTM / 16, FN = WTN / 16;
-    static constexpr int K_MULT = 4 * BK;          // the rings walk K in multiples of this
+    // the rings walk K in multiples of this (one loop trip)
+    static constexpr int K_MULT = ring_lcm(ring_lcm(2 * ANS_, BNS_), 4) * BK;
     // Ring of each operand for the layouts of A and B.  A k-contiguous
     // operand reads 64 bytes of every row per step, half a 128-byte line, and
     // such loads run at about 60% of the rate of whole lines: a k-contiguous
@@ -175,13 +182,13 @@ struct RingCfg {
     template <bool KCA, bool KCB>
     struct Plan {
         static constexpr bool DA = KCA;
-        using OA = RingOperand<BM, KCA, DA ? 2 : 1, DA ? 2 : 4>;
-        using OB = RingOperand<BN, KCB, 1, 4>;
+        using OA = RingOperand<BM, KCA, DA ? 2 : 1, DA ? ANS_ : 2 * ANS_>;
+        using OB = RingOperand<BN, KCB, 1, BNS_>;
         static constexpr int LA = OA::BLOCKS / WAVES, LB = OB::BLOCKS / WAVES;  // loads per wave and stage
         static constexpr int LDS_BYTES = OA::RING + OB::RING;
         // steps per loop trip: both rings and the two fragment buffers return
         // to their first state
-        static constexpr int U = 4;
+        static constexpr int U = ring_lcm(ring_lcm(OA::D * OA::NS, OB::D * OB::NS), 4);
         static constexpr int loads_at(int v) { return (OA::issues_at(v) ? LA : 0) + (OB::issues_at(v) ? LB : 0); }
         // loads issued after those that step j's stages need, counted at the
         // start of step `now` (the wait before step j's fragments are read)
@@ -205,7 +212,7 @@ struct RingCfg {
     // key: tiles narrower than 128 rows take row-major A only
     static constexpr bool A_COL_OK = BM >= 128;
     // how far past K the ring loads (steps of 32)
-    static constexpr int LOOKAHEAD = 4;
+    static constexpr int LOOKAHEAD = 2 * ANS_ > BNS_ ? 2 * ANS_ : BNS_;
     // the rings of row-major A and B (the default layouts)
     static constexpr int A_BK = 32 * Plan<true, false>::OA::D, A_STAGES = Plan<true, false>::OA::NS;
     static constexpr int B_BK = 32, B_STAGES = Plan<true, false>::OB::NS;
