@@ -336,12 +336,20 @@ __device__ __forceinline__ float load_value(const char* p, int64_t i, int dt, in
 __device__ __forceinline__ float logistic_times(float x, float z) {  // x / (1 + exp(-z))
     return x * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
 }
+template <int ACT>
+__device__ __forceinline__ float activate_t(float x) {
+    if constexpr (ACT == ACT_RELU) return x > 0.f ? x : 0.f;
+    else if constexpr (ACT == ACT_GELU) return 0.5f * x * (1.f + erff(x * 0.70710678118654752f));
+    else if constexpr (ACT == ACT_GELU_TANH) return logistic_times(x, 1.5957691216057308f * (x + 0.044715f * x * x * x));
+    else if constexpr (ACT == ACT_SILU) return logistic_times(x, x);
+    else return x;
+}
 __device__ __forceinline__ float activate(float x, int act) {
     switch (act) {
-        case ACT_RELU: return x > 0.f ? x : 0.f;
-        case ACT_GELU: return 0.5f * x * (1.f + erff(x * 0.70710678118654752f));
-        case ACT_GELU_TANH: return logistic_times(x, 1.5957691216057308f * (x + 0.044715f * x * x * x));
-        case ACT_SILU: return logistic_times(x, x);
+        case ACT_RELU: return activate_t<ACT_RELU>(x);
+        case ACT_GELU: return activate_t<ACT_GELU>(x);
+        case ACT_GELU_TANH: return activate_t<ACT_GELU_TANH>(x);
+        case ACT_SILU: return activate_t<ACT_SILU>(x);
         default: return x;
     }
 }
@@ -441,9 +449,10 @@ __device__ __forceinline__ void store4_fused(const GemmArgs& p, int row, int col
 //     are taken EB at a time: the old C of all EB is loaded together (one
 //     wait), then each group's alpha * acc + beta * C + bias (the bias from
 //     LDS) is written back in place;
-//  3. one loop over the groups applies alpha (when step 2 did not run), the
-//     activation and the output rounding, and stores; a partial group (n <
-//     4) is formed there element by element.
+//  3. one loop over the whole groups, compiled once per activation and
+//     chosen by one uniform switch, applies alpha (when step 2 did not run),
+//     the activation and the output rounding, and stores; then the partial
+//     groups (n < 4) are formed and stored element by element.
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 typedef __attribute__((address_space(3))) float lds_float;
@@ -567,19 +576,38 @@ __device__ __forceinline__ void fused_epilogue(const GemmArgs& p, lds_f32x4* reg
                 });
             }
         }
-        // 3: activation, output rounding and stores
-        for (int i = 0; i < NG; ++i) {
-            int row, col, n;
-            bool vec;
-            at(i, row, col, n, vec);
-            if (n <= 0) continue;
-            f32x4 t = region[i * 64 + lane];
-            if (WHOLE || n == 4) {
-                if (!combine) t *= p.alpha;
-            } else {
-                t = fused_pre<OUT>(p, row, col, n, t);
+        // 3: activation, output rounding and stores of the whole groups, in
+        // a loop compiled for the call's activation (one uniform switch),
+        // then the partial groups (N % 4 != 0: element by element, rare)
+        const bool scale = !combine && p.alpha != 1.f;
+        auto whole = [&](auto act_t) __attribute__((always_inline)) {
+            constexpr int ACT = decltype(act_t)::value;
+            for (int i = 0; i < NG; ++i) {
+                int row, col, n;
+                bool vec;
+                at(i, row, col, n, vec);
+                if (WHOLE ? n <= 0 : n != 4) continue;
+                f32x4 t = region[i * 64 + lane];
+                if (scale) t *= p.alpha;
+                store4<OUT>(p.C + ((int64_t)row * p.ldc + col) * OB, activate_t<ACT>(t[0]), activate_t<ACT>(t[1]),
+                            activate_t<ACT>(t[2]), activate_t<ACT>(t[3]), vec, p.fp8_e5m2);
             }
-            fused_post<OUT>(p, row, col, WHOLE ? 4 : n, vec, t);
+        };
+        switch (p.act) {
+            case ACT_RELU: whole(IntTag<ACT_RELU>{}); break;
+            case ACT_GELU: whole(IntTag<ACT_GELU>{}); break;
+            case ACT_GELU_TANH: whole(IntTag<ACT_GELU_TANH>{}); break;
+            case ACT_SILU: whole(IntTag<ACT_SILU>{}); break;
+            default: whole(IntTag<ACT_NONE>{}); break;
+        }
+        if constexpr (!WHOLE) {
+            for (int i = 0; i < NG; ++i) {
+                int row, col, n;
+                bool vec;
+                at(i, row, col, n, vec);
+                if (n <= 0 || n == 4) continue;
+                fused_post<OUT>(p, row, col, n, vec, fused_pre<OUT>(p, row, col, n, region[i * 64 + lane]));
+            }
         }
     });
 }
