@@ -178,8 +178,9 @@ def _kernel(M, N, K, lda=None, ldb=None, ldc=None, in_dt=T.F16, out_dt=T.F16, ci
 
 def test_kernel_choice_ring_path():
     """The direct-to-LDS ring kernel runs exactly for 16-bit inputs with K a
-    multiple of 128 or above 128 (the K-tail variant) and 16-byte aligned
-    operands, whatever M, N and the alignment of C (edge tiles store masked;
+    multiple of 128 or above 128 (the K-tail variant) and operands whose
+    every element its range-checked loads keep, whatever M, N and the
+    alignment of C (edge tiles store masked;
     partial column groups and unaligned C rows through the fused epilogue's
     stores); anything else falls back to a register-staged kernel of the same
     tile."""
@@ -197,13 +198,13 @@ def test_kernel_choice_ring_path():
     assert _kernel(8192 - 256, 8192, 8192) == R          # still whole tiles
     assert _kernel(8191, 8192, 8192) == R                # ragged M: masked edge tiles
     assert _kernel(8191, 8000, 8192) == R                # ragged M and N
-    assert _kernel(8192, 8190, 8192) == GE               # B rows not whole 16-byte chunks
+    assert _kernel(8192, 8190, 8192) == R                # B rows not whole 16-byte chunks
     assert _kernel(8192, 8192, 8192, ldc=8194) == R      # C rows not 4-element aligned
     assert _kernel(8192, 8192, 8192, offs=(0, 0, 1)) == R  # C base not 4-element aligned
     assert _kernel(8192, 8190, 8192, ldb=8192, ldc=8192) == R   # N % 4 != 0: partial column groups
-    assert _kernel(8192, 8192, 8192, lda=8196) == GE     # rows not whole 16-byte chunks
+    assert _kernel(8192, 8192, 8192, lda=8196) == R      # rows not whole 16-byte chunks
     assert _kernel(8192, 8192, 8192, lda=8192 + 8) == R  # padded, still aligned
-    assert _kernel(8192, 8192, 8192, offs=(1, 0, 0)) == GE
+    assert _kernel(8192, 8192, 8192, offs=(1, 0, 0)) == R
     assert _kernel(8192, 8192, 8192, cid=2) == TI        # configuration without a ring kernel
     assert _kernel(1024, 1024, 1024, in_dt=T.F32, out_dt=T.F32) != R
     # B offsets beyond 2^31 bytes: register-staged kernel
@@ -240,8 +241,8 @@ def test_fp8_outputs_are_checked_and_routed():
             assert _kernel_t(1000, 1000, 1000, C_, C_, C_, in_dt=in_dt, out_dt=fmt)[0] == RING
             assert _kernel(127, 255, 512, ldb=255, ldc=255, in_dt=in_dt, out_dt=fmt) == DIRECT
             # unaligned rows: the table's register-staged tile is replaced by the direct kernel
-            assert _kernel(1024, 1024, 301, lda=302, ldb=1027, in_dt=in_dt, out_dt=T.F32) == T.KERNEL_GENERAL
-            assert _kernel_t(1024, 1024, 301, R_, R_, R_, lda=302, ldb=1027, in_dt=in_dt, out_dt=fmt) == (DIRECT, 6)
+            assert _kernel(1024, 1024, 301, lda=301, ldb=1027, in_dt=in_dt, out_dt=T.F32) == T.KERNEL_GENERAL
+            assert _kernel_t(1024, 1024, 301, R_, R_, R_, lda=301, ldb=1027, in_dt=in_dt, out_dt=fmt) == (DIRECT, 6)
             assert _kernel(256, 256, 64, cid=2, in_dt=in_dt, out_dt=fmt) == DIRECT
         assert _kernel(64, 64, 64, in_dt=T.F32, out_dt=fmt) == T.ERR_DTYPE
         assert _kernel(64, 64, 64, in_dt=fmt, out_dt=fmt) == T.ERR_DTYPE
@@ -261,7 +262,9 @@ def test_ring_only_configuration_falls_back_to_128x128():
     assert _kernel_t(1024, 2048, 512, R_, R_, R_, cid=8) == (RING, 8)
     assert _kernel_t(1024, 2048, 512, R_, C_, R_, cid=8) == (RING, 8)      # column-major B: k-contiguous
     assert _kernel_t(1024, 2048, 512, C_, R_, R_, cid=8) == (RING, 1)      # column-major A
-    assert _kernel_t(1024, 2048, 512, R_, R_, R_, lda=516, cid=8)[1] == 1  # A rows not whole chunks
+    assert _kernel_t(1024, 2048, 512, R_, R_, R_, lda=516, cid=8) == (RING, 8)  # A rows not whole chunks
+    # A's last element dropped by the ring's range check (odd K at 2 mod 4)
+    assert _kernel_t(1024, 2048, 513, R_, R_, R_, lda=513, cid=8)[1] == 1
     assert _kernel_t(1024, 2048, 64, R_, R_, R_, cid=8) == (T.KERNEL_TILED, 1)  # K below the ring's multiple
     assert _kernel_t(1000, 2000, 1000, R_, R_, R_, cid=8) == (RING, 8)     # ragged, K tail
     assert _kernel_t(4, 4, 4, R_, R_, R_, in_dt=T.F32, out_dt=T.F32, cid=8)[0] == T.ERR_CONFIG
@@ -276,6 +279,51 @@ def _kernel_t(M, N, K, la, lb, lc, lda=None, ldb=None, ldc=None, in_dt=T.F16, ou
     ldc = (N if lc == R_ else M) if ldc is None else ldc
     return T.gemm_select_kernel_t(M, N, K, FAKE, lda, la, FAKE + (1 << 36), ldb, lb, FAKE + (2 << 36), ldc, lc,
                                   in_dt, out_dt, cid)
+
+
+def _keeps_last(base, ld, kcontig, outer, K):
+    """The range-check rule the ring's loads are held to, restated: the
+    operand's last element is lost only if it starts a 4-byte part of its
+    16-byte load (an odd number of elements from the row's first loaded one:
+    K along a k-contiguous row, M or N along a k-strided one) at an address of
+    2 mod 4."""
+    rows, cols = (outer, K) if kcontig else (K, outer)
+    last = base + 2 * ((rows - 1) * ld + cols - 1)
+    return not (cols % 2 == 1 and last % 4 == 2)
+
+
+def test_ring_takes_unaligned_rows_where_every_element_is_kept():
+    """Operands off 16-byte alignment or with rows not whole 16-byte chunks
+    run the ring kernel exactly when its loads keep every element of both
+    operands; odd byte addresses never do.  Every layout pair, odd and even
+    sizes, element offsets 0..7 and leading dimensions with every residue
+    mod 8."""
+    RING = T.KERNEL_RING
+    A0, B0, C0 = FAKE, FAKE + (1 << 36), FAKE + (2 << 36)
+    n_ring = n_other = 0
+    for la in (R_, C_):
+        for lb in (R_, C_):
+            for M, N, K in ((1024, 1024, 1024), (1023, 1021, 1025), (1024, 1023, 1023), (1021, 1024, 1026)):
+                for oa, ob, pa, pb in ((0, 0, 0, 0), (1, 0, 0, 0), (0, 1, 0, 0), (3, 5, 1, 2), (2, 7, 3, 5),
+                                       (1, 1, 1, 1), (0, 0, 7, 6), (6, 2, 4, 0)):
+                    lda = (K if la == R_ else M) + pa
+                    ldb = (N if lb == R_ else K) + pb
+                    A, B = A0 + 2 * oa, B0 + 2 * ob
+                    got = T.gemm_select_kernel_t(M, N, K, A, lda, la, B, ldb, lb, C0, N, R_, T.F16, T.F16, 1)
+                    aligned = A % 16 == 0 and B % 16 == 0 and lda % 8 == 0 and ldb % 8 == 0
+                    keeps = _keeps_last(A, lda, la == R_, M, K) and _keeps_last(B, ldb, lb == C_, N, K)
+                    want_ring = aligned or keeps
+                    assert (got[0] == RING) == want_ring, (la, lb, M, N, K, oa, ob, pa, pb, got)
+                    n_ring += want_ring
+                    n_other += not want_ring
+                    # an odd byte address: never the ring
+                    got = T.gemm_select_kernel_t(M, N, K, A + 1, lda, la, B, ldb, lb, C0, N, R_, T.F16, T.F16, 1)
+                    assert got[0] != RING
+    assert n_ring > 0 and n_other > 0
+    # the square odd sizes: every element kept with contiguous rows
+    for n in (8191, 4095, 2047):
+        assert _kernel(n, n, n) == RING
+        assert _kernel(n, n, n, offs=(1, 0, 0)) != RING
 
 
 def test_layout_arguments_are_checked():
@@ -319,8 +367,11 @@ def test_kernel_choice_for_layouts():
     # register-staged kernel
     assert _kernel_t(256, 256, 256, C_, R_, R_, cid=2)[0] == T.ERR_CONFIG
     assert _kernel_t(256, 256, 256, R_, R_, R_, cid=2)[0] == T.KERNEL_TILED
-    # forced ring configuration on a ragged shape: the direct kernel runs
-    assert _kernel_t(250, 256, 256, C_, C_, R_, cid=0) == (DIRECT, 6)
+    # forced ring configuration on a ragged shape: the ring (column-major A
+    # rows of 250 elements), or the direct kernel where the ring's range
+    # check would drop A's last element (rows of 249 at 2 mod 4)
+    assert _kernel_t(250, 256, 256, C_, C_, R_, cid=0) == (RING, 0)
+    assert _kernel_t(249, 256, 256, C_, C_, R_, cid=0) == (DIRECT, 6)
     # a column-major C swaps the roles of A and B: its 128 rows become the
     # N of the row-major product (128 x 128 tiles)
     assert _kernel_t(128, 8192, 8192, R_, R_, C_)[0] == RING

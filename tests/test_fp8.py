@@ -148,24 +148,26 @@ def test_fp8_plain_product_and_partial_groups():
 
 
 def test_fp8_unaligned_operands_take_the_direct_kernel():
-    """Operand rows that are not whole 16-byte chunks would take a
-    register-staged kernel, which writes no 8-bit output: the direct kernel
-    runs instead."""
+    """Operands the ring cannot read whole (rows of an odd K, contiguous, the
+    last element of A at an address of 2 mod 4) would take a register-staged
+    kernel, which writes no 8-bit output: the direct kernel runs instead.
+    With one padding element per row of A the ring reads them and runs."""
     M, N, K = 1024, 1024, 301   # the table's choice: the 64 x 64 register-staged tile
     a, b = W.integer_inputs(M, N, K, W.F16, seed=3)
-    assert T.gemm_select_kernel_t(M, N, K, 1 << 40, K + 1, ROW, 1 << 41, N + 3, ROW, 1 << 42, N, ROW, W.F16,
+    assert T.gemm_select_kernel_t(M, N, K, 1 << 40, K, ROW, 1 << 41, N + 3, ROW, 1 << 42, N, ROW, W.F16,
                                   W.F16, -1)[0] == T.KERNEL_GENERAL
-    ad = G.to_device(a, W.F16, pad_cols=1)           # lda = 302
-    bd = G.to_device(b, W.F16, pad_cols=3)           # ldb = 263
-    cd = fp8_tensor(np.full((M, N), 0x7F, np.uint8), T.FP8_E4M3)
-    kind = T.gemm_select_kernel_t(M, N, K, ad.data_ptr(), K + 1, ROW, bd.data_ptr(), N + 3, ROW, cd.data_ptr(), N,
-                                  ROW, W.F16, T.FP8_E4M3, -1)[0]
-    G.say(f"[case] fp8 unaligned operands -> {KIND.get(kind, kind)}")
-    assert kind == T.KERNEL_DIRECT
-    T.gemm_tensors(ad, bd, cd, alpha=0.25)
-    torch.cuda.synchronize()
     o = oracle.gemm_fused(a, b, W.F16, alpha=0.25, nthreads=G.NTHREADS)
-    assert np.array_equal(fp8_bits(cd), oracle.encode_fp8(o, T.FP8_E4M3))
+    for pad_a, want_kind in ((0, T.KERNEL_DIRECT), (1, T.KERNEL_RING)):
+        ad = G.to_device(a, W.F16, pad_cols=pad_a)       # lda = 301 / 302
+        bd = G.to_device(b, W.F16, pad_cols=3)           # ldb = 1027
+        cd = fp8_tensor(np.full((M, N), 0x7F, np.uint8), T.FP8_E4M3)
+        kind = T.gemm_select_kernel_t(M, N, K, ad.data_ptr(), K + pad_a, ROW, bd.data_ptr(), N + 3, ROW,
+                                      cd.data_ptr(), N, ROW, W.F16, T.FP8_E4M3, -1)[0]
+        G.say(f"[case] fp8 unaligned operands lda={K + pad_a} -> {KIND.get(kind, kind)}")
+        assert kind == want_kind
+        T.gemm_tensors(ad, bd, cd, alpha=0.25)
+        torch.cuda.synchronize()
+        assert np.array_equal(fp8_bits(cd), oracle.encode_fp8(o, T.FP8_E4M3))
 
 
 def test_fp8_guard_band_and_k_zero():

@@ -166,14 +166,15 @@ def test_layouts_fp32_inputs(lay):
 
 @pytest.mark.parametrize("lay", [l for l in LAYOUTS if not effective_row_row(l)], ids=lid)
 def test_layouts_padded_and_misaligned(lay):
-    """Padded leading dimensions that keep 16-byte alignment stay on the
-    ring kernel; odd padding or a base one element off alignment moves the
-    call to the direct kernel; both must be exact (integer inputs)."""
+    """Padded leading dimensions and operand bases off 16-byte alignment stay
+    on the ring kernel (even sizes: its loads keep every element); a C whose
+    rows are not 4-element aligned moves this small product to the direct
+    kernel; both must be exact (integer inputs)."""
     M, N, K = 256, 512, 384
     a, b = W.integer_inputs(M, N, K, W.F16, seed=77)
-    for pads, offs, ring in (((8, 16, 8), (0, 0, 0), True), ((3, 5, 1), (0, 0, 0), False),
-                             ((0, 0, 0), (1, 0, 0), False), ((0, 0, 0), (0, 1, 0), False),
-                             ((0, 0, 0), (0, 0, 1), False)):
+    for pads, offs, ring in (((8, 16, 8), (0, 0, 0), True), ((3, 5, 0), (0, 0, 0), True),
+                             ((3, 5, 1), (0, 0, 0), False), ((0, 0, 0), (1, 0, 0), True),
+                             ((0, 0, 0), (0, 1, 0), True), ((0, 0, 0), (0, 0, 1), False)):
         for out_dt in (W.F16, W.F32):
             c, o, kind = run_layout(a, b, W.F16, out_dt, lay, pads=pads, offs=offs, label="layout pad/offset")
             assert (kind == T.KERNEL_RING) == ring

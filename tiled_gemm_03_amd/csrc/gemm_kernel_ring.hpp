@@ -220,8 +220,9 @@ struct RingCfg {
 };
 
 // Preconditions (checked by the host): 16-bit inputs; K % K_MULT == 0, or
-// K > K_MULT with KT; A and B 16-byte aligned with lda and ldb multiples of
-// 8; without EPI, N % 4 == 0 and C aligned for 4-element stores with
+// K > K_MULT with KT; A and B element-aligned, and where their rows are not
+// whole 16-byte chunks (16-byte aligned, ld a multiple of 8), no operand whose
+// last element starts a 4-byte part of its load at an address of 2 mod 4; without EPI, N % 4 == 0 and C aligned for 4-element stores with
 // ldc % 4 == 0 (the fused epilogue, EPI, takes any N and C alignment; a plain
 // product that needs it runs EPI with alpha 1, beta 0, no bias and no
 // activation, which store the product unchanged); the buffer offsets (a tile's rows or
@@ -262,14 +263,20 @@ void gemm_kernel_ring(GemmArgs p) {
     const int swz = p.swz_mask != 0 ? 1 : 0;
 
     // ---------------------------------------------------------- a2: loads
-    // The range is rounded up to whole dwords: the range check zeroes a dword
-    // that straddles the end, which would drop the operand's last element
-    // when a k-strided tile row ends at an odd M or N.  The element after it
-    // is row padding (ld is a multiple of 8, so an odd row length leaves at
-    // least one), and it only reaches outputs past M or N, never stored.
+    // The range check keeps a 4-byte part of a load only if the part ends
+    // inside the range, counted from the load's own offset (measured on
+    // gfx950, 16-byte loads at every even offset).  A part that holds the
+    // operand's last element and the 2 bytes after it would be dropped with
+    // the element, so the range's end is rounded up to a dword boundary of
+    // the address space: it then never reaches past the aligned dword that
+    // holds the last element (no other page), and the bytes it adds reach
+    // only outputs past M or N, never stored.  With rows of whole 16-byte
+    // chunks this keeps every element; with other rows the host takes the
+    // ring only when it does (an element that starts a part at an address of
+    // 2 mod 4 would still be dropped).
     auto make_rsrc = [&](const char* base, int64_t bytes) __attribute__((always_inline)) {
         const uint64_t a = (uint64_t)base;
-        bytes = (bytes + 3) & ~(int64_t)3;
+        if (bytes > 0) bytes = (int64_t)(((a + (uint64_t)bytes + 3) & ~(uint64_t)3) - a);
         const uint32_t n = bytes <= 0 ? 0u : bytes > 0xffffffffLL ? 0xffffffffu : (uint32_t)bytes;
         return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
                      __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)),
@@ -497,7 +504,8 @@ void gemm_kernel_ring(GemmArgs p) {
         // the K tail: steps of 32 from k = 32 nk, fragments from global
         // memory through buffer loads over the same ranges as the rings'
         auto tail_rsrc = [&](const char* base, int64_t bytes) __attribute__((always_inline)) {
-            bytes = (bytes + 3) & ~(int64_t)3;
+            const uint64_t a = (uint64_t)base;
+            if (bytes > 0) bytes = (int64_t)(((a + (uint64_t)bytes + 3) & ~(uint64_t)3) - a);
             const int n = bytes <= 0 ? 0 : bytes > 0x7fffffffLL ? 0x7fffffff : (int)bytes;
             return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, n, 0x00020000);
         };

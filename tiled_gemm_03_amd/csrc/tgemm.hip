@@ -214,15 +214,37 @@ int64_t operand_reach(bool kcontig, int64_t ext, int64_t ld, int64_t K, int64_t 
     return (kcontig ? ext * ld + K + extra : (K + extra) * ld + ext) * eb;
 }
 
+// Whether the ring kernel reads every element of a 16-bit operand stored
+// with rows of `outer` elements (k contiguous: the row is K long) at leading
+// dimension ld from base X.  Its 16-byte loads (any even address) keep a
+// 4-byte part only when the part ends inside the buffer range, which ends at
+// the dword boundary after the operand's last element: the last element is
+// dropped if it starts a part (the row's element count from the tile's first
+// one is odd: K for a k-contiguous operand, M or N for a k-strided one) at an
+// address of 2 mod 4.  Rows of whole 16-byte chunks never do.
+bool ring_reads_all(const void* X, int64_t ld, bool kcontig, int64_t outer, int64_t K) {
+    const int64_t rows = kcontig ? outer : K, cols = kcontig ? K : outer;
+    if (rows <= 0 || cols <= 0) return true;
+    const uintptr_t last = (uintptr_t)X + (uintptr_t)((rows - 1) * ld + cols - 1) * 2;
+    const bool starts_part = (cols % 2) == 1;
+    return !(starts_part && last % 4 == 2);
+}
+
 // Whether a configuration with a ring kernel runs it.
 bool ring_applies(const ConfigEntry& c, const Problem& p) {
     if (c.ring == nullptr || !tuning().direct_lds) return false;
     if (p.la == LAYOUT_COL && !c.ring_a_col) return false;
     // the ring loads ring_lookahead steps past K
     const int64_t extra = (int64_t)c.ring_lookahead * c.ring_bk;
+    // 16-bit elements at even addresses; rows of whole 16-byte chunks, or
+    // ranges that keep every element (ring_reads_all)
+    const bool loads_ok = (uintptr_t)p.A % 2 == 0 && (uintptr_t)p.B % 2 == 0 &&
+                          (loads_aligned(c, p) ||
+                           (ring_reads_all(p.A, p.lda, p.la == LAYOUT_ROW, p.M, p.K) &&
+                            ring_reads_all(p.B, p.ldb, p.lb == LAYOUT_COL, p.N, p.K)));
     // K a multiple of ring_k_mult, or above it (the K-tail variant); any N
     // and C alignment (ring_plain_stores)
-    return loads_aligned(c, p) && (p.K % c.ring_k_mult == 0 || p.K > c.ring_k_mult) &&
+    return loads_ok && (p.K % c.ring_k_mult == 0 || p.K > c.ring_k_mult) &&
            operand_reach(p.la == LAYOUT_ROW, c.bm, p.lda, p.K, extra, c.eb) < (1LL << 31) &&
            operand_reach(p.lb == LAYOUT_COL, c.bn, p.ldb, p.K, extra, c.eb) < (1LL << 31);
 }
