@@ -200,12 +200,13 @@ void attention_kernel(AttnArgs p) {
     };
     // issued through inline asm: the compiler then adds no waits for these
     // loads before LDS reads; the kernel waits for them itself (vmcnt) before
-    // the barrier that publishes a buffer
+    // the barrier that publishes a buffer.  The block writes M0 (the LDS
+    // destination) and declares it clobbered.
     auto dma = [&](int lds_addr, int vo, i32x4 rs) __attribute__((always_inline)) {
         asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                      :
                      : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(vo), "s"(rs), "s"(0)
-                     : "memory");
+                     : "memory", "m0");
     };
     // The i-th key block a wave walks: block i, or (SPLIT) wave + NW i.  LDS:
     // K of walk positions i, i + 1 at (i % 2) K_BYTES, V at 2 K_BYTES +

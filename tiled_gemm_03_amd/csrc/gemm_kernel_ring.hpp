@@ -319,15 +319,17 @@ void gemm_kernel_ring(GemmArgs p) {
     // K advance per stage: 32 D elements along a row (KC) or 32 rows (KS)
     const int a_kstep = OA::KC ? 64 * OA::D : (int)(32 * lda * 2);
     const int b_kstep = OB_::KC ? 64 * OB_::D : (int)(32 * ldb * 2);
-    // Issued through inline asm (M0 = LDS destination, then the load): the
-    // compiler then does not guard later LDS reads with waits for these
-    // loads; the kernel waits for them itself (vmcnt) before the barrier that
-    // publishes a stage.
+    // Issued through inline asm: the compiler then does not guard later LDS
+    // reads with waits for these loads; the kernel waits for them itself
+    // (vmcnt) before the barrier that publishes a stage.  The block writes M0
+    // (the LDS destination) and declares it clobbered, so the compiler keeps
+    // nothing of its own in M0 across it.  (An "{m0}" input operand instead
+    // made the compiler move accumulators in the 256 x 256 main loop.)
     auto dma = [&](int lds_addr, int vo, i32x4 rs, int so) __attribute__((always_inline)) {
         asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                      :
                      : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(vo), "s"(rs), "s"(so)
-                     : "memory");
+                     : "memory", "m0");
     };
     // the loads of one operand's stage st at K byte offset k
     auto load_a = [&](int st, int x, int k) __attribute__((always_inline)) {
