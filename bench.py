@@ -333,8 +333,9 @@ def main():
     ap.add_argument("--no-attention", action="store_true")
     ap.add_argument("--no-clock", action="store_true", help="do not start the clock sampler")
     ap.add_argument("--settle-ms", type=float, default=250.0,
-                    help="run the product for this long before the warmup steps, so that the timed steps see the "
-                         "clock of sustained use rather than the power controller's response to leaving idle")
+                    help="run the product for this long before the warmup steps (and each attention workload "
+                         "before its timed calls), so that the timed calls see the clock of sustained use rather "
+                         "than the power controller's response to a change of load")
     ap.add_argument("--hold-ms", type=float, default=3000.0,
                     help="after the timed steps, keep running the product this long while the clock sampler reads "
                          "the metrics table (which the firmware refreshes about once per second)")
@@ -584,6 +585,14 @@ def main():
             call = lambda: T.attention_tensors(q_, k_, v_, o_, scale=aw.scale, causal=aw.causal,
                                                stream=stream.cuda_stream)
             reps = 200 if aw.N <= 1024 else 20
+            # settle on this kernel's own sustained clock (the product before
+            # it leaves the power controller at the product's clock), as the
+            # product itself settles before its steps
+            ts0 = time.perf_counter()
+            while (time.perf_counter() - ts0) * 1e3 < args.settle_ms:
+                for _ in range(5):
+                    call()
+                torch.cuda.synchronize()
             aev = time_calls(call, reps, max(3, reps // 10), stream)["events_ms"]
             med = float(np.median(aev))
             af = aw.flops()

@@ -122,6 +122,7 @@ void attention_kernel(AttnArgs p) {
     constexpr int K_BYTES = BKV * D * 2, V_BYTES = BKV * D * 2, BUF = K_BYTES + V_BYTES;
     static_assert((SPLIT ? NW : 1) * 2 * BUF == attn_lds_bytes<D, NW, SPLIT>(), "");
     constexpr float TH = 8.f;               // reference-point slack (log2 units)
+    constexpr bool PRIO_S = D == 64;        // raised wave priority from the S phase (else from PV)
     // dynamic LDS of attn_lds_bytes<D, NW, SPLIT>() bytes (declared at launch: a
     // static array this size would make the compiler budget registers for
     // the one wave per SIMD that it leaves room for, and move the
@@ -201,12 +202,15 @@ void attention_kernel(AttnArgs p) {
     // issued through inline asm: the compiler then adds no waits for these
     // loads before LDS reads; the kernel waits for them itself (vmcnt) before
     // the barrier that publishes a buffer.  The block writes M0 (the LDS
-    // destination) and declares it clobbered.
+    // destination) and names M0 as its output operand (the compiler keeps
+    // nothing of its own in M0 across it).
     auto dma = [&](int lds_addr, int vo, i32x4 rs) __attribute__((always_inline)) {
-        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                     :
+        int m0_written;
+        asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, %4 offen lds"
+                     : "={m0}"(m0_written)
                      : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(vo), "s"(rs), "s"(0)
-                     : "memory", "m0");
+                     : "memory");
+        (void)m0_written;
     };
     // The i-th key block a wave walks: block i, or (SPLIT) wave + NW i.  LDS:
     // K of walk positions i, i + 1 at (i % 2) K_BYTES, V at 2 K_BYTES +
@@ -290,6 +294,24 @@ void attention_kernel(AttnArgs p) {
     // registers.
     auto step = [&](int kb, f32x4 (&sc)[2][4], f32x4 (&nx)[2][4], auto masked_t) __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(masked_t)::value;
+        lds_attn_char* const knext = ring + ((kb + 1) & 1) * K_BYTES + koff;
+        lds_attn_char* const vbase = ring + 2 * K_BYTES + (kb & 1) * V_BYTES;
+        // K fragments of S(kb + 1), key group g, d-step s
+        auto read_k = [&](int g, attn_i16x8 (&dst)[KS]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+                dst[s] = __builtin_bit_cast(attn_i16x8, *(const lds_attn_u32x4*)(knext + s * (BKV * 64) + g * 1024));
+        };
+        // V fragment u = DB t + db: keys 32 t + ..., columns 16 db + ...
+        auto read_v = [&](int u) __attribute__((always_inline)) {
+            const int t = u / DB, db = u % DB;
+            const attn_i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_attn_i16x4*)(vbase + voff(t, 0, db)));
+            const attn_i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_attn_i16x4*)(vbase + voff(t, 1, db)));
+            return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        };
+        constexpr int NU = 2 * DB;
+        attn_i16x8 kf[2][KS], vf[3];
+        read_k(0, kf[0]);
         if (kb + 2 < nwalk) issue_k(kb + 2);
         if (kb + 1 < nwalk) issue_v(kb + 1);
         const int key0 = kb_of(kb) * BKV;
@@ -333,21 +355,32 @@ void attention_kernel(AttnArgs p) {
                 lacc[rs] *= alpha;
             }
         }
+        // Wave priority 1 over the MFMA phases (measured: the S and PV
+        // phases with head dimension 64, the PV phase alone with 128), 0
+        // over the row maxima and the rescale, so that of the two waves on
+        // a SIMD the one issuing MFMAs is served first.
+        if constexpr (PRIO_S) __builtin_amdgcn_s_setprio(1);
         // S(kb + 1) on the matrix cores and p = 2^(c s - m) on the SIMD, one
         // key group at a time (each group's 2 KS MFMAs beside its 8 exp2).
         // On the last block the next scores come from a stale LDS slot and
-        // are not used: no branch splits the interleaved code.
-        lds_attn_char* const knext = ring + ((kb + 1) & 1) * K_BYTES + koff;
+        // are not used: no branch splits the interleaved code.  LDS reads run
+        // ahead of the MFMAs that take them: the K fragments of group g + 1
+        // are read before the MFMAs of group g (group 0's at the top of the
+        // step, before the row maxima), the first two V fragments with group
+        // 3, and each V fragment two MFMA pairs ahead.
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
+            if (g + 1 < 4) read_k(g + 1, kf[(g + 1) & 1]);
+            if (g == 3) {
+                vf[0] = read_v(0);
+                vf[1] = read_v(1);
+            }
             nx[0][g] = f32x4{0.f, 0.f, 0.f, 0.f};
             nx[1][g] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
-                const attn_i16x8 kf =
-                    __builtin_bit_cast(attn_i16x8, *(const lds_attn_u32x4*)(knext + s * (BKV * 64) + g * 1024));
-                nx[0][g] = attn_mfma<IN>(kf, qf[0][s], nx[0][g]);
-                nx[1][g] = attn_mfma<IN>(kf, qf[1][s], nx[1][g]);
+                nx[0][g] = attn_mfma<IN>(kf[g & 1][s], qf[0][s], nx[0][g]);
+                nx[1][g] = attn_mfma<IN>(kf[g & 1][s], qf[1][s], nx[1][g]);
             }
 #pragma unroll
             for (int rs = 0; rs < 2; ++rs)
@@ -361,31 +394,37 @@ void attention_kernel(AttnArgs p) {
             if constexpr (D == 128) __builtin_amdgcn_sched_barrier(0);
         }
         // O += P V, 32 keys at a time: P = this lane's keys 4q..4q+3 of
-        // groups 2t and 2t+1
-        lds_attn_char* const vbase = ring + 2 * K_BYTES + (kb & 1) * V_BYTES;
+        // groups 2t and 2t+1; V fragment u = DB t + db in vf[u % 3]
+        attn_i16x8 pf[2];
+        if constexpr (!PRIO_S) __builtin_amdgcn_s_setprio(1);
+        static_for<0, NU>([&](auto u_t) __attribute__((always_inline)) {
+            constexpr int u = decltype(u_t)::value, t = u / DB, db = u % DB;
+            if constexpr (db == 0) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            attn_i16x8 pf[2];
-#pragma unroll
-            for (int rs = 0; rs < 2; ++rs) {
-                const uint32_t w0 = attn_pack2<IN>(sc[rs][2 * t][0], sc[rs][2 * t][1]);
-                const uint32_t w1 = attn_pack2<IN>(sc[rs][2 * t][2], sc[rs][2 * t][3]);
-                const uint32_t w2 = attn_pack2<IN>(sc[rs][2 * t + 1][0], sc[rs][2 * t + 1][1]);
-                const uint32_t w3 = attn_pack2<IN>(sc[rs][2 * t + 1][2], sc[rs][2 * t + 1][3]);
-                pf[rs] = __builtin_bit_cast(attn_i16x8, u32x4{w0, w1, w2, w3});
+                for (int rs = 0; rs < 2; ++rs) {
+                    const uint32_t w0 = attn_pack2<IN>(sc[rs][2 * t][0], sc[rs][2 * t][1]);
+                    const uint32_t w1 = attn_pack2<IN>(sc[rs][2 * t][2], sc[rs][2 * t][3]);
+                    const uint32_t w2 = attn_pack2<IN>(sc[rs][2 * t + 1][0], sc[rs][2 * t + 1][1]);
+                    const uint32_t w3 = attn_pack2<IN>(sc[rs][2 * t + 1][2], sc[rs][2 * t + 1][3]);
+                    pf[rs] = __builtin_bit_cast(attn_i16x8, u32x4{w0, w1, w2, w3});
+                }
             }
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const attn_i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_attn_i16x4*)(vbase + voff(t, 0, db)));
-                const attn_i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_attn_i16x4*)(vbase + voff(t, 1, db)));
-                const attn_i16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                o[0][db] = attn_mfma<IN>(vf, pf[0], o[0][db]);
-                o[1][db] = attn_mfma<IN>(vf, pf[1], o[1][db]);
+            if constexpr (u + 2 < NU) vf[(u + 2) % 3] = read_v(u + 2);
+            o[0][db] = attn_mfma<IN>(vf[u % 3], pf[0], o[0][db]);
+            o[1][db] = attn_mfma<IN>(vf[u % 3], pf[1], o[1][db]);
+            // each read two fragments ahead of its MFMAs (the compiler would
+            // otherwise move the reads down to their MFMAs)
+            if constexpr (db == 0) __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // the 8 packs
+            if constexpr (u + 2 < NU) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            if constexpr (db == DB - 1) {
+                lacc[0] = attn_mfma<IN>(ones, pf[0], lacc[0]);
+                lacc[1] = attn_mfma<IN>(ones, pf[1], lacc[1]);
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                if constexpr (D == 128) __builtin_amdgcn_sched_barrier(0);
             }
-            lacc[0] = attn_mfma<IN>(ones, pf[0], lacc[0]);
-            lacc[1] = attn_mfma<IN>(ones, pf[1], lacc[1]);
-            if constexpr (D == 128) __builtin_amdgcn_sched_barrier(0);
-        }
+        });
+        __builtin_amdgcn_s_setprio(0);
         wait_vmcnt<0>();
         if constexpr (!SPLIT) __syncthreads();  // SPLIT: the ring is the wave's own
     };

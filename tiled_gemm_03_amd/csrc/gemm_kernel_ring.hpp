@@ -322,14 +322,17 @@ void gemm_kernel_ring(GemmArgs p) {
     // Issued through inline asm: the compiler then does not guard later LDS
     // reads with waits for these loads; the kernel waits for them itself
     // (vmcnt) before the barrier that publishes a stage.  The block writes M0
-    // (the LDS destination) and declares it clobbered, so the compiler keeps
-    // nothing of its own in M0 across it.  (An "{m0}" input operand instead
-    // made the compiler move accumulators in the 256 x 256 main loop.)
+    // (the LDS destination) and names M0 as its output operand, so the
+    // compiler knows M0 is overwritten and keeps nothing of its own there
+    // across it.  (An "{m0}" input operand instead made the compiler move
+    // accumulators in the 256 x 256 main loop.)
     auto dma = [&](int lds_addr, int vo, i32x4 rs, int so) __attribute__((always_inline)) {
-        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                     :
+        int m0_written;
+        asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, %4 offen lds"
+                     : "={m0}"(m0_written)
                      : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(vo), "s"(rs), "s"(so)
-                     : "memory", "m0");
+                     : "memory");
+        (void)m0_written;
     };
     // the loads of one operand's stage st at K byte offset k
     auto load_a = [&](int st, int x, int k) __attribute__((always_inline)) {
