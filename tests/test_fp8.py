@@ -149,21 +149,27 @@ def test_fp8_plain_product_and_partial_groups():
 
 def test_fp8_unaligned_operands_take_the_direct_kernel():
     """Operands the ring cannot read whole (rows of an odd K, contiguous, the
-    last element of A at an address of 2 mod 4) would take a register-staged
-    kernel, which writes no 8-bit output: the direct kernel runs instead.
-    With one padding element per row of A the ring reads them and runs."""
+    last element of A ending at a 4 KiB page boundary: its range cannot be
+    padded) would take a register-staged kernel, which writes no 8-bit
+    output: the direct kernel runs instead.  Placed elsewhere (a padded
+    range) or with one padding element per row, the ring runs."""
     M, N, K = 1024, 1024, 301   # the table's choice: the 64 x 64 register-staged tile
     a, b = W.integer_inputs(M, N, K, W.F16, seed=3)
-    assert T.gemm_select_kernel_t(M, N, K, 1 << 40, K, ROW, 1 << 41, N + 3, ROW, 1 << 42, N, ROW, W.F16,
-                                  W.F16, -1)[0] == T.KERNEL_GENERAL
     o = oracle.gemm_fused(a, b, W.F16, alpha=0.25, nthreads=G.NTHREADS)
-    for pad_a, want_kind in ((0, T.KERNEL_DIRECT), (1, T.KERNEL_RING)):
-        ad = G.to_device(a, W.F16, pad_cols=pad_a)       # lda = 301 / 302
-        bd = G.to_device(b, W.F16, pad_cols=3)           # ldb = 1027
+    bd = G.to_device(b, W.F16, pad_cols=3)           # ldb = 1027
+    n = M * K
+    flat = torch.full((n + 4096 + 8,), float("nan"), dtype=torch.float16, device=G.DEV)
+    at_page = ((-(flat.data_ptr() + 2 * n)) % 4096) // 2
+    placements = [("A ends at a page", flat[at_page:at_page + n].view(M, K), K, T.KERNEL_DIRECT),
+                  ("A padded range", flat[at_page + 2:at_page + 2 + n].view(M, K), K, T.KERNEL_RING),
+                  ("lda 302", G.to_device(a, W.F16, pad_cols=1), K + 1, T.KERNEL_RING)]
+    for label, ad, lda, want_kind in placements:
+        if lda == K:
+            ad.copy_(torch.from_numpy(a).to(G.DEV))
         cd = fp8_tensor(np.full((M, N), 0x7F, np.uint8), T.FP8_E4M3)
-        kind = T.gemm_select_kernel_t(M, N, K, ad.data_ptr(), K + pad_a, ROW, bd.data_ptr(), N + 3, ROW,
+        kind = T.gemm_select_kernel_t(M, N, K, ad.data_ptr(), lda, ROW, bd.data_ptr(), N + 3, ROW,
                                       cd.data_ptr(), N, ROW, W.F16, T.FP8_E4M3, -1)[0]
-        G.say(f"[case] fp8 unaligned operands lda={K + pad_a} -> {KIND.get(kind, kind)}")
+        G.say(f"[case] fp8 unaligned operands, {label} -> {KIND.get(kind, kind)}")
         assert kind == want_kind
         T.gemm_tensors(ad, bd, cd, alpha=0.25)
         torch.cuda.synchronize()

@@ -4,9 +4,12 @@ address, for every operand-layout pair, against the oracle.
 
 The ring's 16-byte loads then start at 2-byte-aligned addresses; their range
 check keeps a 4-byte part only if it ends inside the operand's range, which
-ends at the dword boundary after the operand's last element.  The library
-takes the ring exactly when that keeps every element (the rule restated in
-`keeps_last` below) and another kernel otherwise; both cases are run.
+ends at the dword boundary after the operand's last element, or 2 bytes
+further where the last element starts a part at an address of 2 mod 4 (those
+bytes are then read, so they must lie in the element's page).  The library
+takes the ring exactly when one of the two keeps every element (the rule
+restated in `ring_reads` below) and another kernel otherwise; both cases are
+run.
 
 Every operand sits in a NaN-filled buffer (NaN in the row padding, in the
 elements before the base and after the last element), so a read past K that
@@ -35,14 +38,29 @@ def lid(lay):
     return "".join("r" if x == ROW else "c" for x in lay)
 
 
-def keeps_last(base, ld, kcontig, outer, K):
-    """Whether the ring's range check keeps the operand's last element: it is
-    lost only if it starts a 4-byte part of its load (an odd element count
-    along the row from the row's first loaded element) at an address of
-    2 mod 4."""
+def ring_reads(base, ld, kcontig, outer, K):
+    """Whether the ring reads the operand whole: its last element is lost only
+    if it starts a 4-byte part of its load (an odd element count along the row
+    from the row's first loaded element) at an address of 2 mod 4 and the 2
+    bytes after it start a new 4 KiB page (else the range is padded)."""
     rows, cols = (outer, K) if kcontig else (K, outer)
     last = base + 2 * ((rows - 1) * ld + cols - 1)
-    return not (cols % 2 == 1 and last % 4 == 2)
+    return not (cols % 2 == 1 and last % 4 == 2) or (last + 2) % 4096 != 0
+
+
+def place_ending_at_page(x, dt):
+    """Row-major device copy of x (rows x cols, ld = cols) whose last element
+    ends exactly at a 4 KiB page boundary, in a NaN-filled buffer."""
+    rows, cols = x.shape
+    n = rows * cols
+    flat = torch.full((n + 4096,), float("nan"), dtype=G.TORCH[dt], device=G.DEV)
+    off = ((-(flat.data_ptr() + 2 * n)) % 4096) // 2
+    view = flat[off:off + n].view(rows, cols)
+    host = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16) if dt == W.BF16 \
+        else torch.from_numpy(np.ascontiguousarray(x))
+    view.copy_(host.to(G.DEV))
+    assert (view.data_ptr() + 2 * n) % 4096 == 0
+    return view
 
 
 def place(x, dt, layout, pad, offset):
@@ -65,7 +83,7 @@ def run_exact(M, N, K, in_dt, out_dt, lay, pads, offs, cid, seed):
     G.say(f"[case] unaligned {M}x{N}x{K} lay={lid(lay)} in={in_dt} out={out_dt} lda={lda} ldb={ldb} "
           f"offs={offs} cfg{cid} -> {KIND.get(kind, kind)} cfg{cfg}")
     aligned = ad.data_ptr() % 16 == 0 and bd.data_ptr() % 16 == 0 and lda % 8 == 0 and ldb % 8 == 0
-    keeps = keeps_last(ad.data_ptr(), lda, la == ROW, M, K) and keeps_last(bd.data_ptr(), ldb, lb == COL, N, K)
+    keeps = ring_reads(ad.data_ptr(), lda, la == ROW, M, K) and ring_reads(bd.data_ptr(), ldb, lb == COL, N, K)
     assert (kind == T.KERNEL_RING) == (aligned or keeps), (kind, aligned, keeps)
     G.run(ad, bd, cd, cid)
     got = G.values(cd, out_dt)
@@ -97,10 +115,25 @@ def test_unaligned_operands_exact(shape, lay):
 
 def test_unaligned_operands_both_outcomes_of_the_rule():
     """The same shape with the last element of A at 0 and at 2 mod 4 (K odd,
-    rows of K elements): ring, then the fallback, both exact."""
+    rows of K elements: the ring, with and without the range pad), then with
+    that element ending at a page boundary (the fallback); all exact, NaN in
+    the bytes after A's last element."""
     M, N, K = 511, 512, 513
     kinds = [run_exact(M, N, K, W.F16, W.F16, (ROW, ROW), (0, 0), (oa, 0), 1, seed=5 + oa) for oa in (0, 1, 2, 3)]
-    assert T.KERNEL_RING in kinds and any(k != T.KERNEL_RING for k in kinds), kinds
+    # (run_exact checks each kind against the rule; at most one of the four
+    # placements can end A at a page boundary)
+    assert kinds.count(T.KERNEL_RING) >= 3, kinds
+    a, b = W.integer_inputs(M, N, K, W.F16, seed=9)
+    ad = place_ending_at_page(a, W.F16)
+    bd = G.to_device(b, W.F16)
+    _, cd = G.out_tensor(M, N, W.F16)
+    kind = T.gemm_select_kernel(M, N, K, ad.data_ptr(), K, bd.data_ptr(), N, cd.data_ptr(), N, W.F16, W.F16, 1)
+    G.say(f"[case] unaligned A ending at a page boundary {M}x{N}x{K} -> {KIND.get(kind, kind)}")
+    assert kind != T.KERNEL_RING and not ring_reads(ad.data_ptr(), K, True, M, K)
+    G.run(ad, bd, cd, 1)
+    want = G.round_to(G.oracle_values(a, b, W.F16), W.F16)
+    got = G.values(cd, W.F16)
+    assert np.array_equal(got, want), f"{int((got != want).sum())} entries differ"
 
 
 def test_unaligned_operands_random_values():
@@ -118,8 +151,8 @@ def test_unaligned_operands_random_values():
                                     N, in_dt, out_dt)
         G.say(f"[case] unaligned random {M}x{N}x{K} in={in_dt} out={out_dt} pads={pads} offs={offs} "
               f"-> {KIND.get(kind, kind)}")
-        assert keeps_last(ad.data_ptr(), K + pads[0], True, M, K)
-        assert keeps_last(bd.data_ptr(), N + pads[1], False, N, K)
+        assert ring_reads(ad.data_ptr(), K + pads[0], True, M, K)
+        assert ring_reads(bd.data_ptr(), N + pads[1], False, N, K)
         assert kind == T.KERNEL_RING
         G.run(ad, bd, cd)
         G.check(G.values(cd, out_dt), G.oracle_values(a, b, in_dt), a, b, in_dt, out_dt, K, label="unaligned")
@@ -132,7 +165,7 @@ def test_unaligned_operands_fused_and_fp8():
     a, b = W.integer_inputs(M, N, K, W.F16, seed=77)
     ad = G.to_device(a, W.F16, pad_cols=1, offset_elems=2)
     bd = G.to_device(b, W.F16, pad_cols=3, offset_elems=2)
-    assert keeps_last(ad.data_ptr(), K + 1, True, M, K) and keeps_last(bd.data_ptr(), N + 3, False, N, K)
+    assert ring_reads(ad.data_ptr(), K + 1, True, M, K) and ring_reads(bd.data_ptr(), N + 3, False, N, K)
     rng = np.random.default_rng(78)
     c_old = rng.integers(-8, 9, size=(M, N)).astype(np.float32)
     bias = rng.integers(-4, 5, size=N).astype(np.float32)

@@ -76,6 +76,10 @@ struct GemmArgs {
     const char* bias;       // bias_kind BIAS_ROW: M values, BIAS_COL: N values, of type bias_dt
     int bias_kind, bias_dt, act;
     int fp8_e5m2;           // DT_FP8 output: 0 = E4M3, 1 = E5M2
+    // ring kernels: bytes added to A's / B's buffer range past its dword
+    // rounding (0, or 2 when the last element would otherwise be dropped;
+    // the host checks that they lie in the last element's page)
+    int range_pad_a, range_pad_b;
 };
 
 enum { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU = 2, ACT_GELU_TANH = 3, ACT_SILU = 4 };

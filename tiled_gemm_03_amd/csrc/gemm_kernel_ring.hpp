@@ -221,8 +221,9 @@ struct RingCfg {
 
 // Preconditions (checked by the host): 16-bit inputs; K % K_MULT == 0, or
 // K > K_MULT with KT; A and B element-aligned, and where their rows are not
-// whole 16-byte chunks (16-byte aligned, ld a multiple of 8), no operand whose
-// last element starts a 4-byte part of its load at an address of 2 mod 4; without EPI, N % 4 == 0 and C aligned for 4-element stores with
+// whole 16-byte chunks (16-byte aligned, ld a multiple of 8), range_pad_a /
+// range_pad_b 2 for an operand whose last element starts a 4-byte part of its
+// load at an address of 2 mod 4 (the 2 bytes after it in its page), else 0; without EPI, N % 4 == 0 and C aligned for 4-element stores with
 // ldc % 4 == 0 (the fused epilogue, EPI, takes any N and C alignment; a plain
 // product that needs it runs EPI with alpha 1, beta 0, no bias and no
 // activation, which store the product unchanged); the buffer offsets (a tile's rows or
@@ -270,13 +271,14 @@ void gemm_kernel_ring(GemmArgs p) {
     // the element, so the range's end is rounded up to a dword boundary of
     // the address space: it then never reaches past the aligned dword that
     // holds the last element (no other page), and the bytes it adds reach
-    // only outputs past M or N, never stored.  With rows of whole 16-byte
-    // chunks this keeps every element; with other rows the host takes the
-    // ring only when it does (an element that starts a part at an address of
-    // 2 mod 4 would still be dropped).
-    auto make_rsrc = [&](const char* base, int64_t bytes) __attribute__((always_inline)) {
+    // only outputs past M or N or positions past K, never stored or zeroed.
+    // With rows of whole 16-byte chunks this keeps every element.  Otherwise
+    // an element that starts a part at an address of 2 mod 4 is kept only
+    // with the 2 bytes after it in range: the host then passes a pad of 2
+    // (it checks that those bytes lie in the element's page).
+    auto make_rsrc = [&](const char* base, int64_t bytes, int pad) __attribute__((always_inline)) {
         const uint64_t a = (uint64_t)base;
-        if (bytes > 0) bytes = (int64_t)(((a + (uint64_t)bytes + 3) & ~(uint64_t)3) - a);
+        if (bytes > 0) bytes = (int64_t)(((a + (uint64_t)bytes + 3) & ~(uint64_t)3) - a) + pad;
         const uint32_t n = bytes <= 0 ? 0u : bytes > 0xffffffffLL ? 0xffffffffu : (uint32_t)bytes;
         return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
                      __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)),
@@ -301,8 +303,8 @@ void gemm_kernel_ring(GemmArgs p) {
     const char* const b_start = operand_start(OB_{}, p.B, ldb, n0);
     const int64_t a_bytes = operand_bytes(OA{}, lda, m0, p.M);
     const int64_t b_bytes = operand_bytes(OB_{}, ldb, n0, p.N);
-    const i32x4 rs_a = make_rsrc(a_start, a_bytes);
-    const i32x4 rs_b = make_rsrc(b_start, b_bytes);
+    const i32x4 rs_a = make_rsrc(a_start, a_bytes, p.range_pad_a);
+    const i32x4 rs_b = make_rsrc(b_start, b_bytes, p.range_pad_b);
     // per-lane byte offset of a load (block blk of a stage): lane l fills
     // byte 16 l of the block with the chunk the layout puts there
     auto load_voff = [&](auto op_t, int blk, int64_t ld) __attribute__((always_inline)) {
@@ -508,14 +510,14 @@ void gemm_kernel_ring(GemmArgs p) {
     if constexpr (KT) {
         // the K tail: steps of 32 from k = 32 nk, fragments from global
         // memory through buffer loads over the same ranges as the rings'
-        auto tail_rsrc = [&](const char* base, int64_t bytes) __attribute__((always_inline)) {
+        auto tail_rsrc = [&](const char* base, int64_t bytes, int pad) __attribute__((always_inline)) {
             const uint64_t a = (uint64_t)base;
-            if (bytes > 0) bytes = (int64_t)(((a + (uint64_t)bytes + 3) & ~(uint64_t)3) - a);
+            if (bytes > 0) bytes = (int64_t)(((a + (uint64_t)bytes + 3) & ~(uint64_t)3) - a) + pad;
             const int n = bytes <= 0 ? 0 : bytes > 0x7fffffffLL ? 0x7fffffff : (int)bytes;
             return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, n, 0x00020000);
         };
-        const auto ta = tail_rsrc(a_start, a_bytes);
-        const auto tb = tail_rsrc(b_start, b_bytes);
+        const auto ta = tail_rsrc(a_start, a_bytes, p.range_pad_a);
+        const auto tb = tail_rsrc(b_start, b_bytes, p.range_pad_b);
         // lane's 8 k (k ..) of row / column o (from the tile's corner)
         auto tail_frag = [&](auto op_t, const auto& rs, int o, int64_t ld, int k) __attribute__((always_inline)) {
             using O = decltype(op_t);

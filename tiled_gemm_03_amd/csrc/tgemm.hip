@@ -214,21 +214,27 @@ int64_t operand_reach(bool kcontig, int64_t ext, int64_t ld, int64_t K, int64_t 
     return (kcontig ? ext * ld + K + extra : (K + extra) * ld + ext) * eb;
 }
 
-// Whether the ring kernel reads every element of a 16-bit operand stored
-// with rows of `outer` elements (k contiguous: the row is K long) at leading
-// dimension ld from base X.  Its 16-byte loads (any even address) keep a
-// 4-byte part only when the part ends inside the buffer range, which ends at
-// the dword boundary after the operand's last element: the last element is
-// dropped if it starts a part (the row's element count from the tile's first
-// one is odd: K for a k-contiguous operand, M or N for a k-strided one) at an
-// address of 2 mod 4.  Rows of whole 16-byte chunks never do.
-bool ring_reads_all(const void* X, int64_t ld, bool kcontig, int64_t outer, int64_t K) {
+// Buffer-range pad that makes the ring kernel read every element of a 16-bit
+// operand stored with rows of `outer` elements (k contiguous: the row is K
+// long) at leading dimension ld from base X: 0, 2, or -1 for none.  Its
+// 16-byte loads (any even address) keep a 4-byte part only when the part ends
+// inside the buffer range, which ends at the dword boundary after the
+// operand's last element: the last element is dropped if it starts a part
+// (an odd element count from the row's first loaded one: K for a
+// k-contiguous operand, M or N for a k-strided one) at an address of 2 mod 4.
+// Then 2 more bytes keep it; they are read (their values reach only outputs
+// past N or positions past K), so they must lie in the element's page: -1
+// when they start a new 4 KiB page.  Rows of whole 16-byte chunks never need
+// a pad.
+int ring_range_pad(const void* X, int64_t ld, bool kcontig, int64_t outer, int64_t K) {
     const int64_t rows = kcontig ? outer : K, cols = kcontig ? K : outer;
-    if (rows <= 0 || cols <= 0) return true;
+    if (rows <= 0 || cols <= 0) return 0;
     const uintptr_t last = (uintptr_t)X + (uintptr_t)((rows - 1) * ld + cols - 1) * 2;
-    const bool starts_part = (cols % 2) == 1;
-    return !(starts_part && last % 4 == 2);
+    if ((cols % 2) == 0 || last % 4 != 2) return 0;
+    return (last + 2) % 4096 != 0 ? 2 : -1;
 }
+int ring_pad_a(const Problem& p) { return ring_range_pad(p.A, p.lda, p.la == LAYOUT_ROW, p.M, p.K); }
+int ring_pad_b(const Problem& p) { return ring_range_pad(p.B, p.ldb, p.lb == LAYOUT_COL, p.N, p.K); }
 
 // Whether a configuration with a ring kernel runs it.
 bool ring_applies(const ConfigEntry& c, const Problem& p) {
@@ -237,11 +243,9 @@ bool ring_applies(const ConfigEntry& c, const Problem& p) {
     // the ring loads ring_lookahead steps past K
     const int64_t extra = (int64_t)c.ring_lookahead * c.ring_bk;
     // 16-bit elements at even addresses; rows of whole 16-byte chunks, or
-    // ranges that keep every element (ring_reads_all)
+    // ranges that keep every element, padded where needed (ring_range_pad)
     const bool loads_ok = (uintptr_t)p.A % 2 == 0 && (uintptr_t)p.B % 2 == 0 &&
-                          (loads_aligned(c, p) ||
-                           (ring_reads_all(p.A, p.lda, p.la == LAYOUT_ROW, p.M, p.K) &&
-                            ring_reads_all(p.B, p.ldb, p.lb == LAYOUT_COL, p.N, p.K)));
+                          (loads_aligned(c, p) || (ring_pad_a(p) >= 0 && ring_pad_b(p) >= 0));
     // K a multiple of ring_k_mult, or above it (the K-tail variant); any N
     // and C alignment (ring_plain_stores)
     return loads_ok && (p.K % c.ring_k_mult == 0 || p.K > c.ring_k_mult) &&
@@ -459,6 +463,9 @@ int run(const Problem& p, void* stream, int config_id) {
     args.bias_dt = p.ep.bias_dt;
     args.act = p.ep.act;
     args.fp8_e5m2 = p.out == TGEMM_FP8_E5M2 ? 1 : 0;
+    const bool ring = plan.kind == TGEMM_KERNEL_RING;
+    args.range_pad_a = ring && ring_pad_a(p) > 0 ? ring_pad_a(p) : 0;
+    args.range_pad_b = ring && ring_pad_b(p) > 0 ? ring_pad_b(p) : 0;
     const int64_t grid = (int64_t)args.tiles_m * args.tiles_n;
 
     void* kargs[] = {&args};
