@@ -176,6 +176,37 @@ def test_fp8_unaligned_operands_take_the_direct_kernel():
         assert np.array_equal(fp8_bits(cd), oracle.encode_fp8(o, T.FP8_E4M3))
 
 
+@pytest.mark.parametrize("shape", [(256, 512, 256, -1), (100, 72, 40, 6)], ids=["ring", "direct"])
+def test_fp8_nan_and_infinity(shape):
+    """A NaN in row 0 of A makes row 0 of C NaN: an 8-bit NaN pattern (E4M3
+    S.1111.111, E5M2 exponent 31 with a nonzero fraction; the sign of a NaN
+    the arithmetic makes is not defined).  An infinity in row 1 of A, times
+    a row of B that is all ones, makes row 1 +infinity: the largest finite
+    value (saturating).  The other rows against the oracle, exactly."""
+    M, N, K, cid = shape
+    a, b = W.integer_inputs(M, N, K, W.F16, seed=21)
+    a[0, 3] = np.float16(np.nan)
+    a[1, 0] = np.float16(np.inf)
+    b[0, :] = np.float16(1.0)
+    ad, bd = G.to_device(a, W.F16), G.to_device(b, W.F16)
+    rest = np.ascontiguousarray(a[2:])
+    o = oracle.gemm_fused(rest, b, W.F16, alpha=0.5, nthreads=G.NTHREADS)
+    for fmt, top in ((T.FP8_E4M3, 0x7E), (T.FP8_E5M2, 0x7B)):
+        cd = fp8_tensor(np.zeros((M, N), np.uint8), fmt)
+        kind = T.gemm_select_kernel(M, N, K, ad.data_ptr(), K, bd.data_ptr(), N, cd.data_ptr(), N, W.F16, fmt, cid)
+        G.say(f"[case] fp8 NaN / infinity {M}x{N}x{K} fmt={fmt} -> {KIND.get(kind, kind)}")
+        T.gemm_tensors(ad, bd, cd, config_id=cid, alpha=0.5)
+        torch.cuda.synchronize()
+        got = fp8_bits(cd)
+        mag = got[0] & 0x7F
+        if fmt == T.FP8_E4M3:
+            assert (mag == 0x7F).all(), np.unique(got[0])
+        else:
+            assert ((mag >> 2) == 0x1F).all() and ((mag & 3) != 0).all(), np.unique(got[0])
+        assert (got[1] == top).all(), np.unique(got[1])
+        assert np.array_equal(got[2:], oracle.encode_fp8(o, fmt))
+
+
 def test_fp8_guard_band_and_k_zero():
     """Padding bytes after each row of C are untouched; K = 0 writes +0."""
     M, N, K = 200, 264, 256

@@ -59,6 +59,10 @@ __host__ __device__ constexpr int out_bytes() {
     return OUT == DT_F32 ? 4 : OUT == DT_FP8 ? 1 : 2;
 }
 
+#ifndef TGEMM_EPI_BATCH
+#define TGEMM_EPI_BATCH 8
+#endif
+
 struct GemmArgs {
     const char* A;
     const char* B;
@@ -241,28 +245,41 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 // fp32 -> 8 bits: nearest, ties to even; magnitudes beyond the largest finite
 // value, infinities included, become the largest finite value of the sign
 // (the saturating conversion); NaN becomes the all-ones pattern with the sign.
+// The rounding is the hardware conversion's (v_cvt_pk_fp8_f32 /
+// v_cvt_pk_bf8_f32), which agrees with this definition for every value up to
+// the largest finite one (checked on gfx950 over a stride of all fp32
+// patterns, every midpoint between 8-bit values, subnormals and zeros); above
+// it the instruction gives NaN (E4M3) or infinity (E5M2), so the input is
+// clamped first, and NaN is set apart (the instruction drops its sign).
+__device__ __forceinline__ float fp8_clamp(float x, int e5m2) {
+    const float mx = e5m2 ? 57344.f : 448.f;
+    return fminf(fmaxf(x, -mx), mx);
+}
+__device__ __forceinline__ uint32_t fp8_nan(float x) {
+    return ((__builtin_bit_cast(uint32_t, x) >> 24) & 0x80u) | 0x7fu;
+}
 __device__ __forceinline__ uint32_t to_fp8(float x, int e5m2) {
-    const uint32_t u = __builtin_bit_cast(uint32_t, x);
-    const uint32_t sign = (u >> 24) & 0x80u;
-    const uint32_t a = u & 0x7fffffffu;
-    if (a > 0x7f800000u) return sign | 0x7fu;
-    const int F = e5m2 ? 2 : 3;
-    const uint32_t top = e5m2 ? 0x7bu : 0x7eu;   // largest finite pattern
-    uint32_t r;
-    if (a < (e5m2 ? 0x38800000u : 0x3c800000u)) {  // below 2^-14 / 2^-6: subnormal spacing
-        // |x| / spacing is exact (a power-of-two scale of a value below 2^F);
-        // rint rounds it to nearest even; 2^F is the smallest normal's pattern
-        r = (uint32_t)__builtin_rintf(__builtin_bit_cast(float, a) * (e5m2 ? 65536.f : 512.f));
+    const float c = fp8_clamp(x, e5m2);
+    const uint32_t r = (uint32_t)(e5m2 ? __builtin_amdgcn_cvt_pk_bf8_f32(c, 0.f, 0, false)
+                                       : __builtin_amdgcn_cvt_pk_fp8_f32(c, 0.f, 0, false)) & 0xffu;
+    return x != x ? fp8_nan(x) : r;
+}
+// four values -> their four 8-bit patterns, a in the low byte
+__device__ __forceinline__ uint32_t to_fp8x4(float a, float b, float c, float d, int e5m2) {
+    const float ca = fp8_clamp(a, e5m2), cb = fp8_clamp(b, e5m2), cc = fp8_clamp(c, e5m2), cd = fp8_clamp(d, e5m2);
+    uint32_t w;
+    if (e5m2) {
+        w = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(ca, cb, 0, false);
+        w = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(cc, cd, (int)w, true);
     } else {
-        // drop 23 - F fraction bits, nearest even, carrying into the
-        // exponent; then re-bias the exponent (127 -> 15 or 7)
-        const int drop = 23 - F;
-        const uint32_t rnd = a + ((1u << (drop - 1)) - 1u) + ((a >> drop) & 1u);
-        const uint32_t e = (rnd >> 23) - (e5m2 ? 112u : 120u);
-        r = (e << F) | ((rnd >> drop) & ((1u << F) - 1u));
-        r = r > top ? top : r;
+        w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, 0, false);
+        w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(cc, cd, (int)w, true);
     }
-    return sign | r;
+    if (a != a) w = (w & 0xffffff00u) | fp8_nan(a);
+    if (b != b) w = (w & 0xffff00ffu) | (fp8_nan(b) << 8);
+    if (c != c) w = (w & 0xff00ffffu) | (fp8_nan(c) << 16);
+    if (d != d) w = (w & 0x00ffffffu) | (fp8_nan(d) << 24);
+    return w;
 }
 __device__ __forceinline__ float from_fp8(uint32_t b, int e5m2) {
     if (e5m2) {
@@ -280,8 +297,7 @@ __device__ __forceinline__ float from_fp8(uint32_t b, int e5m2) {
 template <int OUT>
 __device__ __forceinline__ void store4(char* p, float a, float b, float c, float d, bool vec, int fp8_e5m2 = 0) {
     if constexpr (OUT == DT_FP8) {
-        const uint32_t w = to_fp8(a, fp8_e5m2) | (to_fp8(b, fp8_e5m2) << 8) | (to_fp8(c, fp8_e5m2) << 16) |
-                           (to_fp8(d, fp8_e5m2) << 24);
+        const uint32_t w = to_fp8x4(a, b, c, d, fp8_e5m2);
         if (vec) *(uint32_t*)p = w;
         else __builtin_memcpy(p, &w, 4);
     } else if constexpr (OUT == DT_F32) {
@@ -528,7 +544,7 @@ __device__ __forceinline__ void fused_epilogue(const GemmArgs& p, lds_f32x4* reg
     static_assert(NB % PB == 0 && VPL % 4 == 0, "");
     constexpr int G = VPL / 4;   // groups per block
     constexpr int NG = PB * G;   // groups per pass
-    constexpr int EB = NG < 8 ? NG : 8;  // groups whose loads of C are in flight together
+    constexpr int EB = NG < TGEMM_EPI_BATCH ? NG : TGEMM_EPI_BATCH;  // groups whose loads of C are in flight together
     static_assert(NG % EB == 0, "");
     constexpr int OB = out_bytes<OUT>();
     const int lane = threadIdx.x & 63;
