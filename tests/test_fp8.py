@@ -207,6 +207,45 @@ def test_fp8_nan_and_infinity(shape):
         assert np.array_equal(got[2:], oracle.encode_fp8(o, fmt))
 
 
+@pytest.mark.parametrize("cid", [1, 6], ids=["ring", "direct"])
+def test_fp8_every_half_value(cid):
+    """Every fp16 bit pattern through the output conversion: C = alpha A B
+    with A's column 0 holding all 65536 patterns (the other columns zero) and
+    B's row 0 all ones, so each row of C is alpha times one fp16 value,
+    exact in fp32 (alpha 1, 2^-8, 3; -0 sums to +0).  Each 8-bit pattern
+    must equal the oracle's rounding of that value (nearest even,
+    saturating), NaN inputs an 8-bit NaN; both formats, a ring and the
+    direct kernel."""
+    M, N, K = 65536, 16, 128
+    col = np.arange(65536, dtype=np.uint16).view(np.float16)
+    a = np.zeros((M, K), np.float16)
+    a[:, 0] = col
+    b = np.zeros((K, N), np.float16)
+    b[0, :] = 1.0
+    ad, bd = G.to_device(a, W.F16), G.to_device(b, W.F16)
+    nan = np.isnan(col.astype(np.float64))
+    for fmt in (T.FP8_E4M3, T.FP8_E5M2):
+        for alpha in (1.0, 2.0 ** -8, 3.0):
+            cd = fp8_tensor(np.zeros((M, N), np.uint8), fmt)
+            kind = T.gemm_select_kernel(M, N, K, ad.data_ptr(), K, bd.data_ptr(), N, cd.data_ptr(), N, W.F16, fmt,
+                                        cid)
+            G.say(f"[case] fp8 every fp16 value fmt={fmt} alpha={alpha} cfg{cid} -> {KIND.get(kind, kind)}")
+            T.gemm_tensors(ad, bd, cd, config_id=cid, alpha=alpha)
+            torch.cuda.synchronize()
+            got = fp8_bits(cd)
+            assert (got == got[:, :1]).all()
+            # the product's value: alpha (a_i0 * 1 + the zero products): +0 for -0
+            vals = np.where(nan, 0.0, col.astype(np.float64))
+            want = oracle.encode_fp8(vals * alpha + 0.0, fmt)
+            g0 = got[:, 0]
+            assert np.array_equal(g0[~nan], want[~nan]), f"{int((g0[~nan] != want[~nan]).sum())} patterns differ"
+            mag = g0[nan] & 0x7F
+            if fmt == T.FP8_E4M3:
+                assert (mag == 0x7F).all()
+            else:
+                assert ((mag >> 2) == 0x1F).all() and ((mag & 3) != 0).all()
+
+
 def test_fp8_guard_band_and_k_zero():
     """Padding bytes after each row of C are untouched; K = 0 writes +0."""
     M, N, K = 200, 264, 256
