@@ -220,6 +220,19 @@ def test_kernel_choice_ring_path():
     assert _kernel(64, 64, 1 << 20, ldb=1 << 12, cid=6) in (T.KERNEL_GENERAL, T.KERNEL_TILED)
 
 
+def test_table_prefers_256_tiles_beyond_two_rounds_of_128_tiles():
+    """256 x 256 tiles when they fill the 256 CUs or when 128 x 128 tiles
+    would need three or more rounds; else 128 x 128 (or 64 x 128)."""
+    RING = T.KERNEL_RING
+    assert _kernel_t(3072, 3072, 3072, R_, R_, R_) == (RING, 0)      # 144 big tiles, 576 mid ones
+    assert _kernel_t(3000, 3000, 3000, R_, R_, R_) == (RING, 0)
+    assert _kernel_t(2048, 2048, 2048, R_, R_, R_) == (RING, 1)      # 64 big, 256 mid
+    assert _kernel_t(8192, 1024, 8192, R_, R_, R_) == (RING, 1)      # 128 big, 512 mid
+    assert _kernel_t(1024, 8192, 1024, R_, R_, R_) == (RING, 1)
+    assert _kernel_t(3072, 3072, 3072, C_, R_, R_) == (RING, 0)      # other layouts alike
+    assert _kernel_t(4096, 4096, 1024, R_, R_, R_) == (RING, 0)
+
+
 def test_ring_configs_report_their_ring_kernel():
     for cid in (0, 1, 8):
         c = T.gemm_config_info(cid)

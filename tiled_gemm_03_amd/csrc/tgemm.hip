@@ -303,6 +303,15 @@ int tuned_choice(const Problem& p) {
     return -1;
 }
 
+// Whether 256 x 256 tiles beat 128 x 128 ones: when they fill every CU, or
+// when 128 x 128 tiles would take three or more rounds of the 256 CUs (a
+// 256 x 256 tile does its four times the work in ~2.4 times the time of a
+// 128 x 128 one, measured: 3072^3 62 against 75 us; with two rounds the
+// smaller tile still wins, 8192 x 1024 x 8192 118 against 134 us).
+bool big_tiles_pay(int64_t M, int64_t N) {
+    return tiles_for(kConfigs[CFG_BIG], M, N) >= 256 || tiles_for(kConfigs[CFG_MID], M, N) > 512;
+}
+
 int table_choice(const Problem& p) {
     const int tuned = tuned_choice(p);
     if (tuned >= 0) return tuned;
@@ -315,13 +324,13 @@ int table_choice(const Problem& p) {
         return CFG_F32_TINY;
     }
     if (!row_row(p)) {
-        if (tiles_for(kConfigs[CFG_BIG], M, N) >= 256 && ring_applies(kConfigs[CFG_BIG], p)) return CFG_BIG;
+        if (big_tiles_pay(M, N) && ring_applies(kConfigs[CFG_BIG], p)) return CFG_BIG;
         // small products whose C the ring could store only through the fused
         // epilogue stay on the direct kernel
         if (ring_applies(kConfigs[CFG_MID], p) && (ring_plain_stores(p) || !small)) return CFG_MID;
         return CFG_DIRECT;
     }
-    if (tiles_for(kConfigs[CFG_BIG], M, N) >= 256) return CFG_BIG;
+    if (big_tiles_pay(M, N)) return CFG_BIG;
     // fewer 128 x 128 tiles than CUs: 64 x 128 tiles (twice the workgroups)
     if (tiles_for(kConfigs[CFG_MID], M, N) >= 64 && tiles_for(kConfigs[CFG_MID], M, N) < 256 &&
         ring_applies(kConfigs[CFG_RING_SMALL], p))
