@@ -239,6 +239,15 @@ int gemm_select_config(int64_t M, int64_t N, int64_t K,
                                   of 128 or above 128 (configurations 0, 1 and 8)           */
 #define TGEMM_KERNEL_DIRECT 3  /* operands straight from memory to registers, no LDS: small,
                                   ragged or unaligned products (configurations 6 and 7)     */
+#define TGEMM_KERNEL_RING_SPLITK 4 /* the ring kernel over slices of K (products with too few
+                                  output tiles for the CUs and a long K: configuration 8, or
+                                  1 for column-major operands), each slice's fp32 partial in
+                                  a workspace, then a second kernel that sums the slices in
+                                  a fixed order and applies the epilogue; the workspace
+                                  (slices x M x N rounded up to 4, fp32) comes from the
+                                  stream's memory pool (hipMallocAsync / hipFreeAsync on the
+                                  call's stream).  Only the table's choice (config_id -1)
+                                  splits; TGEMM_NO_SPLITK=1 in the environment turns it off */
 
 /* Host-side lookup only (no GPU call): which kernel gemm_ex(..., config_id)
  * would launch for these arguments (config_id -1: the table's choice), as a
@@ -257,6 +266,16 @@ int gemm_select_kernel_t(int64_t M, int64_t N, int64_t K,
                          const void* B, int64_t ldb, int layout_b,
                          const void* C, int64_t ldc, int layout_c,
                          int in_dtype, int out_dtype, int config_id, int* config_out);
+
+/* Host-side lookup only (no GPU call): the number of K slices gemm_t with
+ * these arguments and the table's choice would run (1: none; see
+ * TGEMM_KERNEL_RING_SPLITK), or a negative TGEMM_ERR_* if the call would be
+ * rejected. */
+int gemm_split_count_t(int64_t M, int64_t N, int64_t K,
+                       const void* A, int64_t lda, int layout_a,
+                       const void* B, int64_t ldb, int layout_b,
+                       const void* C, int64_t ldc, int layout_c,
+                       int in_dtype, int out_dtype);
 
 /* Host-side copy of the workgroup -> output-tile map the kernels use (no GPU
  * call), for checking that it is a bijection: workgroup `bid` of a grid of

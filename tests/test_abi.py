@@ -233,6 +233,47 @@ def test_table_prefers_256_tiles_beyond_two_rounds_of_128_tiles():
     assert _kernel_t(4096, 4096, 1024, R_, R_, R_) == (RING, 0)
 
 
+def _splits(M, N, K, la=T.ROW_MAJOR, lb=T.ROW_MAJOR, lc=T.ROW_MAJOR, lda=None, ldb=None, ldc=None, in_dt=T.F16,
+            out_dt=T.F16):
+    row = T.ROW_MAJOR
+    lda = (K if la == row else M) if lda is None else lda
+    ldb = (N if lb == row else K) if ldb is None else ldb
+    ldc = (N if lc == row else M) if ldc is None else ldc
+    return T.gemm_split_count_t(M, N, K, FAKE, lda, la, FAKE + (1 << 36), ldb, lb, FAKE + (2 << 36), ldc, lc, in_dt,
+                                out_dt)
+
+
+def test_split_k_choice():
+    """Products whose ring tiles leave most CUs idle (128 or fewer) and
+    whose K is long (4096 or more) run in slices of K: about as many
+    workgroups as the CUs hold at once (512 for these tiles), slices of at
+    least 256 of K that are whole ring steps (the last one may carry the K
+    tail), at most 32.  Never for a forced configuration, N % 4 != 0,
+    unaligned operand rows, fp32 inputs or short K."""
+    SPLIT, RING = T.KERNEL_RING_SPLITK, T.KERNEL_RING
+    R_, C_ = T.ROW_MAJOR, T.COL_MAJOR
+    assert _kernel_t(512, 512, 16384, R_, R_, R_) == (SPLIT, 8)        # 32 tiles of 64 x 128
+    assert _splits(512, 512, 16384) == 16
+    assert _splits(256, 256, 65536) == 32
+    assert _splits(1024, 1024, 8192) == 4                              # 128 tiles: 512 workgroups
+    assert _splits(32, 4096, 4096) == 16
+    assert _splits(1024, 512, 2048) == 1                               # K below 4096
+    assert _kernel_t(32, 4096, 4096, R_, R_, R_) == (SPLIT, 8)
+    assert _splits(512, 512, 16384 + 100, lda=16384 + 128) > 1         # the last slice carries the tail
+    assert _kernel_t(512, 512, 16384, R_, R_, R_, cid=8) == (RING, 8)  # forced: no slices
+    assert _splits(512, 512, 1024) == 1                                # short K
+    assert _splits(512, 510, 16384) == 1                               # N % 4 != 0
+    assert _splits(512, 512, 16384, lda=16384 + 4) == 1                # rows not whole 16-byte chunks
+    assert _splits(512, 512, 16384, in_dt=T.F32, out_dt=T.F32) == 1
+    assert _splits(4096, 4096, 4096) == 1                              # enough tiles
+    assert _kernel_t(512, 512, 16384, C_, R_, R_) == (SPLIT, 1)       # column-major A: 128 x 128 tiles
+    for fmt in (T.F32, T.BF16):
+        assert _kernel_t(512, 512, 16384, R_, R_, R_, in_dt=T.BF16, out_dt=fmt) == (SPLIT, 8)
+    assert _kernel_t(512, 512, 16384, R_, R_, R_, out_dt=T.FP8_E4M3) == (SPLIT, 8)
+    # the workspace stays within 256 MiB: fewer slices
+    assert _splits(8192, 8192 // 128, 1 << 20, ldb=64) >= 1
+
+
 def test_ring_configs_report_their_ring_kernel():
     for cid in (0, 1, 8):
         c = T.gemm_config_info(cid)
@@ -412,7 +453,9 @@ def test_kernel_choice_for_layouts():
                                   T.F16, T.F16, 0) == (DIRECT, 6)
     # a column-major C swaps the roles of A and B: its 128 rows become the
     # N of the row-major product (128 x 128 tiles)
-    assert _kernel_t(128, 8192, 8192, R_, R_, C_)[0] == RING
+    # (64 of them, K = 8192: in slices of K)
+    assert _kernel_t(128, 8192, 8192, R_, R_, C_) == (T.KERNEL_RING_SPLITK, 1)
+    assert _kernel_t(128, 8192, 1024, R_, R_, C_) == (RING, 1)
 
 
 def test_fused_epilogue_arguments_are_checked():

@@ -29,7 +29,8 @@ ERR_DIM, ERR_NULL, ERR_LD, ERR_DTYPE, ERR_ALIAS, ERR_CONFIG, ERR_LAYOUT, ERR_EPI
 ERR_HEAD_DIM = -9
 
 EXPORTED = ["gemm", "gemm_ex", "gemm_t", "gemm_fused", "gemm_strerror", "gemm_num_configs", "gemm_config_info",
-            "gemm_select_config", "gemm_select_kernel", "gemm_select_kernel_t", "gemm_tile_map", "gemm_version",
+            "gemm_select_config", "gemm_select_kernel", "gemm_select_kernel_t", "gemm_split_count_t",
+            "gemm_tile_map", "gemm_version",
             "attention_fwd", "attention_waves"]
 
 # operand layouts (gemm_t)
@@ -40,7 +41,7 @@ ACT_NONE, ACT_RELU, ACT_GELU, ACT_GELU_TANH, ACT_SILU = 0, 1, 2, 3, 4
 BIAS_NONE, BIAS_ROW, BIAS_COL = 0, 1, 2
 
 # gemm_select_kernel results
-KERNEL_GENERAL, KERNEL_TILED, KERNEL_RING, KERNEL_DIRECT = 0, 1, 2, 3
+KERNEL_GENERAL, KERNEL_TILED, KERNEL_RING, KERNEL_DIRECT, KERNEL_RING_SPLITK = 0, 1, 2, 3, 4
 
 
 class ConfigInfo(ctypes.Structure):
@@ -101,6 +102,8 @@ def lib():
     L.gemm_fused.argtypes = [i64, i64, i64, p, i64, i, p, i64, i, p, i64, i, i, i, ctypes.POINTER(Epilogue), p, i]
     L.gemm_select_kernel_t.restype = i
     L.gemm_select_kernel_t.argtypes = [i64, i64, i64, p, i64, i, p, i64, i, p, i64, i, i, i, i, ctypes.POINTER(i)]
+    L.gemm_split_count_t.restype = i
+    L.gemm_split_count_t.argtypes = [i64, i64, i64, p, i64, i, p, i64, i, p, i64, i, i, i]
     L.gemm_select_kernel.restype = i
     L.gemm_select_kernel.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, i, i, i]
     L.gemm_tile_map.restype = i
@@ -165,6 +168,12 @@ def gemm_select_kernel_t(M, N, K, A, lda, layout_a, B, ldb, layout_b, C, ldc, la
     k = lib().gemm_select_kernel_t(M, N, K, A, lda, layout_a, B, ldb, layout_b, C, ldc, layout_c, in_dtype,
                                    out_dtype, config_id, ctypes.byref(cfg))
     return k, cfg.value
+
+
+def gemm_split_count_t(M, N, K, A, lda, layout_a, B, ldb, layout_b, C, ldc, layout_c, in_dtype, out_dtype):
+    """K slices the table's choice would run (1: none), or a negative error."""
+    return lib().gemm_split_count_t(M, N, K, A, lda, layout_a, B, ldb, layout_b, C, ldc, layout_c, in_dtype,
+                                    out_dtype)
 
 
 def gemm_select_kernel(M, N, K, A, lda, B, ldb, C, ldc, in_dtype, out_dtype, config_id=-1):

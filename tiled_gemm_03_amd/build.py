@@ -21,7 +21,7 @@ SOURCES = [os.path.join(CSRC, f) for f in (
     "k_tiled_big_fused.hip", "k_ring_big_fused.hip", "k_ring_mid_fused.hip", "k_direct_fused.hip",
     "k_ring_big_kt.hip", "k_ring_mid_kt.hip", "k_ring_big_fused_kt.hip", "k_ring_mid_fused_kt.hip",
     "k_ring_big_fp8.hip", "k_ring_big_fp8_kt.hip", "k_ring_mid_fp8.hip", "k_ring_small_fp8.hip", "k_direct_fp8.hip",
-    "attention.hip")]
+    "k_splitk.hip", "attention.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

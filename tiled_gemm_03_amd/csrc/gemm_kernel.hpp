@@ -84,6 +84,11 @@ struct GemmArgs {
     // rounding (0, or 2 when the last element would otherwise be dropped;
     // the host checks that they lie in the last element's page)
     int range_pad_a, range_pad_b;
+    // split-K (ring kernels, plain fp32 output): splits > 1 slices of K of
+    // k_split elements (the last one the rest), slice s written to C plus
+    // s * split_stride bytes
+    int splits, k_split;
+    int64_t split_stride;
 };
 
 enum { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU = 2, ACT_GELU_TANH = 3, ACT_SILU = 4 };

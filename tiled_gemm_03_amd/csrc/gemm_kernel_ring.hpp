@@ -253,12 +253,29 @@ void gemm_kernel_ring(GemmArgs p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / T::WN, wn = wave % T::WN;
 
+    // split-K (p.splits > 1, plain epilogue only): workgroup g takes slice
+    // s = g / tiles of K, [s k_split, min(K, (s + 1) k_split)), and writes
+    // its fp32 partial tile to slice s of the workspace that C points to
+    int bid = blockIdx.x;
+    int K = p.K;
+    const char* A = p.A;
+    const char* B = p.B;
+    char* C = p.C;
+    const int64_t lda = p.lda, ldb = p.ldb;
+    if (!EPI && p.splits > 1) {
+        const int tiles = p.tiles_m * p.tiles_n;
+        const int s = bid / tiles;
+        bid -= s * tiles;
+        const int k0 = s * p.k_split;
+        K = p.K - k0 < p.k_split ? p.K - k0 : p.k_split;
+        A += (OA::KC ? (int64_t)k0 : (int64_t)k0 * lda) * 2;
+        B += (OB_::KC ? (int64_t)k0 : (int64_t)k0 * ldb) * 2;
+        C += (int64_t)s * p.split_stride;
+    }
     // a1: which tile
     int tm, tn;
-    tile_of(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+    tile_of(bid, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
     const int m0 = tm * T::BM, n0 = tn * T::BN;
-    const int K = p.K;
-    const int64_t lda = p.lda, ldb = p.ldb;
     // 1: XOR-swizzled LDS layouts; 0: plain LDS rows (kept for measuring
     // bank conflicts against the swizzle)
     const int swz = p.swz_mask != 0 ? 1 : 0;
@@ -299,8 +316,8 @@ void gemm_kernel_ring(GemmArgs p) {
         else                  // element (o, k) at k * ld + o
             return ((int64_t)(K - 1) * ld + outer - outer0) * 2;
     };
-    const char* const a_start = operand_start(OA{}, p.A, lda, m0);
-    const char* const b_start = operand_start(OB_{}, p.B, ldb, n0);
+    const char* const a_start = operand_start(OA{}, A, lda, m0);
+    const char* const b_start = operand_start(OB_{}, B, ldb, n0);
     const int64_t a_bytes = operand_bytes(OA{}, lda, m0, p.M);
     const int64_t b_bytes = operand_bytes(OB_{}, ldb, n0, p.N);
     const i32x4 rs_a = make_rsrc(a_start, a_bytes, p.range_pad_a);
@@ -601,7 +618,7 @@ void gemm_kernel_ring(GemmArgs p) {
         const int row = m0 + wm * T::WTM + 16 * i + i16;
         const int col = n0 + wn * T::WTN + 16 * j + 4 * q;
         if (row < p.M && col < p.N)
-            store4<OUT>(p.C + ((int64_t)row * ldc + col) * OB, acc[i][j][0], acc[i][j][1], acc[i][j][2],
+            store4<OUT>(C + ((int64_t)row * ldc + col) * OB, acc[i][j][0], acc[i][j][1], acc[i][j][2],
                         acc[i][j][3], true);
     });
 }

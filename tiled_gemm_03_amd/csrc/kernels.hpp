@@ -51,6 +51,13 @@ KernelFn ring_kernel_mid(int in, int out, int la, int lb, bool epi, bool kt);
 KernelFn ring_kernel_small(int in, int out, int la, int lb, bool epi, bool kt);
 KernelFn ring_kernel_small_fused(int in, int out, int la, int lb, bool kt);
 
+// The sum of the split-K slices with the call's epilogue, for output type
+// out (DT_*): k_splitk.hip.  Arguments: the call's GemmArgs (C, ldc and the
+// epilogue of the call), the workspace, its row stride in floats (a multiple
+// of 4), floats per slice, and the number of slices.
+typedef void (*SplitkReduceFn)(GemmArgs, const float*, int64_t, int64_t, int);
+SplitkReduceFn splitk_reduce_kernel_for(int out);
+
 // Direct kernel for (in, out), the layouts of A and B, and whether each
 // operand takes 16-byte loads.  k_direct.hip.
 KernelFn direct_kernel(int in, int out, int la, int lb, bool va, bool vb, bool epi);

@@ -7,6 +7,7 @@
 // layout), compiled in units of their own (k_*.hip) behind the selectors of
 // kernels.hpp; the ABI is declared (and documented) in include/tgemm.h.
 #include <hip/hip_runtime.h>
+#include <mutex>
 #include <stdint.h>
 #include <stdlib.h>
 
@@ -79,6 +80,7 @@ struct Tuning {
     int group_m = 4;
     bool swizzle = true;
     bool direct_lds = true;
+    bool split_k = true;
     Tuning() {
         if (const char* s = getenv("TGEMM_GROUP_M")) {
             const int g = atoi(s);
@@ -86,6 +88,7 @@ struct Tuning {
         }
         if (const char* s = getenv("TGEMM_NO_SWIZZLE")) swizzle = !(s[0] == '1');
         if (const char* s = getenv("TGEMM_NO_DL")) direct_lds = !(s[0] == '1');
+        if (const char* s = getenv("TGEMM_NO_SPLITK")) split_k = !(s[0] == '1');
     }
 };
 const Tuning& tuning() {
@@ -303,6 +306,45 @@ int tuned_choice(const Problem& p) {
     return -1;
 }
 
+// Split-K: slices of K for a ring configuration whose tiles leave CUs idle
+// (128 workgroups or fewer on the 256 CUs) when K is long (4096 or more;
+// at 2048 the second kernel and the workspace cost more than the slices
+// gain: 1024 x 512 x 2048 28 against 26 us).  Each slice is
+// a multiple of the ring's K step (the last one takes the rest, with the K
+// tail when K is not a multiple), at least 512 long, and the slices bring
+// the workgroups to about 256; the fp32 partials go through a workspace of
+// splits x M x roundup(N, 4) floats (at most 256 MiB).  Needs the plain
+// epilogue's whole groups (N % 4 == 0) and rows of whole 16-byte chunks.
+// Returns the slice count (1: no split) and the slice length.
+#ifndef SPLIT_MIN_K
+#define SPLIT_MIN_K 256
+#endif
+int split_count(const ConfigEntry& c, const Problem& p, int& k_split) {
+    k_split = (int)p.K;
+    if (!tuning().split_k || c.ring == nullptr || p.N % 4 != 0 || !loads_aligned(c, p)) return 1;
+    const int64_t tiles = tiles_for(c, p.M, p.N);
+    if (tiles > 128 || p.K < 4096) return 1;
+    const int64_t km = c.ring_k_mult;
+    // workgroups the CUs hold at once: two per CU where the ring's LDS allows
+    const int64_t slots = 256 * (c.ring_lds <= 80 * 1024 ? 2 : 1);
+    int64_t s = slots / tiles;
+    if (s > p.K / SPLIT_MIN_K) s = p.K / SPLIT_MIN_K;
+    if (s > 32) s = 32;
+    const int64_t ldw = (p.N + 3) / 4 * 4;
+    while (s > 1 && s * p.M * ldw * 4 > ((int64_t)256 << 20)) --s;
+    for (; s > 1; --s) {
+        const int64_t len = ((p.K + s - 1) / s + km - 1) / km * km;
+        const int64_t n = (p.K + len - 1) / len;
+        const int64_t last = p.K - (n - 1) * len;
+        // every slice a whole number of K steps or above one (the K tail)
+        if (n > 1 && (last % km == 0 || last > km)) {
+            k_split = (int)len;
+            return (int)n;
+        }
+    }
+    return 1;
+}
+
 // Whether 256 x 256 tiles beat 128 x 128 ones: when they fill every CU, or
 // when 128 x 128 tiles would take three or more rounds of the 256 CUs (a
 // 256 x 256 tile does its four times the work in ~2.4 times the time of a
@@ -326,8 +368,12 @@ int table_choice(const Problem& p) {
     if (!row_row(p)) {
         if (big_tiles_pay(M, N) && ring_applies(kConfigs[CFG_BIG], p)) return CFG_BIG;
         // small products whose C the ring could store only through the fused
-        // epilogue stay on the direct kernel
-        if (ring_applies(kConfigs[CFG_MID], p) && (ring_plain_stores(p) || !small)) return CFG_MID;
+        // epilogue stay on the direct kernel, unless K is long enough for
+        // slices of K
+        int k_split;
+        if (ring_applies(kConfigs[CFG_MID], p) &&
+            (ring_plain_stores(p) || !small || split_count(kConfigs[CFG_MID], p, k_split) > 1))
+            return CFG_MID;
         return CFG_DIRECT;
     }
     if (big_tiles_pay(M, N)) return CFG_BIG;
@@ -337,6 +383,10 @@ int table_choice(const Problem& p) {
         return CFG_RING_SMALL;
     if (tiles_for(kConfigs[CFG_MID], M, N) >= 128 && ring_applies(kConfigs[CFG_MID], p)) return CFG_MID;
     if (tiles_for(kConfigs[CFG_MID], M, N) >= 256) return CFG_MID;
+    // few tiles and a long K: the 64 x 128 ring in slices of K
+    int k_split;
+    if (ring_applies(kConfigs[CFG_RING_SMALL], p) && split_count(kConfigs[CFG_RING_SMALL], p, k_split) > 1)
+        return CFG_RING_SMALL;
     if (tiles_for(kConfigs[CFG_SMALL], M, N) >= 256) return CFG_SMALL;
     if (small && !tiled_fast(kConfigs[CFG_TINY], p)) return CFG_DIRECT;
     return CFG_TINY;
@@ -349,6 +399,8 @@ struct Plan {
     int config;
     int kind;  // TGEMM_KERNEL_*
     KernelFn fn;
+    int splits = 1, k_split = 0;          // split-K (kind TGEMM_KERNEL_RING_SPLITK)
+    SplitkReduceFn reduce = nullptr;      // the sum of the slices
 };
 
 int plan_direct(const Problem& p, Plan& plan) {
@@ -387,6 +439,21 @@ int make_plan(const Problem& p, int config_id, Plan& plan) {
         !ring_applies(kConfigs[plan.config], p))
         plan.config = CFG_MID;
     const ConfigEntry& c = kConfigs[plan.config];
+    if (!c.direct && ring_applies(c, p) && config_id < 0) {
+        int k_split;
+        const int splits = split_count(c, p, k_split);
+        if (splits > 1) {
+            // fp32 partials of the slices (plain epilogue), then their sum
+            // with the call's epilogue and output type
+            plan.kind = TGEMM_KERNEL_RING_SPLITK;
+            plan.splits = splits;
+            plan.k_split = k_split;
+            plan.fn = c.ring(p.in, DT_F32, p.la, p.lb, false, p.K % c.ring_k_mult != 0);
+            plan.reduce = splitk_reduce_kernel_for(kernel_out(p.out));
+            if (plan.fn == nullptr || plan.reduce == nullptr) return TGEMM_ERR_DTYPE;
+            return ceil_div(p.M, c.bm) * ceil_div(p.N, c.bn) * splits > 0x7fffffff ? TGEMM_ERR_DIM : TGEMM_OK;
+        }
+    }
     if (!c.direct && ring_applies(c, p)) {
         plan.kind = TGEMM_KERNEL_RING;
         // 8-bit outputs are written by the fused epilogue's kernels
@@ -441,6 +508,81 @@ int make_problem(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, in
     return TGEMM_OK;
 }
 
+// The library's memory pool of the current device, for split-K workspaces:
+// stream-ordered allocations (a call on one stream never shares its
+// workspace with a call on another), and memory kept in the pool between
+// calls rather than returned to the driver at each synchronisation (the
+// default pool's release threshold is 0).
+hipMemPool_t workspace_pool(hipError_t& e) {
+    static std::mutex mu;
+    static hipMemPool_t pools[64] = {};
+    int dev = 0;
+    e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (pools[dev] == nullptr) {
+        hipMemPoolProps props = {};
+        props.allocType = hipMemAllocationTypePinned;
+        props.location.type = hipMemLocationTypeDevice;
+        props.location.id = dev;
+        hipMemPool_t pool = nullptr;
+        e = hipMemPoolCreate(&pool, &props);
+        if (e != hipSuccess) return nullptr;
+        uint64_t keep = UINT64_MAX;
+        e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+        if (e != hipSuccess) return nullptr;
+        pools[dev] = pool;
+    }
+    return pools[dev];
+}
+
+// Split-K: the slices' fp32 partials into a workspace taken from the
+// library's pool in the call's stream order, then their sum with the call's
+// epilogue into C; the workspace goes back to the pool after the second
+// kernel, in stream order.
+int run_split(const Problem& p, const Plan& plan, const ConfigEntry& c, const GemmArgs& args, void* stream) {
+    const hipStream_t st = (hipStream_t)stream;
+    const int64_t ldw = (p.N + 3) / 4 * 4, slice = p.M * ldw;
+    float* w = nullptr;
+    hipError_t e = hipSuccess;
+    hipMemPool_t pool = workspace_pool(e);
+    if (pool == nullptr) return (int)e;
+    e = hipMallocFromPoolAsync((void**)&w, (size_t)(plan.splits * slice * 4), pool, st);
+    if (e != hipSuccess) return (int)e;
+    GemmArgs pa = args;
+    pa.C = (char*)w;
+    pa.ldc = ldw;
+    pa.epi = 0;
+    pa.vec_c = 1;
+    pa.range_pad_a = pa.range_pad_b = 0;
+    pa.splits = plan.splits;
+    pa.k_split = plan.k_split;
+    pa.split_stride = slice * 4;
+    const int64_t tiles = (int64_t)pa.tiles_m * pa.tiles_n;
+    void* kargs[] = {&pa};
+    e = hipLaunchKernel((const void*)plan.fn, dim3((unsigned)(tiles * plan.splits)), dim3(c.threads), kargs, 0, st);
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e == hipSuccess) {
+        GemmArgs ra = args;
+        if (!p.ep.on) {  // the identity epilogue: C := the sum
+            ra.alpha = 1.f;
+            ra.beta = 0.f;
+            ra.bias_kind = TGEMM_BIAS_NONE;
+            ra.act = ACT_NONE;
+        }
+        const int64_t groups = p.M * ((p.N + 3) / 4);
+        const float* wc = w;
+        int64_t ldw_ = ldw, slice_ = slice;
+        int splits = plan.splits;
+        void* rargs[] = {&ra, &wc, &ldw_, &slice_, &splits};
+        e = hipLaunchKernel((const void*)plan.reduce, dim3((unsigned)((groups + 255) / 256)), dim3(256), rargs, 0, st);
+        if (e == hipSuccess) e = hipGetLastError();
+    }
+    const hipError_t f = hipFreeAsync(w, st);
+    if (e == hipSuccess) e = f;
+    return e == hipSuccess ? TGEMM_OK : (int)e;
+}
+
 int run(const Problem& p, void* stream, int config_id) {
     Plan plan;
     const int v = make_plan(p, config_id, plan);
@@ -461,7 +603,8 @@ int run(const Problem& p, void* stream, int config_id) {
     args.tiles_n = (int)ceil_div(p.N, c.bn);
     args.group_m = tuning().group_m;
     args.swz_mask = tuning().swizzle ? c.cpr - 1 : 0;
-    if (plan.kind == TGEMM_KERNEL_RING) args.swz_mask = tuning().swizzle ? 1 : 0;
+    if (plan.kind == TGEMM_KERNEL_RING || plan.kind == TGEMM_KERNEL_RING_SPLITK)
+        args.swz_mask = tuning().swizzle ? 1 : 0;
     args.vec_ab = loads_aligned(c, p);
     args.vec_c = stores_aligned(p);
     args.epi = p.ep.on ? 1 : 0;
@@ -472,11 +615,15 @@ int run(const Problem& p, void* stream, int config_id) {
     args.bias_dt = p.ep.bias_dt;
     args.act = p.ep.act;
     args.fp8_e5m2 = p.out == TGEMM_FP8_E5M2 ? 1 : 0;
+    args.splits = 1;
+    args.k_split = (int)p.K;
+    args.split_stride = 0;
     const bool ring = plan.kind == TGEMM_KERNEL_RING;
     args.range_pad_a = ring && ring_pad_a(p) > 0 ? ring_pad_a(p) : 0;
     args.range_pad_b = ring && ring_pad_b(p) > 0 ? ring_pad_b(p) : 0;
     const int64_t grid = (int64_t)args.tiles_m * args.tiles_n;
 
+    if (plan.kind == TGEMM_KERNEL_RING_SPLITK) return run_split(p, plan, c, args, stream);
     void* kargs[] = {&args};
     hipError_t e = hipLaunchKernel((const void*)plan.fn, dim3((unsigned)grid), dim3(c.threads), kargs, 0,
                                    (hipStream_t)stream);
@@ -602,6 +749,18 @@ int gemm_select_kernel_t(int64_t M, int64_t N, int64_t K, const void* A, int64_t
     if (v != TGEMM_OK) return v;
     if (config_out != nullptr) *config_out = plan.config;
     return plan.kind;
+}
+
+int gemm_split_count_t(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int layout_a, const void* B,
+                       int64_t ldb, int layout_b, const void* C, int64_t ldc, int layout_c, int in_dtype,
+                       int out_dtype) {
+    Problem p;
+    int v = make_problem(M, N, K, A, lda, layout_a, B, ldb, layout_b, (void*)C, ldc, layout_c, in_dtype, out_dtype, p);
+    if (v != TGEMM_OK) return v;
+    Plan plan;
+    v = make_plan(p, -1, plan);
+    if (v != TGEMM_OK) return v;
+    return plan.splits;
 }
 
 int gemm_tile_map(int bid, int tiles_m, int tiles_n, int group_m, int* tm, int* tn) {
