@@ -82,6 +82,8 @@ extern "C" {
 #define TGEMM_ERR_EPILOGUE (-8)    /* gemm_fused: bad activation, bias kind or
                                       bias type, or a bias kind without bias  */
 #define TGEMM_ERR_HEAD_DIM (-9)    /* attention_fwd: head_dim not 64 or 128     */
+#define TGEMM_ERR_SCRATCH (-10)    /* gemm_fused_noalloc: the call's split-K
+                                      workspace exceeds the fixed scratch  */
 
 /* Operand layouts (gemm_t): the row-major default and the column-major option
  * of page "TileLang实战：用Python DSL自动生成高性能GPU计算内核", §5.1. */
@@ -193,6 +195,28 @@ int gemm_fused(int64_t M, int64_t N, int64_t K,
                const void* B, int64_t ldb, int layout_b,
                void* C, int64_t ldc, int layout_c,
                int in_dtype, int out_dtype, const tgemm_epilogue* epilogue, void* stream, int config_id);
+
+/*
+ * gemm_fused_noalloc: gemm_fused for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  The same plan, kernels and results as gemm_fused with
+ * the same arguments, except that a split-K plan (TGEMM_KERNEL_RING_SPLITK)
+ * keeps its fp32 partials in the library's own fixed device array of 32 MiB
+ * (one per GPU, held until the process ends) rather than in memory from the
+ * library's pool: the call allocates and frees nothing.  Every call on a GPU
+ * uses that GPU's one array, so calls that overlap on one GPU (on different
+ * streams, or concurrently from several host threads) race; calls on one
+ * stream are ordered and safe.  The array keeps the last call's contents
+ * (nothing in it needs to start at zero).  Errors as gemm_fused, plus
+ * TGEMM_ERR_SCRATCH if the call's workspace would exceed 32 MiB (no split
+ * plan of the library's table does: at most 512 partial tiles of 128 x 128).
+ */
+int gemm_fused_noalloc(int64_t M, int64_t N, int64_t K,
+                       const void* A, int64_t lda, int layout_a,
+                       const void* B, int64_t ldb, int layout_b,
+                       void* C, int64_t ldc, int layout_c,
+                       int in_dtype, int out_dtype,
+                       const tgemm_epilogue* epilogue, void* stream, int config_id);
 
 /* Human-readable text for a return code of gemm / gemm_ex / gemm_t /
  * gemm_fused (never NULL; the string is static). */

@@ -27,8 +27,10 @@ F32, F16, BF16, FP8_E4M3, FP8_E5M2 = 0, 1, 2, 3, 4
 OK = 0
 ERR_DIM, ERR_NULL, ERR_LD, ERR_DTYPE, ERR_ALIAS, ERR_CONFIG, ERR_LAYOUT, ERR_EPILOGUE = -1, -2, -3, -4, -5, -6, -7, -8
 ERR_HEAD_DIM = -9
+ERR_SCRATCH = -10
 
-EXPORTED = ["gemm", "gemm_ex", "gemm_t", "gemm_fused", "gemm_strerror", "gemm_num_configs", "gemm_config_info",
+EXPORTED = ["gemm", "gemm_ex", "gemm_t", "gemm_fused", "gemm_fused_noalloc", "gemm_strerror", "gemm_num_configs",
+            "gemm_config_info",
             "gemm_select_config", "gemm_select_kernel", "gemm_select_kernel_t", "gemm_split_count_t",
             "gemm_tile_map", "gemm_version",
             "attention_fwd", "attention_waves"]
@@ -98,6 +100,9 @@ def lib():
     L.gemm_select_config.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, i, i]
     L.gemm_t.restype = i
     L.gemm_t.argtypes = [i64, i64, i64, p, i64, i, p, i64, i, p, i64, i, i, i, p, i]
+    L.gemm_fused_noalloc.restype = i
+    L.gemm_fused_noalloc.argtypes = [i64, i64, i64, p, i64, i, p, i64, i, p, i64, i, i, i, ctypes.POINTER(Epilogue), p,
+                                     i]
     L.gemm_fused.restype = i
     L.gemm_fused.argtypes = [i64, i64, i64, p, i64, i, p, i64, i, p, i64, i, i, i, ctypes.POINTER(Epilogue), p, i]
     L.gemm_select_kernel_t.restype = i
@@ -159,6 +164,15 @@ def gemm_fused(M, N, K, A, lda, layout_a, B, ldb, layout_b, C, ldc, layout_c, in
     ep = ctypes.byref(epilogue) if epilogue is not None else None
     return lib().gemm_fused(M, N, K, A, lda, layout_a, B, ldb, layout_b, C, ldc, layout_c, in_dtype, out_dtype, ep,
                             stream, config_id)
+
+
+def gemm_fused_noalloc(M, N, K, A, lda, layout_a, B, ldb, layout_b, C, ldc, layout_c, in_dtype, out_dtype,
+                       epilogue=None, stream=None, config_id=-1):
+    """gemm_fused that allocates nothing (the split-K workspace in the
+    library's fixed scratch; calls overlapping on one GPU race)."""
+    ep = ctypes.byref(epilogue) if epilogue is not None else None
+    return lib().gemm_fused_noalloc(M, N, K, A, lda, layout_a, B, ldb, layout_b, C, ldc, layout_c, in_dtype,
+                                    out_dtype, ep, stream, config_id)
 
 
 def gemm_select_kernel_t(M, N, K, A, lda, layout_a, B, ldb, layout_b, C, ldc, layout_c, in_dtype, out_dtype,

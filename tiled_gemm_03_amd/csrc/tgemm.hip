@@ -508,6 +508,37 @@ int make_problem(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, in
     return TGEMM_OK;
 }
 
+// The scratch of the allocation-free entry point (gemm_fused_noalloc): the
+// split-K workspace as a file-scope device array, which every GPU that loads
+// the library holds until the process ends, each its own copy.  32 MiB: the
+// largest workspace a split plan takes (slices x tiles stay within the 512
+// workgroups that the CUs hold at once, each partial tile at most 128 x 128
+// fp32 values).  Host code uses its device address (scratch_address), never
+// the array's name.
+constexpr int64_t kScratchFloats = (int64_t)8 << 20;
+static __device__ __align__(256) float scratch[kScratchFloats];
+
+// This GPU's address of `scratch`: looked up once per device, with that
+// device current, and kept.
+int scratch_address(float** out) {
+    static std::mutex mu;
+    static float* addr[64] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return (int)e;
+    if (dev < 0 || dev >= 64) return TGEMM_ERR_SCRATCH;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return (int)e;
+        if (ptr == nullptr) return TGEMM_ERR_SCRATCH;
+        addr[dev] = (float*)ptr;
+    }
+    *out = addr[dev];
+    return TGEMM_OK;
+}
+
 // The library's memory pool of the current device, for split-K workspaces:
 // stream-ordered allocations (a call on one stream never shares its
 // workspace with a call on another), and memory kept in the pool between
@@ -540,15 +571,22 @@ hipMemPool_t workspace_pool(hipError_t& e) {
 // library's pool in the call's stream order, then their sum with the call's
 // epilogue into C; the workspace goes back to the pool after the second
 // kernel, in stream order.
-int run_split(const Problem& p, const Plan& plan, const ConfigEntry& c, const GemmArgs& args, void* stream) {
+// With `fixed` (the allocation-free entry point) the workspace is that
+// device array instead, and nothing is allocated or freed.
+int run_split(const Problem& p, const Plan& plan, const ConfigEntry& c, const GemmArgs& args, void* stream,
+              float* fixed) {
     const hipStream_t st = (hipStream_t)stream;
     const int64_t ldw = (p.N + 3) / 4 * 4, slice = p.M * ldw;
-    float* w = nullptr;
+    float* w = fixed;
     hipError_t e = hipSuccess;
-    hipMemPool_t pool = workspace_pool(e);
-    if (pool == nullptr) return (int)e;
-    e = hipMallocFromPoolAsync((void**)&w, (size_t)(plan.splits * slice * 4), pool, st);
-    if (e != hipSuccess) return (int)e;
+    if (fixed != nullptr) {
+        if (plan.splits * slice > kScratchFloats) return TGEMM_ERR_SCRATCH;
+    } else {
+        hipMemPool_t pool = workspace_pool(e);
+        if (pool == nullptr) return (int)e;
+        e = hipMallocFromPoolAsync((void**)&w, (size_t)(plan.splits * slice * 4), pool, st);
+        if (e != hipSuccess) return (int)e;
+    }
     GemmArgs pa = args;
     pa.C = (char*)w;
     pa.ldc = ldw;
@@ -578,12 +616,14 @@ int run_split(const Problem& p, const Plan& plan, const ConfigEntry& c, const Ge
         e = hipLaunchKernel((const void*)plan.reduce, dim3((unsigned)((groups + 255) / 256)), dim3(256), rargs, 0, st);
         if (e == hipSuccess) e = hipGetLastError();
     }
-    const hipError_t f = hipFreeAsync(w, st);
-    if (e == hipSuccess) e = f;
+    if (fixed == nullptr) {
+        const hipError_t f = hipFreeAsync(w, st);
+        if (e == hipSuccess) e = f;
+    }
     return e == hipSuccess ? TGEMM_OK : (int)e;
 }
 
-int run(const Problem& p, void* stream, int config_id) {
+int run(const Problem& p, void* stream, int config_id, float* fixed = nullptr) {
     Plan plan;
     const int v = make_plan(p, config_id, plan);
     if (v != TGEMM_OK || plan.fn == nullptr) return v;
@@ -623,7 +663,7 @@ int run(const Problem& p, void* stream, int config_id) {
     args.range_pad_b = ring && ring_pad_b(p) > 0 ? ring_pad_b(p) : 0;
     const int64_t grid = (int64_t)args.tiles_m * args.tiles_n;
 
-    if (plan.kind == TGEMM_KERNEL_RING_SPLITK) return run_split(p, plan, c, args, stream);
+    if (plan.kind == TGEMM_KERNEL_RING_SPLITK) return run_split(p, plan, c, args, stream, fixed);
     void* kargs[] = {&args};
     hipError_t e = hipLaunchKernel((const void*)plan.fn, dim3((unsigned)grid), dim3(c.threads), kargs, 0,
                                    (hipStream_t)stream);
@@ -666,6 +706,19 @@ int gemm_fused(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int 
     return run(p, stream, config_id);
 }
 
+int gemm_fused_noalloc(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int layout_a, const void* B,
+                       int64_t ldb, int layout_b, void* C, int64_t ldc, int layout_c, int in_dtype, int out_dtype,
+                       const tgemm_epilogue* epilogue, void* stream, int config_id) {
+    Problem p;
+    const int v = make_problem(M, N, K, A, lda, layout_a, B, ldb, layout_b, C, ldc, layout_c, in_dtype, out_dtype, p,
+                               epilogue);
+    if (v != TGEMM_OK) return v;
+    float* fixed = nullptr;
+    const int a = scratch_address(&fixed);
+    if (a != TGEMM_OK) return a;
+    return run(p, stream, config_id, fixed);
+}
+
 const char* gemm_strerror(int code) {
     switch (code) {
         case TGEMM_OK: return "success";
@@ -681,6 +734,8 @@ const char* gemm_strerror(int code) {
         case TGEMM_ERR_EPILOGUE:
             return "epilogue: unknown activation, bias kind or bias type, or a bias kind without a bias pointer";
         case TGEMM_ERR_HEAD_DIM: return "attention: head dimension is neither 64 nor 128";
+        case TGEMM_ERR_SCRATCH:
+            return "gemm_fused_noalloc: the call needs more workspace than the library's fixed scratch holds";
         default: break;
     }
     if (code > 0) return hipGetErrorString((hipError_t)code);
