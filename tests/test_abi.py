@@ -222,7 +222,8 @@ def test_kernel_choice_ring_path():
 
 def test_table_prefers_256_tiles_beyond_two_rounds_of_128_tiles():
     """256 x 256 tiles when they fill the 256 CUs or when 128 x 128 tiles
-    would need three or more rounds; else 128 x 128 (or 64 x 128)."""
+    would need three or more rounds; else 128 x 128 (or 64 x 128, also for
+    small products)."""
     RING = T.KERNEL_RING
     assert _kernel_t(3072, 3072, 3072, R_, R_, R_) == (RING, 0)      # 144 big tiles, 576 mid ones
     assert _kernel_t(3000, 3000, 3000, R_, R_, R_) == (RING, 0)
@@ -231,6 +232,11 @@ def test_table_prefers_256_tiles_beyond_two_rounds_of_128_tiles():
     assert _kernel_t(1024, 8192, 1024, R_, R_, R_) == (RING, 1)
     assert _kernel_t(3072, 3072, 3072, C_, R_, R_) == (RING, 0)      # other layouts alike
     assert _kernel_t(4096, 4096, 1024, R_, R_, R_) == (RING, 0)
+    # small products: the 64 x 128 ring from 4 of its tiles
+    for n in (256, 384, 512, 768):
+        assert _kernel_t(n, n, n, R_, R_, R_) == (RING, 8), n
+    assert _kernel_t(512, 512, 2048, R_, R_, R_) == (RING, 8)
+    assert _kernel_t(128, 128, 256, R_, R_, R_)[1] != 8             # 2 tiles: not the ring
 
 
 def _splits(M, N, K, la=T.ROW_MAJOR, lb=T.ROW_MAJOR, lc=T.ROW_MAJOR, lda=None, ldb=None, ldc=None, in_dt=T.F16,

@@ -383,9 +383,15 @@ int table_choice(const Problem& p) {
         return CFG_RING_SMALL;
     if (tiles_for(kConfigs[CFG_MID], M, N) >= 128 && ring_applies(kConfigs[CFG_MID], p)) return CFG_MID;
     if (tiles_for(kConfigs[CFG_MID], M, N) >= 256) return CFG_MID;
-    // few tiles and a long K: the 64 x 128 ring in slices of K
+    // fewer tiles: the 64 x 128 ring (in slices of K when K is long).  It
+    // beats the register-staged 64 x 64 tile on every product measured from
+    // 256^3 to 768^3 and 512 x 512 x 2048 (7.8 against 9.3 us at 512^3, 12.8
+    // against 23.6 us at 512 x 512 x 2048); below 4 of its tiles, or with a
+    // small C it could store only through the fused epilogue, the other
+    // kernels stay
     int k_split;
-    if (ring_applies(kConfigs[CFG_RING_SMALL], p) && split_count(kConfigs[CFG_RING_SMALL], p, k_split) > 1)
+    if (tiles_for(kConfigs[CFG_RING_SMALL], M, N) >= 4 && ring_applies(kConfigs[CFG_RING_SMALL], p) &&
+        (ring_plain_stores(p) || !small || split_count(kConfigs[CFG_RING_SMALL], p, k_split) > 1))
         return CFG_RING_SMALL;
     if (tiles_for(kConfigs[CFG_SMALL], M, N) >= 256) return CFG_SMALL;
     if (small && !tiled_fast(kConfigs[CFG_TINY], p)) return CFG_DIRECT;
