@@ -316,9 +316,6 @@ int tuned_choice(const Problem& p) {
 // splits x M x roundup(N, 4) floats (at most 256 MiB).  Needs the plain
 // epilogue's whole groups (N % 4 == 0) and rows of whole 16-byte chunks.
 // Returns the slice count (1: no split) and the slice length.
-#ifndef SPLIT_MIN_K
-#define SPLIT_MIN_K 256
-#endif
 int split_count(const ConfigEntry& c, const Problem& p, int& k_split) {
     k_split = (int)p.K;
     if (!tuning().split_k || c.ring == nullptr || p.N % 4 != 0 || !loads_aligned(c, p)) return 1;
@@ -328,7 +325,7 @@ int split_count(const ConfigEntry& c, const Problem& p, int& k_split) {
     // workgroups the CUs hold at once: two per CU where the ring's LDS allows
     const int64_t slots = 256 * (c.ring_lds <= 80 * 1024 ? 2 : 1);
     int64_t s = slots / tiles;
-    if (s > p.K / SPLIT_MIN_K) s = p.K / SPLIT_MIN_K;
+    if (s > p.K / 256) s = p.K / 256;
     if (s > 32) s = 32;
     const int64_t ldw = (p.N + 3) / 4 * 4;
     while (s > 1 && s * p.M * ldw * 4 > ((int64_t)256 << 20)) --s;
