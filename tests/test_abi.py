@@ -300,16 +300,15 @@ def test_fp8_outputs_are_checked_and_routed():
             assert _kernel_t(1024, 2048, 512, R_, R_, R_, in_dt=in_dt, out_dt=fmt) == (RING, 8)
             assert _kernel_t(1000, 1000, 1000, C_, C_, C_, in_dt=in_dt, out_dt=fmt)[0] == RING
             assert _kernel(127, 255, 512, ldb=255, ldc=255, in_dt=in_dt, out_dt=fmt) == DIRECT
-            # rows the ring cannot read (A's last element ends at a page
-            # boundary): the table's register-staged tile is replaced by the
-            # direct kernel
-            A = FAKE + (-(2 * 1024 * 301)) % 4096
+            # an operand at an odd address (no ring): the table's
+            # register-staged tile is replaced by the direct kernel
+            A = FAKE + 1
             Bp, Cp = FAKE + (1 << 36), FAKE + (2 << 36)
             assert T.gemm_select_kernel(1024, 1024, 301, A, 301, Bp, 1027, Cp, 1024, in_dt, T.F32) == \
                 T.KERNEL_GENERAL
             assert T.gemm_select_kernel_t(1024, 1024, 301, A, 301, R_, Bp, 1027, R_, Cp, 1024, R_, in_dt, fmt,
                                           -1) == (DIRECT, 6)
-            assert T.gemm_select_kernel(1024, 1024, 301, A + 2, 301, Bp, 1027, Cp, 1024, in_dt, fmt) == RING
+            assert T.gemm_select_kernel(1024, 1024, 301, FAKE, 301, Bp, 1027, Cp, 1024, in_dt, fmt) == RING
             assert _kernel(256, 256, 64, cid=2, in_dt=in_dt, out_dt=fmt) == DIRECT
         assert _kernel(64, 64, 64, in_dt=T.F32, out_dt=fmt) == T.ERR_DTYPE
         assert _kernel(64, 64, 64, in_dt=fmt, out_dt=fmt) == T.ERR_DTYPE
@@ -330,10 +329,11 @@ def test_ring_only_configuration_falls_back_to_128x128():
     assert _kernel_t(1024, 2048, 512, R_, C_, R_, cid=8) == (RING, 8)      # column-major B: k-contiguous
     assert _kernel_t(1024, 2048, 512, C_, R_, R_, cid=8) == (RING, 1)      # column-major A
     assert _kernel_t(1024, 2048, 512, R_, R_, R_, lda=516, cid=8) == (RING, 8)  # A rows not whole chunks
-    # A's last element ending at a page boundary (odd K at 2 mod 4, no pad)
+    # A's last element ending at a page boundary (odd K at 2 mod 4, no pad:
+    # loaded on its own in the K tail)
     A = FAKE + (-(2 * 1024 * 513)) % 4096
     assert T.gemm_select_kernel_t(1024, 2048, 513, A, 513, R_, FAKE + (1 << 36), 2048, R_, FAKE + (2 << 36), 2048,
-                                  R_, T.F16, T.F16, 8)[1] == 1
+                                  R_, T.F16, T.F16, 8) == (RING, 8)
     assert _kernel_t(1024, 2048, 64, R_, R_, R_, cid=8) == (T.KERNEL_TILED, 1)  # K below the ring's multiple
     assert _kernel_t(1000, 2000, 1000, R_, R_, R_, cid=8) == (RING, 8)     # ragged, K tail
     assert _kernel_t(4, 4, 4, R_, R_, R_, in_dt=T.F32, out_dt=T.F32, cid=8)[0] == T.ERR_CONFIG
@@ -350,27 +350,27 @@ def _kernel_t(M, N, K, la, lb, lc, lda=None, ldb=None, ldc=None, in_dt=T.F16, ou
                                   in_dt, out_dt, cid)
 
 
-def _ring_reads(base, ld, kcontig, outer, K):
+def _last_fix(base, ld, kcontig, outer, K):
     """The range-check rule the ring's loads are held to, restated: the
     operand's last element is lost only if it starts a 4-byte part of its
     16-byte load (an odd number of elements from the row's first loaded one:
     K along a k-contiguous row, M or N along a k-strided one) at an address of
     2 mod 4; the range then takes the 2 bytes after it, unless they start a
-    new 4 KiB page (the ring is not used then)."""
+    new 4 KiB page: then the kernel loads that element on its own in its K
+    tail.  True for that last case."""
     rows, cols = (outer, K) if kcontig else (K, outer)
     last = base + 2 * ((rows - 1) * ld + cols - 1)
-    dropped = cols % 2 == 1 and last % 4 == 2
-    return not dropped or (last + 2) % 4096 != 0
+    return cols % 2 == 1 and last % 4 == 2 and (last + 2) % 4096 == 0
 
 
 def test_ring_takes_unaligned_rows_where_every_element_is_kept():
     """Operands off 16-byte alignment or with rows not whole 16-byte chunks
-    run the ring kernel exactly when its loads keep every element of both
-    operands (with a 2-byte range pad inside the last element's page where
-    needed); odd byte addresses never do.  Every layout pair, odd and even
-    sizes, element offsets 0..7 and leading dimensions with every residue
-    mod 8, and placements that put the end of the last element at a page
-    boundary."""
+    run the ring kernel whenever their elements are at even addresses (a
+    2-byte range pad inside the last element's page, or that element loaded
+    on its own in the K tail where the pad would reach the next page); odd
+    byte addresses never do.  Every layout pair, odd and even sizes, element
+    offsets 0..7 and leading dimensions with every residue mod 8, and
+    placements that put the end of the last element at a page boundary."""
     RING = T.KERNEL_RING
     A0, B0, C0 = FAKE, FAKE + (1 << 36), FAKE + (2 << 36)
     n_ring = n_other = 0
@@ -383,24 +383,25 @@ def test_ring_takes_unaligned_rows_where_every_element_is_kept():
                     ldb = (N if lb == R_ else K) + pb
                     A, B = A0 + 2 * oa, B0 + 2 * ob
                     got = T.gemm_select_kernel_t(M, N, K, A, lda, la, B, ldb, lb, C0, N, R_, T.F16, T.F16, 1)
-                    aligned = A % 16 == 0 and B % 16 == 0 and lda % 8 == 0 and ldb % 8 == 0
-                    keeps = _ring_reads(A, lda, la == R_, M, K) and _ring_reads(B, ldb, lb == C_, N, K)
-                    want_ring = aligned or keeps
-                    assert (got[0] == RING) == want_ring, (la, lb, M, N, K, oa, ob, pa, pb, got)
-                    n_ring += want_ring
-                    n_other += not want_ring
+                    assert got[0] == RING, (la, lb, M, N, K, oa, ob, pa, pb, got)
+                    n_ring += 1
+                    n_other += _last_fix(A, lda, la == R_, M, K) or _last_fix(B, ldb, lb == C_, N, K)
                     # an odd byte address: never the ring
                     got = T.gemm_select_kernel_t(M, N, K, A + 1, lda, la, B, ldb, lb, C0, N, R_, T.F16, T.F16, 1)
                     assert got[0] != RING
     assert n_ring > 0
-    # the last element of A ending at a page boundary: no pad possible
+    # the last element of A ending at a page boundary (no pad possible: the
+    # element loaded on its own), a pad, no pad
     M, N, K = 1024, 1024, 301
     end = 2 * M * K  # bytes from A to the end of its last element (lda = K)
     A = A0 + (-end) % 4096
-    assert (A + end) % 4096 == 0 and A % 2 == 0
-    assert T.gemm_select_kernel(M, N, K, A, K, B0, N, C0, N, T.F16, T.F16, -1) != RING
-    assert T.gemm_select_kernel(M, N, K, A + 2, K, B0, N, C0, N, T.F16, T.F16, -1) == RING   # pad 2
-    assert T.gemm_select_kernel(M, N, K, A + 4, K, B0, N, C0, N, T.F16, T.F16, -1) == RING   # 0 mod 4
+    assert (A + end) % 4096 == 0 and A % 2 == 0 and _last_fix(A, K, True, M, K)
+    for a in (A, A + 2, A + 4):
+        assert T.gemm_select_kernel(M, N, K, a, K, B0, N, C0, N, T.F16, T.F16, -1) == RING
+    # an M that is a multiple of 2048 with an odd K and contiguous rows always
+    # ends A at a page boundary (from a page-aligned base)
+    assert _last_fix(A0, 8191, True, 8192, 8191)
+    assert _kernel(8192, 8192, 8191) == RING
     # the square odd sizes: every element kept with contiguous rows, with or
     # without a base offset
     for n in (8191, 4095, 2047):
@@ -450,13 +451,16 @@ def test_kernel_choice_for_layouts():
     assert _kernel_t(256, 256, 256, C_, R_, R_, cid=2)[0] == T.ERR_CONFIG
     assert _kernel_t(256, 256, 256, R_, R_, R_, cid=2)[0] == T.KERNEL_TILED
     # forced ring configuration on a ragged shape: the ring (column-major A
-    # rows of 250 elements, or of 249 with its range padded), or the direct
-    # kernel where no pad is possible (the last element ends a page)
+    # rows of 250 elements, or of 249 with its range padded or its last
+    # element loaded on its own), the direct kernel for an odd address
     assert _kernel_t(250, 256, 256, C_, C_, R_, cid=0) == (RING, 0)
     assert _kernel_t(249, 256, 256, C_, C_, R_, cid=0) == (RING, 0)  # padded range
     A = FAKE + (-(2 * 256 * 249)) % 4096  # A's last element ending at a page boundary
     assert T.gemm_select_kernel_t(249, 256, 256, A, 249, C_, FAKE + (1 << 36), 256, C_, FAKE + (2 << 36), 256, R_,
-                                  T.F16, T.F16, 0) == (DIRECT, 6)
+                                  T.F16, T.F16, 0) == (RING, 0)
+    # an odd address: the direct kernel
+    assert T.gemm_select_kernel_t(249, 256, 256, FAKE + 1, 249, C_, FAKE + (1 << 36), 256, C_, FAKE + (2 << 36), 256,
+                                  R_, T.F16, T.F16, 0) == (DIRECT, 6)
     # a column-major C swaps the roles of A and B: its 128 rows become the
     # N of the row-major product (128 x 128 tiles)
     # (64 of them, K = 8192: in slices of K)

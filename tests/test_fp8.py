@@ -147,20 +147,22 @@ def test_fp8_plain_product_and_partial_groups():
             assert np.array_equal(d, oracle.encode_fp8(o, fmt))
 
 
-def test_fp8_unaligned_operands_take_the_direct_kernel():
-    """Operands the ring cannot read whole (rows of an odd K, contiguous, the
-    last element of A ending at a 4 KiB page boundary: its range cannot be
-    padded) would take a register-staged kernel, which writes no 8-bit
-    output: the direct kernel runs instead.  Placed elsewhere (a padded
-    range) or with one padding element per row, the ring runs."""
-    M, N, K = 1024, 1024, 301   # the table's choice: the 64 x 64 register-staged tile
+def test_fp8_unaligned_operands():
+    """Operands whose rows are not whole 16-byte chunks (rows of an odd K,
+    contiguous) with an 8-bit output, through the ring's fused epilogue: the
+    last element of A ending at a 4 KiB page boundary (loaded on its own in
+    the K tail), a padded range, one padding element per row.  The
+    register-staged tiles the table would take without the ring write no
+    8-bit output; that routing (to the direct kernel) is checked on the host
+    with an odd address."""
+    M, N, K = 1024, 1024, 301   # without the ring: the 64 x 64 register-staged tile
     a, b = W.integer_inputs(M, N, K, W.F16, seed=3)
     o = oracle.gemm_fused(a, b, W.F16, alpha=0.25, nthreads=G.NTHREADS)
     bd = G.to_device(b, W.F16, pad_cols=3)           # ldb = 1027
     n = M * K
     flat = torch.full((n + 4096 + 8,), float("nan"), dtype=torch.float16, device=G.DEV)
     at_page = ((-(flat.data_ptr() + 2 * n)) % 4096) // 2
-    placements = [("A ends at a page", flat[at_page:at_page + n].view(M, K), K, T.KERNEL_DIRECT),
+    placements = [("A ends at a page", flat[at_page:at_page + n].view(M, K), K, T.KERNEL_RING),
                   ("A padded range", flat[at_page + 2:at_page + 2 + n].view(M, K), K, T.KERNEL_RING),
                   ("lda 302", G.to_device(a, W.F16, pad_cols=1), K + 1, T.KERNEL_RING)]
     for label, ad, lda, want_kind in placements:

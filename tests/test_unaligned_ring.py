@@ -6,10 +6,11 @@ The ring's 16-byte loads then start at 2-byte-aligned addresses; their range
 check keeps a 4-byte part only if it ends inside the operand's range, which
 ends at the dword boundary after the operand's last element, or 2 bytes
 further where the last element starts a part at an address of 2 mod 4 (those
-bytes are then read, so they must lie in the element's page).  The library
-takes the ring exactly when one of the two keeps every element (the rule
-restated in `ring_reads` below) and another kernel otherwise; both cases are
-run.
+bytes are then read, so they must lie in the element's page).  Where they
+would start a new 4 KiB page (the rule restated in `last_fix` below) the
+kernel loads that element on its own in its K tail, leaving a k-strided
+operand's last k-row to the tail; those placements are run for each operand
+and layout.  Every even-address operand runs the ring.
 
 Every operand sits in a NaN-filled buffer (NaN in the row padding, in the
 elements before the base and after the last element), so a read past K that
@@ -38,29 +39,31 @@ def lid(lay):
     return "".join("r" if x == ROW else "c" for x in lay)
 
 
-def ring_reads(base, ld, kcontig, outer, K):
-    """Whether the ring reads the operand whole: its last element is lost only
-    if it starts a 4-byte part of its load (an odd element count along the row
-    from the row's first loaded element) at an address of 2 mod 4 and the 2
-    bytes after it start a new 4 KiB page (else the range is padded)."""
+def last_fix(base, ld, kcontig, outer, K):
+    """Whether the ring loads the operand's last element on its own: that
+    element starts a 4-byte part of its 16-byte load (an odd element count
+    along the row from the row's first loaded element) at an address of
+    2 mod 4, and the 2 bytes after it start a new 4 KiB page (else the range
+    is padded by them)."""
     rows, cols = (outer, K) if kcontig else (K, outer)
     last = base + 2 * ((rows - 1) * ld + cols - 1)
-    return not (cols % 2 == 1 and last % 4 == 2) or (last + 2) % 4096 != 0
+    return cols % 2 == 1 and last % 4 == 2 and (last + 2) % 4096 == 0
 
 
-def place_ending_at_page(x, dt):
-    """Row-major device copy of x (rows x cols, ld = cols) whose last element
-    ends exactly at a 4 KiB page boundary, in a NaN-filled buffer."""
-    rows, cols = x.shape
+def place_ending_at_page(x, dt, layout=ROW):
+    """Device copy of x (rows x cols) stored row- or column-major with no
+    padding, whose last stored element ends exactly at a 4 KiB page
+    boundary, in a NaN-filled buffer."""
+    s = np.ascontiguousarray(x if layout == ROW else x.T)
+    rows, cols = s.shape
     n = rows * cols
     flat = torch.full((n + 4096,), float("nan"), dtype=G.TORCH[dt], device=G.DEV)
     off = ((-(flat.data_ptr() + 2 * n)) % 4096) // 2
     view = flat[off:off + n].view(rows, cols)
-    host = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16) if dt == W.BF16 \
-        else torch.from_numpy(np.ascontiguousarray(x))
+    host = torch.from_numpy(s.view(np.int16)).view(torch.bfloat16) if dt == W.BF16 else torch.from_numpy(s)
     view.copy_(host.to(G.DEV))
     assert (view.data_ptr() + 2 * n) % 4096 == 0
-    return view
+    return view if layout == ROW else view.t()
 
 
 def place(x, dt, layout, pad, offset):
@@ -69,28 +72,29 @@ def place(x, dt, layout, pad, offset):
     return G.to_device(np.ascontiguousarray(x.T), dt, pad_cols=pad, offset_elems=offset).t()
 
 
-def run_exact(M, N, K, in_dt, out_dt, lay, pads, offs, cid, seed):
-    """Integer inputs through gemm_t; asserts the kernel the rule predicts
-    and bit-exact results; returns the kernel kind."""
+def run_exact(M, N, K, in_dt, out_dt, lay, pads, offs, cid, seed, at_page=(False, False)):
+    """Integer inputs through gemm_t (an operand flagged in at_page is placed
+    with its last element ending at a page boundary instead of by pad and
+    offset); asserts the ring and bit-exact results; returns whether an
+    operand's last element was loaded on its own."""
     a, b = W.integer_inputs(M, N, K, in_dt, seed=seed)
-    ad = place(a, in_dt, lay[0], pads[0], offs[0])
-    bd = place(b, in_dt, lay[1], pads[1], offs[1])
+    ad = place_ending_at_page(a, in_dt, lay[0]) if at_page[0] else place(a, in_dt, lay[0], pads[0], offs[0])
+    bd = place_ending_at_page(b, in_dt, lay[1]) if at_page[1] else place(b, in_dt, lay[1], pads[1], offs[1])
     _, cd = G.out_tensor(M, N, out_dt)
     la, lda = T._layout(ad)
     lb, ldb = T._layout(bd)
     kind, cfg = T.gemm_select_kernel_t(M, N, K, ad.data_ptr(), lda, la, bd.data_ptr(), ldb, lb, cd.data_ptr(), N,
                                        ROW, in_dt, out_dt, cid)
+    fix = (last_fix(ad.data_ptr(), lda, la == ROW, M, K), last_fix(bd.data_ptr(), ldb, lb == COL, N, K))
     G.say(f"[case] unaligned {M}x{N}x{K} lay={lid(lay)} in={in_dt} out={out_dt} lda={lda} ldb={ldb} "
-          f"offs={offs} cfg{cid} -> {KIND.get(kind, kind)} cfg{cfg}")
-    aligned = ad.data_ptr() % 16 == 0 and bd.data_ptr() % 16 == 0 and lda % 8 == 0 and ldb % 8 == 0
-    keeps = ring_reads(ad.data_ptr(), lda, la == ROW, M, K) and ring_reads(bd.data_ptr(), ldb, lb == COL, N, K)
-    assert (kind == T.KERNEL_RING) == (aligned or keeps), (kind, aligned, keeps)
+          f"offs={offs} at_page={at_page} last_fix={fix} cfg{cid} -> {KIND.get(kind, kind)} cfg{cfg}")
+    assert kind == T.KERNEL_RING, kind
     G.run(ad, bd, cd, cid)
     got = G.values(cd, out_dt)
     want = G.round_to(G.oracle_values(a, b, in_dt), out_dt)
     bad = got != want
     assert not bad.any(), f"{int(bad.sum())} entries differ, first at {np.argwhere(bad)[0].tolist()}"
-    return kind
+    return any(fix)
 
 
 # (M, N, K, configuration): odd and even sizes, K tails of odd length, one
@@ -106,34 +110,38 @@ def test_unaligned_operands_exact(shape, lay):
     M, N, K, cid = shape
     if cid == 8 and lay[0] == COL:
         cid = 1  # the 64 x 128 ring reads row-major A only
-    kinds = []
     for i, (pa, pb, oa, ob) in enumerate(PLACEMENTS):
         in_dt, out_dt = ((W.F16, W.F16), (W.BF16, W.F32), (W.F16, W.F32), (W.BF16, W.BF16))[i % 4]
-        kinds.append(run_exact(M, N, K, in_dt, out_dt, lay, (pa, pb), (oa, ob), cid, seed=M + N + K + 11 * i))
-    assert T.KERNEL_RING in kinds
+        run_exact(M, N, K, in_dt, out_dt, lay, (pa, pb), (oa, ob), cid, seed=M + N + K + 11 * i)
 
 
-def test_unaligned_operands_both_outcomes_of_the_rule():
-    """The same shape with the last element of A at 0 and at 2 mod 4 (K odd,
-    rows of K elements: the ring, with and without the range pad), then with
-    that element ending at a page boundary (the fallback); all exact, NaN in
-    the bytes after A's last element."""
-    M, N, K = 511, 512, 513
-    kinds = [run_exact(M, N, K, W.F16, W.F16, (ROW, ROW), (0, 0), (oa, 0), 1, seed=5 + oa) for oa in (0, 1, 2, 3)]
-    # (run_exact checks each kind against the rule; at most one of the four
-    # placements can end A at a page boundary)
-    assert kinds.count(T.KERNEL_RING) >= 3, kinds
-    a, b = W.integer_inputs(M, N, K, W.F16, seed=9)
-    ad = place_ending_at_page(a, W.F16)
-    bd = G.to_device(b, W.F16)
-    _, cd = G.out_tensor(M, N, W.F16)
-    kind = T.gemm_select_kernel(M, N, K, ad.data_ptr(), K, bd.data_ptr(), N, cd.data_ptr(), N, W.F16, W.F16, 1)
-    G.say(f"[case] unaligned A ending at a page boundary {M}x{N}x{K} -> {KIND.get(kind, kind)}")
-    assert kind != T.KERNEL_RING and not ring_reads(ad.data_ptr(), K, True, M, K)
-    G.run(ad, bd, cd, 1)
-    want = G.round_to(G.oracle_values(a, b, W.F16), W.F16)
-    got = G.values(cd, W.F16)
-    assert np.array_equal(got, want), f"{int((got != want).sum())} entries differ"
+# (M, N, K, layouts, A / B at a page, configuration): the last element of a
+# k-contiguous operand (odd K: it is in the K tail) and of a k-strided one
+# (odd M or N; K a multiple of the ring's step, so the tail exists only for
+# the operand's last k-row), of A, of B, of both, in the 128 x 128, 256 x 256
+# and 64 x 128 rings and the table's choice
+AT_PAGE = [(511, 512, 513, (ROW, ROW), (True, False), 1), (511, 512, 512, (COL, ROW), (True, False), 1),
+           (512, 509, 512, (ROW, ROW), (False, True), 1), (512, 512, 513, (ROW, COL), (False, True), 1),
+           (511, 509, 512, (COL, ROW), (True, True), 1), (1023, 1024, 1024, (COL, COL), (True, False), 0),
+           (1024, 1021, 2048, (ROW, ROW), (False, True), 0), (300, 512, 1025, (ROW, COL), (True, True), 8),
+           (2048, 2048, 2047, (ROW, ROW), (True, False), -1), (2048, 1024, 1536, (COL, ROW), (True, False), -1)]
+
+
+@pytest.mark.parametrize("case", AT_PAGE, ids=lambda c: "x".join(map(str, c[:3])) + "_" + lid(c[3]) +
+                         "".join("ab"[i] for i in (0, 1) if c[4][i]) + f"_cfg{c[5]}")
+def test_unaligned_last_element_at_page_boundary(case):
+    """An operand whose last element starts a 4-byte part at 2 mod 4 and
+    ends at a 4 KiB page boundary (its range cannot be padded): the kernel
+    loads that element on its own.  NaN fills the buffer before the operand
+    and the page after it; exact on integer values, with two of the input
+    and output types."""
+    M, N, K, lay, at_page, cid = case
+    for i, (in_dt, out_dt) in enumerate(((W.F16, W.F16), (W.BF16, W.F32))):
+        fixed = run_exact(M, N, K, in_dt, out_dt, lay, (0, 0), (0, 0), cid, seed=M + N + K + i, at_page=at_page)
+        # an odd extent along the contiguous dimension at a page end puts
+        # the last element at 2 mod 4: the element loaded on its own
+        contig = (K if lay[0] == ROW else M, K if lay[1] == COL else N)
+        assert fixed == any(at_page[j] and contig[j] % 2 == 1 for j in (0, 1)), (fixed, at_page, contig)
 
 
 def test_unaligned_operands_random_values():
@@ -151,8 +159,6 @@ def test_unaligned_operands_random_values():
                                     N, in_dt, out_dt)
         G.say(f"[case] unaligned random {M}x{N}x{K} in={in_dt} out={out_dt} pads={pads} offs={offs} "
               f"-> {KIND.get(kind, kind)}")
-        assert ring_reads(ad.data_ptr(), K + pads[0], True, M, K)
-        assert ring_reads(bd.data_ptr(), N + pads[1], False, N, K)
         assert kind == T.KERNEL_RING
         G.run(ad, bd, cd)
         G.check(G.values(cd, out_dt), G.oracle_values(a, b, in_dt), a, b, in_dt, out_dt, K, label="unaligned")
@@ -165,7 +171,6 @@ def test_unaligned_operands_fused_and_fp8():
     a, b = W.integer_inputs(M, N, K, W.F16, seed=77)
     ad = G.to_device(a, W.F16, pad_cols=1, offset_elems=2)
     bd = G.to_device(b, W.F16, pad_cols=3, offset_elems=2)
-    assert ring_reads(ad.data_ptr(), K + 1, True, M, K) and ring_reads(bd.data_ptr(), N + 3, False, N, K)
     rng = np.random.default_rng(78)
     c_old = rng.integers(-8, 9, size=(M, N)).astype(np.float32)
     bias = rng.integers(-4, 5, size=N).astype(np.float32)

@@ -80,6 +80,11 @@ struct GemmArgs {
     // rounding (0, or 2 when the last element would otherwise be dropped;
     // the host checks that they lie in the last element's page)
     int range_pad_a, range_pad_b;
+    // ring kernels: bit 0 (A) / bit 1 (B): the operand's last element cannot
+    // be kept by a pad (the 2 bytes after it start a new page); the K tail
+    // loads it on its own, and a k-strided operand's last k-row is left to
+    // the tail (the host then runs the KT variant)
+    int last_fix;
     // split-K (ring kernels, plain fp32 output): splits > 1 slices of K of
     // k_split elements (the last one the rest), slice s written to C plus
     // s * split_stride bytes

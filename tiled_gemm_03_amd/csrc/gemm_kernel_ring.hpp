@@ -499,7 +499,10 @@ void gemm_kernel_ring(GemmArgs p) {
     };
 
     // steps of the rings: a multiple of U (without KT, K % K_MULT == 0)
-    const int nk = K / (T::BK * P::U) * P::U;
+    // (KT with a k-strided operand's last element loaded on its own: the
+    // rings stop before the last k-row, which the tail's element loads keep)
+    const bool ks_fix = (!OA::KC && (p.last_fix & 1)) || (!OB_::KC && (p.last_fix & 2));
+    const int nk = ((KT && ks_fix) ? K - 1 : K) / (T::BK * P::U) * P::U;
     if (nk > 0) {
         // prologue: the loads of the virtual steps before step 0, then the
         // fragments of step 0
@@ -536,11 +539,20 @@ void gemm_kernel_ring(GemmArgs p) {
         const auto ta = tail_rsrc(a_start, a_bytes, p.range_pad_a);
         const auto tb = tail_rsrc(b_start, b_bytes, p.range_pad_b);
         // lane's 8 k (k ..) of row / column o (from the tile's corner)
-        auto tail_frag = [&](auto op_t, const auto& rs, int o, int64_t ld, int k) __attribute__((always_inline)) {
+        auto tail_frag = [&](auto op_t, const auto& rs, int o, int64_t ld, int k, bool fix) __attribute__((always_inline)) {
             using O = decltype(op_t);
             i16x8 v;
             if constexpr (O::KC) {
                 v = __builtin_bit_cast(i16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(((int64_t)o * ld + k) * 2), 0, 0));
+                // element K - 1 of the row on its own (a 2-byte load ends
+                // inside the range where the 4-byte part of the 16-byte one
+                // would not): the operand's last element at 2 mod 4
+                const int kk = K - 1 - k;
+                if (fix && kk >= 0 && kk < 8) {
+                    const short e = (short)__builtin_amdgcn_raw_buffer_load_b16(rs, (int)(((int64_t)o * ld + K - 1) * 2), 0, 0);
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) v[t] = t == kk ? e : v[t];
+                }
             } else {
 #pragma unroll
                 for (int t = 0; t < 8; ++t)
@@ -555,11 +567,11 @@ void gemm_kernel_ring(GemmArgs p) {
             const int k = k0 + 8 * q;
             static_for<0, T::FN>([&](auto j_t) __attribute__((always_inline)) {
                 constexpr int j = decltype(j_t)::value;
-                fb[0][j] = tail_frag(OB_{}, tb, wn * T::WTN + 16 * j + i16, ldb, k);
+                fb[0][j] = tail_frag(OB_{}, tb, wn * T::WTN + 16 * j + i16, ldb, k, (p.last_fix & 2) != 0);
             });
             static_for<0, T::FM>([&](auto i_t) __attribute__((always_inline)) {
                 constexpr int i = decltype(i_t)::value;
-                fa[0][i] = tail_frag(OA{}, ta, wm * T::WTM + 16 * i + i16, lda, k);
+                fa[0][i] = tail_frag(OA{}, ta, wm * T::WTM + 16 * i + i16, lda, k, (p.last_fix & 1) != 0);
             });
             static_for<0, NMF>([&](auto mt) __attribute__((always_inline)) { mfma_one(0, decltype(mt)::value); });
         }

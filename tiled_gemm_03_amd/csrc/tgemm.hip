@@ -227,8 +227,9 @@ int64_t operand_reach(bool kcontig, int64_t ext, int64_t ld, int64_t K, int64_t 
 // k-contiguous operand, M or N for a k-strided one) at an address of 2 mod 4.
 // Then 2 more bytes keep it; they are read (their values reach only outputs
 // past N or positions past K), so they must lie in the element's page: -1
-// when they start a new 4 KiB page.  Rows of whole 16-byte chunks never need
-// a pad.
+// when they start a new 4 KiB page, and the kernel then loads that element
+// on its own in its K tail (GemmArgs::last_fix).  Rows of whole 16-byte
+// chunks never need a pad.
 int ring_range_pad(const void* X, int64_t ld, bool kcontig, int64_t outer, int64_t K) {
     const int64_t rows = kcontig ? outer : K, cols = kcontig ? K : outer;
     if (rows <= 0 || cols <= 0) return 0;
@@ -238,6 +239,13 @@ int ring_range_pad(const void* X, int64_t ld, bool kcontig, int64_t outer, int64
 }
 int ring_pad_a(const Problem& p) { return ring_range_pad(p.A, p.lda, p.la == LAYOUT_ROW, p.M, p.K); }
 int ring_pad_b(const Problem& p) { return ring_range_pad(p.B, p.ldb, p.lb == LAYOUT_COL, p.N, p.K); }
+// GemmArgs::last_fix of a ring call, and whether it needs the KT variant for
+// it (a k-strided operand's last k-row left to the tail)
+int ring_last_fix(const Problem& p) { return (ring_pad_a(p) < 0 ? 1 : 0) | (ring_pad_b(p) < 0 ? 2 : 0); }
+bool ring_fix_needs_tail(const Problem& p) {
+    const int f = ring_last_fix(p);
+    return ((f & 1) && p.la == LAYOUT_COL) || ((f & 2) && p.lb == LAYOUT_ROW);
+}
 
 // Whether a configuration with a ring kernel runs it.
 bool ring_applies(const ConfigEntry& c, const Problem& p) {
@@ -245,10 +253,10 @@ bool ring_applies(const ConfigEntry& c, const Problem& p) {
     if (p.la == LAYOUT_COL && !c.ring_a_col) return false;
     // the ring loads ring_lookahead steps past K
     const int64_t extra = (int64_t)c.ring_lookahead * c.ring_bk;
-    // 16-bit elements at even addresses; rows of whole 16-byte chunks, or
-    // ranges that keep every element, padded where needed (ring_range_pad)
-    const bool loads_ok = (uintptr_t)p.A % 2 == 0 && (uintptr_t)p.B % 2 == 0 &&
-                          (loads_aligned(c, p) || (ring_pad_a(p) >= 0 && ring_pad_b(p) >= 0));
+    // 16-bit elements at even addresses: rows of whole 16-byte chunks, or
+    // ranges padded where needed, or the last element loaded on its own
+    // (ring_range_pad)
+    const bool loads_ok = (uintptr_t)p.A % 2 == 0 && (uintptr_t)p.B % 2 == 0;
     // K a multiple of ring_k_mult, or above it (the K-tail variant); any N
     // and C alignment (ring_plain_stores)
     return loads_ok && (p.K % c.ring_k_mult == 0 || p.K > c.ring_k_mult) &&
@@ -461,7 +469,7 @@ int make_plan(const Problem& p, int config_id, Plan& plan) {
         plan.kind = TGEMM_KERNEL_RING;
         // 8-bit outputs are written by the fused epilogue's kernels
         plan.fn = c.ring(p.in, kernel_out(p.out), p.la, p.lb, p.ep.on || is_fp8(p.out) || !ring_plain_stores(p),
-                         p.K % c.ring_k_mult != 0);
+                         p.K % c.ring_k_mult != 0 || ring_fix_needs_tail(p));
         if (plan.fn == nullptr) return TGEMM_ERR_DTYPE;
         return ceil_div(p.M, c.bm) * ceil_div(p.N, c.bn) > 0x7fffffff ? TGEMM_ERR_DIM : TGEMM_OK;
     }
@@ -596,6 +604,7 @@ int run_split(const Problem& p, const Plan& plan, const ConfigEntry& c, const Ge
     pa.epi = 0;
     pa.vec_c = 1;
     pa.range_pad_a = pa.range_pad_b = 0;
+    pa.last_fix = 0;
     pa.splits = plan.splits;
     pa.k_split = plan.k_split;
     pa.split_stride = slice * 4;
@@ -664,6 +673,7 @@ int run(const Problem& p, void* stream, int config_id, float* fixed = nullptr) {
     const bool ring = plan.kind == TGEMM_KERNEL_RING;
     args.range_pad_a = ring && ring_pad_a(p) > 0 ? ring_pad_a(p) : 0;
     args.range_pad_b = ring && ring_pad_b(p) > 0 ? ring_pad_b(p) : 0;
+    args.last_fix = ring ? ring_last_fix(p) : 0;
     const int64_t grid = (int64_t)args.tiles_m * args.tiles_n;
 
     if (plan.kind == TGEMM_KERNEL_RING_SPLITK) return run_split(p, plan, c, args, stream, fixed);
