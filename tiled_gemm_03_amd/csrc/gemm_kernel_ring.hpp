@@ -591,15 +591,18 @@ void gemm_kernel_ring(GemmArgs p) {
         constexpr int PB = REGION / 1024 < NMF ? REGION / 1024 : NMF;
         static_assert(PB >= 1 && NMF % PB == 0, "");
         lds_f32x4* region = (lds_f32x4*)(lds_void*)smem + wave * (REGION / 16);
-        // The blocks of the later passes wait in VGPRs (free once the loop
-        // is done): kept in the accumulator registers across the first
-        // pass's loop, they make the register allocator move accumulators
-        // around inside the main loop.
+        // Every block passes through VGPRs (free once the loop is done; an
+        // empty asm): the blocks of the later passes, kept in the
+        // accumulator registers across the first pass's loop, and the first
+        // pass's, written to LDS straight from them, made the register
+        // allocator move accumulators around inside the main loop (the
+        // latter with column-major A and row-major B: 870 instructions and
+        // 348 moves per loop trip against 469 and none).
         f32x4 held[NMF];
         static_for<0, NMF>([&](auto b_t) __attribute__((always_inline)) {
             constexpr int b = decltype(b_t)::value;
             held[b] = acc[b / T::FN][b % T::FN];
-            if constexpr (b >= PB) asm volatile("" : "+v"(held[b]));
+            asm volatile("" : "+v"(held[b]));
         });
         // any N and C alignment: the last group of a row may be partial
         // (element stores, in the run-time loop of values read back from
@@ -624,14 +627,19 @@ void gemm_kernel_ring(GemmArgs p) {
     // products of zeros or of elements outside the tile's operand rows and
     // columns, never mixed into the stored ones.  (Element stores for a
     // partial group make the compiler move every accumulator to VGPRs ahead
-    // of the stores, and spill.)
+    // of the stores, and spill.)  fp32 outputs pass through VGPRs (an empty
+    // asm) as the converted 16-bit ones do: stored straight from the
+    // accumulator registers, they made the register allocator move
+    // accumulators around the main loop of the 256 x 256 kernel with
+    // column-major A and row-major B (1049 instructions and 484 moves per
+    // loop trip against 469 and none).
     static_for<0, NMF>([&](auto bt) __attribute__((always_inline)) {
         constexpr int i = decltype(bt)::value / T::FN, j = decltype(bt)::value % T::FN;
         const int row = m0 + wm * T::WTM + 16 * i + i16;
         const int col = n0 + wn * T::WTN + 16 * j + 4 * q;
-        if (row < p.M && col < p.N)
-            store4<OUT>(C + ((int64_t)row * ldc + col) * OB, acc[i][j][0], acc[i][j][1], acc[i][j][2],
-                        acc[i][j][3], true);
+        f32x4 v = acc[i][j];
+        if constexpr (OUT == DT_F32) asm volatile("" : "+v"(v));
+        if (row < p.M && col < p.N) store4<OUT>(C + ((int64_t)row * ldc + col) * OB, v[0], v[1], v[2], v[3], true);
     });
 }
 
