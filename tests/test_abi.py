@@ -193,8 +193,9 @@ def test_kernel_choice_ring_path():
     assert _kernel(8192, 8192, 8192 + 64) == R           # K not a multiple of 128: the K tail
     assert _kernel(8192, 8192, 8192 - 32) == R
     assert _kernel(256, 256, 129, lda=136, cid=0) == R   # K just above 128
-    assert _kernel(256, 256, 120, cid=0) == TI           # K below 128 and not a multiple of it
-    assert _kernel(256, 256, 64, cid=1) == TI
+    assert _kernel(256, 256, 120, cid=0) == R            # K below 128: the tail alone
+    assert _kernel(4096, 4096, 16) == R and _kernel(4096, 4096, 100) == R
+    assert _kernel(256, 256, 64, cid=1) == R
     assert _kernel(8192 - 256, 8192, 8192) == R          # still whole tiles
     assert _kernel(8191, 8192, 8192) == R                # ragged M: masked edge tiles
     assert _kernel(8191, 8000, 8192) == R                # ragged M and N
@@ -334,7 +335,11 @@ def test_ring_only_configuration_falls_back_to_128x128():
     A = FAKE + (-(2 * 1024 * 513)) % 4096
     assert T.gemm_select_kernel_t(1024, 2048, 513, A, 513, R_, FAKE + (1 << 36), 2048, R_, FAKE + (2 << 36), 2048,
                                   R_, T.F16, T.F16, 8) == (RING, 8)
-    assert _kernel_t(1024, 2048, 64, R_, R_, R_, cid=8) == (T.KERNEL_TILED, 1)  # K below the ring's multiple
+    assert _kernel_t(1024, 2048, 64, R_, R_, R_, cid=8) == (RING, 8)       # K below the ring's step: the tail
+    # an operand at an odd address: the register-staged kernel of
+    # configuration 1 (checked)
+    assert T.gemm_select_kernel_t(1024, 2048, 64, FAKE + 1, 64, R_, FAKE + (1 << 36), 2048, R_, FAKE + (2 << 36),
+                                  2048, R_, T.F16, T.F16, 8) == (T.KERNEL_GENERAL, 1)
     assert _kernel_t(1000, 2000, 1000, R_, R_, R_, cid=8) == (RING, 8)     # ragged, K tail
     assert _kernel_t(4, 4, 4, R_, R_, R_, in_dt=T.F32, out_dt=T.F32, cid=8)[0] == T.ERR_CONFIG
 
