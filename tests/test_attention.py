@@ -214,6 +214,9 @@ CASES = [
     (1, 2, 300, 300, 64, W.BF16, W.F32, 0.125, True, "bnhd", 0, 1),  # split, causal, tiles along the diagonal
     (1, 2, 130, 140, 64, W.F16, W.F16, 0.125, False, "bhnd_odd", 1, 1),         # odd row strides (65)
     (1, 3, 200, 333, 128, W.BF16, W.F32, 128 ** -0.5, True, "bhnd_odd", 2, 4),  # odd row strides (129)
+    # causal, 64 tiles in 8 XCD runs of 2 whole heads: longest tiles first
+    # across the heads of a run
+    (2, 8, 512, 512, 128, W.F16, W.F16, 128 ** -0.5, True, "bhnd", 0, 4),
 ]
 
 

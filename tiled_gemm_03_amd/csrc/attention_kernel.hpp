@@ -88,12 +88,23 @@ __device__ __forceinline__ f32x4 attn_mfma(attn_i16x8 a, attn_i16x8 b, f32x4 c) 
 
 // Workgroup g -> (batch-head, query tile).  Workgroups are dispatched to the
 // 8 XCDs in turn (g % 8); the map gives each XCD a contiguous run of tiles,
-// so that the tiles of one head share that XCD's L2 for K and V.  Causal:
-// the tiles of a head are taken last to first (the longest first).
+// so that the tiles of one head share that XCD's L2 for K and V.  Causal
+// (the tile of query rows q0.. walks q0 / 64 + 1 key blocks): the longest
+// tiles first, across the heads of the XCD's run when it holds whole heads
+// (all their last tiles, then all their second to last, ...), else within
+// each head.  Longest-first over the run measured 5% faster than per head
+// on 4 x 16 heads of 4096 positions (275-281 against 292-294 us).
 __device__ __forceinline__ void attn_tile_of(int g, int total, int tiles, bool reverse, int& bh, int& qt) {
     const int full = total & ~7;
+    const int run = full >> 3;
+    if (reverse && g < full && run % tiles == 0) {
+        const int nh = run / tiles, pos = g >> 3;
+        qt = tiles - 1 - pos / nh;
+        bh = (g & 7) * nh + pos % nh;
+        return;
+    }
     int lin = g;
-    if (g < full) lin = (g & 7) * (full >> 3) + (g >> 3);
+    if (g < full) lin = (g & 7) * run + (g >> 3);
     bh = lin / tiles;
     qt = lin - bh * tiles;
     if (reverse) qt = tiles - 1 - qt;
