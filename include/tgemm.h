@@ -21,7 +21,9 @@
  *    outside the M x N window (columns N .. ldc-1) are never written.
  *  - A, B and C are DEVICE pointers (memory of the current HIP device), owned
  *    by the caller; the library keeps no reference after the call.  C must
- *    not overlap A or B.
+ *    not overlap A or B.  Each pointer is aligned to its element's size
+ *    (TGEMM_ERR_ALIGN otherwise); no other alignment is needed: leading
+ *    dimensions and base offsets may be any number of elements.
  *  - The call enqueues one kernel on `stream` (a hipStream_t; NULL = the
  *    null stream) and returns without waiting for it.  The library allocates
  *    no memory and keeps no per-call state; concurrent calls are safe.
@@ -84,6 +86,11 @@ extern "C" {
 #define TGEMM_ERR_HEAD_DIM (-9)    /* attention_fwd: head_dim not 64 or 128     */
 #define TGEMM_ERR_SCRATCH (-10)    /* gemm_fused_noalloc: the call's split-K
                                       workspace exceeds the fixed scratch  */
+#define TGEMM_ERR_ALIGN (-11)      /* a pointer not aligned to its element's
+                                      size: 2 bytes for F16 / BF16, 4 for F32
+                                      (A, B, C, the epilogue's bias;
+                                      attention's Q, K, V, O); 8-bit outputs
+                                      may start at any byte               */
 
 /* Operand layouts (gemm_t): the row-major default and the column-major option
  * of page "TileLang实战：用Python DSL自动生成高性能GPU计算内核", §5.1. */
@@ -132,10 +139,10 @@ int gemm_ex(int64_t M, int64_t N, int64_t K,
  * A column-major C is computed as the row-major C^T = B^T x A^T.  Kernels:
  * row-major A and B take every configuration; with a column-major operand
  * the direct-to-LDS ring kernels of configurations 0 and 1 (8 with a
- * row-major A) run whole aligned tiles, the direct kernels of
- * configurations 6 and 7 everything else
- * (configurations 2 to 5 return TGEMM_ERR_CONFIG there, and products whose
- * 32-bit buffer offsets would overflow return TGEMM_ERR_DIM).  config_id -1:
+ * row-major A; its other products run configuration 1) and the direct
+ * kernels of configurations 6 and 7 (configurations 2 to 5 return
+ * TGEMM_ERR_CONFIG there, and products whose 32-bit buffer offsets would
+ * overflow return TGEMM_ERR_DIM).  config_id -1:
  * the table's choice.  Other arguments, ownership and errors as gemm_ex.
  */
 int gemm_t(int64_t M, int64_t N, int64_t K,
@@ -259,8 +266,8 @@ int gemm_select_config(int64_t M, int64_t N, int64_t K,
 /* Kernels a call can run (gemm_select_kernel). */
 #define TGEMM_KERNEL_GENERAL 0 /* register-staged, every access checked (ragged or unaligned) */
 #define TGEMM_KERNEL_TILED 1   /* register-staged, whole tiles, aligned operands              */
-#define TGEMM_KERNEL_RING 2    /* direct-to-LDS rings: 16-bit inputs, aligned, K a multiple
-                                  of 128 or above 128 (configurations 0, 1 and 8)           */
+#define TGEMM_KERNEL_RING 2    /* direct-to-LDS rings: 16-bit inputs, any M, N, K, layout and
+                                  leading dimension (configurations 0, 1 and 8)             */
 #define TGEMM_KERNEL_DIRECT 3  /* operands straight from memory to registers, no LDS: small,
                                   ragged or unaligned products (configurations 6 and 7)     */
 #define TGEMM_KERNEL_RING_SPLITK 4 /* the ring kernel over slices of K (products with too few

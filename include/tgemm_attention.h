@@ -35,7 +35,8 @@ extern "C" {
  *                     contiguous.  A NULL stride pointer means the packed
  *                     layout {H n d, n d, d}.  The stride arrays are read on
  *                     the host during the call.  Elements need only be
- *                     aligned to their size; overlapping inputs are fine.
+ *                     aligned to their size (else TGEMM_ERR_ALIGN);
+ *                     overlapping inputs are fine.
  *                     The row strides of K and V must keep 64 rows within
  *                     32-bit byte offsets: (64 max(k_stride[2], v_stride[2])
  *                     + d) * 2 < 2^31 (else TGEMM_ERR_LD).

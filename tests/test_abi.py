@@ -104,6 +104,12 @@ FAKE = 1 << 40  # a well-aligned address that is never dereferenced
     ((4, 4, 4, FAKE, 4, FAKE, 4, None, 4, 1, 1), T.ERR_NULL),
     ((4, 4, 4, FAKE, 4, FAKE + 4096, 4, FAKE + 16, 4, 1, 1), T.ERR_ALIAS),
     ((4, 4, 4, FAKE, 4, FAKE + 4096, 4, FAKE + 4096 + 30, 4, 1, 1), T.ERR_ALIAS),
+    # pointers not aligned to their element's size
+    ((4, 4, 4, FAKE + 1, 4, FAKE + 4096, 4, FAKE + 8192, 4, 1, 1), T.ERR_ALIGN),
+    ((4, 4, 4, FAKE, 4, FAKE + 4097, 4, FAKE + 8192, 4, 2, 2), T.ERR_ALIGN),
+    ((4, 4, 4, FAKE, 4, FAKE + 4096, 4, FAKE + 8193, 4, 1, 1), T.ERR_ALIGN),
+    ((4, 4, 4, FAKE, 4, FAKE + 4096, 4, FAKE + 8194, 4, 1, 0), T.ERR_ALIGN),
+    ((4, 4, 4, FAKE + 2, 4, FAKE + 4096, 4, FAKE + 8192, 4, 0, 0), T.ERR_ALIGN),
 ])
 def test_invalid_arguments_rejected_without_launch(args, code):
     a, s = _codes(*args)
@@ -301,15 +307,11 @@ def test_fp8_outputs_are_checked_and_routed():
             assert _kernel_t(1024, 2048, 512, R_, R_, R_, in_dt=in_dt, out_dt=fmt) == (RING, 8)
             assert _kernel_t(1000, 1000, 1000, C_, C_, C_, in_dt=in_dt, out_dt=fmt)[0] == RING
             assert _kernel(127, 255, 512, ldb=255, ldc=255, in_dt=in_dt, out_dt=fmt) == DIRECT
-            # an operand at an odd address (no ring): the table's
-            # register-staged tile is replaced by the direct kernel
-            A = FAKE + 1
+            # an operand at an odd address: rejected; an 8-bit C at any byte
             Bp, Cp = FAKE + (1 << 36), FAKE + (2 << 36)
-            assert T.gemm_select_kernel(1024, 1024, 301, A, 301, Bp, 1027, Cp, 1024, in_dt, T.F32) == \
-                T.KERNEL_GENERAL
-            assert T.gemm_select_kernel_t(1024, 1024, 301, A, 301, R_, Bp, 1027, R_, Cp, 1024, R_, in_dt, fmt,
-                                          -1) == (DIRECT, 6)
-            assert T.gemm_select_kernel(1024, 1024, 301, FAKE, 301, Bp, 1027, Cp, 1024, in_dt, fmt) == RING
+            assert T.gemm_select_kernel(1024, 1024, 301, FAKE + 1, 301, Bp, 1027, Cp, 1024, in_dt, fmt) == \
+                T.ERR_ALIGN
+            assert T.gemm_select_kernel(1024, 1024, 301, FAKE, 301, Bp, 1027, Cp + 1, 1024, in_dt, fmt) == RING
             assert _kernel(256, 256, 64, cid=2, in_dt=in_dt, out_dt=fmt) == DIRECT
         assert _kernel(64, 64, 64, in_dt=T.F32, out_dt=fmt) == T.ERR_DTYPE
         assert _kernel(64, 64, 64, in_dt=fmt, out_dt=fmt) == T.ERR_DTYPE
@@ -336,9 +338,9 @@ def test_ring_only_configuration_falls_back_to_128x128():
     assert T.gemm_select_kernel_t(1024, 2048, 513, A, 513, R_, FAKE + (1 << 36), 2048, R_, FAKE + (2 << 36), 2048,
                                   R_, T.F16, T.F16, 8) == (RING, 8)
     assert _kernel_t(1024, 2048, 64, R_, R_, R_, cid=8) == (RING, 8)       # K below the ring's step: the tail
-    # an operand at an odd address: the register-staged kernel of
-    # configuration 1 (checked)
-    assert T.gemm_select_kernel_t(1024, 2048, 64, FAKE + 1, 64, R_, FAKE + (1 << 36), 2048, R_, FAKE + (2 << 36),
+    # a product the ring does not take (buffer offsets beyond 31 bits):
+    # the register-staged kernel of configuration 1
+    assert T.gemm_select_kernel_t(1024, 2048, 64, FAKE, 1 << 24, R_, FAKE + (1 << 38), 2048, R_, FAKE + (2 << 38),
                                   2048, R_, T.F16, T.F16, 8) == (T.KERNEL_GENERAL, 1)
     assert _kernel_t(1000, 2000, 1000, R_, R_, R_, cid=8) == (RING, 8)     # ragged, K tail
     assert _kernel_t(4, 4, 4, R_, R_, R_, in_dt=T.F32, out_dt=T.F32, cid=8)[0] == T.ERR_CONFIG
@@ -391,9 +393,9 @@ def test_ring_takes_unaligned_rows_where_every_element_is_kept():
                     assert got[0] == RING, (la, lb, M, N, K, oa, ob, pa, pb, got)
                     n_ring += 1
                     n_other += _last_fix(A, lda, la == R_, M, K) or _last_fix(B, ldb, lb == C_, N, K)
-                    # an odd byte address: never the ring
+                    # an odd byte address: rejected
                     got = T.gemm_select_kernel_t(M, N, K, A + 1, lda, la, B, ldb, lb, C0, N, R_, T.F16, T.F16, 1)
-                    assert got[0] != RING
+                    assert got[0] == T.ERR_ALIGN
     assert n_ring > 0
     # the last element of A ending at a page boundary (no pad possible: the
     # element loaded on its own), a pad, no pad
@@ -463,9 +465,9 @@ def test_kernel_choice_for_layouts():
     A = FAKE + (-(2 * 256 * 249)) % 4096  # A's last element ending at a page boundary
     assert T.gemm_select_kernel_t(249, 256, 256, A, 249, C_, FAKE + (1 << 36), 256, C_, FAKE + (2 << 36), 256, R_,
                                   T.F16, T.F16, 0) == (RING, 0)
-    # an odd address: the direct kernel
+    # an odd address: rejected
     assert T.gemm_select_kernel_t(249, 256, 256, FAKE + 1, 249, C_, FAKE + (1 << 36), 256, C_, FAKE + (2 << 36), 256,
-                                  R_, T.F16, T.F16, 0) == (DIRECT, 6)
+                                  R_, T.F16, T.F16, 0)[0] == T.ERR_ALIGN
     # a column-major C swaps the roles of A and B: its 128 rows become the
     # N of the row-major product (128 x 128 tiles)
     # (64 of them, K = 8192: in slices of K)

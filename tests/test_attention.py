@@ -67,6 +67,9 @@ def _call(B=1, H=1, nq=4, nk=4, d=64, q=FAKE, qs=None, k=FAKE + (1 << 30), ks=No
     (dict(H=2, os_=(512, 32, 128)), T.ERR_LD),       # head 1 starts inside a row of head 0
     (dict(o=FAKE + 100), T.ERR_ALIAS),                # output overlaps Q
     (dict(o=FAKE + (2 << 30) + 510), T.ERR_ALIAS),   # output overlaps the end of V
+    (dict(q=FAKE + 1), T.ERR_ALIGN),                  # elements not aligned to their size
+    (dict(k=FAKE + (1 << 30) + 3), T.ERR_ALIGN),
+    (dict(o=FAKE + (3 << 30) + 2, out=W.F32), T.ERR_ALIGN),
 ])
 def test_attention_arguments_are_checked(kw, code):
     assert _call(**kw) == code

@@ -28,6 +28,7 @@ OK = 0
 ERR_DIM, ERR_NULL, ERR_LD, ERR_DTYPE, ERR_ALIAS, ERR_CONFIG, ERR_LAYOUT, ERR_EPILOGUE = -1, -2, -3, -4, -5, -6, -7, -8
 ERR_HEAD_DIM = -9
 ERR_SCRATCH = -10
+ERR_ALIGN = -11
 
 EXPORTED = ["gemm", "gemm_ex", "gemm_t", "gemm_fused", "gemm_fused_noalloc", "gemm_strerror", "gemm_num_configs",
             "gemm_config_info",

@@ -133,8 +133,10 @@ int attention_fwd(int64_t batch, int64_t heads, int64_t n_q, int64_t n_k, int64_
     // row with 32-bit byte offsets
     if ((64 * (k.s[2] > v.s[2] ? k.s[2] : v.s[2]) + d) * 2 >= ((int64_t)1 << 31)) return TGEMM_ERR_LD;
     if (Q == nullptr || K == nullptr || V == nullptr || O == nullptr) return TGEMM_ERR_NULL;
-    if (!non_overlapping(o.s, batch, heads, n_q, d)) return TGEMM_ERR_LD;
     const int ob = out_dtype == TGEMM_F32 ? 4 : 2;
+    if ((uintptr_t)Q % 2 != 0 || (uintptr_t)K % 2 != 0 || (uintptr_t)V % 2 != 0 || (uintptr_t)O % ob != 0)
+        return TGEMM_ERR_ALIGN;
+    if (!non_overlapping(o.s, batch, heads, n_q, d)) return TGEMM_ERR_LD;
     uintptr_t o0, o1;
     byte_range(o, batch, heads, n_q, d, ob, o0, o1);
     const Tensor4* ins[3] = {&q, &k, &v};

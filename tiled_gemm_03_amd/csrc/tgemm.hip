@@ -144,6 +144,13 @@ bool layout_ok(int l) { return l == TGEMM_ROW_MAJOR || l == TGEMM_COL_MAJOR; }
 // Bytes spanned by a stored matrix of `rows` x `cols` in its storage order.
 uintptr_t span(int64_t rows, int64_t cols, int64_t ld, int eb) { return (uintptr_t)((rows - 1) * ld + cols) * eb; }
 
+// Every pointer aligned to its element's size (8-bit outputs: any address).
+bool elems_aligned(const Problem& p) {
+    const uintptr_t ie = elem_bytes(p.in), oe = elem_bytes(p.out);
+    if ((uintptr_t)p.A % ie != 0 || (uintptr_t)p.B % ie != 0 || (uintptr_t)p.C % oe != 0) return false;
+    return !(p.ep.on && p.ep.bias_kind != TGEMM_BIAS_NONE && (uintptr_t)p.ep.bias % elem_bytes(p.ep.bias_dt) != 0);
+}
+
 int validate(const Problem& p) {
     const int64_t M = p.M, N = p.N, K = p.K;
     if (M < 0 || N < 0 || K < 0 || M > TGEMM_MAX_DIM || N > TGEMM_MAX_DIM || K > TGEMM_MAX_DIM)
@@ -156,6 +163,7 @@ int validate(const Problem& p) {
     if (M == 0 || N == 0) return TGEMM_OK;
     if (p.C == nullptr) return TGEMM_ERR_NULL;
     if (K > 0 && (p.A == nullptr || p.B == nullptr)) return TGEMM_ERR_NULL;
+    if (!elems_aligned(p)) return TGEMM_ERR_ALIGN;
     const uintptr_t c0 = (uintptr_t)p.C, c1 = c0 + span(M, N, p.ldc, elem_bytes(p.out));
     if (K > 0) {
         const int ie = elem_bytes(p.in);
@@ -753,6 +761,7 @@ const char* gemm_strerror(int code) {
         case TGEMM_ERR_HEAD_DIM: return "attention: head dimension is neither 64 nor 128";
         case TGEMM_ERR_SCRATCH:
             return "gemm_fused_noalloc: the call needs more workspace than the library's fixed scratch holds";
+        case TGEMM_ERR_ALIGN: return "a pointer not aligned to the size of its element type";
         default: break;
     }
     if (code > 0) return hipGetErrorString((hipError_t)code);
@@ -816,6 +825,7 @@ int gemm_select_kernel_t(int64_t M, int64_t N, int64_t K, const void* A, int64_t
     Problem p;
     int v = make_problem(M, N, K, A, lda, layout_a, B, ldb, layout_b, (void*)C, ldc, layout_c, in_dtype, out_dtype, p);
     if (v != TGEMM_OK) return v;
+    if (!elems_aligned(p)) return TGEMM_ERR_ALIGN;
     Plan plan;
     v = make_plan(p, config_id, plan);
     if (v != TGEMM_OK) return v;
@@ -829,6 +839,7 @@ int gemm_split_count_t(int64_t M, int64_t N, int64_t K, const void* A, int64_t l
     Problem p;
     int v = make_problem(M, N, K, A, lda, layout_a, B, ldb, layout_b, (void*)C, ldc, layout_c, in_dtype, out_dtype, p);
     if (v != TGEMM_OK) return v;
+    if (!elems_aligned(p)) return TGEMM_ERR_ALIGN;
     Plan plan;
     v = make_plan(p, -1, plan);
     if (v != TGEMM_OK) return v;
