@@ -485,14 +485,14 @@ __device__ __forceinline__ void store4_fused(const GemmArgs& p, int row, int col
 // copy of every branch per group.  Per pass:
 //  1. the pass's accumulators go to the region (compile-time register
 //     indices, no loads), group i at region[64 i + lane];
-//  2. unless the epilogue is alpha and an activation only, the whole groups
-//     are taken EB at a time: the old C of all EB is loaded together (one
-//     wait), then each group's alpha * acc + beta * C + bias (the bias from
-//     LDS) is written back in place;
+//  2. when C is read (beta != 0), the whole groups are taken EB at a time:
+//     the old C of all EB is loaded together (one wait), then each group's
+//     alpha * acc + beta * C + bias (the bias from LDS) is written back in
+//     place;
 //  3. one loop over the whole groups, compiled once per activation and
-//     chosen by one uniform switch, applies alpha (when step 2 did not run),
-//     the activation and the output rounding, and stores; then the partial
-//     groups (n < 4) are formed and stored element by element.
+//     chosen by one uniform switch, applies alpha and the bias (when step 2
+//     did not run), the activation and the output rounding, and stores; then
+//     the partial groups (n < 4) are formed and stored element by element.
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 typedef __attribute__((address_space(3))) float lds_float;
@@ -573,7 +573,8 @@ __device__ __forceinline__ void fused_epilogue(const GemmArgs& p, lds_f32x4* reg
     const float alpha = arg_value(p.alpha), beta = arg_value(p.beta);
     const bool rd_c = beta != 0.f;
     const bool has_bias = p.bias_kind != BIAS_NONE;
-    const bool combine = rd_c || has_bias;
+    // step 2 runs only when C is read; a bias alone is added in step 3
+    const bool combine = rd_c;
     static_for<0, NB / PB>([&](auto pass_t) {
         constexpr int b0 = decltype(pass_t)::value * PB;
         // 1: the pass's accumulators into the region
@@ -630,6 +631,7 @@ __device__ __forceinline__ void fused_epilogue(const GemmArgs& p, lds_f32x4* reg
         // a loop compiled for the call's activation (one uniform switch),
         // then the partial groups (N % 4 != 0: element by element, rare)
         const bool scale = !combine && alpha != 1.f;
+        const bool late_bias = !combine && has_bias;
         auto whole = [&](auto act_t) __attribute__((always_inline)) {
             constexpr int ACT = decltype(act_t)::value;
             for (int i = 0; i < NG; ++i) {
@@ -639,6 +641,11 @@ __device__ __forceinline__ void fused_epilogue(const GemmArgs& p, lds_f32x4* reg
                 if (WHOLE ? n <= 0 : n != 4) continue;
                 f32x4 t = region[i * 64 + lane];
                 if (scale) t *= alpha;
+                if (late_bias) {
+                    const f32x4 bc = *(const lds_f32x4*)(bias_col + (col - col0));
+                    const float br = bias_row[row - row0];
+                    t += p.bias_kind == BIAS_COL ? bc : f32x4{br, br, br, br};
+                }
                 store4<OUT>(p.C + ((int64_t)row * p.ldc + col) * OB, activate_t<ACT>(t[0]), activate_t<ACT>(t[1]),
                             activate_t<ACT>(t[2]), activate_t<ACT>(t[3]), vec, p.fp8_e5m2);
             }
