@@ -565,7 +565,7 @@ int scratch_address(float** out) {
 // The library's memory pool of the current device, for split-K workspaces:
 // stream-ordered allocations (a call on one stream never shares its
 // workspace with a call on another), and memory kept in the pool between
-// calls rather than returned to the driver at each synchronisation (the
+// calls rather than released to the HIP runtime at each synchronisation (the
 // default pool's release threshold is 0).
 hipMemPool_t workspace_pool(hipError_t& e) {
     static std::mutex mu;

@@ -16,7 +16,7 @@ which `table_choice` in tgemm.hip consults before its rule (exact matches of
 row-major calls only; rebuild the library afterwards), and a JSON record of
 every timing.
 
-Usage (on the GPU machine):
+Usage (on an MI355X, with the library built):
     python -m tiled_gemm_03_amd.tune [--shapes M,N,K,in,out[,lda,ldb,ldc] ...]
                                      [--emit] [--json FILE]
 Without --shapes it tunes the five workloads of the benchmark table.
