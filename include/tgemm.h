@@ -140,7 +140,7 @@ int gemm_ex(int64_t M, int64_t N, int64_t K,
  * row-major A and B take every configuration; with a column-major operand
  * the direct-to-LDS ring kernels of configurations 0 and 1 (8 with a
  * row-major A; its other products run configuration 1) and the direct
- * kernels of configurations 6 and 7 (configurations 2 to 5 return
+ * kernels of configurations 6 and 7 (configurations 2 to 5 and 9 return
  * TGEMM_ERR_CONFIG there, and products whose 32-bit buffer offsets would
  * overflow return TGEMM_ERR_DIM).  config_id -1:
  * the table's choice.  Other arguments, ownership and errors as gemm_ex.

@@ -13,6 +13,7 @@ KernelFn f32_pick(bool fast) {
 KernelFn tiled_kernel_f32(int cfg, int in, int out, bool fast, bool epi) {
     if (in != DT_F32 || out != DT_F32) return nullptr;
     if (cfg == CFG_F32_MID) return epi ? f32_pick<CfgF32Mid, true>(fast) : f32_pick<CfgF32Mid, false>(fast);
+    if (cfg == CFG_F32_BIG) return epi ? f32_pick<CfgF32Big, true>(fast) : f32_pick<CfgF32Big, false>(fast);
     if (cfg == CFG_F32_TINY) return epi ? f32_pick<CfgF32Tiny, true>(fast) : f32_pick<CfgF32Tiny, false>(fast);
     return nullptr;
 }

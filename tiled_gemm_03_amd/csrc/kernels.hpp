@@ -19,6 +19,7 @@ using CfgSmall = TileCfg<64, 64, 64, 2, 2, 2, 2>;    // 4 waves, 32x32 per wave
 using CfgTiny = TileCfg<32, 32, 64, 1, 1, 2, 4>;     // 1 wave
 using CfgF32Mid = TileCfg<64, 64, 32, 2, 2, 4, 2>;   // fp32 inputs
 using CfgF32Tiny = TileCfg<32, 32, 32, 1, 1, 4, 4>;  // fp32 inputs, 1 wave
+using CfgF32Big = TileCfg<128, 128, 32, 2, 2, 4, 2>; // fp32 inputs, 64x64 per wave
 // direct-to-LDS ring kernels of the two largest tiles
 using RingBig = RingCfg<256, 256, 2, 2, 1>;
 using RingMid = RingCfg<128, 128, 2, 2, 2>;
@@ -28,11 +29,11 @@ using RingMid = RingCfg<128, 128, 2, 2, 2>;
 using RingSmall = RingCfg<64, 128, 2, 2, 2>;
 
 enum { CFG_BIG = 0, CFG_MID = 1, CFG_SMALL = 2, CFG_TINY = 3, CFG_F32_MID = 4, CFG_F32_TINY = 5,
-       CFG_DIRECT = 6, CFG_F32_DIRECT = 7, CFG_RING_SMALL = 8, NUM_CONFIGS = 9 };
+       CFG_DIRECT = 6, CFG_F32_DIRECT = 7, CFG_RING_SMALL = 8, CFG_F32_BIG = 9, NUM_CONFIGS = 10 };
 
 typedef void (*KernelFn)(GemmArgs);
 
-// Register-staged kernel of configuration cfg (CFG_BIG .. CFG_F32_TINY) for
+// Register-staged kernel of configuration cfg (CFG_BIG .. CFG_F32_TINY, CFG_F32_BIG) for
 // (in, out) (DT_* values); fast: the unchecked whole-tile path; epi: the
 // fused epilogue (GemmArgs::epi ... act).  nullptr if the pair is not served.
 // One definition per configuration (k_tiled_<cfg>.hip).
