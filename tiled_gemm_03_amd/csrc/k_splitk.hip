@@ -11,16 +11,28 @@
 
 namespace tgemm {
 
+// One wave per workgroup: a skinny product's few output groups still spread
+// over every CU.  The loads of eight slices are issued together and added in
+// slice order afterwards, so the memory latency is paid once per eight
+// slices and the sum is the same as slice by slice.
 template <int OUT>
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p, const float* w, int64_t ldw, int64_t slice,
-                                                             int splits) {
+__global__ __launch_bounds__(kSplitkReduceThreads) void splitk_reduce_kernel(GemmArgs p, const float* w, int64_t ldw,
+                                                                             int64_t slice, int splits) {
     const int64_t groups = ((int64_t)p.N + 3) / 4;  // of each row
-    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t gid = (int64_t)blockIdx.x * kSplitkReduceThreads + threadIdx.x;
     if (gid >= (int64_t)p.M * groups) return;
     const int row = (int)(gid / groups), col = (int)(gid - (int64_t)row * groups) * 4;
     const float* src = w + (int64_t)row * ldw + col;  // ldw % 4 == 0: 16-byte aligned groups
     f32x4 acc = *(const f32x4*)src;
-    for (int s = 1; s < splits; ++s) acc += *(const f32x4*)(src + s * slice);
+    for (int s = 1; s < splits; s += 8) {
+        f32x4 v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (s + j < splits) v[j] = *(const f32x4*)(src + (s + j) * slice);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (s + j < splits) acc += v[j];
+    }
     const int n = p.N - col < 4 ? p.N - col : 4;
     store4_fused<OUT>(p, row, col, n, p.vec_c != 0 && n == 4, acc);
 }

@@ -58,6 +58,8 @@ KernelFn ring_kernel_small_fused(int in, int out, int la, int lb, bool kt);
 // of 4), floats per slice, and the number of slices.
 typedef void (*SplitkReduceFn)(GemmArgs, const float*, int64_t, int64_t, int);
 SplitkReduceFn splitk_reduce_kernel_for(int out);
+// Threads per workgroup of that kernel, one group of 4 outputs each.
+constexpr int kSplitkReduceThreads = 64;
 
 // Direct kernel for (in, out), the layouts of A and B, and whether each
 // operand takes 16-byte loads.  k_direct.hip.

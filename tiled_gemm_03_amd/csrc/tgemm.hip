@@ -333,7 +333,7 @@ int tuned_choice(const Problem& p) {
 // at 2048 the second kernel and the workspace cost more than the slices
 // gain: 1024 x 512 x 2048 28 against 26 us).  Each slice is
 // a multiple of the ring's K step (the last one takes the rest, with the K
-// tail when K is not a multiple), at least 512 long, and the slices bring
+// tail when K is not a multiple), at least 256 long, and the slices bring
 // the workgroups to about 256; the fp32 partials go through a workspace of
 // splits x M x roundup(N, 4) floats (at most 256 MiB).  Needs the plain
 // epilogue's whole groups (N % 4 == 0) and rows of whole 16-byte chunks.
@@ -642,7 +642,8 @@ int run_split(const Problem& p, const Plan& plan, const ConfigEntry& c, const Ge
         int64_t ldw_ = ldw, slice_ = slice;
         int splits = plan.splits;
         void* rargs[] = {&ra, &wc, &ldw_, &slice_, &splits};
-        e = hipLaunchKernel((const void*)plan.reduce, dim3((unsigned)((groups + 255) / 256)), dim3(256), rargs, 0, st);
+        const int64_t rb = (groups + kSplitkReduceThreads - 1) / kSplitkReduceThreads;
+        e = hipLaunchKernel((const void*)plan.reduce, dim3((unsigned)rb), dim3(kSplitkReduceThreads), rargs, 0, st);
         if (e == hipSuccess) e = hipGetLastError();
     }
     if (fixed == nullptr) {
