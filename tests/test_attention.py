@@ -282,3 +282,36 @@ def test_attention_rejects_before_launch_on_device_tensors():
     o32 = torch.zeros(1, 1, 8, 32, dtype=torch.float16, device="cuda:0")
     assert T.attention_tensors(q32, q32, q32, o32, check=False) == T.ERR_HEAD_DIM
     assert torch.all(o == 0).item()
+
+
+def _random_case(seed):
+    """One seeded draw of every argument the kernel takes: head size, types,
+    batch and heads, ragged query and key counts, scale and its sign, the
+    causal mask, the memory layout and the rows after each head's."""
+    rng = np.random.default_rng(5000 + seed)
+    d = int(rng.choice([64, 128]))
+    dt = int(rng.choice([W.F16, W.BF16]))
+    out = int(rng.choice([dt, W.F32]))
+    B, H = int(rng.integers(1, 3)), int(rng.integers(1, 7))
+    nq, nk = int(rng.integers(1, 400)), int(rng.integers(1, 400))
+    scale = float(rng.choice([d ** -0.5, 0.125, 1.0, -0.25]))
+    causal = bool(rng.random() < 0.5)
+    layout = str(rng.choice(["bhnd", "bnhd", "bhnd_odd"]))
+    tail = int(rng.choice([0, 1, 5]))
+    return B, H, nq, nk, d, dt, out, scale, causal, layout, tail
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("seed", range(32))
+def test_attention_random_sweep(seed):
+    """Seeded random calls, each held to the bound of the full-parity cases,
+    with the rows past each head's queries left unwritten."""
+    from gpu_helpers import say
+    case = _random_case(seed)
+    B, H, nq, nk, d, dt, out, scale, causal, layout, tail = case
+    say(f"[attention] sweep {seed}: {case}")
+    q, k, v = W.attention_inputs(B, H, nq, nk, d, dt, seed=seed)
+    o, untouched = _run(q, k, v, dt, out, scale, causal, layout, tail)
+    assert untouched, "rows past n_q were written"
+    ref = oracle_attention(q, k, v, dt, scale=scale, causal=causal)
+    _check(o, ref, _bound(q, k, v, ref, dt, out, scale, causal), str(case))
