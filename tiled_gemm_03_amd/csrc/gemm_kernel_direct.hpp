@@ -32,6 +32,15 @@
 // The MFMA takes B as its first operand and A as its second, so the
 // accumulator holds C transposed: lane l owns row l % 16 and columns
 // 4 q .. 4 q + 3 of the block.
+//
+// K split over the waves (p.splits == 4; else 1): when the steps of K are
+// more than one ring holds but a quarter of them fits one, a workgroup
+// computes one 16 x 16 block and its four waves take a quarter of the steps
+// each (the partial last step to the fourth), all loads issued at once:
+// one memory round trip instead of several.  The four partial blocks meet in
+// LDS and the first wave adds them in wave order (the same order on every
+// run) before the epilogue.  The sum is that of the unsplit kernel up to
+// the order of the fp32 additions.
 
 #pragma once
 #include <type_traits>
@@ -61,9 +70,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void gemm_kern
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int q = lane >> 4, l16 = lane & 15;
 
+    const bool ks = p.splits == 4;  // K split over the waves, 16 x 16 tiles
     int tm, tn;
     tile_of(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
-    const int m0 = tm * 32 + 16 * (wave >> 1), n0 = tn * 32 + 16 * (wave & 1);
+    const int m0 = ks ? tm * 16 : tm * 32 + 16 * (wave >> 1), n0 = ks ? tn * 16 : tn * 32 + 16 * (wave & 1);
     const int M = p.M, N = p.N, K = p.K;
     const int64_t lda = p.lda, ldb = p.ldb;
 
@@ -165,7 +175,24 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void gemm_kern
     // are issued when step s is computed.  Loads past the last full step read
     // zeros or in-bounds data that is never used.
     const int nfull = K / 32;
-    if (K > 0) {
+    if (K > 0 && ks) {
+        // this wave's steps [s0, s1), at most D (the host's condition), and
+        // the fourth wave's partial step: every load issued before the first
+        // MFMA
+        const int quarter = (nfull + 3) / 4;
+        const int s0 = wave * quarter < nfull ? wave * quarter : nfull;
+        const int s1 = s0 + quarter < nfull ? s0 + quarter : nfull;
+        const bool tail = K % 32 != 0 && wave == 3;
+        Frag ring[D], f;
+#pragma unroll
+        for (int t = 0; t < D; ++t)
+            if (s0 + t < s1) load_step(ring[t], s0 + t);
+        if (tail) load_step(f, nfull);
+#pragma unroll
+        for (int t = 0; t < D; ++t)
+            if (s0 + t < s1) mma_step(nomask, ring[t], s0 + t);
+        if (tail) mma_step(mask, f, nfull);
+    } else if (K > 0) {
         Frag ring[D];
 #pragma unroll
         for (int t = 0; t < D; ++t) load_step(ring[t], t);
@@ -187,6 +214,16 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void gemm_kern
             load_step(f, nfull);
             mma_step(mask, f, nfull);
         }
+    }
+
+    if (ks) {  // the waves' partial blocks, added by the first wave
+        __shared__ f32x4 part[3][64];
+        if (wave > 0) part[wave - 1][lane] = acc;
+        __syncthreads();
+        if (wave > 0) return;
+        acc += part[0][lane];
+        acc += part[1][lane];
+        acc += part[2][lane];
     }
 
     // epilogue: row m0 + l%16, columns n0 + 4q .. +3; fp32 -> fp16 / bf16

@@ -428,8 +428,17 @@ struct Plan {
     int kind;  // TGEMM_KERNEL_*
     KernelFn fn;
     int splits = 1, k_split = 0;          // split-K (kind TGEMM_KERNEL_RING_SPLITK)
+    bool wave_split = false;              // direct kernel: K over the four waves, 16 x 16 tiles
     SplitkReduceFn reduce = nullptr;      // the sum of the slices
 };
+
+// Steps of 32 of K that the direct kernel keeps in flight (its register
+// ring): as many as keep its loads within the 63 that vmcnt counts, 2 to 8.
+int direct_depth(const Problem& p, bool va, bool vb) {
+    const int per_step = p.in == TGEMM_F32 ? 16 : (va ? 1 : 8) + (vb ? 1 : 8);
+    const int d = 63 / per_step;
+    return d < 2 ? 2 : d > 8 ? 8 : d;
+}
 
 int plan_direct(const Problem& p, Plan& plan) {
     const bool kca = p.la == LAYOUT_ROW, kcb = p.lb == LAYOUT_COL;
@@ -439,7 +448,12 @@ int plan_direct(const Problem& p, Plan& plan) {
     plan.kind = TGEMM_KERNEL_DIRECT;
     plan.fn = direct_kernel(p.in, kernel_out(p.out), p.la, p.lb, va, vb, p.ep.on || is_fp8(p.out));
     if (plan.fn == nullptr) return TGEMM_ERR_DTYPE;
-    if (ceil_div(p.M, 32) * ceil_div(p.N, 32) > 0x7fffffff) return TGEMM_ERR_DIM;
+    // K over the four waves when one ring of steps does not cover K and a
+    // quarter of the steps fits one: a single memory round trip
+    const int64_t steps = p.K / 32, depth = direct_depth(p, va, vb);
+    plan.wave_split = steps > depth && (steps + 3) / 4 <= depth;
+    const int t = plan.wave_split ? 16 : 32;
+    if (ceil_div(p.M, t) * ceil_div(p.N, t) > 0x7fffffff) return TGEMM_ERR_DIM;
     return TGEMM_OK;
 }
 
@@ -669,8 +683,8 @@ int run(const Problem& p, void* stream, int config_id, float* fixed = nullptr) {
     args.M = (int)p.M;
     args.N = (int)p.N;
     args.K = (int)p.K;
-    args.tiles_m = (int)ceil_div(p.M, c.bm);
-    args.tiles_n = (int)ceil_div(p.N, c.bn);
+    args.tiles_m = (int)ceil_div(p.M, plan.wave_split ? 16 : c.bm);
+    args.tiles_n = (int)ceil_div(p.N, plan.wave_split ? 16 : c.bn);
     args.group_m = tuning().group_m;
     args.swz_mask = tuning().swizzle ? c.cpr - 1 : 0;
     if (plan.kind == TGEMM_KERNEL_RING || plan.kind == TGEMM_KERNEL_RING_SPLITK)
@@ -685,7 +699,7 @@ int run(const Problem& p, void* stream, int config_id, float* fixed = nullptr) {
     args.bias_dt = p.ep.bias_dt;
     args.act = p.ep.act;
     args.fp8_e5m2 = p.out == TGEMM_FP8_E5M2 ? 1 : 0;
-    args.splits = 1;
+    args.splits = plan.wave_split ? 4 : 1;  // the direct kernel's K over its waves
     args.k_split = (int)p.K;
     args.split_stride = 0;
     const bool ring = plan.kind == TGEMM_KERNEL_RING;
