@@ -230,7 +230,7 @@ def test_kernel_choice_ring_path():
 def test_table_prefers_256_tiles_beyond_two_rounds_of_128_tiles():
     """256 x 256 tiles when they fill the 256 CUs or when 128 x 128 tiles
     would need three or more rounds; else 128 x 128 (or 64 x 128, also for
-    small products)."""
+    small products that the direct kernel does not take)."""
     RING = T.KERNEL_RING
     assert _kernel_t(3072, 3072, 3072, R_, R_, R_) == (RING, 0)      # 144 big tiles, 576 mid ones
     assert _kernel_t(3000, 3000, 3000, R_, R_, R_) == (RING, 0)
@@ -239,11 +239,30 @@ def test_table_prefers_256_tiles_beyond_two_rounds_of_128_tiles():
     assert _kernel_t(1024, 8192, 1024, R_, R_, R_) == (RING, 1)
     assert _kernel_t(3072, 3072, 3072, C_, R_, R_) == (RING, 0)      # other layouts alike
     assert _kernel_t(4096, 4096, 1024, R_, R_, R_) == (RING, 0)
-    # small products: the 64 x 128 ring from 4 of its tiles
-    for n in (256, 384, 512, 768):
+    # small products: the 64 x 128 ring from 4 of its tiles, or one tile
+    # with K >= 1024, where the direct kernel does not take them
+    for n in (512, 768):
         assert _kernel_t(n, n, n, R_, R_, R_) == (RING, 8), n
     assert _kernel_t(512, 512, 2048, R_, R_, R_) == (RING, 8)
-    assert _kernel_t(128, 128, 256, R_, R_, R_)[1] != 8             # 2 tiles: not the ring
+    assert _kernel_t(64, 64, 1024, R_, R_, R_) == (RING, 8)
+
+
+def test_table_sends_small_products_with_medium_k_to_the_direct_kernel():
+    """128 <= K <= 512 (16-bit) or K >= 128 (fp32) with all of K's loads in
+    flight at once and at most 576 (fp32: 256) workgroups: the direct kernel;
+    K = 64, or more workgroups, or a longer K: the tiles or rings."""
+    D, RING, TI = T.KERNEL_DIRECT, T.KERNEL_RING, T.KERNEL_TILED
+    for n in (128, 256, 384):            # 384^3: K over the waves, 24 x 24 workgroups of 16 x 16
+        assert _kernel_t(n, n, n, R_, R_, R_) == (D, 6), n
+    assert _kernel_t(128, 128, 256, R_, R_, R_) == (D, 6)
+    assert _kernel_t(128, 128, 64, R_, R_, R_) == (TI, 3)           # K = 64: 32 x 32 tiles
+    assert _kernel_t(512, 512, 256, R_, R_, R_) == (RING, 8)       # 1024 workgroups of 16 x 16
+    f32 = dict(in_dt=T.F32, out_dt=T.F32)
+    assert _kernel_t(128, 128, 256, R_, R_, R_, **f32) == (D, 7)
+    assert _kernel_t(256, 256, 256, R_, R_, R_, **f32) == (D, 7)     # 256 workgroups of 16 x 16
+    assert _kernel_t(512, 512, 128, R_, R_, R_, **f32) == (TI, 5)    # 1024 of them
+    assert _kernel_t(128, 128, 512, R_, R_, R_, **f32) == (TI, 5)    # a quarter of K exceeds the ring
+    assert _kernel_t(128, 128, 64, R_, R_, R_, **f32) == (TI, 5)
 
 
 def _splits(M, N, K, la=T.ROW_MAJOR, lb=T.ROW_MAJOR, lc=T.ROW_MAJOR, lda=None, ldb=None, ldc=None, in_dt=T.F16,

@@ -373,6 +373,36 @@ bool big_tiles_pay(int64_t M, int64_t N) {
     return tiles_for(kConfigs[CFG_BIG], M, N) >= 256 || tiles_for(kConfigs[CFG_MID], M, N) > 512;
 }
 
+// Steps of 32 of K that the direct kernel keeps in flight (its register
+// ring): as many as keep its loads within the 63 that vmcnt counts, 2 to 8.
+int direct_depth(const Problem& p, bool va, bool vb) {
+    const int per_step = p.in == TGEMM_F32 ? 16 : (va ? 1 : 8) + (vb ? 1 : 8);
+    const int d = 63 / per_step;
+    return d < 2 ? 2 : d > 8 ? 8 : d;
+}
+
+// How the direct kernel runs a call: its 16-byte load flags, whether K goes
+// over the four waves (when one ring of steps does not cover K and a quarter
+// of the steps fits one), whether all of a wave's loads are in flight at
+// once (one memory round trip), and its workgroups.
+struct DirectShape {
+    bool va, vb, wave_split, one_trip;
+    int64_t workgroups;
+};
+DirectShape direct_shape(const Problem& p) {
+    DirectShape d;
+    const bool kca = p.la == LAYOUT_ROW, kcb = p.lb == LAYOUT_COL;
+    const bool half = p.in != TGEMM_F32;
+    d.va = half && kca && (uintptr_t)p.A % 16 == 0 && p.lda % 8 == 0 && p.K % 8 == 0;
+    d.vb = half && kcb && (uintptr_t)p.B % 16 == 0 && p.ldb % 8 == 0 && p.K % 8 == 0;
+    const int64_t steps = p.K / 32, depth = direct_depth(p, d.va, d.vb);
+    d.wave_split = steps > depth && (steps + 3) / 4 <= depth;
+    d.one_trip = steps <= depth || d.wave_split;
+    const int t = d.wave_split ? 16 : 32;
+    d.workgroups = ceil_div(p.M, t) * ceil_div(p.N, t);
+    return d;
+}
+
 int table_choice(const Problem& p) {
     const int tuned = tuned_choice(p);
     if (tuned >= 0) return tuned;
@@ -384,6 +414,14 @@ int table_choice(const Problem& p) {
         // 1099 us on 64 x 64, 2048^3: 138 against 145 us), else 64 x 64
         if (tiles_for(kConfigs[CFG_F32_BIG], M, N) >= 256) return CFG_F32_BIG;
         if (tiles_for(kConfigs[CFG_F32_MID], M, N) >= 256) return CFG_F32_MID;
+        // the direct kernel where all of K's loads go out at once, from
+        // K = 128 and up to 256 workgroups (traced: 128^3 3.8 against 5.2 us
+        // on 32 x 32 tiles, 256^2 x 256 5.0 against 7.9; K = 64, longer K
+        // or more workgroups: the 32 x 32 tile)
+        if (small && p.K >= 128 && direct_fits(p)) {
+            const DirectShape d = direct_shape(p);
+            if (d.one_trip && d.workgroups <= 256) return CFG_F32_DIRECT;
+        }
         if (small && !tiled_fast(kConfigs[CFG_F32_TINY], p)) return CFG_F32_DIRECT;
         return CFG_F32_TINY;
     }
@@ -405,14 +443,26 @@ int table_choice(const Problem& p) {
         return CFG_RING_SMALL;
     if (tiles_for(kConfigs[CFG_MID], M, N) >= 128 && ring_applies(kConfigs[CFG_MID], p)) return CFG_MID;
     if (tiles_for(kConfigs[CFG_MID], M, N) >= 256) return CFG_MID;
+    // small products with 128 <= K <= 512: the direct kernel where all of
+    // K's loads go out at once and it runs at most 576 workgroups (traced
+    // kernel times: 128^2 x 512 3.4 us against 5.0 on the 64 x 128 ring and
+    // 7.5 on 32 x 32 tiles, 384^2 x 512 5.2 against 5.8; 512^2 x 256, 1024
+    // workgroups: 5.2 against 4.9 on the ring)
+    if (small && p.K >= 128 && p.K <= 512 && direct_fits(p)) {
+        const DirectShape d = direct_shape(p);
+        if (d.one_trip && d.workgroups <= 576) return CFG_DIRECT;
+    }
     // fewer tiles: the 64 x 128 ring (in slices of K when K is long).  It
     // beats the register-staged 64 x 64 tile on every product measured from
     // 256^3 to 768^3 and 512 x 512 x 2048 (7.8 against 9.3 us at 512^3, 12.8
-    // against 23.6 us at 512 x 512 x 2048); below 4 of its tiles, or with a
-    // small C it could store only through the fused epilogue, the other
-    // kernels stay
+    // against 23.6 us at 512 x 512 x 2048), and from K = 1024 every other
+    // kernel even on one or two of its tiles (64^2 x 1024 6.1 us against 7.5
+    // direct and 11.9 on 32 x 32 tiles); below 4 of its tiles and a shorter
+    // K, or with a small C it could store only through the fused epilogue,
+    // the other kernels stay
     int k_split;
-    if (tiles_for(kConfigs[CFG_RING_SMALL], M, N) >= 4 && ring_applies(kConfigs[CFG_RING_SMALL], p) &&
+    if ((tiles_for(kConfigs[CFG_RING_SMALL], M, N) >= 4 || p.K >= 1024) &&
+        ring_applies(kConfigs[CFG_RING_SMALL], p) &&
         (ring_plain_stores(p) || !small || split_count(kConfigs[CFG_RING_SMALL], p, k_split) > 1))
         return CFG_RING_SMALL;
     if (tiles_for(kConfigs[CFG_SMALL], M, N) >= 256) return CFG_SMALL;
@@ -432,28 +482,13 @@ struct Plan {
     SplitkReduceFn reduce = nullptr;      // the sum of the slices
 };
 
-// Steps of 32 of K that the direct kernel keeps in flight (its register
-// ring): as many as keep its loads within the 63 that vmcnt counts, 2 to 8.
-int direct_depth(const Problem& p, bool va, bool vb) {
-    const int per_step = p.in == TGEMM_F32 ? 16 : (va ? 1 : 8) + (vb ? 1 : 8);
-    const int d = 63 / per_step;
-    return d < 2 ? 2 : d > 8 ? 8 : d;
-}
-
 int plan_direct(const Problem& p, Plan& plan) {
-    const bool kca = p.la == LAYOUT_ROW, kcb = p.lb == LAYOUT_COL;
-    const bool half = p.in != TGEMM_F32;
-    const bool va = half && kca && (uintptr_t)p.A % 16 == 0 && p.lda % 8 == 0 && p.K % 8 == 0;
-    const bool vb = half && kcb && (uintptr_t)p.B % 16 == 0 && p.ldb % 8 == 0 && p.K % 8 == 0;
+    const DirectShape d = direct_shape(p);
     plan.kind = TGEMM_KERNEL_DIRECT;
-    plan.fn = direct_kernel(p.in, kernel_out(p.out), p.la, p.lb, va, vb, p.ep.on || is_fp8(p.out));
+    plan.fn = direct_kernel(p.in, kernel_out(p.out), p.la, p.lb, d.va, d.vb, p.ep.on || is_fp8(p.out));
     if (plan.fn == nullptr) return TGEMM_ERR_DTYPE;
-    // K over the four waves when one ring of steps does not cover K and a
-    // quarter of the steps fits one: a single memory round trip
-    const int64_t steps = p.K / 32, depth = direct_depth(p, va, vb);
-    plan.wave_split = steps > depth && (steps + 3) / 4 <= depth;
-    const int t = plan.wave_split ? 16 : 32;
-    if (ceil_div(p.M, t) * ceil_div(p.N, t) > 0x7fffffff) return TGEMM_ERR_DIM;
+    plan.wave_split = d.wave_split;
+    if (d.workgroups > 0x7fffffff) return TGEMM_ERR_DIM;
     return TGEMM_OK;
 }
 
