@@ -268,8 +268,9 @@ int gemm_select_config(int64_t M, int64_t N, int64_t K,
 #define TGEMM_KERNEL_TILED 1   /* register-staged, whole tiles, aligned operands              */
 #define TGEMM_KERNEL_RING 2    /* direct-to-LDS rings: 16-bit inputs, any M, N, K, layout and
                                   leading dimension (configurations 0, 1 and 8)             */
-#define TGEMM_KERNEL_DIRECT 3  /* operands straight from memory to registers, no LDS: small,
-                                  ragged or unaligned products (configurations 6 and 7)     */
+#define TGEMM_KERNEL_DIRECT 3  /* operands straight from memory to registers, no LDS stage:
+                                  small, ragged or unaligned products (configurations 6 and
+                                  7)                                                        */
 #define TGEMM_KERNEL_RING_SPLITK 4 /* the ring kernel over slices of K (products with too few
                                   output tiles for the CUs and a long K: configuration 8, or
                                   1 for column-major operands), each slice's fp32 partial in

@@ -6,7 +6,8 @@
 // latency per stage.  Here each wave owns one 16 x 16 block of C (the output
 // tile of page "企业官网建设流程全解析" §3.3 shrunk to one MFMA block; a
 // workgroup is 2 x 2 waves, 32 x 32) and reads the MFMA operands straight
-// from global memory into registers, with no LDS and no barrier, through a
+// from global memory into registers, with no LDS stage and no barrier in the
+// K loop, through a
 // ring of D register slots (2 to 8, as many as keep the loads in flight within
 // what vmcnt counts): the loads of step s + D (steps of 32 of K) are issued
 // when step s is computed.

@@ -22,7 +22,7 @@ namespace {
 struct ConfigEntry {
     const char* name;
     int in_family;  // TGEMM_F16 (serves F16 and BF16) or TGEMM_F32
-    bool direct;    // the direct kernel (32 x 32 per workgroup, no LDS)
+    bool direct;    // the direct kernel (32 x 32 per workgroup, or 16 x 16 with K over its waves)
     int bm, bn, bk, wm, wn, eb, lds_bytes, threads, cpr;
     // register-staged kernels (row-major operands only)
     KernelFn (*tiled)(int in, int out, bool fast, bool epi);
@@ -55,7 +55,8 @@ KernelFn tiled_f32_tiny(int in, int out, bool fast, bool epi) {
 #define ENTRY_RING_ONLY(name, R, rsel)                                                                          \
     {name, TGEMM_F16, false, R::BM, R::BN, R::BK, R::WM, R::WN, 2, R::LDS_BYTES, R::THREADS, 1, nullptr, rsel, \
      R::B_BK, R::B_STAGES, R::K_MULT, R::LDS_BYTES, R::LOOKAHEAD, R::A_BK, R::A_STAGES, R::A_COL_OK}
-// direct kernel: 32 x 32 per workgroup of 2 x 2 waves, steps of 32 of K
+// direct kernel: 32 x 32 per workgroup of 2 x 2 waves (16 x 16 when its four
+// waves split K), steps of 32 of K
 #define ENTRY_DIRECT(name, fam, eb) \
     {name, fam, true, 32, 32, 32, 2, 2, eb, 0, 256, 1, nullptr, nullptr, 0, 0, 0, 0, 0, 0, 0, false}
 
@@ -838,7 +839,8 @@ int gemm_config_info(int id, tgemm_config_info* out) {
     out->waves_n = c.wn;
     out->name = c.name;
     if (c.direct) {
-        // operands go straight to registers: no LDS stage
+        // operands go straight to registers: no LDS stage (the 3 KiB where the
+        // waves' partial blocks meet when they split K are not a stage)
         out->block_k = 32;
         out->stages = 0;
         out->mfma_m = 16;
