@@ -276,9 +276,13 @@ int gemm_select_config(int64_t M, int64_t N, int64_t K,
                                   1 for column-major operands), each slice's fp32 partial in
                                   a workspace, then a second kernel that sums the slices in
                                   a fixed order and applies the epilogue; the workspace
-                                  (slices x M x N rounded up to 4, fp32) comes from the
-                                  stream's memory pool (hipMallocAsync / hipFreeAsync on the
-                                  call's stream).  Only the table's choice (config_id -1)
+                                  (slices x M x N rounded up to 4, fp32) is the stream's own,
+                                  kept between calls for the last 8 streams of each device
+                                  (from the library's memory pool, held until the process
+                                  ends; a call waits on an event of the workspace's previous
+                                  call, and calls from several host threads are serialised
+                                  around its two launches).  Under stream capture use
+                                  gemm_fused_noalloc.  Only the table's choice (config_id -1)
                                   splits; TGEMM_NO_SPLITK=1 in the environment turns it off */
 
 /* Host-side lookup only (no GPU call): which kernel gemm_ex(..., config_id)

@@ -143,8 +143,8 @@ def test_split_k_random_values_and_determinism():
 
 
 def test_split_k_other_stream():
-    """A call on a stream of its own (the workspace is taken and returned in
-    that stream's order) next to one on the current stream."""
+    """A call on a stream of its own (the workspace is that stream's) next to
+    one on the current stream."""
     M, N, K = 512, 512, 16384
     a, b = W.integer_inputs(M, N, K, W.F16, seed=8)
     ad, bd = G.to_device(a, W.F16), G.to_device(b, W.F16)
@@ -160,3 +160,31 @@ def test_split_k_other_stream():
     want = G.oracle_values(a, b, W.F16)
     assert np.array_equal(G.values(c1, W.F32), want)
     assert np.array_equal(G.values(c2, W.F32), want)
+
+
+def test_split_k_workspaces_across_many_streams():
+    """The library keeps one workspace per stream for its last 8 streams:
+    calls on 10 streams in turn, three rounds, take workspaces over from one
+    another (the least recently used one, after its last call's kernels) and
+    grow them (4, 8, then 16 MiB of partials), with no synchronisation
+    between the calls; every result exact."""
+    shapes = [(256, 256, 4096), (256, 256, 65536), (512, 512, 16384)]
+    rounds = []
+    for i, (M, N, K) in enumerate(shapes):
+        a, b = W.integer_inputs(M, N, K, W.F16, seed=30 + i)
+        ad, bd = G.to_device(a, W.F16), G.to_device(b, W.F16)
+        outs = [G.out_tensor(M, N, W.F32)[1] for _ in range(10)]
+        kind, cfg, s = plan_of(ad, bd, outs[0], W.F16, W.F32)
+        assert kind == SPLIT and s > 1, (M, N, K, kind, s)
+        rounds.append((ad, bd, outs, G.oracle_values(a, b, W.F16), s))
+    streams = [torch.cuda.Stream() for _ in range(10)]
+    torch.cuda.synchronize()  # inputs and NaN-filled outputs in place before any other stream runs
+    for ad, bd, outs, _, s in rounds:
+        G.say(f"[case] split-K {tuple(ad.shape)} x {tuple(bd.shape)}, {s} slices, on 10 streams")
+        for st, c in zip(streams, outs):
+            with torch.cuda.stream(st):
+                T.gemm_tensors(ad, bd, c, stream=st.cuda_stream)
+    torch.cuda.synchronize()
+    for _, _, outs, want, _ in rounds:
+        for c in outs:
+            assert np.array_equal(G.values(c, W.F32), want)

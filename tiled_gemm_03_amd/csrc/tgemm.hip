@@ -618,10 +618,10 @@ int scratch_address(float** out) {
 }
 
 // The library's memory pool of the current device, for split-K workspaces:
-// stream-ordered allocations (a call on one stream never shares its
-// workspace with a call on another), and memory kept in the pool between
-// calls rather than released to the HIP runtime at each synchronisation (the
-// default pool's release threshold is 0).
+// stream-ordered allocations (a workspace of one stream is never another's
+// while in use), and memory kept in the pool rather than released to the HIP
+// runtime at each synchronisation (the default pool's release threshold is
+// 0).
 hipMemPool_t workspace_pool(hipError_t& e) {
     static std::mutex mu;
     static hipMemPool_t pools[64] = {};
@@ -645,25 +645,91 @@ hipMemPool_t workspace_pool(hipError_t& e) {
     return pools[dev];
 }
 
-// Split-K: the slices' fp32 partials into a workspace taken from the
-// library's pool in the call's stream order, then their sum with the call's
-// epilogue into C; the workspace goes back to the pool after the second
-// kernel, in stream order.
+// Split-K workspaces kept between calls: one per stream for the last
+// kWorkspaces streams of each device.  Taking a workspace from the pool and
+// giving it back cost 10 to 30 us of host time per call (measured on MI355X
+// with ROCm 7), more than the two kernels of a small product take on the
+// GPU; an event recorded after a call's kernels and waited on by the next
+// user of the workspace costs about 1.6 us.  The wait also covers a stream
+// handle that the runtime hands out again after a stream was destroyed with
+// work still queued on the workspace.  An entry that must grow, or that
+// another stream takes over (the least recently used one), gives its memory
+// back to the pool in the new user's stream order after that event.
+constexpr int kWorkspaces = 8;
+struct StreamWorkspace {
+    hipStream_t stream = nullptr;
+    void* ptr = nullptr;
+    size_t bytes = 0;
+    hipEvent_t last = nullptr;  // recorded after the last call's kernels
+    uint64_t used = 0;          // least recently used: smallest stamp
+};
+std::mutex workspace_mu;  // held across a call's kernels (see run_split)
+StreamWorkspace workspaces[64][kWorkspaces];
+uint64_t workspace_clock = 0;
+
+// The workspace of `st` on device `dev` with at least `need` bytes, ordered
+// after the previous call that used its memory (workspace_mu held).
+hipError_t stream_workspace(int dev, hipStream_t st, size_t need, StreamWorkspace*& out) {
+    StreamWorkspace* row = workspaces[dev];
+    StreamWorkspace* w = nullptr;
+    for (int i = 0; i < kWorkspaces && w == nullptr; ++i)
+        if (row[i].ptr != nullptr && row[i].stream == st) w = &row[i];
+    if (w == nullptr) {  // a free entry, else the least recently used one
+        w = &row[0];
+        for (int i = 0; i < kWorkspaces; ++i) {
+            if (row[i].ptr == nullptr) { w = &row[i]; break; }
+            if (row[i].used < w->used) w = &row[i];
+        }
+    }
+    hipError_t e = hipSuccess;
+    if (w->last == nullptr && (e = hipEventCreateWithFlags(&w->last, hipEventDisableTiming)) != hipSuccess) return e;
+    if (w->ptr != nullptr && (e = hipStreamWaitEvent(st, w->last, 0)) != hipSuccess) return e;
+    if (w->ptr == nullptr || w->bytes < need) {
+        if (w->ptr != nullptr) {
+            e = hipFreeAsync(w->ptr, st);
+            w->ptr = nullptr;
+            w->bytes = 0;
+            if (e != hipSuccess) return e;
+        }
+        hipMemPool_t pool = workspace_pool(e);
+        if (pool == nullptr) return e;
+        const size_t bytes = (need + ((size_t)2 << 20) - 1) / ((size_t)2 << 20) * ((size_t)2 << 20);  // 2 MiB steps
+        if ((e = hipMallocFromPoolAsync(&w->ptr, bytes, pool, st)) != hipSuccess) {
+            w->ptr = nullptr;
+            return e;
+        }
+        w->bytes = bytes;
+    }
+    w->stream = st;
+    w->used = ++workspace_clock;
+    out = w;
+    return hipSuccess;
+}
+
+// Split-K: the slices' fp32 partials into the stream's workspace, then their
+// sum with the call's epilogue into C.  The library's lock is held from the
+// workspace lookup to the event after the second kernel, so that two host
+// threads calling on one stream cannot interleave their kernels on one
+// workspace.
 // With `fixed` (the allocation-free entry point) the workspace is that
-// device array instead, and nothing is allocated or freed.
+// device array instead, and nothing is allocated, freed or recorded.
 int run_split(const Problem& p, const Plan& plan, const ConfigEntry& c, const GemmArgs& args, void* stream,
               float* fixed) {
     const hipStream_t st = (hipStream_t)stream;
     const int64_t ldw = (p.N + 3) / 4 * 4, slice = p.M * ldw;
     float* w = fixed;
     hipError_t e = hipSuccess;
+    std::unique_lock<std::mutex> lock(workspace_mu, std::defer_lock);
+    StreamWorkspace* ws = nullptr;
     if (fixed != nullptr) {
         if (plan.splits * slice > kScratchFloats) return TGEMM_ERR_SCRATCH;
     } else {
-        hipMemPool_t pool = workspace_pool(e);
-        if (pool == nullptr) return (int)e;
-        e = hipMallocFromPoolAsync((void**)&w, (size_t)(plan.splits * slice * 4), pool, st);
-        if (e != hipSuccess) return (int)e;
+        int dev = 0;
+        if ((e = hipGetDevice(&dev)) != hipSuccess) return (int)e;
+        if (dev < 0 || dev >= 64) return (int)hipErrorInvalidDevice;
+        lock.lock();
+        if ((e = stream_workspace(dev, st, (size_t)(plan.splits * slice * 4), ws)) != hipSuccess) return (int)e;
+        w = (float*)ws->ptr;
     }
     GemmArgs pa = args;
     pa.C = (char*)w;
@@ -696,8 +762,8 @@ int run_split(const Problem& p, const Plan& plan, const ConfigEntry& c, const Ge
         e = hipLaunchKernel((const void*)plan.reduce, dim3((unsigned)rb), dim3(kSplitkReduceThreads), rargs, 0, st);
         if (e == hipSuccess) e = hipGetLastError();
     }
-    if (fixed == nullptr) {
-        const hipError_t f = hipFreeAsync(w, st);
+    if (ws != nullptr) {
+        const hipError_t f = hipEventRecord(ws->last, st);
         if (e == hipSuccess) e = f;
     }
     return e == hipSuccess ? TGEMM_OK : (int)e;
