@@ -76,11 +76,11 @@ constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 static_assert(kNumConfigs == NUM_CONFIGS, "");
 
 // Measurement-only switches, read once from the environment:
-//   TGEMM_GROUP_M=<n>    tile rows per raster group (default 4)
+//   TGEMM_GROUP_M=<n>    tile rows per raster group (default: group_rows)
 //   TGEMM_NO_SWIZZLE=1   plain LDS rows (for bank-conflict A/B runs)
 //   TGEMM_NO_DL=1        register-staged kernel instead of the direct-to-LDS ring
 struct Tuning {
-    int group_m = 4;
+    int group_m = 0;  // 0: group_rows decides
     bool swizzle = true;
     bool direct_lds = true;
     bool split_k = true;
@@ -769,6 +769,18 @@ int run_split(const Problem& p, const Plan& plan, const ConfigEntry& c, const Ge
     return e == hipSuccess ? TGEMM_OK : (int)e;
 }
 
+// Tile rows per raster group of the tile map.  4 (8 ties at 8192^3; 2 and
+// 16 are 1-4% slower there), except for a short K with rows of C a multiple
+// of 32 KiB apart, where 2 is faster (medians on one box, ring kernel:
+// 16384^2 x 1024 fp16 547 against 587 us, x 512 379 against 403, x 2048 895
+// against 926; 8192 x 16384 x 1024 275 against 289; 8192^2 x 1024 with fp32
+// C 144 against 161), and 4 stays ahead with other row pitches (12288^2 x
+// 1536 399 against 408, 8192^2 x 1024 to 4096 with fp16 C by 0.5-1%).
+int group_rows(const Problem& p) {
+    const int64_t pitch = p.ldc * elem_bytes(p.out);
+    return p.K <= 2048 && pitch % (32 * 1024) == 0 ? 2 : 4;
+}
+
 int run(const Problem& p, void* stream, int config_id, float* fixed = nullptr) {
     Plan plan;
     const int v = make_plan(p, config_id, plan);
@@ -787,7 +799,7 @@ int run(const Problem& p, void* stream, int config_id, float* fixed = nullptr) {
     args.K = (int)p.K;
     args.tiles_m = (int)ceil_div(p.M, plan.wave_split ? 16 : c.bm);
     args.tiles_n = (int)ceil_div(p.N, plan.wave_split ? 16 : c.bn);
-    args.group_m = tuning().group_m;
+    args.group_m = tuning().group_m > 0 ? tuning().group_m : group_rows(p);
     args.swz_mask = tuning().swizzle ? c.cpr - 1 : 0;
     if (plan.kind == TGEMM_KERNEL_RING || plan.kind == TGEMM_KERNEL_RING_SPLITK)
         args.swz_mask = tuning().swizzle ? 1 : 0;
