@@ -209,8 +209,9 @@ int gemm_fused(int64_t M, int64_t N, int64_t K,
  * forbid hipMalloc).  The same plan, kernels and results as gemm_fused with
  * the same arguments, except that a split-K plan (TGEMM_KERNEL_RING_SPLITK)
  * keeps its fp32 partials in the library's own fixed device array of 32 MiB
- * (one per GPU, held until the process ends) rather than in memory from the
- * library's pool: the call allocates and frees nothing.  Every call on a GPU
+ * (one per GPU, held until the process ends) rather than in the stream's
+ * workspace from the library's pool: the call allocates, frees and records
+ * nothing.  Every call on a GPU
  * uses that GPU's one array, so calls that overlap on one GPU (on different
  * streams, or concurrently from several host threads) race; calls on one
  * stream are ordered and safe.  The array keeps the last call's contents
